@@ -1,0 +1,33 @@
+"""CPU oracle for the block-quantized matmul: TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check in ``__graft_entry__`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run anything in this
+package.  The product path (the HIP library and its Python binding) never
+imports it and shares no code, table or helper with it.
+
+What is here:
+
+* ``mq_oracle``     -- plain numpy (f64 / int64) definitions of what the hot
+                       path computes: block decoders, the activation
+                       quantizer, the GEMV, the int block dots and the MMQ
+                       product.
+* ``bitwise_decode`` -- a second, independently written per-block decoder that
+                       assembles every field bit by bit; it exists only to
+                       cross-check ``mq_oracle``'s vectorised decoders.
+
+Pinning status (each function's docstring repeats it):
+
+* The arithmetic of every function is pinned by tests that do not retype it:
+  hand-worked blocks with closed-form values, a brute-force product in exact
+  rationals, closed forms, invariants and planted-mistake (mutation) checks.
+* The *bit layouts* of Q4_K and Q6_K are the public GGUF layouts; the pages
+  state only the block byte sizes.  Agreement with real GGUF files is
+  **parity unpinned**: no GGUF file exists in this environment to pin it.
+"""
+
+from .mq_oracle import (  # noqa: F401
+    Q8_0, Q4_K, Q6_K, BLOCK_VALUES, BLOCK_BYTES,
+    f16_bits_to_f64, row_bytes,
+    q8_0_fields, q4_k_fields, q6_k_fields, decode,
+    gemv, quantize_act, block_dots, mmq, mmq_from_block_dots,
+)

@@ -1,0 +1,96 @@
+"""Second, independent block decoder (TEST INFRASTRUCTURE ONLY).
+
+It decodes ONE block at a time in plain Python, building every field bit by
+bit from a table of (byte, bit) positions, and reads f16 through the standard
+library's IEEE half codec (``struct`` format 'e').  It shares no code with
+``mq_oracle`` so that a slip in either (a swapped nibble, a wrong scale index,
+a shifted qh pair) shows up as a disagreement on random bytes.
+
+The layouts it reads are the public GGUF ones (Q8_0 34 B, Q4_K 144 B,
+Q6_K 210 B per block); only the sizes are on the pages ("minfer CUDA Backend
+Design", 2.3 Weight residency and registry).  GGUF interop: parity unpinned.
+"""
+
+import struct
+
+
+def _bit(block, byte_index, bit_index):
+    return (block[byte_index] >> bit_index) & 1
+
+
+def _field(block, positions):
+    """Assemble an unsigned integer; positions[k] = (byte, bit) of result bit k."""
+    value = 0
+    for k, (byte_index, bit_index) in enumerate(positions):
+        value |= _bit(block, byte_index, bit_index) << k
+    return value
+
+
+def _half(block, offset):
+    return struct.unpack("<e", bytes(block[offset:offset + 2]))[0]
+
+
+def decode_q8_0_block(block):
+    """34 bytes -> 32 floats: d (f16) times each signed byte."""
+    block = bytes(bytearray(int(b) for b in block))
+    assert len(block) == 34
+    d = _half(block, 0)
+    out = []
+    for i in range(32):
+        u = _field(block, [(2 + i, k) for k in range(8)])
+        s = u - 256 if u >= 128 else u
+        out.append(d * s)
+    return out
+
+
+def _q4_k_scale_min_positions(j):
+    """(byte, bit) tables for the 6-bit scale and min of sub-block j (scale bytes start at 4)."""
+    base = 4
+    if j < 4:
+        sc = [(base + j, k) for k in range(6)]
+        mn = [(base + j + 4, k) for k in range(6)]
+    else:
+        sc = [(base + j + 4, k) for k in range(4)] + [(base + j - 4, 6), (base + j - 4, 7)]
+        mn = [(base + j + 4, 4 + k) for k in range(4)] + [(base + j, 6), (base + j, 7)]
+    return sc, mn
+
+
+def decode_q4_k_block(block):
+    """144 bytes -> 256 floats."""
+    block = bytes(bytearray(int(b) for b in block))
+    assert len(block) == 144
+    d = _half(block, 0)
+    dmin = _half(block, 2)
+    out = []
+    for e in range(256):
+        j = e // 32
+        sc_pos, mn_pos = _q4_k_scale_min_positions(j)
+        sc = _field(block, sc_pos)
+        mn = _field(block, mn_pos)
+        chunk, r = divmod(e, 64)
+        byte_index = 16 + 32 * chunk + (r % 32)
+        first_bit = 0 if r < 32 else 4
+        code = _field(block, [(byte_index, first_bit + k) for k in range(4)])
+        out.append(d * sc * code - dmin * mn)
+    return out
+
+
+def decode_q6_k_block(block):
+    """210 bytes -> 256 floats."""
+    block = bytes(bytearray(int(b) for b in block))
+    assert len(block) == 210
+    d = _half(block, 208)
+    out = []
+    for e in range(256):
+        h, r = divmod(e, 128)
+        t, l = divmod(r, 32)
+        ql_byte = 64 * h + l + (32 if t in (1, 3) else 0)
+        ql_first = 4 if t >= 2 else 0
+        qh_byte = 128 + 32 * h + l
+        positions = [(ql_byte, ql_first + k) for k in range(4)]
+        positions += [(qh_byte, 2 * t), (qh_byte, 2 * t + 1)]
+        code = _field(block, positions)
+        su = block[192 + e // 16]
+        scale = su - 256 if su >= 128 else su
+        out.append(d * scale * (code - 32))
+    return out

@@ -1,0 +1,287 @@
+"""Plain numpy oracle for GGUF block-quantized matmul (TEST INFRASTRUCTURE).
+
+Only the tests, the smoke check and bench.py's CPU-baseline leg use this
+module.  It shares nothing with the HIP library.
+
+Everything here is a direct definition: decode each block to f64 values, then
+take ordinary products and sums.  Floating point is f64 except where the
+method itself fixes f32 (the activation quantizer, whose integer codes must be
+reproduced bit for bit).
+
+Sources (page title, section):
+
+* "minfer CUDA Backend Design", 2.3 Weight residency and registry -- a Q4_K
+  payload is exactly od*(id/256)*144 bytes (row-major: output rows, then
+  256-value super-blocks along the input dimension); q8_0 is 34 bytes per 32
+  values; the Q6_K block is repacked into 224-byte slots, so its raw block is
+  smaller than 224 bytes.
+* "minfer CUDA Backend Design", 4.3 Eligibility -- a quantized matmul needs
+  the input dimension to be a multiple of 32.
+* "minfer CUDA Backend Design", 4.4 Execution dispatch -- decode uses int dot
+  products over q8_0-quantized activations; prefill uses the int8 MMQ GEMM
+  over a pre-quantized activation plane.
+* "minfer Architecture Execution Plan", C4 S2b design decision 4 (and
+  "minfer CUDA Backend Design", 4.7) -- the Q8_0 quantizer: amax over the
+  32-block, scale = amax/127, codes rounded half to even.
+
+Readings where the pages are silent (each also listed in the design doc):
+
+* R1  Block bit layouts (d/dmin/scales/qs for Q4_K; ql/qh/scales/d for Q6_K;
+      d then q[32] for Q8_0) are the public GGUF layouts.  The pages give only
+      sizes.  GGUF interop is parity unpinned (no GGUF file is available).
+* R2  Q6_K is 128 (ql) + 64 (qh) + 16 (int8 scales) + 2 (f16 d) = 210 bytes.
+* R3  Q6_K sub-scales are signed int8.
+* R4  The activation scale is f32: d = f32(amax) / f32(127), IEEE division.
+* R5  Codes are round-half-to-even of the IEEE f32 quotient x / d (a true
+      division, not a multiply by 1/d), clamped to [-127, 127]; a block with
+      amax == 0 has d == 0 and all codes 0.
+* R6  The per-block code sum S = sum(q) is part of the quantized activation
+      (it carries the Q4_K min term through the int path).
+* R7  Block dots are exact integers: per 32-value block for Q8_0 and Q4_K
+      (Q4_K codes in [0, 15], unsigned), per 16-value group for Q6_K with the
+      signed code (c - 32).
+"""
+
+import numpy as np
+
+# GGUF tensor-type ids.
+Q8_0 = 8
+Q4_K = 12
+Q6_K = 14
+
+BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q6_K: 210}
+
+ACT_BLOCK = 32
+
+
+def row_bytes(qtype, K):
+    """Bytes of one weight row of K values (K a multiple of the block size)."""
+    bv = BLOCK_VALUES[qtype]
+    if K % bv:
+        raise ValueError(f"K={K} is not a multiple of {bv}")
+    return (K // bv) * BLOCK_BYTES[qtype]
+
+
+def f16_bits_to_f64(lo_byte, hi_byte):
+    """IEEE binary16 (little-endian byte pair) -> f64, exactly.
+
+    Written from the binary16 definition (1 sign, 5 exponent, 10 fraction
+    bits; exponent 0 is subnormal), not via numpy's float16, so that it is a
+    second implementation next to the library conversion used by the tests.
+    Inf/NaN encodings are outside the contract and raise.
+    """
+    bits = lo_byte.astype(np.int64) | (hi_byte.astype(np.int64) << 8)
+    sign = np.where(bits >> 15, -1.0, 1.0)
+    exp = (bits >> 10) & 0x1F
+    frac = (bits & 0x3FF).astype(np.float64)
+    if np.any(exp == 0x1F):
+        raise ValueError("f16 Inf/NaN scale in a weight block")
+    normal = sign * (1.0 + frac / 1024.0) * np.exp2(exp.astype(np.float64) - 15.0)
+    subnormal = sign * frac * 2.0 ** -24
+    return np.where(exp == 0, subnormal, normal)
+
+
+def _blocks(raw, qtype, N, K):
+    raw = np.ascontiguousarray(raw, dtype=np.uint8).reshape(-1)
+    nbytes = N * row_bytes(qtype, K)
+    if raw.size != nbytes:
+        raise ValueError(f"payload is {raw.size} bytes, expected exactly {nbytes}")
+    nb = K // BLOCK_VALUES[qtype]
+    return raw.reshape(N, nb, BLOCK_BYTES[qtype])
+
+
+def q8_0_fields(raw, N, K):
+    """Q8_0 fields: d f64 [N, nb] and signed codes int64 [N, nb, 32].
+
+    Block (34 bytes): f16 d at bytes 0..1, then 32 int8 codes (R1).
+    value_i = d * q_i.
+    """
+    b = _blocks(raw, Q8_0, N, K)
+    d = f16_bits_to_f64(b[..., 0], b[..., 1])
+    q = b[..., 2:34].astype(np.int8).astype(np.int64)
+    return d, q
+
+
+def q4_k_fields(raw, N, K):
+    """Q4_K fields: d, dmin f64 [N, nb]; sc, m int64 [N, nb, 8]; codes int64 [N, nb, 256].
+
+    Block (144 bytes, R1): f16 d (bytes 0-1), f16 dmin (2-3), 12 bytes of
+    packed 6-bit (scale, min) pairs for the eight 32-value sub-blocks (4-15),
+    then 128 bytes of 4-bit codes (16-143).
+
+    Sub-block j's 6-bit scale and min, with b = the 12 packed bytes:
+      j < 4 : scale = low 6 bits of b[j],   min = low 6 bits of b[j+4]
+      j >= 4: scale = low nibble of b[j+4]  plus the top 2 bits of b[j-4] as bits 4-5
+              min   = high nibble of b[j+4] plus the top 2 bits of b[j]   as bits 4-5
+    Codes: value e lies in 64-value chunk c = e // 64 at offset r = e % 64;
+    its code is the low nibble of qs[32c + r] when r < 32, else the high
+    nibble of qs[32c + r - 32].
+    value_e = d * scale_j * code_e - dmin * min_j, with j = e // 32.
+    """
+    b = _blocks(raw, Q4_K, N, K)
+    d = f16_bits_to_f64(b[..., 0], b[..., 1])
+    dmin = f16_bits_to_f64(b[..., 2], b[..., 3])
+    s = b[..., 4:16].astype(np.int64)
+    sc = np.empty(s.shape[:-1] + (8,), dtype=np.int64)
+    mn = np.empty_like(sc)
+    for j in range(4):
+        sc[..., j] = s[..., j] & 63
+        mn[..., j] = s[..., j + 4] & 63
+    for j in range(4, 8):
+        sc[..., j] = (s[..., j + 4] & 15) | ((s[..., j - 4] >> 6) << 4)
+        mn[..., j] = (s[..., j + 4] >> 4) | ((s[..., j] >> 6) << 4)
+    qs = b[..., 16:144].astype(np.int64)
+    codes = np.empty(b.shape[:-1] + (256,), dtype=np.int64)
+    for c in range(4):
+        chunk = qs[..., 32 * c:32 * c + 32]
+        codes[..., 64 * c:64 * c + 32] = chunk & 15
+        codes[..., 64 * c + 32:64 * c + 64] = chunk >> 4
+    return d, dmin, sc, mn, codes
+
+
+def q6_k_fields(raw, N, K):
+    """Q6_K fields: d f64 [N, nb]; scales int64 [N, nb, 16]; codes int64 [N, nb, 256] in [0, 63].
+
+    Block (210 bytes, R1/R2): 128 bytes ql (low 4 bits of each code), 64 bytes
+    qh (high 2 bits), 16 signed int8 sub-scales (one per 16 values, R3), f16 d.
+    For value e: half h = e // 128, r = e % 128, quarter t = r // 32,
+    l = r % 32.  Low 4 bits: ql[64h + l + 32*(t % 2)], low nibble for t < 2,
+    high nibble for t >= 2.  High 2 bits: bits 2t..2t+1 of qh[32h + l].
+    value_e = d * scales[e // 16] * (code_e - 32).
+    """
+    b = _blocks(raw, Q6_K, N, K)
+    ql = b[..., 0:128].astype(np.int64)
+    qh = b[..., 128:192].astype(np.int64)
+    scales = b[..., 192:208].astype(np.int8).astype(np.int64)
+    d = f16_bits_to_f64(b[..., 208], b[..., 209])
+    codes = np.empty(b.shape[:-1] + (256,), dtype=np.int64)
+    for h in range(2):
+        for t in range(4):
+            low_src = ql[..., 64 * h + 32 * (t % 2): 64 * h + 32 * (t % 2) + 32]
+            low = (low_src >> (4 * (t // 2))) & 15
+            high = (qh[..., 32 * h: 32 * h + 32] >> (2 * t)) & 3
+            e0 = 128 * h + 32 * t
+            codes[..., e0:e0 + 32] = low | (high << 4)
+    return d, scales, codes
+
+
+def decode(raw, qtype, N, K):
+    """O1: deq(W) as f64 [N, K] (exact: every value is a short product of f16 and small ints)."""
+    if qtype == Q8_0:
+        d, q = q8_0_fields(raw, N, K)
+        w = d[..., None] * q
+    elif qtype == Q4_K:
+        d, dmin, sc, mn, codes = q4_k_fields(raw, N, K)
+        sub_scale = np.repeat(d[..., None] * sc, 32, axis=-1)
+        sub_min = np.repeat(dmin[..., None] * mn, 32, axis=-1)
+        w = sub_scale * codes - sub_min
+    elif qtype == Q6_K:
+        d, scales, codes = q6_k_fields(raw, N, K)
+        group_scale = np.repeat(d[..., None] * scales, 16, axis=-1)
+        w = group_scale * (codes - 32)
+    else:
+        raise ValueError(f"unsupported type {qtype}")
+    return w.reshape(N, K)
+
+
+def gemv(raw, qtype, x, N, K, row_chunk=4096):
+    """O2: y[n] = sum_k deq(W)[n, k] * x[k] in f64 (x f32 promoted exactly).
+
+    Decodes in row chunks so a large weight (e.g. a vocab head) fits in memory.
+    """
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64).reshape(K)
+    raw = np.ascontiguousarray(raw, dtype=np.uint8).reshape(N, row_bytes(qtype, K))
+    y = np.empty(N, dtype=np.float64)
+    for r0 in range(0, N, row_chunk):
+        r1 = min(N, r0 + row_chunk)
+        y[r0:r1] = decode(raw[r0:r1], qtype, r1 - r0, K) @ x64
+    return y
+
+
+def quantize_act(X):
+    """O3: per row, per 32-value block: amax, d = amax/127 in f32, q = rne(x/d).
+
+    Returns (q int8 [M, K], d f32 [M, K/32], S int32 [M, K/32]) with S the sum
+    of the block's codes (R4-R6).  All arithmetic that decides a code is IEEE
+    f32, as the method fixes it.
+    """
+    X = np.asarray(X, dtype=np.float32)
+    M, K = X.shape
+    if K % ACT_BLOCK:
+        raise ValueError(f"K={K} is not a multiple of {ACT_BLOCK}")
+    xb = X.reshape(M, K // ACT_BLOCK, ACT_BLOCK)
+    amax = np.max(np.abs(xb), axis=-1)
+    d = (amax / np.float32(127.0)).astype(np.float32)
+    safe_d = np.where(d > 0, d, np.float32(1.0)).astype(np.float32)
+    ratio = (xb / safe_d[..., None]).astype(np.float32)
+    q = np.clip(np.rint(ratio), -127, 127)
+    q = np.where(d[..., None] > 0, q, 0).astype(np.int8)
+    S = q.astype(np.int32).sum(axis=-1, dtype=np.int32)
+    return q.reshape(M, K), d, S
+
+
+def block_dots(raw, qtype, q, N, K):
+    """O4: exact int64 block dot products between weight codes and activation codes.
+
+    * Q8_0: D[m, n, b] = sum_{i<32} qw[n, 32b+i] * qx[m, 32b+i]
+    * Q4_K: D[m, n, b] = sum_{i<32} code[n, 32b+i] * qx[m, 32b+i]   (codes 0..15)
+    * Q6_K: D[m, n, g] = sum_{i<16} (code[n, 16g+i] - 32) * qx[m, 16g+i]
+    """
+    q = np.asarray(q, dtype=np.int8).astype(np.int64)
+    M = q.shape[0]
+    if qtype == Q8_0:
+        _, wq = q8_0_fields(raw, N, K)
+        grp = 32
+    elif qtype == Q4_K:
+        wq = q4_k_fields(raw, N, K)[4]
+        grp = 32
+    elif qtype == Q6_K:
+        wq = q6_k_fields(raw, N, K)[2] - 32
+        grp = 16
+    else:
+        raise ValueError(f"unsupported type {qtype}")
+    wq = wq.reshape(N, K // grp, grp)
+    xq = q.reshape(M, K // grp, grp)
+    return np.einsum("ngi,mgi->mng", wq, xq)
+
+
+def mmq(raw, qtype, q, d, N, K):
+    """O5: Y[m, n] = sum_k deq(W)[n, k] * dx[m, k//32] * qx[m, k] in f64.
+
+    The activation is the dequantized q8 value x_hat = dx * qx (exact in f64).
+    """
+    q = np.asarray(q, dtype=np.int8).astype(np.float64)
+    d = np.asarray(d, dtype=np.float32).astype(np.float64)
+    M = q.shape[0]
+    x_hat = (q.reshape(M, K // 32, 32) * d[..., None]).reshape(M, K)
+    return x_hat @ decode(raw, qtype, N, K).T
+
+
+def mmq_from_block_dots(raw, qtype, q, d, S, N, K):
+    """O5 in block-dot form (what an int path accumulates), f64.
+
+    * Q8_0: Y = sum_b dx[m,b] * d[n,b] * D[m,n,b]
+    * Q4_K: Y = sum_j dx[m,j] * (d*sc_j * D[m,n,j] - dmin*m_j * S[m,j])
+    * Q6_K: Y = sum_g dx[m,g//2] * d*s_g * D[m,n,g]
+    Tests check that this equals ``mmq`` to ~1e-15 relative.
+    """
+    D = block_dots(raw, qtype, q, N, K).astype(np.float64)
+    dx = np.asarray(d, dtype=np.float32).astype(np.float64)
+    if qtype == Q8_0:
+        dw, _ = q8_0_fields(raw, N, K)
+        return np.einsum("mb,nb,mnb->mn", dx, dw.reshape(N, K // 32), D)
+    if qtype == Q4_K:
+        dd, dmin, sc, mn, _ = q4_k_fields(raw, N, K)
+        wscale = (dd[..., None] * sc).reshape(N, K // 32)
+        wmin = (dmin[..., None] * mn).reshape(N, K // 32)
+        S = np.asarray(S, dtype=np.int64).astype(np.float64)
+        main = np.einsum("mb,nb,mnb->mn", dx, wscale, D)
+        minterm = np.einsum("mb,nb,mb->mn", dx, wmin, S)
+        return main - minterm
+    if qtype == Q6_K:
+        dd, scales, _ = q6_k_fields(raw, N, K)
+        gscale = (dd[..., None] * scales).reshape(N, K // 16)
+        dxg = np.repeat(dx, 2, axis=-1)
+        return np.einsum("mg,ng,mng->mn", dxg, gscale, D)
+    raise ValueError(f"unsupported type {qtype}")

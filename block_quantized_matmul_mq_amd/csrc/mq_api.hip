@@ -1,0 +1,234 @@
+// libmq C ABI: argument validation, device checks and kernel dispatch.
+//
+// Every entry point validates its arguments before making any HIP call and
+// returns a negative MQ_ERR_* code with a message on failure; a refused launch
+// is an error, never a fallback to another kernel ("minfer CUDA Backend
+// Design", 4.3 Eligibility and 4.9 GPU safety: errors are errors, launch
+// returns are read at the call site, device limits are queried at run time).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/mq.h"
+#include "mq_internal.h"
+
+namespace mq {
+
+namespace {
+
+thread_local std::string g_error;
+thread_local const char* g_last_kernel = "";
+
+constexpr int kMaxDevices = 64;
+DeviceInfo g_devices[kMaxDevices];
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return code;
+}
+
+int block_values(int type) {
+    switch (type) {
+        case MQ_Q8_0: return 32;
+        case MQ_Q4_K: return 256;
+        case MQ_Q6_K: return 256;
+        default: return 0;
+    }
+}
+
+int block_bytes(int type) {
+    switch (type) {
+        case MQ_Q8_0: return 34;
+        case MQ_Q4_K: return 144;
+        case MQ_Q6_K: return 210;
+        default: return 0;
+    }
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shape/type checks shared by the weight-consuming calls.
+int check_weight_shape(const char* fn, int type, int64_t N, int64_t K) {
+    if (block_values(type) == 0) return fail(MQ_ERR_TYPE, "%s: unsupported weight type %d", fn, type);
+    if (N <= 0 || K <= 0) return fail(MQ_ERR_ARG, "%s: N=%lld K=%lld must be positive", fn, (long long)N, (long long)K);
+    if (K % block_values(type) != 0)
+        return fail(MQ_ERR_SHAPE, "%s: K=%lld is not a multiple of the %d-value block of type %d", fn,
+                    (long long)K, block_values(type), type);
+    if (K > MQ_MAX_K || N > MQ_MAX_N)
+        return fail(MQ_ERR_SHAPE, "%s: N=%lld K=%lld exceeds the limits N<=%d K<=%d", fn, (long long)N,
+                    (long long)K, MQ_MAX_N, MQ_MAX_K);
+    return MQ_OK;
+}
+
+int check_ready(const char* fn) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MQ_ERR_DEVICE, "%s: hipGetDevice failed: %s", fn, hipGetErrorName(e));
+    if (dev < 0 || dev >= kMaxDevices || !g_devices[dev].ready)
+        return fail(MQ_ERR_NOINIT, "%s: mq_init has not succeeded on device %d", fn, dev);
+    return MQ_OK;
+}
+
+int launch_status(const char* fn, hipError_t e, const char* kernel) {
+    g_last_kernel = kernel;
+    if (e != hipSuccess)
+        return fail(MQ_ERR_LAUNCH, "%s: launch of %s refused: %s", fn, kernel, hipGetErrorName(e));
+    return MQ_OK;
+}
+
+}  // namespace
+
+const DeviceInfo* device_info() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    return g_devices[dev].ready ? &g_devices[dev] : nullptr;
+}
+
+}  // namespace mq
+
+using namespace mq;
+
+extern "C" {
+
+const char* mq_version(void) { return "libmq 0.1 (gfx950)"; }
+
+const char* mq_last_error(void) { return g_error.c_str(); }
+
+const char* mq_last_kernel(void) { return g_last_kernel; }
+
+int mq_init(int device) {
+    if (device < 0 || device >= kMaxDevices) return fail(MQ_ERR_ARG, "mq_init: device %d out of range", device);
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count <= 0)
+        return fail(MQ_ERR_DEVICE, "mq_init: no HIP device (%s)", hipGetErrorName(e));
+    if (device >= count) return fail(MQ_ERR_DEVICE, "mq_init: device %d of %d", device, count);
+    e = hipSetDevice(device);
+    if (e != hipSuccess) return fail(MQ_ERR_DEVICE, "mq_init: hipSetDevice(%d): %s", device, hipGetErrorName(e));
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, device);
+    if (e != hipSuccess)
+        return fail(MQ_ERR_DEVICE, "mq_init: hipGetDeviceProperties(%d): %s", device, hipGetErrorName(e));
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(MQ_ERR_DEVICE, "mq_init: device %d is %s, this library is built for gfx950 only", device,
+                    prop.gcnArchName);
+    DeviceInfo& info = g_devices[device];
+    info.cu_count = prop.multiProcessorCount;
+    info.lds_per_block = prop.sharedMemPerBlock;
+    info.ready = true;
+    return MQ_OK;
+}
+
+size_t mq_weight_bytes(int type, int64_t N, int64_t K) {
+    const int bv = block_values(type);
+    if (bv == 0 || N <= 0 || K <= 0 || K % bv != 0) return 0;
+    return size_t(N) * size_t(K / bv) * size_t(block_bytes(type));
+}
+
+size_t mq_act_bytes(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0 || K % 32 != 0) return 0;
+    return act_bytes(M, K);
+}
+
+size_t mq_act_scale_offset(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0 || K % 32 != 0) return 0;
+    return act_scale_offset(M, K);
+}
+
+size_t mq_act_sum_offset(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0 || K % 32 != 0) return 0;
+    return act_sum_offset(M, K);
+}
+
+size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
+    (void)type; (void)M; (void)N; (void)K;
+    return 0;
+}
+
+int mq_quantize_act(const float* X, void* Xq, int64_t M, int64_t K, void* stream) {
+    const char* fn = "mq_quantize_act";
+    if (!X || !Xq) return fail(MQ_ERR_ARG, "%s: null pointer (X=%p Xq=%p)", fn, (const void*)X, Xq);
+    if (M <= 0 || K <= 0) return fail(MQ_ERR_ARG, "%s: M=%lld K=%lld must be positive", fn, (long long)M, (long long)K);
+    if (K % 32 != 0) return fail(MQ_ERR_SHAPE, "%s: K=%lld is not a multiple of 32", fn, (long long)K);
+    if (K > MQ_MAX_K || M > MQ_MAX_M)
+        return fail(MQ_ERR_SHAPE, "%s: M=%lld K=%lld exceeds M<=%d K<=%d", fn, (long long)M, (long long)K, MQ_MAX_M, MQ_MAX_K);
+    if (!aligned(X, 16) || !aligned(Xq, 256))
+        return fail(MQ_ERR_ALIGN, "%s: X must be 16-byte and Xq 256-byte aligned (X=%p Xq=%p)", fn, (const void*)X, Xq);
+    int rc = check_ready(fn);
+    if (rc) return rc;
+    uint8_t* base = static_cast<uint8_t*>(Xq);
+    hipError_t e = launch_quantize_act(X, reinterpret_cast<int8_t*>(base),
+                                       reinterpret_cast<float*>(base + act_scale_offset(M, K)),
+                                       reinterpret_cast<int32_t*>(base + act_sum_offset(M, K)), M, K,
+                                       static_cast<hipStream_t>(stream));
+    return launch_status(fn, e, "quantize_act");
+}
+
+int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_t K, void* stream) {
+    const char* fn = "mq_gemv";
+    if (!W || !x || !y) return fail(MQ_ERR_ARG, "%s: null pointer (W=%p x=%p y=%p)", fn, W, (const void*)x, (void*)y);
+    int rc = check_weight_shape(fn, type, N, K);
+    if (rc) return rc;
+    if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4))
+        return fail(MQ_ERR_ALIGN, "%s: W and x must be 16-byte, y 4-byte aligned (W=%p x=%p y=%p)", fn, W,
+                    (const void*)x, (void*)y);
+    rc = check_ready(fn);
+    if (rc) return rc;
+    const char* kernel = "gemv";
+    hipError_t e = launch_gemv(type, static_cast<const uint8_t*>(W), x, y, N, K, static_cast<hipStream_t>(stream),
+                               &kernel);
+    return launch_status(fn, e, kernel);
+}
+
+static int gemm_common(const char* fn, const void* W, int type, const void* Xq, float* Y, int32_t* D,
+                       int64_t M, int64_t N, int64_t K, void* stream) {
+    if (!W || !Xq || (!Y && !D))
+        return fail(MQ_ERR_ARG, "%s: null pointer (W=%p Xq=%p out=%p)", fn, W, Xq, Y ? (void*)Y : (void*)D);
+    int rc = check_weight_shape(fn, type, N, K);
+    if (rc) return rc;
+    if (M <= 0) return fail(MQ_ERR_ARG, "%s: M=%lld must be positive", fn, (long long)M);
+    if (M > MQ_MAX_M) return fail(MQ_ERR_SHAPE, "%s: M=%lld exceeds %d", fn, (long long)M, MQ_MAX_M);
+    const int64_t groups = type == MQ_Q6_K ? K / 16 : K / 32;
+    if (D && int64_t(M) * N * groups > (int64_t(1) << 32))
+        return fail(MQ_ERR_SHAPE, "%s: block-dot export of M=%lld N=%lld K=%lld is too large", fn, (long long)M,
+                    (long long)N, (long long)K);
+    if (!aligned(W, 16) || !aligned(Xq, 256) || (Y && !aligned(Y, 4)) || (D && !aligned(D, 4)))
+        return fail(MQ_ERR_ALIGN, "%s: W 16-byte, Xq 256-byte, outputs 4-byte alignment required", fn);
+    rc = check_ready(fn);
+    if (rc) return rc;
+    const uint8_t* base = static_cast<const uint8_t*>(Xq);
+    const char* kernel = "mmq";
+    float* Yout = Y;
+    hipError_t e = launch_mmq(type, static_cast<const uint8_t*>(W), reinterpret_cast<const int8_t*>(base),
+                              reinterpret_cast<const float*>(base + act_scale_offset(M, K)),
+                              reinterpret_cast<const int32_t*>(base + act_sum_offset(M, K)), Yout, D, M, N, K,
+                              static_cast<hipStream_t>(stream), &kernel);
+    return launch_status(fn, e, kernel);
+}
+
+int mq_gemm(const void* W, int type, const void* Xq, float* Y, int64_t M, int64_t N, int64_t K, void* scratch,
+            size_t scratch_bytes, void* stream) {
+    const char* fn = "mq_gemm";
+    if (!Y) return fail(MQ_ERR_ARG, "%s: null Y", fn);
+    const size_t need = mq_gemm_scratch_bytes(type, M, N, K);
+    if (scratch_bytes < need || (need && !scratch))
+        return fail(MQ_ERR_SIZE, "%s: scratch of %zu bytes at %p, %zu required", fn, scratch_bytes, scratch, need);
+    return gemm_common(fn, W, type, Xq, Y, nullptr, M, N, K, stream);
+}
+
+int mq_debug_gemm_blockdots(const void* W, int type, const void* Xq, int32_t* D, int64_t M, int64_t N, int64_t K,
+                            void* stream) {
+    const char* fn = "mq_debug_gemm_blockdots";
+    if (!D) return fail(MQ_ERR_ARG, "%s: null D", fn);
+    return gemm_common(fn, W, type, Xq, nullptr, D, M, N, K, stream);
+}
+
+}  // extern "C"

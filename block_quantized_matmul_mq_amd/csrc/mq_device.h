@@ -1,0 +1,73 @@
+// Device-side helpers shared by the libmq kernels (gfx950, wave64).
+//
+// Block layouts read here ("minfer CUDA Backend Design", 2.3 fixes the sizes;
+// the field layouts are the public GGUF ones):
+//   Q8_0  34 B / 32 values : f16 d | int8 q[32]
+//   Q4_K 144 B / 256 values: f16 d | f16 dmin | 12 B packed 6-bit (scale,min) x 8 | 128 B 4-bit codes
+//   Q6_K 210 B / 256 values: 128 B low nibbles | 64 B high 2-bit pairs | int8 scales[16] | f16 d
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mq {
+
+constexpr int kQ8_0 = 8;
+constexpr int kQ4_K = 12;
+constexpr int kQ6_K = 14;
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+    // v_cvt_f32_f16: exact, subnormal halves included (f16 denormals are not flushed).
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+
+// Byte k (0..3) of a dword as float; lowers to v_cvt_f32_ubyte{k}.
+template <int k>
+__device__ __forceinline__ float ubyte_f(uint32_t v) {
+    return static_cast<float>((v >> (8 * k)) & 0xFFu);
+}
+
+// {hi:lo} >> (8 * sel), low 32 bits (v_alignbyte_b32).
+__device__ __forceinline__ uint32_t align_byte(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_alignbyte(hi, lo, sel);
+}
+
+// A dword at an address that is only 2-byte aligned, built from the one or two
+// naturally aligned dwords that contain it.  Never touches a dword that holds
+// none of the requested bytes, so it cannot read past the end of a buffer.
+__device__ __forceinline__ uint32_t load_u32_a2(const uint8_t* p) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(a & ~uintptr_t(3));
+    const uint32_t lo = q[0];
+    if (a & 2) return align_byte(q[1], lo, 2);
+    return lo;
+}
+
+__device__ __forceinline__ uint32_t load_u16(const uint8_t* p) {
+    return *reinterpret_cast<const uint16_t*>(p);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Q4_K: 6-bit scale and min of sub-block j from the packed bytes
+// s0 = bytes 0..3, s1 = bytes 4..7, s2 = bytes 8..11 of the 12-byte field.
+//   j < 4 : scale = b[j] & 63,                         min = b[j+4] & 63
+//   j >= 4: scale = (b[j+4] & 15) | (b[j-4] >> 6) << 4, min = (b[j+4] >> 4) | (b[j] >> 6) << 4
+__device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, int j,
+                                              uint32_t& sc, uint32_t& mn) {
+    if (j < 4) {
+        sc = (s0 >> (8 * j)) & 63u;
+        mn = (s1 >> (8 * j)) & 63u;
+    } else {
+        const int k = j - 4;
+        const uint32_t b_hi = (s2 >> (8 * k)) & 0xFFu;
+        sc = (b_hi & 15u) | (((s0 >> (8 * k + 6)) & 3u) << 4);
+        mn = (b_hi >> 4) | (((s1 >> (8 * k + 6)) & 3u) << 4);
+    }
+}
+
+}  // namespace mq

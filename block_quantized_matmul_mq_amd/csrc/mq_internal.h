@@ -1,0 +1,38 @@
+// Host-side declarations shared by the libmq translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mq {
+
+// Activation plane layout (see include/mq.h): codes [M][K] | scales [M][K/32] | sums [M][K/32],
+// each array starting on a 256-byte boundary.
+inline size_t round_up256(size_t v) { return (v + 255) & ~size_t(255); }
+inline size_t act_scale_offset(int64_t M, int64_t K) { return round_up256(size_t(M) * size_t(K)); }
+inline size_t act_sum_offset(int64_t M, int64_t K) {
+    return act_scale_offset(M, K) + round_up256(size_t(M) * size_t(K / 32) * 4);
+}
+inline size_t act_bytes(int64_t M, int64_t K) {
+    return act_sum_offset(M, K) + round_up256(size_t(M) * size_t(K / 32) * 4);
+}
+
+struct DeviceInfo {
+    int cu_count = 0;
+    size_t lds_per_block = 0;
+    bool ready = false;
+};
+const DeviceInfo* device_info();  // null if mq_init has not succeeded on the current device
+
+// Kernel launchers: they enqueue on `s` and return the launch status (hipGetLastError read
+// right after the launch).  Arguments are validated by the callers in mq_api.hip.
+hipError_t launch_quantize_act(const float* X, int8_t* codes, float* scales, int32_t* sums,
+                               int64_t M, int64_t K, hipStream_t s);
+hipError_t launch_gemv(int type, const uint8_t* W, const float* x, float* y, int64_t N, int64_t K,
+                       hipStream_t s, const char** kernel_name);
+hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* codes, const float* scales,
+                      const int32_t* sums, float* Y, int32_t* dots, int64_t M, int64_t N, int64_t K,
+                      hipStream_t s, const char** kernel_name);
+
+}  // namespace mq

@@ -170,18 +170,36 @@ def encode_q6_k(W):
 ENCODERS = {Q8_0: encode_q8_0, Q4_K: encode_q4_k, Q6_K: encode_q6_k}
 
 
-def quantized_weight(qtype, N, K, config_index, tensor_index, sigma=0.02):
-    """Seeded W f32 [N, K] ~ N(0, sigma^2), generated in row chunks and encoded.
+def weights_f32(N, K, config_index, tensor_index, sigma=0.02, rows=None):
+    """Seeded W f32 ~ N(0, sigma^2).  Row chunk c (of 2048 rows) draws from
+    SeedSequence([0, config_index, tensor_index, c]), so any row range can be
+    regenerated on its own.  ``rows`` = (r0, r1) returns just that range."""
+    r0, r1 = rows if rows is not None else (0, N)
+    out = np.empty((r1 - r0, K), dtype=np.float32)
+    for c in range(r0 // _ROW_CHUNK, (r1 + _ROW_CHUNK - 1) // _ROW_CHUNK):
+        c0, c1 = c * _ROW_CHUNK, min(N, (c + 1) * _ROW_CHUNK)
+        rng = np.random.default_rng(np.random.SeedSequence([0, config_index, tensor_index, c]))
+        chunk = normal_f32(rng, (c1 - c0, K), sigma)
+        lo, hi = max(c0, r0), min(c1, r1)
+        out[lo - r0:hi - r0] = chunk[lo - c0:hi - c0]
+    return out
 
-    Returns uint8 [N, row_bytes].  Memory stays bounded for a vocab-sized head.
-    """
-    rng = rng_for(config_index, tensor_index)
+
+def quantized_weight(qtype, N, K, config_index, tensor_index, sigma=0.02, threads=8):
+    """Seeded W (see weights_f32) encoded to uint8 [N, row_bytes], chunk by chunk
+    on a thread pool (numpy releases the GIL); memory stays bounded for a
+    vocab-sized head and the bytes do not depend on the thread count."""
+    from concurrent.futures import ThreadPoolExecutor
     enc = ENCODERS[qtype]
-    rows = []
-    for r0 in range(0, N, _ROW_CHUNK):
+    starts = list(range(0, N, _ROW_CHUNK))
+
+    def one(r0):
         r1 = min(N, r0 + _ROW_CHUNK)
-        rows.append(enc(normal_f32(rng, (r1 - r0, K), sigma)))
-    return np.concatenate(rows, axis=0)
+        return enc(weights_f32(N, K, config_index, tensor_index, sigma, rows=(r0, r1)))
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        parts = list(ex.map(one, starts))
+    return np.concatenate(parts, axis=0)
 
 
 def _random_f16(rng, shape, exp_lo, exp_hi, allow_negative=True):

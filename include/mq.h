@@ -1,0 +1,169 @@
+/*
+ * mq.h -- C ABI of libmq: matrix products of GGUF block-quantized weights
+ * (Q8_0, Q4_K, Q6_K) with f32 activations on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (page title, section):
+ *   [BD2.3] "minfer CUDA Backend Design", 2.3 Weight residency and registry:
+ *           Q4_K payload is exactly od * (id / 256) * 144 bytes; q8_0 is 34 bytes
+ *           per 32 values; Q6_K is repacked into 16-byte-aligned 224-byte slots;
+ *           a derived plane is admitted by a type gate plus an exact-length
+ *           payload gate ("equality, not a lower bound").
+ *   [BD4.3] same page, 4.3 Eligibility: a quantized matmul needs id % 32 == 0;
+ *           an invariant violation is an error, never a silent fallback.
+ *   [BD4.4] same page, 4.4 Execution dispatch: decode (one token) runs a
+ *           matrix-vector product; prefill runs the int8 "MMQ" GEMM over an
+ *           activation plane quantized to q8 blocks, which is computed once and
+ *           can be reused by consecutive matmuls that share the input.
+ *   [BD4.9] same page, 4.9 GPU safety: errors are errors; a return value that
+ *           gates a later launch is read at the call site; device limits are
+ *           queried at run time.
+ *   [EP-C4] "minfer Architecture Execution Plan", C4 S2b design decision 4:
+ *           the Q8_0 quantizer is amax over the 32-block, scale amax / 127,
+ *           codes rounded half to even.
+ *
+ * Layouts (all little-endian):
+ *   W  : N rows (outputs) x K columns (inputs), row-major; each row is K / bv
+ *        consecutive blocks (bv = 32 for Q8_0, 256 for Q4_K and Q6_K).  Block
+ *        bytes: Q8_0 34 (f16 d, int8 q[32]); Q4_K 144 (f16 d, f16 dmin,
+ *        12 bytes of 6-bit scale/min pairs, 128 bytes of 4-bit codes); Q6_K 210
+ *        (128 bytes low 4 bits, 64 bytes high 2 bits, 16 int8 sub-scales, f16 d).
+ *        These are the public GGUF layouts; the pages fix only the sizes.
+ *   x  : K f32.   y : N f32.   X : M x K f32 row-major.   Y : M x N f32 row-major.
+ *   Xq : the quantized activation plane written by mq_quantize_act, three
+ *        arrays in one buffer of mq_act_bytes(M, K) bytes:
+ *          codes  int8  [M][K]        at offset 0
+ *          scales f32   [M][K / 32]   at offset mq_act_scale_offset(M, K)
+ *          sums   int32 [M][K / 32]   at offset mq_act_sum_offset(M, K)
+ *        For block b of row m: scale = f32(amax) / f32(127) with IEEE division,
+ *        code_i = clamp(round_half_even(x_i / scale), -127, 127) (a true f32
+ *        division), scale 0 and codes 0 when amax == 0, and sum = sum of the 32
+ *        codes.
+ *
+ * Ownership and streams: the caller allocates and frees every buffer (device
+ * memory, e.g. from torch).  Weights and inputs are read only.  No call
+ * allocates, frees or synchronizes; every kernel runs on the caller's stream
+ * (a hipStream_t passed as void*, NULL = the null stream), so calls may be
+ * captured into a HIP graph.  Pointers must be 16-byte aligned unless stated.
+ *
+ * Errors: every call returns MQ_OK (0) or a negative MQ_ERR_* code and never
+ * falls back to another kernel or to the host.  Argument checks run before
+ * any HIP call.  mq_last_error() returns a thread-local message naming the
+ * call, the offending values and, for HIP failures, hipGetErrorName.
+ */
+#ifndef MQ_H
+#define MQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight type ids: the GGUF tensor-type ids. */
+#define MQ_Q8_0 8
+#define MQ_Q4_K 12
+#define MQ_Q6_K 14
+
+/* Status codes. */
+#define MQ_OK 0
+#define MQ_ERR_ARG (-1)    /* null pointer, negative or zero size            */
+#define MQ_ERR_SHAPE (-2)  /* K not a multiple of the block size, M/N/K limit */
+#define MQ_ERR_TYPE (-3)   /* unsupported weight type id                      */
+#define MQ_ERR_SIZE (-4)   /* a byte count that is not exactly the required one */
+#define MQ_ERR_ALIGN (-5)  /* pointer not 16-byte aligned                     */
+#define MQ_ERR_DEVICE (-6) /* no usable gfx950 device, or a HIP runtime error */
+#define MQ_ERR_LAUNCH (-7) /* a kernel launch was refused                     */
+#define MQ_ERR_NOINIT (-8) /* mq_init has not succeeded on the current device */
+
+/* Upper bounds accepted by the calls (sizes beyond them are MQ_ERR_SHAPE). */
+#define MQ_MAX_K 65536          /* inputs per row                 */
+#define MQ_MAX_N (1 << 24)      /* output rows                    */
+#define MQ_MAX_M (1 << 20)      /* activation rows for mq_gemm    */
+
+/*
+ * mq_init -- select `device`, check that it is gfx950, record its compute-unit
+ * count and LDS limit, and set every kernel attribute the library needs.  Call
+ * once per device before any other call on it, outside any stream capture
+ * [BD4.9: limits queried at run time].  Returns MQ_ERR_DEVICE when there is no
+ * such device or it is not gfx950.  Idempotent.
+ */
+int mq_init(int device);
+
+/* Exact byte size of a GGUF payload of N x K weights of `type` [BD2.3];
+ * 0 for an unsupported type or a K that is not a whole number of blocks. */
+size_t mq_weight_bytes(int type, int64_t N, int64_t K);
+
+/* Bytes of the quantized activation plane for M x K, and the offsets of its
+ * scale and sum arrays (both 256-byte aligned).  0 if K % 32 != 0. */
+size_t mq_act_bytes(int64_t M, int64_t K);
+size_t mq_act_scale_offset(int64_t M, int64_t K);
+size_t mq_act_sum_offset(int64_t M, int64_t K);
+
+/*
+ * mq_quantize_act -- X f32 [M][K] (device) -> Xq (device, mq_act_bytes(M, K)
+ * bytes) per the Xq layout above [EP-C4; BD4.4].  K % 32 == 0.  The output is
+ * bit-exact: the same codes, scales and sums as the definition for any finite
+ * X.  X must be finite (NaN/Inf are outside the contract).
+ */
+int mq_quantize_act(const float* X, void* Xq, int64_t M, int64_t K, void* stream);
+
+/*
+ * mq_gemv -- y[n] = sum_k deq(W)[n][k] * x[k] for a single f32 activation row
+ * (the decode product, [BD4.4]).  W: mq_weight_bytes(type, N, K) bytes of GGUF
+ * payload (device, 16-byte aligned); x: K f32 (device); y: N f32 (device,
+ * overwritten).  K must be a multiple of the block size (32 or 256) [BD4.3].
+ * f32 accumulation; the result is within 2e-4 of the exact product relative to
+ * ||deq(W)[n]|| * ||x||.
+ */
+int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_t K, void* stream);
+
+/*
+ * mq_gemm_scratch_bytes -- device scratch that mq_gemm needs for (type, M, N,
+ * K); 0 when the chosen kernel needs none.  Pass at least this many bytes.
+ */
+size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
+
+/*
+ * mq_gemm -- the prefill product on the int8 path [BD4.4]:
+ *   Y[m][n] = sum_b scale_x[m][b] * sum_{i<32} deq(W)[n][32b+i] * code_x[m][32b+i]
+ * Xq is a plane written by mq_quantize_act(.., M, K, ..) (it may be reused for
+ * several weights that share the input).  Per 32-value block the kernel forms
+ * exact int32 dot products of weight codes and activation codes on int8 MFMA
+ * (per 16-value group for Q6_K) and applies the block scales in f32 (and, for
+ * Q4_K, the min term through the block's code sum).  Y: M x N f32 (device,
+ * overwritten).  scratch / scratch_bytes: device memory of at least
+ * mq_gemm_scratch_bytes(type, M, N, K) bytes (may be NULL/0 when that is 0).
+ */
+int mq_gemm(const void* W, int type, const void* Xq, float* Y, int64_t M, int64_t N, int64_t K,
+            void* scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * mq_debug_gemm_blockdots -- test export: the exact int32 block dot products
+ * the mq_gemm kernel forms, written to D (device) as int32 [M][N][G] with
+ * G = K / 32 for Q8_0 and Q4_K (code dot per 32-value block, Q4_K codes 0..15)
+ * and G = K / 16 for Q6_K (dot of (code - 32) per 16-value group).  Runs the
+ * same kernel template as mq_gemm with its store of block dots switched on.
+ * D must hold M * N * G int32.
+ */
+int mq_debug_gemm_blockdots(const void* W, int type, const void* Xq, int32_t* D,
+                            int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * mq_last_error -- the message of the last failing call on this thread (empty
+ * string if none).  Valid until the next failing call on the same thread.
+ */
+const char* mq_last_error(void);
+
+/* Name of the kernel the last successful launching call on this thread ran
+ * (for tests that must prove which path executed). */
+const char* mq_last_kernel(void);
+
+/* Library version string. */
+const char* mq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQ_H */

@@ -1,0 +1,106 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, computes sizes, and refuses bad arguments before any HIP call.
+
+No kernel is launched here (this machine may have no GPU): every call that
+passes validation would need mq_init, and the refusals tested below happen
+first.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_quantized_matmul_mq_amd import mq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mq.h")
+FAKE = 0x10000  # a 256-byte aligned non-null pointer value that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mq.load()
+    names = declared_functions()
+    assert "mq_gemv" in names and "mq_gemm" in names and "mq_quantize_act" in names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(mq._SIGNATURES), "binding and header disagree"
+
+
+def test_weight_bytes_are_exact_payload_sizes():
+    assert mq.weight_bytes(mq.Q4_K, 18944, 3584) == 38191104
+    assert mq.weight_bytes(mq.Q4_K, 3584, 18944) == 38191104
+    assert mq.weight_bytes(mq.Q6_K, 152064, 3584) == 447068160
+    assert mq.weight_bytes(mq.Q8_0, 4864, 896) == 4630528
+    assert mq.weight_bytes(mq.Q4_K, 10, 100) == 0      # K not a whole super-block
+    assert mq.weight_bytes(99, 10, 256) == 0           # unknown type
+    assert mq.weight_bytes(mq.Q8_0, 0, 32) == 0
+
+
+def test_activation_plane_layout():
+    M, K = 37, 96
+    total, so, uo = mq.act_layout(M, K)
+    assert so >= M * K and so % 256 == 0
+    assert uo >= so + 4 * M * (K // 32) and uo % 256 == 0
+    assert total >= uo + 4 * M * (K // 32) and total % 256 == 0
+    assert mq.act_bytes(M, 100) == 0
+
+
+def _rc(fn, *args):
+    return fn(*args)
+
+
+def test_quantize_act_refusals():
+    lib = mq.load()
+    assert lib.mq_quantize_act(None, FAKE, 4, 64, None) == -1
+    assert lib.mq_quantize_act(FAKE, FAKE, 0, 64, None) == -1
+    assert lib.mq_quantize_act(FAKE, FAKE, 4, 48, None) == -2
+    assert "multiple of 32" in mq.last_error()
+    assert lib.mq_quantize_act(FAKE + 4, FAKE, 4, 64, None) == -5
+    assert lib.mq_quantize_act(FAKE, FAKE + 16, 4, 64, None) == -5
+    assert lib.mq_quantize_act(FAKE, FAKE, 4, 1 << 20, None) == -2
+
+
+def test_gemv_refusals():
+    lib = mq.load()
+    assert lib.mq_gemv(None, mq.Q4_K, FAKE, FAKE, 8, 256, None) == -1
+    assert lib.mq_gemv(FAKE, 2, FAKE, FAKE, 8, 256, None) == -3        # q4_0 is not served here
+    assert "unsupported weight type 2" in mq.last_error()
+    assert lib.mq_gemv(FAKE, mq.Q4_K, FAKE, FAKE, 8, 128, None) == -2  # K % 256
+    assert "K=128" in mq.last_error()
+    assert lib.mq_gemv(FAKE, mq.Q8_0, FAKE, FAKE, 8, 48, None) == -2   # K % 32
+    assert lib.mq_gemv(FAKE, mq.Q8_0, FAKE, FAKE, -1, 64, None) == -1
+    assert lib.mq_gemv(FAKE + 2, mq.Q8_0, FAKE, FAKE, 8, 64, None) == -5
+    assert lib.mq_gemv(FAKE, mq.Q8_0, FAKE + 8, FAKE, 8, 64, None) == -5
+    assert lib.mq_gemv(FAKE, mq.Q8_0, FAKE, FAKE + 2, 8, 64, None) == -5
+
+
+def test_gemm_refusals():
+    lib = mq.load()
+    assert lib.mq_gemm(FAKE, mq.Q4_K, FAKE, None, 4, 8, 256, None, 0, None) == -1
+    assert lib.mq_gemm(FAKE, mq.Q4_K, FAKE, FAKE, 0, 8, 256, None, 0, None) == -1
+    assert lib.mq_gemm(FAKE, mq.Q6_K, FAKE, FAKE, 4, 8, 96, None, 0, None) == -2
+    assert lib.mq_gemm(FAKE, 7, FAKE, FAKE, 4, 8, 256, None, 0, None) == -3
+    assert lib.mq_gemm(FAKE, mq.Q4_K, FAKE + 16, FAKE, 4, 8, 256, None, 0, None) == -5
+    assert lib.mq_debug_gemm_blockdots(FAKE, mq.Q4_K, FAKE, None, 4, 8, 256, None) == -1
+
+
+def test_calls_without_init_are_refused_not_run():
+    # Valid arguments but mq_init has not succeeded (and there may be no device
+    # at all): the call must return an error code, never launch.
+    lib = mq.load()
+    rc = lib.mq_gemv(FAKE, mq.Q4_K, FAKE, FAKE, 8, 256, None)
+    assert rc in (-6, -8)
+    assert mq.last_error().startswith("mq_gemv")
+
+
+def test_init_refuses_a_bad_device_index():
+    lib = mq.load()
+    assert lib.mq_init(-1) == -1
+    assert lib.mq_init(10 ** 6) == -1

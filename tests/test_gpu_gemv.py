@@ -1,0 +1,97 @@
+"""GPU parity of mq_gemv (f32 activation) against the oracle's f64 GEMV."""
+
+import numpy as np
+import pytest
+
+import oracle
+from block_quantized_matmul_mq_amd import mq, synth
+
+from gpu_cases import BLOCK, NAMES, check_normalized, device, row_norms, say, to_dev, weights
+
+pytestmark = pytest.mark.gpu
+
+TYPES = [mq.Q8_0, mq.Q4_K, mq.Q6_K]
+
+
+def run_gemv(raw, qtype, x, N, K, rows=None, what=""):
+    import torch
+    dev = device()
+    say(f"gemv {NAMES[qtype]} N={N} K={K} {what}")
+    W = to_dev(raw.reshape(-1), dev)
+    y = mq.gemv(W, qtype, to_dev(x, dev), N, K)
+    torch.cuda.synchronize()
+    assert mq.last_kernel().startswith("gemv")
+    y = y.cpu().numpy()
+    rows = np.arange(N) if rows is None else rows
+    sub = raw.reshape(N, -1)[rows]
+    y_ref = oracle.gemv(sub, qtype, x, len(rows), K)
+    wn = row_norms(raw, qtype, N, K, rows)
+    xn = np.array([np.linalg.norm(x.astype(np.float64))])
+    return check_normalized(y[rows][None, :], y_ref[None, :], wn, xn, f"{NAMES[qtype]} {N}x{K} {what}")
+
+
+def small_shapes(qtype):
+    b = BLOCK[qtype]
+    # one block, several K-steps with a ragged last step, ragged N tails
+    return [(1, b), (5, b), (37, 2 * b), (130, 2048 + b), (300, 4096), (67, 8192 + 3 * b)]
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
+@pytest.mark.parametrize("kind", ["quantized", "random"])
+def test_gemv_small_and_ragged(qtype, kind):
+    for i, (N, K) in enumerate(small_shapes(qtype)):
+        raw = weights(qtype, N, K, kind, i)
+        x = synth.activations(1, K, config_index=10, tensor_index=i)[0]
+        run_gemv(raw, qtype, x, N, K, what=kind)
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
+def test_gemv_zero_rows_and_zero_input(qtype):
+    N, K = 20, 2 * BLOCK[qtype]
+    raw = weights(qtype, N, K, "quantized", 3)
+    raw = raw.reshape(N, -1).copy()
+    raw[4] = 0
+    raw[11] = 0
+    x = synth.activations(1, K, config_index=11, tensor_index=0)[0]
+    run_gemv(raw, qtype, x, N, K, what="zero rows")
+    run_gemv(raw, qtype, np.zeros(K, np.float32), N, K, what="zero x")
+
+
+def test_gemv_q8_0_config1_ffn_up():
+    N, K = 4864, 896
+    raw = synth.quantized_weight(mq.Q8_0, N, K, 0, 0)
+    x = synth.activations(1, K, config_index=0)[0]
+    run_gemv(raw, mq.Q8_0, x, N, K, what="0.5B ffn_up")
+
+
+def test_gemv_q8_0_7b_shape():
+    N, K = 18944, 3584
+    raw = synth.quantized_weight(mq.Q8_0, N, K, 0, 5)
+    x = synth.activations(1, K, config_index=0, tensor_index=5)[0]
+    run_gemv(raw, mq.Q8_0, x, N, K, what="7B ffn_up shape")
+
+
+@pytest.mark.parametrize("N,K,tensor", [(18944, 3584, 0), (3584, 18944, 1)], ids=["ffn_up", "ffn_down"])
+def test_gemv_q4_k_config2(N, K, tensor):
+    raw = synth.quantized_weight(mq.Q4_K, N, K, 1, tensor)
+    x = synth.activations(1, K, config_index=1, tensor_index=tensor)[0]
+    run_gemv(raw, mq.Q4_K, x, N, K, what="7B FFN")
+
+
+def test_gemv_q6_k_config3_head_sampled():
+    N, K = 152064, 3584
+    raw = synth.quantized_weight(mq.Q6_K, N, K, 2, 0)
+    x = synth.activations(1, K, config_index=2)[0]
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([rng.integers(0, N, 3000), np.arange(64), np.arange(N - 64, N)]))
+    run_gemv(raw, mq.Q6_K, x, N, K, rows=rows, what="vocab head (sampled rows)")
+
+
+@pytest.mark.parametrize("qtype,N,K,tensor", [(mq.Q4_K, 5120, 5120, 0), (mq.Q4_K, 1024, 5120, 1),
+                                              (mq.Q4_K, 13824, 5120, 2), (mq.Q6_K, 5120, 13824, 3)],
+                         ids=["attn_q", "attn_k", "ffn_up", "ffn_down"])
+def test_gemv_config5_14b(qtype, N, K, tensor):
+    raw = synth.quantized_weight(qtype, N, K, 4, tensor)
+    x = synth.activations(1, K, config_index=4, tensor_index=tensor)[0]
+    rows = None if N * K <= 5120 * 5120 else np.random.default_rng(1).choice(N, 2048, replace=False)
+    run_gemv(raw, qtype, x, N, K, rows=rows, what="14B")

@@ -1,0 +1,160 @@
+"""GPU parity of mq_gemm (the int8 MMQ path) against the oracle.
+
+* The exact int32 block dots the kernel forms (test export from the same
+  kernel template) equal the oracle's block dots bit for bit.
+* Y is within 2e-4 of the oracle's f64 product of deq(q8(X)) and deq(W),
+  normalized per element by ||deq(W)[n]|| * ||x_hat[m]||.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from block_quantized_matmul_mq_amd import mq, synth
+
+from gpu_cases import BLOCK, NAMES, check_normalized, device, row_norms, say, to_dev, weights
+
+pytestmark = pytest.mark.gpu
+
+TYPES = [mq.Q8_0, mq.Q4_K, mq.Q6_K]
+
+
+def quantized_plane(X, dev):
+    import torch
+    M, K = X.shape
+    Xq = mq.quantize_act(to_dev(X, dev))
+    torch.cuda.synchronize()
+    return Xq
+
+
+def x_hat_norms(X):
+    q, d, _ = oracle.quantize_act(X)
+    M, K = X.shape
+    xh = (q.reshape(M, -1, 32).astype(np.float64) * d[..., None].astype(np.float64)).reshape(M, K)
+    return np.linalg.norm(xh, axis=1), q, d
+
+
+def check_blockdots(raw, qtype, X, N, K, what):
+    import torch
+    dev = device()
+    M = X.shape[0]
+    say(f"blockdots {NAMES[qtype]} M={M} N={N} K={K} {what}")
+    Xq = quantized_plane(X, dev)
+    D = mq.gemm_blockdots(to_dev(raw.reshape(-1), dev), qtype, Xq, M, N, K)
+    torch.cuda.synchronize()
+    assert mq.last_kernel().startswith("mmq")
+    D = D.cpu().numpy()
+    q, _, _ = oracle.quantize_act(X)
+    ref = oracle.block_dots(raw, qtype, q, N, K)
+    assert np.array_equal(D, ref), f"{what}: block dots differ at {np.argwhere(D != ref)[:5]}"
+
+
+def check_gemm(raw, qtype, X, N, K, cols=None, what=""):
+    import torch
+    dev = device()
+    M = X.shape[0]
+    say(f"gemm {NAMES[qtype]} M={M} N={N} K={K} {what}")
+    Xq = quantized_plane(X, dev)
+    Y = mq.gemm(to_dev(raw.reshape(-1), dev), qtype, Xq, M, N, K)
+    torch.cuda.synchronize()
+    assert mq.last_kernel().startswith("mmq")
+    Y = Y.cpu().numpy()
+    cols = np.arange(N) if cols is None else cols
+    xn, q, d = x_hat_norms(X)
+    sub = raw.reshape(N, -1)[cols]
+    Y_ref = oracle.mmq(sub, qtype, q, d, len(cols), K)
+    wn = row_norms(raw, qtype, N, K, cols)
+    return check_normalized(Y[:, cols], Y_ref, wn, xn, f"{NAMES[qtype]} M={M} {N}x{K} {what}")
+
+
+def small_cases(qtype):
+    b = BLOCK[qtype]
+    return [(1, 1, b), (3, 33, 2 * b), (37, 130, 4 * b), (130, 300, 2 * b + 512), (129, 257, 1024)]
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
+@pytest.mark.parametrize("kind", ["quantized", "random"])
+def test_blockdots_bitwise_small_ragged(qtype, kind):
+    for i, (M, N, K) in enumerate(small_cases(qtype)):
+        raw = weights(qtype, N, K, kind, 20 + i)
+        X = synth.activations(M, K, config_index=12, tensor_index=i)
+        check_blockdots(raw, qtype, X, N, K, kind)
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
+@pytest.mark.parametrize("kind", ["quantized", "random"])
+def test_gemm_small_ragged(qtype, kind):
+    for i, (M, N, K) in enumerate(small_cases(qtype)):
+        raw = weights(qtype, N, K, kind, 40 + i)
+        X = synth.activations(M, K, config_index=13, tensor_index=i)
+        check_gemm(raw, qtype, X, N, K, what=kind)
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
+def test_gemm_extreme_activations(qtype):
+    M, N, K = 24, 96, 2 * BLOCK[qtype] + 256
+    raw = weights(qtype, N, K, "random", 60)
+    X = synth.activations(M, K, config_index=14)
+    X[0] = 0.0
+    X[1, :64] = 0.0
+    X[2] *= np.float32(1e-30)
+    X[3] *= np.float32(1e30)
+    X[4, ::7] = np.float32(50.0)
+    check_blockdots(raw, qtype, X, N, K, "extreme activations")
+    check_gemm(raw, qtype, X, N, K, what="extreme activations")
+
+
+def test_blockdots_config1_q8_0_m16():
+    N, K = 4864, 896
+    raw = synth.quantized_weight(mq.Q8_0, N, K, 0, 0)
+    X = synth.activations(16, K, config_index=0)
+    check_blockdots(raw, mq.Q8_0, X, N, K, "0.5B ffn_up M=16")
+    check_gemm(raw, mq.Q8_0, X, N, K, what="0.5B ffn_up M=16")
+
+
+@pytest.mark.parametrize("N,K,tensor", [(18944, 3584, 0), (3584, 3584, 1), (512, 3584, 2)],
+                         ids=["ffn_up", "attn_q", "attn_kv"])
+def test_gemm_config4_m512(N, K, tensor):
+    raw = synth.quantized_weight(mq.Q4_K, N, K, 3, tensor)
+    X = synth.activations(512, K, config_index=3)
+    cols = None if N <= 4096 else np.random.default_rng(2).choice(N, 1024, replace=False)
+    check_gemm(raw, mq.Q4_K, X, N, K, cols=cols, what="7B prefill M=512")
+
+
+def test_blockdots_config4_sampled_tiles():
+    # bit-exact block dots at the full ffn_up shape on a sub-block of rows/cols:
+    # the export runs the whole grid; the comparison covers 3 x 2 tiles.
+    N, K = 18944, 3584
+    raw = synth.quantized_weight(mq.Q4_K, N, K, 3, 0)
+    X = synth.activations(512, K, config_index=3)
+    import torch
+    dev = device()
+    say("blockdots q4_K M=512 18944x3584 (sampled tiles)")
+    Xq = quantized_plane(X, dev)
+    D = mq.gemm_blockdots(to_dev(raw.reshape(-1), dev), mq.Q4_K, Xq, 512, N, K)
+    torch.cuda.synchronize()
+    q, _, _ = oracle.quantize_act(X)
+    rows = np.r_[0:128, 384:512]
+    cols = np.r_[0:256, N - 128:N]
+    ref = oracle.block_dots(raw.reshape(N, -1)[cols], mq.Q4_K, q[rows], len(cols), K)
+    got = D[torch.from_numpy(rows).to(dev)][:, torch.from_numpy(cols).to(dev)].cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_gemm_config3_m8_head_sampled():
+    N, K = 152064, 3584
+    raw = synth.quantized_weight(mq.Q6_K, N, K, 2, 0)
+    X = synth.activations(8, K, config_index=2, tensor_index=8)
+    cols = np.unique(np.concatenate([np.random.default_rng(3).choice(N, 2000, replace=False),
+                                     np.arange(N - 40, N)]))
+    check_gemm(raw, mq.Q6_K, X, N, K, cols=cols, what="head M=8 (sampled cols)")
+
+
+@pytest.mark.parametrize("qtype,N,K,tensor", [(mq.Q4_K, 5120, 5120, 0), (mq.Q4_K, 1024, 5120, 1),
+                                              (mq.Q4_K, 13824, 5120, 2), (mq.Q6_K, 5120, 13824, 3)],
+                         ids=["attn_q", "attn_k", "ffn_up", "ffn_down"])
+def test_gemm_config5_m2048_sampled(qtype, N, K, tensor):
+    raw = synth.quantized_weight(qtype, N, K, 4, tensor)
+    X = synth.activations(2048, K, config_index=4, tensor_index=10 + (K == 13824))
+    cols = np.random.default_rng(4).choice(N, 384, replace=False)
+    check_gemm(raw, qtype, X, N, K, cols=cols, what="14B prefill M=2048 (sampled cols)")

@@ -9,21 +9,23 @@ N(0, 1)):
             ffn_up 18944x3584, attn_q 3584x3584, attn_k and attn_v 512x3584
 
 Inputs are resident in HBM before timing starts.  Each GEMV weight is kept in
-several copies that the steps rotate through, so every GEMV launch reads its
-weights from HBM and not from the 256 MB last-level cache.
+several copies that consecutive launches rotate through, so every GEMV launch
+reads its weights from HBM and not from the 256 MB last-level cache.  Launches
+are recorded once into HIP graphs and replayed; HIP events on the launch
+stream bracket the replays (per-kernel time = elapsed / launches).
 
-Printed JSON line (rank 0, one GPU):
-  value     = Q4_K GEMV weight GB/s: GGUF payload bytes of the two decode
-              GEMVs / their summed kernel time (HIP events on the launch stream)
-  mmq_prefill_tops = 2*M*N*K of the four MMQ launches / their kernel time
-  roofline / roofline_mmq = the GEMV against 8 TB/s HBM, the MMQ against
-              5.0 POP/s dense int8 MFMA
-  cpu_baseline = the CPU oracle's GEMV on the same ffn_up + ffn_down weights
+Printed JSON line (one GPU):
+  value        Q4_K GEMV weight GB/s: GGUF payload bytes of the two decode
+               GEMVs / their summed kernel time
+  mmq_prefill_tops   2*M*N*K of the four MMQ launches / their kernel time
+  roofline     the Q4_K GEMV against 8 TB/s HBM
+  roofline_mmq the ffn_up MMQ against 5.0 POP/s dense int8 MFMA
+  secondary    Q6_K vocab-head and Q8_0 GEMV GB/s, the quantizer
+  cpu_baseline the CPU oracle's GEMV on the same ffn_up + ffn_down weights
 """
 
 import argparse
 import json
-import os
 import sys
 import time
 
@@ -31,7 +33,9 @@ import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
 INT8_PEAK_TOPS = 5000.0
+LLC_BYTES = 256 * 2 ** 20
 
+Q8_0, Q4_K, Q6_K = 8, 12, 14
 DECODE = [("ffn_up", 18944, 3584), ("ffn_down", 3584, 18944)]
 PREFILL_M = 512
 PREFILL = [("ffn_up", 18944, 3584), ("attn_q", 3584, 3584), ("attn_k", 512, 3584), ("attn_v", 512, 3584)]
@@ -40,11 +44,16 @@ PREFILL = [("ffn_up", 18944, 3584), ("attn_q", 3584, 3584), ("attn_k", 512, 3584
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--copies", type=int, default=8, help="rotated copies of each GEMV weight")
+    p.add_argument("--steps", type=int, default=20, help="timed replays of the step graph")
+    p.add_argument("--warmup", type=int, default=3, help="untimed replays before timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true")
     return p.parse_args()
+
+
+def copies_for(nbytes):
+    """Copies so that one rotation reads at least twice the last-level cache."""
+    return max(2, -(-2 * LLC_BYTES // nbytes))
 
 
 def cpu_baseline(w_up, w_down, x_up, x_down):
@@ -58,16 +67,42 @@ def cpu_baseline(w_up, w_down, x_up, x_down):
     times = []
     for _ in range(3):
         t0 = time.perf_counter()
-        oracle.gemv(w_up, 12, x_up, 18944, 3584)
-        oracle.gemv(w_down, 12, x_down, 3584, 18944)
+        oracle.gemv(w_up, Q4_K, x_up, 18944, 3584)
+        oracle.gemv(w_down, Q4_K, x_down, 3584, 18944)
         times.append(time.perf_counter() - t0)
     if limit is not None:
         limit.unregister()
     t = float(np.median(times))
     nbytes = w_up.nbytes + w_down.nbytes
-    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "numpy f64 oracle GEMV over the full Q4_K ffn_up 18944x3584 + ffn_down "
                       f"3584x18944 weights, 1 thread, median of 3 ({t:.2f} s per pair)"}
+
+
+class GraphTimer:
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+
+    def per_launch_us(self, launches, replays, warmup=2):
+        """Record `launches` (callables, one kernel each) into a graph; time `replays` replays."""
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for fn in launches:
+                fn()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        s = torch.cuda.current_stream()
+        start.record(s)
+        for _ in range(replays):
+            g.replay()
+        end.record(s)
+        torch.cuda.synchronize()
+        return 1000.0 * start.elapsed_time(end) / (replays * len(launches))
 
 
 def main():
@@ -82,18 +117,21 @@ def main():
 
     dev = torch.device("cuda:0")
     mq.init(0)
-    stream = torch.cuda.current_stream()
+    timer = GraphTimer(torch, torch.cuda.current_stream())
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).to(dev)
 
     # ---- inputs, resident in HBM ----
-    w_host = {name: synth.quantized_weight(12, N, K, 1, i) for i, (name, N, K) in enumerate(DECODE)}
+    w_host = {name: synth.quantized_weight(Q4_K, N, K, 1, i) for i, (name, N, K) in enumerate(DECODE)}
     for i, (name, N, K) in enumerate(PREFILL[1:]):
-        w_host[name] = synth.quantized_weight(12, N, K, 3, i + 1)
+        w_host[name] = synth.quantized_weight(Q4_K, N, K, 3, i + 1)
     x_dec = {name: synth.activations(1, K, 1, tensor_index=10 + i)[0] for i, (name, N, K) in enumerate(DECODE)}
     X_pre = synth.activations(PREFILL_M, 3584, 3)
 
-    copies = {name: [torch.from_numpy(w_host[name].reshape(-1)).to(dev) for _ in range(args.copies)]
-              for name, _, _ in DECODE}
-    w_pre = {name: torch.from_numpy(w_host[name].reshape(-1)).to(dev) for name, _, _ in PREFILL[1:]}
+    ncopy = copies_for(mq.weight_bytes(Q4_K, 18944, 3584))
+    copies = {name: [to_dev(w_host[name]) for _ in range(ncopy)] for name, _, _ in DECODE}
+    w_pre = {name: to_dev(w_host[name]) for name, _, _ in PREFILL[1:]}
     x_dev = {k: torch.from_numpy(v).to(dev) for k, v in x_dec.items()}
     y_dev = {name: torch.empty(N, dtype=torch.float32, device=dev) for name, N, _ in DECODE}
     X_dev = torch.from_numpy(X_pre).to(dev)
@@ -101,62 +139,72 @@ def main():
     Y_dev = {name: torch.empty((PREFILL_M, N), dtype=torch.float32, device=dev) for name, N, _ in PREFILL}
     torch.cuda.synchronize()
 
-    labels = [f"gemv_{n}" for n, _, _ in DECODE] + ["quantize_act"] + [f"mmq_{n}" for n, _, _ in PREFILL]
     kernel_names = {}
 
-    def step(i, events=None):
-        c = i % args.copies
-        k = 0
-
-        def mark():
-            nonlocal k
-            if events is not None:
-                events[k].record(stream)
-            k += 1
-
-        for name, N, K in DECODE:
-            mark()
-            mq.gemv(copies[name][c], 12, x_dev[name], N, K, y=y_dev[name])
+    def gemv_launch(name, N, K, c):
+        def fn():
+            mq.gemv(copies[name][c], Q4_K, x_dev[name], N, K, y=y_dev[name])
             kernel_names[f"gemv_{name}"] = mq.last_kernel()
-        mark()
-        mq.quantize_act(X_dev, Xq)
-        for name, N, K in PREFILL:
-            mark()
-            W = copies["ffn_up"][c] if name == "ffn_up" else w_pre[name]
-            mq.gemm(W, 12, Xq, PREFILL_M, N, K, Y=Y_dev[name])
-            kernel_names[f"mmq_{name}"] = mq.last_kernel()
-        mark()
+        return fn
 
-    for i in range(args.warmup):
-        step(i)
+    def quant_launch():
+        mq.quantize_act(X_dev, Xq)
+
+    def mmq_launch(name, N, K, c):
+        W = copies["ffn_up"][c] if name == "ffn_up" else w_pre[name]
+
+        def fn():
+            mq.gemm(W, Q4_K, Xq, PREFILL_M, N, K, Y=Y_dev[name])
+            kernel_names[f"mmq_{name}"] = mq.last_kernel()
+        return fn
+
+    def step_launches(c):
+        out = [gemv_launch(name, N, K, c) for name, N, K in DECODE]
+        out.append(quant_launch)
+        out += [mmq_launch(name, N, K, c) for name, N, K in PREFILL]
+        return out
+
+    # eager warmup (also sets the kernel names), then the timed step graph
+    for c in range(ncopy):
+        for fn in step_launches(c):
+            fn()
     torch.cuda.synchronize()
 
-    nev = len(labels) + 1
-    all_events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    step_g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(step_g):
+        for c in range(ncopy):
+            for fn in step_launches(c):
+                fn()
+    for _ in range(args.warmup):
+        step_g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(s)
+    for _ in range(args.steps):
+        step_g.replay()
+    t_end.record(s)
     torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i, all_events[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / (args.steps * ncopy)
 
-    total_ms = t_start.elapsed_time(t_end)
-    per = {lab: [] for lab in labels}
-    for ev in all_events:
-        for j, lab in enumerate(labels):
-            per[lab].append(ev[j].elapsed_time(ev[j + 1]))
-    avg_us = {lab: 1000.0 * float(np.mean(v)) for lab, v in per.items()}
+    # per-kernel times: each kernel alone, its launches back to back in a graph
+    reps = max(2, args.steps // 2)
+    avg_us = {}
+    for name, N, K in DECODE:
+        avg_us[f"gemv_{name}"] = timer.per_launch_us([gemv_launch(name, N, K, c) for c in range(ncopy)], reps)
+    avg_us["quantize_act"] = timer.per_launch_us([quant_launch] * 8, reps)
+    for name, N, K in PREFILL:
+        avg_us[f"mmq_{name}"] = timer.per_launch_us([mmq_launch(name, N, K, c % ncopy) for c in range(4)], reps)
 
-    gemv_bytes = sum(mq.weight_bytes(12, N, K) for _, N, K in DECODE)
+    gemv_bytes = sum(mq.weight_bytes(Q4_K, N, K) for _, N, K in DECODE)
     gemv_s = sum(avg_us[f"gemv_{n}"] for n, _, _ in DECODE) * 1e-6
     gemv_gbps = gemv_bytes / gemv_s / 1e9
     mmq_ops = sum(2 * PREFILL_M * N * K for _, N, K in PREFILL)
     mmq_s = sum(avg_us[f"mmq_{n}"] for n, _, _ in PREFILL) * 1e-6
     mmq_tops = mmq_ops / mmq_s / 1e12
-    up_bytes = mq.weight_bytes(12, 18944, 3584)
-    up_gbps = up_bytes / (avg_us["gemv_ffn_up"] * 1e-6) / 1e9
+    up_gbps = mq.weight_bytes(Q4_K, 18944, 3584) / (avg_us["gemv_ffn_up"] * 1e-6) / 1e9
+    down_gbps = mq.weight_bytes(Q4_K, 3584, 18944) / (avg_us["gemv_ffn_down"] * 1e-6) / 1e9
     mmq_up_tops = 2 * PREFILL_M * 18944 * 3584 / (avg_us["mmq_ffn_up"] * 1e-6) / 1e12
 
     result = {
@@ -166,7 +214,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(total_ms / args.steps, 4),
+        "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -175,21 +223,47 @@ def main():
         "config": {
             "workload": "Qwen2.5-7B Q4_K: decode GEMV ffn_up 18944x3584 + ffn_down 3584x18944 (M=1, f32 x); "
                         "prefill M=512: quantize_act 512x3584 + int8 MMQ ffn_up/attn_q/attn_k/attn_v",
-            "M_decode": 1, "M_prefill": PREFILL_M, "weight_copies_rotated": args.copies,
+            "M_decode": 1, "M_prefill": PREFILL_M, "weight_copies_rotated": ncopy,
             "parallelism": "single GPU",
         },
         "mmq_prefill_tops": round(mmq_tops, 2),
         "mmq_dtype": "i8 x i8 -> i32 block dots, f32 scales",
         "roofline": {"bound": "hbm", "achieved": round(gemv_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "gemv Q4_K (ffn_up + ffn_down)",
-                     "ffn_up_GBps": round(up_gbps, 1)},
+                     "kernel": "gemv<q4_K> (ffn_up + ffn_down)",
+                     "ffn_up_GBps": round(up_gbps, 1), "ffn_down_GBps": round(down_gbps, 1)},
         "roofline_mmq": {"bound": "mfma", "achieved": round(mmq_up_tops, 2), "peak": INT8_PEAK_TOPS,
                          "unit": "TOP/s", "frac": round(mmq_up_tops / INT8_PEAK_TOPS, 4), "traffic": None,
-                         "kernel": "mmq Q4_K ffn_up M=512 18944x3584"},
+                         "kernel": "mmq<q4_K> ffn_up M=512 18944x3584"},
         "kernel_avg_us": {lab: round(v, 3) for lab, v in avg_us.items()},
         "kernel_names": kernel_names,
     }
+
+    if not args.no_secondary:
+        sec = {}
+        head = synth.quantized_weight(Q6_K, 152064, 3584, 2, 0)
+        hb = mq.weight_bytes(Q6_K, 152064, 3584)
+        hcop = [to_dev(head) for _ in range(copies_for(hb))]
+        del head
+        xh = torch.from_numpy(synth.activations(1, 3584, 2)[0]).to(dev)
+        yh = torch.empty(152064, dtype=torch.float32, device=dev)
+        us = timer.per_launch_us([lambda W=W: mq.gemv(W, Q6_K, xh, 152064, 3584, y=yh) for W in hcop], reps)
+        sec["gemv_q6_K_head_152064x3584"] = {"us": round(us, 3), "GBps": round(hb / us / 1e3, 1)}
+        del hcop
+        for N, K, tag in [(18944, 3584, "7B_ffn_up_shape"), (4864, 896, "0.5B_ffn_up")]:
+            w8 = synth.quantized_weight(Q8_0, N, K, 0, 0)
+            nb = mq.weight_bytes(Q8_0, N, K)
+            wc = [to_dev(w8) for _ in range(copies_for(nb))]
+            x8 = torch.from_numpy(synth.activations(1, K, 0)[0]).to(dev)
+            y8 = torch.empty(N, dtype=torch.float32, device=dev)
+            us = timer.per_launch_us([lambda W=W: mq.gemv(W, Q8_0, x8, N, K, y=y8) for W in wc], reps)
+            sec[f"gemv_q8_0_{tag}_{N}x{K}"] = {"us": round(us, 3), "GBps": round(nb / us / 1e3, 1)}
+            del wc
+        qa_bytes = PREFILL_M * 3584 * 4
+        sec["quantize_act_512x3584"] = {"us": round(avg_us["quantize_act"], 3),
+                                        "GBps_in": round(qa_bytes / avg_us["quantize_act"] / 1e3, 1)}
+        result["secondary"] = sec
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w_host["ffn_up"], w_host["ffn_down"], x_dec["ffn_up"],
                                               x_dec["ffn_down"])

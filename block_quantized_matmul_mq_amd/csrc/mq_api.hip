@@ -104,6 +104,11 @@ const char* mq_last_error(void) { return g_error.c_str(); }
 
 const char* mq_last_kernel(void) { return g_last_kernel; }
 
+int mq_device_lds_bytes(void) {
+    const DeviceInfo* info = device_info();
+    return info ? int(info->lds_per_block) : 0;
+}
+
 int mq_init(int device) {
     if (device < 0 || device >= kMaxDevices) return fail(MQ_ERR_ARG, "mq_init: device %d out of range", device);
     int count = 0;
@@ -122,7 +127,17 @@ int mq_init(int device) {
                     prop.gcnArchName);
     DeviceInfo& info = g_devices[device];
     info.cu_count = prop.multiProcessorCount;
-    info.lds_per_block = prop.sharedMemPerBlock;
+    // the largest LDS a workgroup may use once its kernel opts in (160 KB on gfx950)
+    size_t lds = prop.sharedMemPerBlockOptin;
+    if (lds < prop.sharedMemPerBlock) lds = prop.sharedMemPerBlock;
+    if (prop.maxSharedMemoryPerMultiProcessor && lds > prop.maxSharedMemoryPerMultiProcessor)
+        lds = prop.maxSharedMemoryPerMultiProcessor;
+    info.lds_per_block = lds;
+    // Kernel attributes are set here, once, so that no call ever sets one inside a stream capture.
+    e = gemv_set_attributes(lds);
+    if (e != hipSuccess)
+        return fail(MQ_ERR_DEVICE, "mq_init: setting the GEMV LDS limit to %zu bytes failed: %s", lds,
+                    hipGetErrorName(e));
     info.ready = true;
     return MQ_OK;
 }
@@ -182,6 +197,9 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
                     (const void*)x, (void*)y);
     rc = check_ready(fn);
     if (rc) return rc;
+    if (gemv_tile_units(type, K, device_info()->lds_per_block) <= 0)
+        return fail(MQ_ERR_SHAPE, "%s: K=%lld does not fit the %zu-byte LDS of this device", fn, (long long)K,
+                    device_info()->lds_per_block);
     const char* kernel = "gemv";
     hipError_t e = launch_gemv(type, static_cast<const uint8_t*>(W), x, y, N, K, static_cast<hipStream_t>(stream),
                                &kernel);

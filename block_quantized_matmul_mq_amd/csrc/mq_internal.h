@@ -29,6 +29,8 @@ const DeviceInfo* device_info();  // null if mq_init has not succeeded on the cu
 // right after the launch).  Arguments are validated by the callers in mq_api.hip.
 hipError_t launch_quantize_act(const float* X, int8_t* codes, float* scales, int32_t* sums,
                                int64_t M, int64_t K, hipStream_t s);
+int gemv_tile_units(int type, int64_t K, size_t lds_limit);
+hipError_t gemv_set_attributes(size_t lds_limit);
 hipError_t launch_gemv(int type, const uint8_t* W, const float* x, float* y, int64_t N, int64_t K,
                        hipStream_t s, const char** kernel_name);
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* codes, const float* scales,

@@ -40,6 +40,7 @@ _SIGNATURES = {
     "mq_debug_gemm_blockdots": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                                ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                                ctypes.c_int64, ctypes.c_void_p]),
+    "mq_device_lds_bytes": (ctypes.c_int, []),
     "mq_last_error": (ctypes.c_char_p, []),
     "mq_last_kernel": (ctypes.c_char_p, []),
     "mq_version": (ctypes.c_char_p, []),

@@ -77,7 +77,7 @@ extern "C" {
 #define MQ_ERR_NOINIT (-8) /* mq_init has not succeeded on the current device */
 
 /* Upper bounds accepted by the calls (sizes beyond them are MQ_ERR_SHAPE). */
-#define MQ_MAX_K 65536          /* inputs per row                 */
+#define MQ_MAX_K 32768          /* inputs per row                 */
 #define MQ_MAX_N (1 << 24)      /* output rows                    */
 #define MQ_MAX_M (1 << 20)      /* activation rows for mq_gemm    */
 
@@ -154,6 +154,9 @@ int mq_debug_gemm_blockdots(const void* W, int type, const void* Xq, int32_t* D,
  * string if none).  Valid until the next failing call on the same thread.
  */
 const char* mq_last_error(void);
+
+/* LDS bytes one workgroup may use on the current device (0 before mq_init). */
+int mq_device_lds_bytes(void);
 
 /* Name of the kernel the last successful launching call on this thread ran
  * (for tests that must prove which path executed). */

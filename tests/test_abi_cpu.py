@@ -64,7 +64,7 @@ def test_quantize_act_refusals():
     assert "multiple of 32" in mq.last_error()
     assert lib.mq_quantize_act(FAKE + 4, FAKE, 4, 64, None) == -5
     assert lib.mq_quantize_act(FAKE, FAKE + 16, 4, 64, None) == -5
-    assert lib.mq_quantize_act(FAKE, FAKE, 4, 1 << 20, None) == -2
+    assert lib.mq_quantize_act(FAKE, FAKE, 4, 1 << 16, None) == -2
 
 
 def test_gemv_refusals():

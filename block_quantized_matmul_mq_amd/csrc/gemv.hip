@@ -40,22 +40,43 @@ __device__ __forceinline__ float combine3(int a2, int a1, int a0) {
     return fmaf(float(a2), 65536.0f, fmaf(float(a1), 256.0f, float(a0)));
 }
 
+// Staged x (LDS).  Each plane holds one signed digit per value, grouped in
+// 16-value chunks laid out unit-major: chunk k of unit u sits at byte
+// (k * S + u) * 16 with S = units + 1.  Lanes own consecutive units, so one
+// ds_read_b128 per lane touches consecutive 16-byte chunks: no bank conflicts.
 struct Stage {
-    const uint32_t* p0;   // digit planes, 4 values per dword
-    const uint32_t* p1;
-    const uint32_t* p2;
-    const int* ex;        // block exponent e_b (x = 2^e_b * v)
-    const float* sum32;   // f32 sum of x per 32-block (Q4_K)
-    const float* sum16;   // f32 sum of x per 16-value run (Q6_K)
+    const uint8_t* p0;
+    const uint8_t* p1;
+    const uint8_t* p2;
+    int S;               // chunk-row stride, in chunks
+    const int* ex;       // block exponent: per 32-block (Q4_K, Q8_0), per (unit, t) (Q6_K)
+    const float* sums;   // f32 sum of x: per 32-block (Q4_K), per (unit, t) 16-run (Q6_K)
+
+    __device__ void chunk(int k, int u, uint4& a, uint4& b, uint4& c) const {
+        const int off = (k * S + u) * 16;
+        a = *reinterpret_cast<const uint4*>(p0 + off);
+        b = *reinterpret_cast<const uint4*>(p1 + off);
+        c = *reinterpret_cast<const uint4*>(p2 + off);
+    }
 };
+
+// Dot of 16 codes (4 dwords, one byte each) with one staged chunk, per plane.
+__device__ __forceinline__ void dot16(const uint32_t* c, const uint4& a, const uint4& b, const uint4& e,
+                                      int& s0, int& s1, int& s2) {
+    s0 = sdot4(c[0], a.x, s0); s0 = sdot4(c[1], a.y, s0); s0 = sdot4(c[2], a.z, s0); s0 = sdot4(c[3], a.w, s0);
+    s1 = sdot4(c[0], b.x, s1); s1 = sdot4(c[1], b.y, s1); s1 = sdot4(c[2], b.z, s1); s1 = sdot4(c[3], b.w, s1);
+    s2 = sdot4(c[0], e.x, s2); s2 = sdot4(c[1], e.y, s2); s2 = sdot4(c[2], e.z, s2); s2 = sdot4(c[3], e.w, s2);
+}
 
 // ---------------------------------------------------------------- Q4_K
 // Unit u of a row: super-block u/4, 64-value group c = u%4 (sub-blocks 2c and
 // 2c+1).  Bytes: 16-byte header (d, dmin, packed scales) and the 32 code bytes
 // at 16 + 32c; byte i holds the code of value 64c+i (low nibble) and of value
-// 64c+32+i (high nibble).
+// 64c+32+i (high nibble).  Staged chunks 0,1 hold values 64u..64u+31 (the low
+// nibbles), chunks 2,3 values 64u+32..64u+63.
 struct UnitQ4K {
     static constexpr int kValues = 64;
+    static constexpr int kChunks = 4;
     uint4 hd, q0, q1;
 
     __device__ void load(const uint8_t* __restrict__ row, int u) {
@@ -66,59 +87,57 @@ struct UnitQ4K {
         q1 = qs[1];
     }
 
-    // exact dot of 32 codes (8 dwords) with the 32 staged values starting at dword w0
-    __device__ static int run_dot(const uint32_t (&c)[8], const Stage& st, int w0) {
-        const uint4* a = reinterpret_cast<const uint4*>(st.p0 + w0);
-        const uint4* b = reinterpret_cast<const uint4*>(st.p1 + w0);
-        const uint4* e = reinterpret_cast<const uint4*>(st.p2 + w0);
+    // exact sum of code * v over a 32-value run: int32 (|s2| <= 32 * 15 * 32)
+    __device__ static int run_dot(const uint32_t (&c)[8], const Stage& st, int k0, int uu) {
         int s0 = 0, s1 = 0, s2 = 0;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const uint4 x0 = a[k], x1 = b[k], x2 = e[k];
-            s0 = sdot4(c[4 * k + 0], x0.x, s0); s0 = sdot4(c[4 * k + 1], x0.y, s0);
-            s0 = sdot4(c[4 * k + 2], x0.z, s0); s0 = sdot4(c[4 * k + 3], x0.w, s0);
-            s1 = sdot4(c[4 * k + 0], x1.x, s1); s1 = sdot4(c[4 * k + 1], x1.y, s1);
-            s1 = sdot4(c[4 * k + 2], x1.z, s1); s1 = sdot4(c[4 * k + 3], x1.w, s1);
-            s2 = sdot4(c[4 * k + 0], x2.x, s2); s2 = sdot4(c[4 * k + 1], x2.y, s2);
-            s2 = sdot4(c[4 * k + 2], x2.z, s2); s2 = sdot4(c[4 * k + 3], x2.w, s2);
-        }
-        // |s2| <= 32 * 15 * 32, so the int32 combination cannot overflow
+        uint4 a, b, e;
+        st.chunk(k0, uu, a, b, e);
+        dot16(c, a, b, e, s0, s1, s2);
+        st.chunk(k0 + 1, uu, a, b, e);
+        dot16(c + 4, a, b, e, s0, s1, s2);
         return (s2 << 16) + (s1 << 8) + s0;
     }
 
-    __device__ float dot(const Stage& st, int u) const {
+    __device__ float dot(const Stage& st, int uu, int u) const {
         const int c = u & 3;
-        const int blk0 = 8 * (u >> 2) + 2 * c;   // 32-block index of sub-block 2c
-        const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
         uint32_t lo[8], hi[8];
+        const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             lo[k] = w[k] & 0x0F0F0F0Fu;
             hi[k] = (w[k] >> 4) & 0x0F0F0F0Fu;
         }
-        const int ilo = run_dot(lo, st, 8 * blk0);
-        const int ihi = run_dot(hi, st, 8 * blk0 + 8);
+        const int ilo = run_dot(lo, st, 0, uu);
+        const int ihi = run_dot(hi, st, 2, uu);
+        // 6-bit (scale, min) of sub-blocks 2c, 2c+1, two per halfword, no branches:
+        // c < 2 reads bytes 2c,2c+1 of the first two dwords; c >= 2 assembles from all three.
+        const uint32_t sh = 16u * uint32_t(c & 1);
+        const uint32_t t0 = hd.y >> sh, t1 = hd.z >> sh, t2 = hd.w >> sh;
+        const uint32_t sc_hi = (t2 & 0x0F0Fu) | ((t0 >> 2) & 0x3030u);
+        const uint32_t mn_hi = ((t2 >> 4) & 0x0F0Fu) | ((t1 >> 2) & 0x3030u);
+        const uint32_t scp = c >= 2 ? sc_hi : (t0 & 0x3F3Fu);
+        const uint32_t mnp = c >= 2 ? mn_hi : (t1 & 0x3F3Fu);
         const float d = half_bits_to_float(hd.x & 0xFFFFu);
         const float dmin = half_bits_to_float(hd.x >> 16);
-        uint32_t sc0, m0, sc1, m1;
-        q4k_scale_min(hd.y, hd.z, hd.w, 2 * c, sc0, m0);
-        q4k_scale_min(hd.y, hd.z, hd.w, 2 * c + 1, sc1, m1);
-        const float codes = ldexpf(float(sc0) * float(ilo), st.ex[blk0]) +
-                            ldexpf(float(sc1) * float(ihi), st.ex[blk0 + 1]);
-        const float mins = fmaf(float(m0), st.sum32[blk0], float(m1) * st.sum32[blk0 + 1]);
+        const int2 e2 = *reinterpret_cast<const int2*>(st.ex + 2 * uu);
+        const float2 s2 = *reinterpret_cast<const float2*>(st.sums + 2 * uu);
+        const float codes = ldexpf(ubyte_f<0>(scp) * float(ilo), e2.x) + ldexpf(ubyte_f<1>(scp) * float(ihi), e2.y);
+        const float mins = fmaf(ubyte_f<0>(mnp), s2.x, ubyte_f<1>(mnp) * s2.y);
         return fmaf(d, codes, -dmin * mins);
     }
 };
 
 // ---------------------------------------------------------------- Q6_K
 // Unit u: super-block u/4, half h = (u/2)%2, lane run l in [l0, l0+16) with
-// l0 = 16*(u%2): values 128h + 32t + l for t < 4 (16 each, one sub-scale each).
+// l0 = 16*(u%2): values 128h + 32t + l for t < 4 (16 each, one sub-scale each);
+// staged chunk t of the unit holds exactly those 16 values.
 // Low 4 bits: ql[64h + l] (t = 0 low nibble, t = 2 high nibble) and
 // ql[64h + 32 + l] (t = 1, 3); high 2 bits: bits 2t..2t+1 of qh[32h + l].
 // Blocks are 210 bytes, so a block starts on a 2-byte boundary: every segment
 // is read as naturally aligned dwords and realigned with v_alignbyte.
 struct UnitQ6K {
     static constexpr int kValues = 64;
+    static constexpr int kChunks = 4;
     uint32_t a[5], b[5], hq[5], s[3];
     uint32_t dbits;
     uint32_t shift;
@@ -142,9 +161,8 @@ struct UnitQ6K {
         dbits = load_u16(blk + 208);
     }
 
-    __device__ float dot(const Stage& st, int u) const {
-        const int h = (u >> 1) & 1, hi16 = u & 1, l0 = 16 * hi16;
-        const int base = 256 * (u >> 2) + 128 * h + l0;   // value index of t = 0, l = l0
+    __device__ float dot(const Stage& st, int uu, int u) const {
+        const int hi16 = u & 1;
         uint32_t A[4], B[4], H[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -153,42 +171,42 @@ struct UnitQ6K {
             H[i] = align_byte(hq[i + 1], hq[i], shift);
         }
         const uint32_t s0 = align_byte(s[1], s[0], shift), s1 = align_byte(s[2], s[1], shift);
+        const int4 e4 = *reinterpret_cast<const int4*>(st.ex + 4 * uu);
+        const float4 m4 = *reinterpret_cast<const float4*>(st.sums + 4 * uu);
+        const int ev[4] = {e4.x, e4.y, e4.z, e4.w};
+        const float sv[4] = {m4.x, m4.y, m4.z, m4.w};
         float acc = 0.f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int v0 = base + 32 * t;               // 16 values v0 .. v0+15
-            const uint4 x0 = *reinterpret_cast<const uint4*>(st.p0 + (v0 >> 2));
-            const uint4 x1 = *reinterpret_cast<const uint4*>(st.p1 + (v0 >> 2));
-            const uint4 x2 = *reinterpret_cast<const uint4*>(st.p2 + (v0 >> 2));
-            const uint32_t xs0[4] = {x0.x, x0.y, x0.z, x0.w};
-            const uint32_t xs1[4] = {x1.x, x1.y, x1.z, x1.w};
-            const uint32_t xs2[4] = {x2.x, x2.y, x2.z, x2.w};
-            int d0 = 0, d1 = 0, d2 = 0;
+            uint32_t code[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t ql = (t & 1) ? B[i] : A[i];
                 const uint32_t lo = (t < 2) ? ql : (ql >> 4);
                 const uint32_t hb = (H[i] >> (2 * t)) & 0x03030303u;
-                const uint32_t code = (lo & 0x0F0F0F0Fu) | (hb << 4);   // bytes: codes 0..63
-                d0 = sdot4(code, xs0[i], d0);
-                d1 = sdot4(code, xs1[i], d1);
-                d2 = sdot4(code, xs2[i], d2);
+                code[i] = (lo & 0x0F0F0F0Fu) | (hb << 4);   // bytes: codes 0..63
             }
+            uint4 xa, xb, xc;
+            st.chunk(t, uu, xa, xb, xc);
+            int d0 = 0, d1 = 0, d2 = 0;
+            dot16(code, xa, xb, xc, d0, d1, d2);
             // sum((c - 32) * x) = 2^e * sum(c * v) - 32 * sum(x)
-            const float cv = ldexpf(combine3(d2, d1, d0), st.ex[v0 >> 5]);
+            const float cv = ldexpf(combine3(d2, d1, d0), ev[t]);
             const int g = 2 * t + hi16;                  // sub-scale byte within this half
             const uint32_t word = g < 4 ? s0 : s1;
             const float sc = float(int32_t(word << (24 - 8 * (g & 3))) >> 24);
-            acc = fmaf(sc, fmaf(-32.0f, st.sum16[v0 >> 4], cv), acc);
+            acc = fmaf(sc, fmaf(-32.0f, sv[t], cv), acc);
         }
         return half_bits_to_float(dbits) * acc;
     }
 };
 
 // ---------------------------------------------------------------- Q8_0
-// Unit u = block u (34 bytes: f16 d, 32 int8 codes), 2-byte aligned.
+// Unit u = block u (34 bytes: f16 d, 32 int8 codes), 2-byte aligned; staged
+// chunks 0,1 hold its 32 values.
 struct UnitQ80 {
     static constexpr int kValues = 32;
+    static constexpr int kChunks = 2;
     uint32_t w[9];
     uint32_t odd;
 
@@ -201,28 +219,18 @@ struct UnitQ80 {
         for (int i = 0; i < 9; ++i) w[i] = p[i];
     }
 
-    __device__ float dot(const Stage& st, int u) const {
+    __device__ float dot(const Stage& st, int uu, int u) const {
         const float d = half_bits_to_float(odd ? (w[0] >> 16) : (w[0] & 0xFFFFu));
-        const uint4* a = reinterpret_cast<const uint4*>(st.p0 + 8 * u);
-        const uint4* b = reinterpret_cast<const uint4*>(st.p1 + 8 * u);
-        const uint4* e = reinterpret_cast<const uint4*>(st.p2 + 8 * u);
+        uint32_t c[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = odd ? w[i + 1] : align_byte(w[i + 1], w[i], 2);
         int s0 = 0, s1 = 0, s2 = 0;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const uint4 x0 = a[k], x1 = b[k], x2 = e[k];
-            const uint32_t xs0[4] = {x0.x, x0.y, x0.z, x0.w};
-            const uint32_t xs1[4] = {x1.x, x1.y, x1.z, x1.w};
-            const uint32_t xs2[4] = {x2.x, x2.y, x2.z, x2.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int i = 4 * k + j;
-                const uint32_t c = odd ? w[i + 1] : align_byte(w[i + 1], w[i], 2);
-                s0 = sdot4(c, xs0[j], s0);
-                s1 = sdot4(c, xs1[j], s1);
-                s2 = sdot4(c, xs2[j], s2);
-            }
-        }
-        return d * ldexpf(combine3(s2, s1, s0), st.ex[u]);
+        uint4 a, b, e;
+        st.chunk(0, uu, a, b, e);
+        dot16(c, a, b, e, s0, s1, s2);
+        st.chunk(1, uu, a, b, e);
+        dot16(c + 4, a, b, e, s0, s1, s2);
+        return d * ldexpf(combine3(s2, s1, s0), st.ex[uu]);
     }
 };
 
@@ -255,24 +263,28 @@ __device__ __forceinline__ uint32_t digits(float x, int k) {
     return (__float_as_uint(f) - 0x4ABF7F80u) ^ 0x00808080u;
 }
 
-// LDS layout (dynamic): planes 3 x K bytes | block exponents int [K/32] |
-// sums f32 [K/32] (Q4_K) or [K/16] (Q6_K) | partials f32 [tile_units]
+// LDS layout (dynamic): three digit planes of plane_bytes(K) | block exponents
+// int | sums f32 | partials f32 [tile_units]  (see lds_layout below)
 template <int QT, int kThreads, int kSlots>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restrict__ W,
                                                         const float* __restrict__ x,
                                                         float* __restrict__ y, int N, int K,
                                                         int64_t row_bytes, int tile_units) {
     using Unit = typename UnitOf<QT>::T;
-    extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
-    uint32_t* p0 = smem;
-    uint32_t* p1 = p0 + (K >> 2);
-    uint32_t* p2 = p1 + (K >> 2);
-    int* ex = reinterpret_cast<int*>(p2 + (K >> 2));
-    float* sums = reinterpret_cast<float*>(ex + (K >> 5));
-    float* part = sums + (QT == kQ6_K ? (K >> 4) : (QT == kQ4_K ? (K >> 5) : 0));
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int U = K / Unit::kValues;
+    const int S = U + 1;
+    const int plane = Unit::kChunks * S * 16;
+    uint8_t* p0 = smem;
+    uint8_t* p1 = p0 + plane;
+    uint8_t* p2 = p1 + plane;
+    int* ex = reinterpret_cast<int*>(p2 + plane);
+    const int nex = (QT == kQ6_K) ? 4 * U : (K >> 5);
+    float* sums = reinterpret_cast<float*>(ex + nex);
+    const int nsum = (QT == kQ6_K) ? 4 * U : (QT == kQ4_K ? (K >> 5) : 0);
+    float* part = sums + nsum;
 
     const int tid = threadIdx.x;
-    const int U = K / Unit::kValues;
     const int r_begin = int((int64_t(blockIdx.x) * N) / gridDim.x);
     const int r_end = int((int64_t(blockIdx.x + 1) * N) / gridDim.x);
     const int rows_per_tile = max(1, tile_units / U);
@@ -303,26 +315,43 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
         }
     };
 
+    // Every slot load is issued unconditionally (a slot past the end of the tile
+    // re-reads the tile's first unit, which is valid and cached), so the number
+    // of loads in flight is static and the compiler can wait for exactly the
+    // slot it needs (loads complete in issue order) instead of for all of them.
     Unit buf[kSlots];
     Cursor ld, cp;
     int t0 = r_begin;
+    const uint8_t* tile = W + int64_t(t0) * row_bytes;
+    int units = 0;
+    auto load_next = [&](int j) {
+        const bool live = ld.f < units;
+        buf[j].load(live ? ld.row : tile, live ? ld.u : 0);
+        advance(ld);
+    };
     auto prime = [&](int tfirst) {
-        const int units = min(rows_per_tile, r_end - tfirst) * U;
-        const uint8_t* tile = W + int64_t(tfirst) * row_bytes;
+        units = min(rows_per_tile, r_end - tfirst) * U;
+        tile = W + int64_t(tfirst) * row_bytes;
         start(ld, tile);
         start(cp, tile);
 #pragma unroll
-        for (int j = 0; j < kSlots; ++j) {
-            if (ld.f < units) buf[j].load(ld.row, ld.u);
-            advance(ld);
-        }
+        for (int j = 0; j < kSlots; ++j) load_next(j);
     };
-    // Issue the first tile's weight loads before staging x.
+    // x first: loads complete in issue order, so x must be requested before the
+    // weight prefetch or staging it would wait for all of that prefetch.
+    constexpr int kEarly = 32768 / 4 / kThreads;   // covers every K the LDS can stage
+    const int nquads = K >> 2;
+    float4 xe[kEarly];
+#pragma unroll
+    for (int e = 0; e < kEarly; ++e) {
+        const int i = tid + e * kThreads;
+        if (i < nquads) xe[e] = reinterpret_cast<const float4*>(x)[i];
+    }
+    // Then the first tile's weight loads.
     prime(t0);
 
     // Stage x: 8 lanes per 32-block, 4 values (one float4) per lane.
-    for (int i = tid; i < (K >> 2); i += kThreads) {
-        const float4 v = reinterpret_cast<const float4*>(x)[i];
+    auto stage = [&](int i, const float4 v) {
         float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
         a = fmaxf(a, __shfl_xor(a, 1, 64));
         a = fmaxf(a, __shfl_xor(a, 2, 64));
@@ -331,39 +360,60 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
         const int k = kFracBits - __builtin_amdgcn_frexp_expf(a);
         uint32_t d0, d1, d2;
         transpose_digits(digits(v.x, k), digits(v.y, k), digits(v.z, k), digits(v.w, k), d0, d1, d2);
-        p0[i] = d0;
-        p1[i] = d1;
-        p2[i] = d2;
-        float s = (v.x + v.y) + (v.z + v.w);
+        // unit and chunk of values 4i .. 4i+3
+        const int val = 4 * i;
+        int uu, kc;
         if constexpr (QT == kQ6_K) {
-            s += __shfl_xor(s, 1, 64);
-            s += __shfl_xor(s, 2, 64);
-            if ((i & 3) == 0) sums[i >> 2] = s;
+            uu = ((val >> 8) << 2) | (((val >> 7) & 1) << 1) | ((val >> 4) & 1);
+            kc = (val >> 5) & 3;
         } else if constexpr (QT == kQ4_K) {
-            s += __shfl_xor(s, 1, 64);
-            s += __shfl_xor(s, 2, 64);
-            s += __shfl_xor(s, 4, 64);
-            if ((i & 7) == 0) sums[i >> 3] = s;
+            uu = val >> 6;
+            kc = (val >> 4) & 3;
+        } else {
+            uu = val >> 5;
+            kc = (val >> 4) & 1;
         }
-        if ((i & 7) == 0) ex[i >> 3] = -k;
+        const int off = (kc * S + uu) * 16 + 4 * (i & 3);
+        *reinterpret_cast<uint32_t*>(p0 + off) = d0;
+        *reinterpret_cast<uint32_t*>(p1 + off) = d1;
+        *reinterpret_cast<uint32_t*>(p2 + off) = d2;
+        float sm = (v.x + v.y) + (v.z + v.w);
+        sm += __shfl_xor(sm, 1, 64);
+        sm += __shfl_xor(sm, 2, 64);
+        if constexpr (QT == kQ6_K) {
+            if ((i & 3) == 0) {            // one 16-run = chunk kc of unit uu
+                sums[4 * uu + kc] = sm;
+                ex[4 * uu + kc] = -k;
+            }
+        } else {
+            if constexpr (QT == kQ4_K) {
+                sm += __shfl_xor(sm, 4, 64);
+                if ((i & 7) == 0) sums[i >> 3] = sm;
+            }
+            if ((i & 7) == 0) ex[i >> 3] = -k;
+        }
+    };
+    // (groups of 8 lanes are either all below nquads or all above: K % 32 == 0)
+#pragma unroll
+    for (int e = 0; e < kEarly; ++e) {
+        const int i = tid + e * kThreads;
+        if (i < nquads) stage(i, xe[e]);
     }
+    for (int i = tid + kEarly * kThreads; i < nquads; i += kThreads)
+        stage(i, reinterpret_cast<const float4*>(x)[i]);
     __syncthreads();
 
-    const Stage st{p0, p1, p2, ex, sums, sums};
+    const Stage st{p0, p1, p2, S, ex, sums};
 
     for (; t0 < r_end; t0 += rows_per_tile) {
         const int rows = min(rows_per_tile, r_end - t0);
-        const int units = rows * U;
 
         for (int base = 0; base < units; base += kSlots * kThreads) {
 #pragma unroll
             for (int j = 0; j < kSlots; ++j) {
-                if (cp.f < units) {
-                    part[cp.f] = buf[j].dot(st, cp.u);
-                    advance(cp);
-                    if (ld.f < units) buf[j].load(ld.row, ld.u);
-                    advance(ld);
-                }
+                if (cp.f < units) part[cp.f] = buf[j].dot(st, cp.u, cp.u);
+                advance(cp);
+                load_next(j);
             }
         }
         // Issue the next tile's first loads before summing this one.
@@ -391,9 +441,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
 }
 
 size_t fixed_lds_bytes(int type, int64_t K) {
-    size_t b = size_t(K) * 3 + size_t(K / 32) * 4;
-    if (type == kQ4_K) b += size_t(K / 32) * 4;
-    if (type == kQ6_K) b += size_t(K / 16) * 4;
+    const int64_t vals = type == kQ8_0 ? 32 : 64;
+    const int64_t chunks = type == kQ8_0 ? 2 : 4;
+    const int64_t U = K / vals;
+    size_t b = 3 * size_t(chunks * (U + 1) * 16);            // digit planes
+    b += size_t(type == kQ6_K ? 4 * U : K / 32) * 4;         // exponents
+    if (type == kQ4_K) b += size_t(K / 32) * 4;              // sums per 32-block
+    if (type == kQ6_K) b += size_t(4 * U) * 4;               // sums per (unit, 16-run)
     return b;
 }
 

@@ -18,10 +18,17 @@ Printed JSON line (one GPU):
   value        Q4_K GEMV weight GB/s: GGUF payload bytes of the two decode
                GEMVs / their summed kernel time
   mmq_prefill_tops   2*M*N*K of the four MMQ launches / their kernel time
-  roofline     the Q4_K GEMV against 8 TB/s HBM
+  roofline     the Q4_K GEMV against 8 TB/s HBM: achieved = algorithmic bytes
+               (payload + x + y) per launch / mean launch time; traffic = HBM
+               bytes per launch from the committed rocprofv3 FETCH_SIZE /
+               WRITE_SIZE summary under profiles/, null once the kernel
+               sources differ from the ones the counters were taken on
   roofline_mmq the ffn_up MMQ against 5.0 POP/s dense int8 MFMA
   secondary    Q6_K vocab-head and Q8_0 GEMV GB/s, the quantizer
   cpu_baseline the CPU oracle's GEMV on the same ffn_up + ffn_down weights
+
+--counters skips timing: every kernel of the step runs a few times eagerly,
+next to a plain 256 MiB device copy that calibrates the HBM byte counters.
 """
 
 import argparse
@@ -34,6 +41,7 @@ import numpy as np
 HBM_PEAK_GBPS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 LLC_BYTES = 256 * 2 ** 20
+COPY_REF_BYTES = 256 * 2 ** 20
 
 Q8_0, Q4_K, Q6_K = 8, 12, 14
 DECODE = [("ffn_up", 18944, 3584), ("ffn_down", 3584, 18944)]
@@ -48,7 +56,34 @@ def parse():
     p.add_argument("--warmup", type=int, default=3, help="untimed replays before timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--counters", action="store_true",
+                   help="no timing: launch each kernel of the step a few times eagerly, plus a plain "
+                        "device copy of known size, for rocprofv3 --pmc passes")
     return p.parse_args()
+
+
+def recorded_traffic(summary, sources):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None.
+
+    The summary records FETCH_SIZE and WRITE_SIZE passes (scaled by a plain copy of
+    known size) and the sha256 of the kernel sources they were taken on; once those
+    sources change the figure no longer describes the kernel and None is returned.
+    """
+    import hashlib
+    import os
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        fields = dict(line.split(": ", 1) for line in open(os.path.join(root, "profiles", summary)).read().splitlines()
+                      if line.startswith(("kernel_source_sha256: ", "traffic_bytes_per_launch: ")))
+    except OSError:
+        return None
+    h = hashlib.sha256()
+    for src in sources:
+        with open(os.path.join(root, "block_quantized_matmul_mq_amd", "csrc", src), "rb") as f:
+            h.update(f.read())
+    if fields.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def copies_for(nbytes):
@@ -164,6 +199,21 @@ def main():
         out += [mmq_launch(name, N, K, c) for name, N, K in PREFILL]
         return out
 
+    if args.counters:
+        # reference copy: 256 MiB read + 256 MiB written, to calibrate FETCH_SIZE / WRITE_SIZE
+        ref_src = torch.empty(COPY_REF_BYTES, dtype=torch.uint8, device=dev)
+        ref_dst = torch.empty_like(ref_src)
+        for _ in range(3):
+            ref_dst.copy_(ref_src)
+        for c in range(min(ncopy, 4)):
+            for fn in step_launches(c):
+                fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": True, "copy_ref_bytes": COPY_REF_BYTES,
+                          "gemv_payload_bytes": {n: mq.weight_bytes(Q4_K, N, K) for n, N, K in DECODE},
+                          "kernel_names": kernel_names}), flush=True)
+        return
+
     # eager warmup (also sets the kernel names), then the timed step graph
     for c in range(ncopy):
         for fn in step_launches(c):
@@ -198,8 +248,11 @@ def main():
         avg_us[f"mmq_{name}"] = timer.per_launch_us([mmq_launch(name, N, K, c % ncopy) for c in range(4)], reps)
 
     gemv_bytes = sum(mq.weight_bytes(Q4_K, N, K) for _, N, K in DECODE)
+    # algorithmic bytes of one GEMV launch: GGUF payload + f32 x + f32 y (the same for both shapes)
+    gemv_alg_bytes = mq.weight_bytes(Q4_K, 18944, 3584) + 4 * (18944 + 3584)
     gemv_s = sum(avg_us[f"gemv_{n}"] for n, _, _ in DECODE) * 1e-6
     gemv_gbps = gemv_bytes / gemv_s / 1e9
+    gemv_alg_gbps = len(DECODE) * gemv_alg_bytes / gemv_s / 1e9
     mmq_ops = sum(2 * PREFILL_M * N * K for _, N, K in PREFILL)
     mmq_s = sum(avg_us[f"mmq_{n}"] for n, _, _ in PREFILL) * 1e-6
     mmq_tops = mmq_ops / mmq_s / 1e12
@@ -228,12 +281,15 @@ def main():
         },
         "mmq_prefill_tops": round(mmq_tops, 2),
         "mmq_dtype": "i8 x i8 -> i32 block dots, f32 scales",
-        "roofline": {"bound": "hbm", "achieved": round(gemv_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+        "roofline": {"bound": "hbm", "achieved": round(gemv_alg_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gemv_alg_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": recorded_traffic("gemv_q4k_7b_ffn_hbm_traffic.txt", ["gemv.hip", "mq_device.h"]),
+                     "algorithmic_bytes_per_launch": gemv_alg_bytes,
                      "kernel": "gemv<q4_K> (ffn_up + ffn_down)",
                      "ffn_up_GBps": round(up_gbps, 1), "ffn_down_GBps": round(down_gbps, 1)},
         "roofline_mmq": {"bound": "mfma", "achieved": round(mmq_up_tops, 2), "peak": INT8_PEAK_TOPS,
-                         "unit": "TOP/s", "frac": round(mmq_up_tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                         "unit": "TOP/s", "frac": round(mmq_up_tops / INT8_PEAK_TOPS, 4),
+                         "traffic": recorded_traffic("mmq_q4k_512x18944x3584_counters.txt", ["mmq.hip", "mq_device.h"]),
                          "kernel": "mmq<q4_K> ffn_up M=512 18944x3584"},
         "kernel_avg_us": {lab: round(v, 3) for lab, v in avg_us.items()},
         "kernel_names": kernel_names,

@@ -172,6 +172,8 @@ def main():
     X_dev = torch.from_numpy(X_pre).to(dev)
     Xq = torch.empty(mq.act_bytes(PREFILL_M, 3584), dtype=torch.uint8, device=dev)
     Y_dev = {name: torch.empty((PREFILL_M, N), dtype=torch.float32, device=dev) for name, N, _ in PREFILL}
+    scratch = {name: torch.empty(max(mq.gemm_scratch_bytes(Q4_K, PREFILL_M, N, K), 256), dtype=torch.uint8,
+                                 device=dev) for name, N, K in PREFILL}
     torch.cuda.synchronize()
 
     kernel_names = {}
@@ -189,7 +191,7 @@ def main():
         W = copies["ffn_up"][c] if name == "ffn_up" else w_pre[name]
 
         def fn():
-            mq.gemm(W, Q4_K, Xq, PREFILL_M, N, K, Y=Y_dev[name])
+            mq.gemm(W, Q4_K, Xq, PREFILL_M, N, K, Y=Y_dev[name], scratch=scratch[name])
             kernel_names[f"mmq_{name}"] = mq.last_kernel()
         return fn
 

@@ -30,6 +30,8 @@
 // Workgroups are numbered so that the ones sharing a weight tile run on the
 // same XCD (consecutive workgroup ids are dealt round-robin to the 8 XCDs, each
 // with its own L2): a weight tile then comes from HBM once per XCD.
+#include <algorithm>
+
 #include "mq_device.h"
 #include "mq_internal.h"
 
@@ -48,6 +50,8 @@ constexpr int KS = 128;        // K values per step
 constexpr int NB = KS / 32;    // 32-blocks per step
 constexpr int LDA = KS + 16;   // padded LDS row (bytes)
 constexpr int kXcds = 8;
+constexpr int kTargetWorkgroups = 512;   // two resident 256-thread workgroups on each of 256 CUs
+constexpr int kMinStepsPerSplit = 2;
 
 template <int QT> struct Groups { static constexpr int per_step = NB; };
 template <> struct Groups<kQ6_K> { static constexpr int per_step = 2 * NB; };
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
                                                      const int32_t* __restrict__ xsum,
                                                      float* __restrict__ Y, int32_t* __restrict__ dots,
                                                      int M, int N, int K, int64_t row_bytes,
-                                                     int tiles_m, int tiles_total) {
+                                                     int tiles_m, int tiles_n, int splits, int total_steps) {
     constexpr int NG = Groups<QT>::per_step;
     __shared__ __attribute__((aligned(16))) int8_t As[BM * LDA];
     __shared__ __attribute__((aligned(16))) int8_t Bs[BN * LDA];
@@ -265,13 +269,21 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
     __shared__ __attribute__((aligned(16))) float dws[NG][BN];
     __shared__ __attribute__((aligned(16))) float mws[NB][BN];
 
-    // XCD-aware tile order: workgroups that land on one XCD take consecutive logical tiles.
+    // XCD-aware order: workgroups that land on one XCD take consecutive logical ids, and
+    // consecutive ids are the M-tiles of one (split, N-tile), which read the same weights.
     const int bid = blockIdx.x;
+    const int total = int(gridDim.x);
     int logical = bid;
-    if (tiles_total % kXcds == 0) logical = (bid % kXcds) * (tiles_total / kXcds) + bid / kXcds;
+    if (total % kXcds == 0) logical = (bid % kXcds) * (total / kXcds) + bid / kXcds;
     const int tm = logical % tiles_m;
-    const int tn = logical / tiles_m;
+    const int tn = (logical / tiles_m) % tiles_n;
+    const int split = logical / (tiles_m * tiles_n);
     const int m0 = tm * BM, n0 = tn * BN;
+    // K range of this split: steps [s0, s1) of KS values; split-K partials go to slice
+    // `split` of the partial buffer (Y itself when there is one split).
+    const int kbeg = int(int64_t(split) * total_steps / splits) * KS;
+    const int kend = min(int(int64_t(split + 1) * total_steps / splits) * KS, K);
+    if (splits > 1 && !DUMP) Y += int64_t(split) * M * N;
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -290,13 +302,13 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     StepRegs<QT> regs;
-    regs.load(W, row_bytes, codes, xscale, xsum, m0, n0, M, N, K, 0);
+    regs.load(W, row_bytes, codes, xscale, xsum, m0, n0, M, N, K, kbeg);
 
-    for (int k0 = 0; k0 < K; k0 += KS) {
+    for (int k0 = kbeg; k0 < kend; k0 += KS) {
         __syncthreads();   // the previous step's LDS reads are done
         regs.store(As, Bs, dxs, txs, dws, mws, k0, K);
         __syncthreads();
-        if (k0 + KS < K) regs.load(W, row_bytes, codes, xscale, xsum, m0, n0, M, N, K, k0 + KS);
+        if (k0 + KS < kend) regs.load(W, row_bytes, codes, xscale, xsum, m0, n0, M, N, K, k0 + KS);
 
         if constexpr (QT != kQ6_K) {
 #pragma unroll
@@ -427,38 +439,78 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
         }
 }
 
+// Sum of the split-K partials P[splits][count] in split order (deterministic).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, float* __restrict__ Y,
+                                                            int64_t count, int splits) {
+    const int64_t stride = int64_t(gridDim.x) * 256;
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < count; i += stride) {
+        float acc = P[i];
+        for (int s = 1; s < splits; ++s) acc += P[int64_t(s) * count + i];
+        Y[i] = acc;
+    }
+}
+
 template <int QT>
 hipError_t launch_typed(const uint8_t* W, const int8_t* codes, const float* xs, const int32_t* xsum,
-                        float* Y, int32_t* dots, int64_t M, int64_t N, int64_t K, int64_t row_bytes,
-                        hipStream_t s) {
+                        float* Y, int32_t* dots, float* partial, int64_t M, int64_t N, int64_t K,
+                        int64_t row_bytes, hipStream_t s) {
+    const MmqPlan plan = mmq_plan(QT, M, N, K);
     const int tiles_m = int((M + BM - 1) / BM);
     const int tiles_n = int((N + BN - 1) / BN);
-    const int total = tiles_m * tiles_n;
+    const int total = tiles_m * tiles_n * plan.splits;
     if (dots) {
         hipLaunchKernelGGL((mmq_kernel<QT, true>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, Y, dots,
-                           int(M), int(N), int(K), row_bytes, tiles_m, total);
-    } else {
-        hipLaunchKernelGGL((mmq_kernel<QT, false>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, Y,
-                           dots, int(M), int(N), int(K), row_bytes, tiles_m, total);
+                           int(M), int(N), int(K), row_bytes, tiles_m, tiles_n, plan.splits, plan.steps);
+        return hipGetLastError();
     }
+    float* out = plan.splits > 1 ? partial : Y;
+    hipLaunchKernelGGL((mmq_kernel<QT, false>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, out, dots,
+                       int(M), int(N), int(K), row_bytes, tiles_m, tiles_n, plan.splits, plan.steps);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || plan.splits == 1) return e;
+    const int64_t count = M * N;
+    const int64_t blocks = std::min<int64_t>((count + 255) / 256, 4096);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, partial, Y, count,
+                       plan.splits);
     return hipGetLastError();
 }
 
 }  // namespace
 
+MmqPlan mmq_plan(int /*type*/, int64_t M, int64_t N, int64_t K) {
+    // Enough workgroups to fill the chip: when the output has fewer tiles than about
+    // 3/4 of kTargetWorkgroups, K is split so that tiles x splits comes near it, with at
+    // least kMinStepsPerSplit K-steps per split.  A function of the shape alone, so the
+    // result does not depend on the device.
+    MmqPlan p;
+    p.steps = int((K + KS - 1) / KS);
+    p.splits = 1;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if (tiles * 4 < int64_t(kTargetWorkgroups) * 3) {
+        const int64_t want = kTargetWorkgroups / tiles;
+        p.splits = int(std::max<int64_t>(1, std::min<int64_t>(want, p.steps / kMinStepsPerSplit)));
+    }
+    return p;
+}
+
+size_t mmq_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
+    const MmqPlan p = mmq_plan(type, M, N, K);
+    return p.splits > 1 ? size_t(p.splits) * size_t(M) * size_t(N) * sizeof(float) : 0;
+}
+
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* codes, const float* xs, const int32_t* xsum,
-                      float* Y, int32_t* dots, int64_t M, int64_t N, int64_t K, hipStream_t s,
+                      float* Y, int32_t* dots, float* partial, int64_t M, int64_t N, int64_t K, hipStream_t s,
                       const char** name) {
     switch (type) {
         case kQ8_0:
             *name = "mmq<q8_0>";
-            return launch_typed<kQ8_0>(W, codes, xs, xsum, Y, dots, M, N, K, (K / 32) * 34, s);
+            return launch_typed<kQ8_0>(W, codes, xs, xsum, Y, dots, partial, M, N, K, (K / 32) * 34, s);
         case kQ4_K:
             *name = "mmq<q4_K>";
-            return launch_typed<kQ4_K>(W, codes, xs, xsum, Y, dots, M, N, K, (K / 256) * 144, s);
+            return launch_typed<kQ4_K>(W, codes, xs, xsum, Y, dots, partial, M, N, K, (K / 256) * 144, s);
         case kQ6_K:
             *name = "mmq<q6_K>";
-            return launch_typed<kQ6_K>(W, codes, xs, xsum, Y, dots, M, N, K, (K / 256) * 210, s);
+            return launch_typed<kQ6_K>(W, codes, xs, xsum, Y, dots, partial, M, N, K, (K / 256) * 210, s);
         default: return hipErrorInvalidValue;
     }
 }

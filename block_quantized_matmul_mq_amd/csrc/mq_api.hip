@@ -164,8 +164,10 @@ size_t mq_act_sum_offset(int64_t M, int64_t K) {
 }
 
 size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
-    (void)type; (void)M; (void)N; (void)K;
-    return 0;
+    if (type != MQ_Q8_0 && type != MQ_Q4_K && type != MQ_Q6_K) return 0;
+    if (M <= 0 || N <= 0 || K <= 0 || M > MQ_MAX_M || N > MQ_MAX_N || K > MQ_MAX_K) return 0;
+    if (K % (type == MQ_Q8_0 ? 32 : 256) != 0) return 0;
+    return mmq_scratch_bytes(type, M, N, K);
 }
 
 int mq_quantize_act(const float* X, void* Xq, int64_t M, int64_t K, void* stream) {
@@ -207,7 +209,7 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
 }
 
 static int gemm_common(const char* fn, const void* W, int type, const void* Xq, float* Y, int32_t* D,
-                       int64_t M, int64_t N, int64_t K, void* stream) {
+                       float* partial, int64_t M, int64_t N, int64_t K, void* stream) {
     if (!W || !Xq || (!Y && !D))
         return fail(MQ_ERR_ARG, "%s: null pointer (W=%p Xq=%p out=%p)", fn, W, Xq, Y ? (void*)Y : (void*)D);
     int rc = check_weight_shape(fn, type, N, K);
@@ -227,7 +229,7 @@ static int gemm_common(const char* fn, const void* W, int type, const void* Xq, 
     float* Yout = Y;
     hipError_t e = launch_mmq(type, static_cast<const uint8_t*>(W), reinterpret_cast<const int8_t*>(base),
                               reinterpret_cast<const float*>(base + act_scale_offset(M, K)),
-                              reinterpret_cast<const int32_t*>(base + act_sum_offset(M, K)), Yout, D, M, N, K,
+                              reinterpret_cast<const int32_t*>(base + act_sum_offset(M, K)), Yout, D, partial, M, N, K,
                               static_cast<hipStream_t>(stream), &kernel);
     return launch_status(fn, e, kernel);
 }
@@ -239,14 +241,17 @@ int mq_gemm(const void* W, int type, const void* Xq, float* Y, int64_t M, int64_
     const size_t need = mq_gemm_scratch_bytes(type, M, N, K);
     if (scratch_bytes < need || (need && !scratch))
         return fail(MQ_ERR_SIZE, "%s: scratch of %zu bytes at %p, %zu required", fn, scratch_bytes, scratch, need);
-    return gemm_common(fn, W, type, Xq, Y, nullptr, M, N, K, stream);
+    if (need && !aligned(scratch, 16))
+        return fail(MQ_ERR_ALIGN, "%s: scratch must be 16-byte aligned (%p)", fn, scratch);
+    return gemm_common(fn, W, type, Xq, Y, nullptr, need ? static_cast<float*>(scratch) : nullptr, M, N, K,
+                       stream);
 }
 
 int mq_debug_gemm_blockdots(const void* W, int type, const void* Xq, int32_t* D, int64_t M, int64_t N, int64_t K,
                             void* stream) {
     const char* fn = "mq_debug_gemm_blockdots";
     if (!D) return fail(MQ_ERR_ARG, "%s: null D", fn);
-    return gemm_common(fn, W, type, Xq, nullptr, D, M, N, K, stream);
+    return gemm_common(fn, W, type, Xq, nullptr, D, nullptr, M, N, K, stream);
 }
 
 }  // extern "C"

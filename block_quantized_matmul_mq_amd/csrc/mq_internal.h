@@ -33,8 +33,18 @@ int gemv_tile_units(int type, int64_t K, size_t lds_limit);
 hipError_t gemv_set_attributes(size_t lds_limit);
 hipError_t launch_gemv(int type, const uint8_t* W, const float* x, float* y, int64_t N, int64_t K,
                        hipStream_t s, const char** kernel_name);
+// MMQ work split: K is cut into `splits` ranges of whole K-steps when the output has
+// too few tiles to fill the chip; the partials then need mmq_scratch_bytes of scratch.
+struct MmqPlan {
+    int splits;
+    int steps;
+};
+MmqPlan mmq_plan(int type, int64_t M, int64_t N, int64_t K);
+size_t mmq_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
+// Y: the product (null for the block-dot export); dots: the export (null for the product);
+// partial: at least mmq_scratch_bytes of device memory when the plan has splits > 1.
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* codes, const float* scales,
-                      const int32_t* sums, float* Y, int32_t* dots, int64_t M, int64_t N, int64_t K,
-                      hipStream_t s, const char** kernel_name);
+                      const int32_t* sums, float* Y, int32_t* dots, float* partial, int64_t M, int64_t N,
+                      int64_t K, hipStream_t s, const char** kernel_name);
 
 }  // namespace mq

@@ -120,7 +120,11 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
 
 /*
  * mq_gemm_scratch_bytes -- device scratch that mq_gemm needs for (type, M, N,
- * K); 0 when the chosen kernel needs none.  Pass at least this many bytes.
+ * K); 0 when the chosen kernel needs none, and 0 for a shape mq_gemm refuses.
+ * When the output has too few 128 x 128 tiles to fill the device, mq_gemm cuts
+ * K into S ranges of whole 128-value steps and sums the S partial products in a
+ * second launch, in range order (deterministic); the scratch then holds
+ * S x M x N f32.  S depends on the shape only, never on the device.
  */
 size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
 
@@ -133,7 +137,10 @@ size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
  * (per 16-value group for Q6_K) and applies the block scales in f32 (and, for
  * Q4_K, the min term through the block's code sum).  Y: M x N f32 (device,
  * overwritten).  scratch / scratch_bytes: device memory of at least
- * mq_gemm_scratch_bytes(type, M, N, K) bytes (may be NULL/0 when that is 0).
+ * mq_gemm_scratch_bytes(type, M, N, K) bytes, 16-byte aligned (may be NULL/0
+ * when that is 0); its contents are overwritten, and calls that share one
+ * scratch buffer must be ordered on one stream.  MQ_ERR_SIZE when it is too
+ * small, MQ_ERR_ALIGN when misaligned.
  */
 int mq_gemm(const void* W, int type, const void* Xq, float* Y, int64_t M, int64_t N, int64_t K,
             void* scratch, size_t scratch_bytes, void* stream);

@@ -91,6 +91,24 @@ def test_gemm_refusals():
     assert lib.mq_debug_gemm_blockdots(FAKE, mq.Q4_K, FAKE, None, 4, 8, 256, None) == -1
 
 
+def test_gemm_scratch_is_sized_by_the_split_plan():
+    # many output tiles: no split, no scratch
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 18944, 3584) == 0
+    # 16 tiles of 128 x 128 over 28 K-steps of 128: 14 splits of 2 steps, f32 partials
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 512, 3584) == 14 * 512 * 512 * 4
+    # 112 tiles: 4 splits
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 3584, 3584) == 4 * 512 * 3584 * 4
+    # invalid shapes report 0 (the call itself refuses them)
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 512, 100) == 0
+    assert mq.gemm_scratch_bytes(99, 512, 512, 3584) == 0
+    lib = mq.load()
+    need = mq.gemm_scratch_bytes(mq.Q4_K, 512, 512, 3584)
+    assert lib.mq_gemm(FAKE, mq.Q4_K, FAKE, FAKE, 512, 512, 3584, None, 0, None) == -4
+    assert "required" in mq.last_error()
+    assert lib.mq_gemm(FAKE, mq.Q4_K, FAKE, FAKE, 512, 512, 3584, FAKE, need - 4, None) == -4
+    assert lib.mq_gemm(FAKE, mq.Q4_K, FAKE, FAKE, 512, 512, 3584, FAKE + 4, need, None) == -5
+
+
 def test_calls_without_init_are_refused_not_run():
     # Valid arguments but mq_init has not succeeded (and there may be no device
     # at all): the call must return an error code, never launch.

@@ -82,6 +82,19 @@ def test_blockdots_bitwise_small_ragged(qtype, kind):
 
 
 @pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
+def test_split_k_uneven_ranges(qtype):
+    # One output tile and a long K: the kernel splits K into many ranges of whole
+    # 128-value steps (uneven lengths; for Q8_0 the last step is cut by K) and sums
+    # the partials in a second launch.
+    M, N, K = 40, 100, (4128 if qtype == mq.Q8_0 else 8192)
+    assert mq.gemm_scratch_bytes(qtype, M, N, K) >= 8 * M * N * 4, "shape must take the split-K path"
+    raw = weights(qtype, N, K, "random", 70)
+    X = synth.activations(M, K, config_index=12, tensor_index=30)
+    check_blockdots(raw, qtype, X, N, K, "split-K")
+    check_gemm(raw, qtype, X, N, K, what="split-K")
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
 @pytest.mark.parametrize("kind", ["quantized", "random"])
 def test_gemm_small_ragged(qtype, kind):
     for i, (M, N, K) in enumerate(small_cases(qtype)):

@@ -10,16 +10,20 @@
 // Q4_K min term) are the weight's per-block factors.
 //
 // Tiling.  A 256-thread workgroup (4 waves, 2 x 2) owns a 128 x 128 tile of Y
-// and walks K in steps of 128 values (4 blocks); each wave owns 2 x 2 MFMA
-// tiles of 32 x 32.  The global data of step s+1 (activation codes, raw weight
-// bytes, block factors) is loaded into registers while step s computes from
-// LDS; between steps the registers are unpacked into LDS (weight codes become
-// int8: Q4_K 0..15, Q6_K code-32, Q8_0 q).  LDS rows are padded by 16 bytes so
-// the 16-byte fragment reads of 32 consecutive rows hit distinct banks.
+// and walks its K range in steps of 128 values (4 blocks); each wave owns 2 x 2
+// MFMA tiles of 32 x 32.  All tile data sits in LDS, double-buffered, so one
+// barrier per step separates the buffer being read from the one being filled:
+//   * activation codes and block scales/sums go global -> LDS directly
+//     (buffer_load ... lds), with no registers in between;
+//   * weight bytes are loaded into registers one step ahead and unpacked into
+//     LDS as int8 codes (Q4_K 0..15, Q6_K code-32, Q8_0 q) plus f32 per-block
+//     factors.
+// LDS tiles are chunk-major (16-byte chunk c of every row, then chunk c+1), so a
+// fragment read of 32 consecutive rows is 512 contiguous bytes.
 //
-// Per block and 32 x 32 tile the work is split between the matrix unit and the
-// vector ALU so that the vector ALU does two operations per output element and
-// block (convert, fused multiply-add):
+// Per block pair and 32 x 32 tile the matrix unit does all the multiplies it
+// can, so the vector ALU does two operations per output element and block
+// (convert, fused multiply-add):
 //   * v_mfma_i32_32x32x32_i8 forms the exact block dots D
 //     (v_mfma_i32_32x32x16_i8 per 16-value group for Q6_K);
 //   * v_mfma_f32_32x32x1_2b_f32 forms the two outer products dx (x) dw of a pair
@@ -27,10 +31,15 @@
 //   * the vector ALU accumulates acc += float(D) * scale;
 //   * for Q4_K the min term sum_b (dx S)[m][b] * mw[n][b] is a small GEMM over
 //     blocks, accumulated straight into acc by v_mfma_f32_32x32x2_f32.
+// The tile products of a step are software-pipelined: the matrix-unit work of
+// product k+1 is issued before the vector work of product k, so the two units
+// run side by side within a wave.
+//
 // Workgroups are numbered so that the ones sharing a weight tile run on the
 // same XCD (consecutive workgroup ids are dealt round-robin to the 8 XCDs, each
 // with its own L2): a weight tile then comes from HBM once per XCD.
 #include <algorithm>
+#include <type_traits>
 
 #include "mq_device.h"
 #include "mq_internal.h"
@@ -43,26 +52,49 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BM = 128;
 constexpr int BN = 128;
-constexpr int KS = 128;        // K values per step
+constexpr int KS = 128;        // K values per step (bytes per LDS row)
 constexpr int NB = KS / 32;    // 32-blocks per step
-constexpr int LDA = KS + 16;   // padded LDS row (bytes)
 constexpr int kXcds = 8;
 constexpr int kTargetWorkgroups = 512;   // two resident 256-thread workgroups on each of 256 CUs
 constexpr int kMinStepsPerSplit = 2;
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource: 32-bit data format, no swizzle
 
 template <int QT> struct Groups { static constexpr int per_step = NB; };
 template <> struct Groups<kQ6_K> { static constexpr int per_step = 2 * NB; };
 
+// LDS tiles are chunk-major: 16-byte chunk c (values 16c..16c+15 of the step) of row r
+// sits at c * 2048 + r * 16.  A fragment read (32 consecutive rows, one chunk) is then
+// 512 contiguous bytes, free of bank conflicts, and every address is a per-lane base
+// plus a compile-time offset.
+__device__ __forceinline__ int chk(int r, int c) { return c * (BM * 16) + r * 16; }
+
 // Row index (within a 32-row MFMA tile) of accumulator element v for lane group g = lane / 32.
 __device__ __forceinline__ int acc_row(int v, int g) { return 8 * (v >> 2) + 4 * g + (v & 3); }
 
-// ------------------------------------------------------------------ staging
-// Raw global data of one K-step, held in registers from the load (issued
-// before the previous step's compute) to the LDS write after it.  Rows past N
-// (M) re-read row N-1 (M-1): their outputs are never stored.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kBufferWord3);
+}
+
+// Wait for every outstanding vector-memory operation of this wave (LDS-direct loads included).
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int QT>
+struct Smem {
+    int8_t A[2][BM * KS];                               // activation codes
+    int8_t B[2][BN * KS];                               // weight codes
+    float dx[2][NB][BM];                                // activation block scales
+    int32_t sx[2][QT == kQ4_K ? NB : 1][BM];            // activation block code sums (Q4_K)
+    float dw[2][Groups<QT>::per_step][BN];              // weight scale per block (per group, Q6_K)
+    float mw[2][QT == kQ4_K ? NB : 1][BN];              // -dmin * m per block (Q4_K)
+};
+
+// ------------------------------------------------------------------ weight staging
+// Raw weight bytes of one K-step, held in registers from the load (issued a step
+// ahead) to the LDS write.  Rows past N re-read row N-1: their outputs are never stored.
 template <int QT> struct WeightRegs;
 
 template <> struct WeightRegs<kQ4_K> {
@@ -81,8 +113,9 @@ template <> struct WeightRegs<kQ4_K> {
             hd[it] = *reinterpret_cast<const uint4*>(blk);
         }
     }
-    __device__ void store(int8_t* Bs, float (*dws)[BN], float (*mws)[BN], int k0) const {
+    __device__ void store(Smem<kQ4_K>& sm, int buf, int k0) const {
         const int t = threadIdx.x, half = (k0 >> 7) & 1;
+        int8_t* Bs = sm.B[buf];
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             const int u = t + 256 * it, row = u >> 2, p = 4 * half + (u & 3);
@@ -91,21 +124,22 @@ template <> struct WeightRegs<kQ4_K> {
             const uint4 lo = make_uint4(v.x & 0x0F0F0F0Fu, v.y & 0x0F0F0F0Fu, v.z & 0x0F0F0F0Fu, v.w & 0x0F0F0F0Fu);
             const uint4 hi = make_uint4((v.x >> 4) & 0x0F0F0F0Fu, (v.y >> 4) & 0x0F0F0F0Fu,
                                         (v.z >> 4) & 0x0F0F0F0Fu, (v.w >> 4) & 0x0F0F0F0Fu);
-            // chunk c holds values 64c..64c+63: low nibbles the first 32, high nibbles the next 32
-            const int pos = 64 * c + 16 * h - 128 * half;   // value offset within this step
-            *reinterpret_cast<uint4*>(Bs + row * LDA + pos) = lo;
-            *reinterpret_cast<uint4*>(Bs + row * LDA + pos + 32) = hi;
+            // code chunk c holds values 64c..64c+63: low nibbles the first 32, high nibbles the next
+            // 32; piece h of it is 16 bytes, i.e. 16-value chunk 4c + h (low) and 4c + h + 2 (high)
+            const int cl = 4 * c + h - 8 * half;   // 16-value chunk within this step
+            *reinterpret_cast<uint4*>(Bs + chk(row, cl)) = lo;
+            *reinterpret_cast<uint4*>(Bs + chk(row, cl + 2)) = hi;
             if (h == 0) {
                 const float d = half_bits_to_float(hd[it].x & 0xFFFFu);
                 const float dmin = half_bits_to_float(hd[it].x >> 16);
                 const int jb = 2 * c - 4 * half;   // step-local block of sub-block 2c
                 uint32_t sc, mn;
                 q4k_scale_min(hd[it].y, hd[it].z, hd[it].w, 2 * c, sc, mn);
-                dws[jb][row] = d * float(sc);
-                mws[jb][row] = -(dmin * float(mn));
+                sm.dw[buf][jb][row] = d * float(sc);
+                sm.mw[buf][jb][row] = -(dmin * float(mn));
                 q4k_scale_min(hd[it].y, hd[it].z, hd[it].w, 2 * c + 1, sc, mn);
-                dws[jb + 1][row] = d * float(sc);
-                mws[jb + 1][row] = -(dmin * float(mn));
+                sm.dw[buf][jb + 1][row] = d * float(sc);
+                sm.mw[buf][jb + 1][row] = -(dmin * float(mn));
             }
         }
     }
@@ -131,8 +165,9 @@ template <> struct WeightRegs<kQ8_0> {
             for (int i = 0; i < 9; ++i) w[it][i] = p[i];
         }
     }
-    __device__ void store(int8_t* Bs, float (*dws)[BN], float (*)[BN], int) const {
+    __device__ void store(Smem<kQ8_0>& sm, int buf, int) const {
         const int t = threadIdx.x;
+        int8_t* Bs = sm.B[buf];
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             const int u = t + 256 * it, row = u >> 2, bi = u & 3;
@@ -143,11 +178,11 @@ template <> struct WeightRegs<kQ8_0> {
             for (int i = 0; i < 8; ++i) c[i] = odd[it] ? w[it][i + 1] : align_byte(w[it][i + 1], w[it][i], 2);
             const float d = half_bits_to_float(odd[it] ? (w[it][0] >> 16) : (w[it][0] & 0xFFFFu));
             const uint32_t keep = live[it] ? 0xFFFFFFFFu : 0u;   // blocks past K contribute nothing
-            *reinterpret_cast<uint4*>(Bs + row * LDA + 32 * bi) =
+            *reinterpret_cast<uint4*>(Bs + chk(row, 2 * bi)) =
                 make_uint4(c[0] & keep, c[1] & keep, c[2] & keep, c[3] & keep);
-            *reinterpret_cast<uint4*>(Bs + row * LDA + 32 * bi + 16) =
+            *reinterpret_cast<uint4*>(Bs + chk(row, 2 * bi + 1)) =
                 make_uint4(c[4] & keep, c[5] & keep, c[6] & keep, c[7] & keep);
-            dws[bi][row] = live[it] ? d : 0.f;
+            sm.dw[buf][bi][row] = live[it] ? d : 0.f;
         }
     }
 };
@@ -175,8 +210,9 @@ template <> struct WeightRegs<kQ6_K> {
         s1 = load_u32_a2(blk + 192 + 8 * h + 4);
         dbits = load_u16(blk + 208);
     }
-    __device__ void store(int8_t* Bs, float (*dws)[BN], float (*)[BN], int) const {
+    __device__ void store(Smem<kQ6_K>& sm, int buf, int) const {
         const int t = threadIdx.x;
+        int8_t* Bs = sm.B[buf];
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int u = t + 256 * it, row = u >> 3, p = u & 7;
@@ -188,7 +224,8 @@ template <> struct WeightRegs<kQ6_K> {
                 uint32_t code = low | (high << 4);
                 // per byte: code - 32 as int8 ((c + 128) - 32, then flip the sign bit back)
                 code = ((code | 0x80808080u) - 0x20202020u) ^ 0x80808080u;
-                *reinterpret_cast<uint32_t*>(Bs + row * LDA + 32 * tt + 4 * p) = code;
+                // values 32tt + 4p .. +3 of the step: chunk 2tt + p/4, bytes 4(p%4)..
+                *reinterpret_cast<uint32_t*>(Bs + chk(row, 2 * tt + (p >> 2)) + 4 * (p & 3)) = code;
             }
         }
         if (t < BN) {
@@ -196,59 +233,61 @@ template <> struct WeightRegs<kQ6_K> {
 #pragma unroll
             for (int gi = 0; gi < 8; ++gi) {
                 const uint32_t word = gi < 4 ? s0 : s1;
-                dws[gi][t] = d * float(int32_t(word << (24 - 8 * (gi & 3))) >> 24);
+                sm.dw[buf][gi][t] = d * float(int32_t(word << (24 - 8 * (gi & 3))) >> 24);
             }
         }
     }
 };
 
+// ------------------------------------------------------------------ activation staging
+// Activation codes and block scales (and Q4_K code sums) of one K-step, loaded by
+// each wave straight into LDS.  One buffer_load ... lds instruction writes 64 lanes x
+// 16 (or 4) consecutive LDS bytes; each lane picks the global bytes that belong at its
+// LDS slot.  Loads past the tile's last row return zeros (buffer range check).
 template <int QT>
-struct StepRegs {
-    uint4 a[4];        // activation codes of row t/2, bytes 64*(t%2) + 16i of the step
-    float dx[NB];      // thread t < 128: block scales of row t
-    int32_t sx[NB];    // Q4_K: block code sums of row t
-    WeightRegs<QT> w;
+struct ActDirect {
+    __amdgpu_buffer_rsrc_t rc, rs, ru;
+    uint32_t voff_a[4];   // codes: lane's byte offset for each of the wave's 4 instructions
+    uint32_t voff_s[2];   // scales / sums: lane's byte offset for each of the wave's 2 instructions
 
-    // Every load is unconditional, from an in-bounds address: values past K are
-    // replaced by zeros when the registers are written to LDS.  (A load under a
-    // branch would make the compiler wait for it right away.)
-    __device__ void load(const uint8_t* W, int64_t rb, const int8_t* codes, const float* xscale,
-                         const int32_t* xsum, int m0, int n0, int M, int N, int K, int k0) {
-        const int t = threadIdx.x;
+    __device__ void init(const int8_t* codes, const float* xscale, const int32_t* xsum, int m0, int M, int K) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int rows = min(BM, M - m0);
         const int KB = K >> 5;
-        const int ma = min(m0 + (t >> 1), M - 1);
+        rc = make_rsrc(codes + int64_t(m0) * K, int64_t(rows) * K);
+        rs = make_rsrc(xscale + int64_t(m0) * KB, int64_t(rows) * KB * 4);
+        ru = make_rsrc(xsum + int64_t(m0) * KB, int64_t(rows) * KB * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int kk = min(k0 + 64 * (t & 1) + 16 * i, K - 16);
-            a[i] = *reinterpret_cast<const uint4*>(codes + int64_t(ma) * K + kk);
+            // instruction i of wave w fills LDS bytes 1024(4w+i) .. +1023: chunk (4w+i)/2 of
+            // rows 64((4w+i)%2) .. +63, one row per lane
+            const int ins = 4 * wave + i;
+            const int row = 64 * (ins & 1) + lane;
+            voff_a[i] = uint32_t(row * K + 16 * (ins >> 1));
         }
-        const int ms = min(m0 + (t & (BM - 1)), M - 1);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const int kb = min((k0 >> 5) + b, KB - 1);
-            dx[b] = xscale[int64_t(ms) * KB + kb];
-            if constexpr (QT == kQ4_K) sx[b] = xsum[int64_t(ms) * KB + kb];
+        for (int j = 0; j < 2; ++j) {
+            // instruction j of wave w fills dword slots 64(2w+j) .. +63 of the [block][row] array
+            const int slot = 64 * (2 * wave + j) + lane;
+            const int b = slot >> 7, row = slot & (BM - 1);
+            voff_s[j] = uint32_t((row * KB + b) * 4);
         }
-        w.load(W, rb, n0, N, k0, K);
     }
 
-    __device__ void store(int8_t* As, int8_t* Bs, float (*dxs)[BM], float (*txs)[BM], float (*dws)[BN],
-                          float (*mws)[BN], int k0, int K) const {
-        const int t = threadIdx.x;
+    __device__ void issue(Smem<QT>& sm, int buf, int k0) const {
+        const int wave = threadIdx.x >> 6;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int kk = 64 * (t & 1) + 16 * i;
-            *reinterpret_cast<uint4*>(As + (t >> 1) * LDA + kk) = (k0 + kk < K) ? a[i] : make_uint4(0, 0, 0, 0);
-        }
-        if (t < BM) {
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void*)(sm.A[buf] + 1024 * (4 * wave + i)), 16,
+                                                     voff_a[i], uint32_t(k0), 0, 0);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const bool in = k0 + 32 * b < K;
-                dxs[b][t] = in ? dx[b] : 0.f;
-                if constexpr (QT == kQ4_K) txs[b][t] = in ? dx[b] * float(sx[b]) : 0.f;
-            }
+        for (int j = 0; j < 2; ++j) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(&sm.dx[buf][0][0] + 64 * (2 * wave + j)), 4,
+                                                     voff_s[j], uint32_t(k0 >> 3), 0, 0);
+            if constexpr (QT == kQ4_K)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (lds_void*)(&sm.sx[buf][0][0] + 64 * (2 * wave + j)),
+                                                         4, voff_s[j], uint32_t(k0 >> 3), 0, 0);
         }
-        w.store(Bs, dws, mws, k0);
     }
 };
 
@@ -259,31 +298,32 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
                                                      const float* __restrict__ xscale,
                                                      const int32_t* __restrict__ xsum,
                                                      float* __restrict__ Y, int32_t* __restrict__ dots,
-                                                     int M, int N, int K, int64_t row_bytes,
-                                                     int tiles_m, int tiles_n, int splits, int total_steps) {
-    constexpr int NG = Groups<QT>::per_step;
-    __shared__ __attribute__((aligned(16))) int8_t As[BM * LDA];
-    __shared__ __attribute__((aligned(16))) int8_t Bs[BN * LDA];
-    __shared__ __attribute__((aligned(16))) float dxs[NB][BM];
-    __shared__ __attribute__((aligned(16))) float txs[NB][BM];
-    __shared__ __attribute__((aligned(16))) float dws[NG][BN];
-    __shared__ __attribute__((aligned(16))) float mws[NB][BN];
+                                                     float* __restrict__ partial, int M, int N, int K,
+                                                     int64_t row_bytes, int tiles_m, int full, int split_tiles,
+                                                     int splits, int total_steps) {
+    __shared__ __attribute__((aligned(16))) Smem<QT> sm;
 
-    // XCD-aware order: workgroups that land on one XCD take consecutive logical ids, and
-    // consecutive ids are the M-tiles of one (split, N-tile), which read the same weights.
-    const int bid = blockIdx.x;
-    const int total = int(gridDim.x);
-    int logical = bid;
-    if (total % kXcds == 0) logical = (bid % kXcds) * (total / kXcds) + bid / kXcds;
-    const int tm = logical % tiles_m;
-    const int tn = (logical / tiles_m) % tiles_n;
-    const int split = logical / (tiles_m * tiles_n);
+    // Work split (MmqPlan): workgroups [0, full) own whole tiles 0..full-1; the remaining
+    // split_tiles tiles are each cut into `splits` K ranges, one workgroup per range, whose
+    // f32 partial tiles a second launch sums.  Within each group the ids are remapped so
+    // that workgroups landing on one XCD take consecutive logical ids, and consecutive ids
+    // are the M-tiles of one N-tile, which read the same weights.
+    const int id = blockIdx.x;
+    const bool whole = id < full;
+    const int group = whole ? full : split_tiles * splits;
+    const int j0 = whole ? id : id - full;
+    const int jj = group % kXcds == 0 ? (j0 % kXcds) * (group / kXcds) + j0 / kXcds : j0;
+    const int tile = whole ? jj : full + jj % split_tiles;
+    const int split = whole ? 0 : jj / split_tiles;
+    const int nsplit = whole ? 1 : splits;
+    const int tm = tile % tiles_m;
+    const int tn = tile / tiles_m;
     const int m0 = tm * BM, n0 = tn * BN;
-    // K range of this split: steps [s0, s1) of KS values; split-K partials go to slice
-    // `split` of the partial buffer (Y itself when there is one split).
-    const int kbeg = int(int64_t(split) * total_steps / splits) * KS;
-    const int kend = min(int(int64_t(split + 1) * total_steps / splits) * KS, K);
-    if (splits > 1 && !DUMP) Y += int64_t(split) * M * N;
+    // K range: steps [s0, s1) of KS values
+    const int kbeg = int(int64_t(split) * total_steps / nsplit) * KS;
+    const int kend = min(int(int64_t(split + 1) * total_steps / nsplit) * KS, K);
+    // a split tile's partial goes to its own 128 x 128 slot of the partial buffer
+    float* Pt = whole ? nullptr : partial + (int64_t(split) * split_tiles + (tile - full)) * (BM * BN);
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -301,152 +341,191 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    StepRegs<QT> regs;
-    regs.load(W, row_bytes, codes, xscale, xsum, m0, n0, M, N, K, kbeg);
+    ActDirect<QT> act;
+    act.init(codes, xscale, xsum, m0, M, K);
+    WeightRegs<QT> wr;
 
-    for (int k0 = kbeg; k0 < kend; k0 += KS) {
-        __syncthreads();   // the previous step's LDS reads are done
-        regs.store(As, Bs, dxs, txs, dws, mws, k0, K);
-        __syncthreads();
-        if (k0 + KS < kend) regs.load(W, row_bytes, codes, xscale, xsum, m0, n0, M, N, K, k0 + KS);
+    // prologue: step kbeg into buffer 0, step kbeg + KS in flight
+    wr.load(W, row_bytes, n0, N, kbeg, K);
+    act.issue(sm, 0, kbeg);
+    wait_vm_all();
+    wr.store(sm, 0, kbeg);
+    __syncthreads();
+    if (kbeg + KS < kend) {
+        wr.load(W, row_bytes, n0, N, kbeg + KS, K);
+        act.issue(sm, 1, kbeg + KS);
+    }
 
-        if constexpr (QT != kQ6_K) {
-#pragma unroll
-            for (int p = 0; p < NB / 2; ++p) {   // block pair (2p, 2p+1)
-                float dxo[2], dwo[2];
-                v4i af[2][2], bf[2][2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    dxo[i] = dxs[2 * p + g][64 * wm + 32 * i + r32];
-                    dwo[i] = dws[2 * p + g][64 * wn + 32 * i + r32];
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const int b = 2 * p + e;
-                        af[i][e] = *reinterpret_cast<const v4i*>(As + (64 * wm + 32 * i + r32) * LDA + 32 * b + 16 * g);
-                        bf[i][e] = *reinterpret_cast<const v4i*>(Bs + (64 * wn + 32 * i + r32) * LDA + 32 * b + 16 * g);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const v32f z32 = {};
-                        const v16i zi = {};
-                        // element scales of block 2p (S[0..15]) and 2p+1 (S[16..31])
-                        const v32f S = __builtin_amdgcn_mfma_f32_32x32x1f32(dxo[i], dwo[j], z32, 0, 0, 0);
-                        const v16i D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i][0], bf[j][0], zi, 0, 0, 0);
-                        const v16i D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i][1], bf[j][1], zi, 0, 0, 0);
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            acc[i][j][v] = fmaf(float(D0[v]), S[v], acc[i][j][v]);
-                            acc[i][j][v] = fmaf(float(D1[v]), S[16 + v], acc[i][j][v]);
-                        }
-                        if constexpr (DUMP) {
-                            const int nn = n0 + 64 * wn + 32 * j + r32;
-                            const int kb = (k0 >> 5) + 2 * p;
-#pragma unroll
-                            for (int v = 0; v < 16; ++v) {
-                                const int m = m0 + 64 * wm + 32 * i + acc_row(v, g);
-                                if (m < M && nn < N) {
-                                    const int64_t o = (int64_t(m) * N + nn) * KB + kb;
-                                    if (kb < KB) dots[o] = D0[v];
-                                    if (kb + 1 < KB) dots[o + 1] = D1[v];
-                                }
-                            }
-                        }
-                    }
+    // One K-step on LDS buffer BUF (a compile-time constant, so every LDS address is a
+    // per-lane base plus an immediate offset); the loop alternates the two buffers.
+    auto step = [&](auto buf_c, int k0) {
+        constexpr int buf = decltype(buf_c)::value;
+        const int8_t* As = sm.A[buf];
+        const int8_t* Bs = sm.B[buf];
+        const int arow0 = 64 * wm + r32;   // + 32 i
+        const int brow0 = 64 * wn + r32;   // + 32 j
+
+        // Tile products of the step, k = 4p + 2i + j (block pair p, or block p for Q6_K's two
+        // 16-value groups; tiles i, j).  Product k needs: S (the scale outer product, 32
+        // regs) and two int32 dot tiles D0, D1 (16 regs each).  Pipeline: S of product k+1
+        // is issued when product k starts; D0 of product k+1 as soon as product k has used
+        // its D0, D1 likewise, so every matrix-unit result has a half product of vector work
+        // to arrive in.
+        constexpr int kProducts = QT == kQ6_K ? 16 : 8;
+        v32f S[2];
+        v16i D0, D1;
+        // operands of the next product's dot tiles
+        v4i na0, na1, nb0, nb1;   // 16-byte fragments (Q8_0, Q4_K)
+        long la0, la1, lb0, lb1;  // 8-byte fragments (Q6_K)
+        float sdx, sdw;           // the next product's scale-outer-product operands
+        auto frag = [&](int k) {
+            const int p = k >> 2, i = (k >> 1) & 1, j = k & 1;
+            const int ar = arow0 + 32 * i, br = brow0 + 32 * j;
+            if constexpr (QT != kQ6_K) {
+                na0 = *reinterpret_cast<const v4i*>(As + chk(ar, 4 * p + g));
+                na1 = *reinterpret_cast<const v4i*>(As + chk(ar, 4 * p + 2 + g));
+                nb0 = *reinterpret_cast<const v4i*>(Bs + chk(br, 4 * p + g));
+                nb1 = *reinterpret_cast<const v4i*>(Bs + chk(br, 4 * p + 2 + g));
+                sdx = sm.dx[buf][2 * p + g][ar];   // block 2p + g (lane group g feeds block g of the pair)
+            } else {
+                la0 = *reinterpret_cast<const long*>(As + chk(ar, 2 * p) + 8 * g);
+                la1 = *reinterpret_cast<const long*>(As + chk(ar, 2 * p + 1) + 8 * g);
+                lb0 = *reinterpret_cast<const long*>(Bs + chk(br, 2 * p) + 8 * g);
+                lb1 = *reinterpret_cast<const long*>(Bs + chk(br, 2 * p + 1) + 8 * g);
+                sdx = sm.dx[buf][p][ar];           // one block scale for both groups
             }
+            sdw = sm.dw[buf][2 * p + g][br];
+        };
+        // Q8_0 / Q4_K: element scales of block 2p (out[0..15]) and 2p+1 (out[16..31]);
+        // Q6_K: of groups 2p (out[0..15]) and 2p+1 (out[16..31]) of block p
+        auto scales = [&](v32f& out) {
+            const v32f z32 = {};
+            out = __builtin_amdgcn_mfma_f32_32x32x1f32(sdx, sdw, z32, 0, 0, 0);
+        };
+        auto dot0 = [&]() {
+            const v16i zi = {};
+            if constexpr (QT != kQ6_K) D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(na0, nb0, zi, 0, 0, 0);
+            else D0 = __builtin_amdgcn_mfma_i32_32x32x16_i8(la0, lb0, zi, 0, 0, 0);
+        };
+        auto dot1 = [&]() {
+            const v16i zi = {};
+            if constexpr (QT != kQ6_K) D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(na1, nb1, zi, 0, 0, 0);
+            else D1 = __builtin_amdgcn_mfma_i32_32x32x16_i8(la1, lb1, zi, 0, 0, 0);
+        };
+        // acc += float(D) * S-half h, and the block-dot export
+        auto consume = [&](int k, const v32f& Sk, const v16i& D, int h) {
+            const int p = k >> 2, i = (k >> 1) & 1, j = k & 1;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = fmaf(float(D[v]), Sk[16 * h + v], acc[i][j][v]);
+            // pin the accumulation here: without it the compiler sinks all vector work of
+            // the step below the matrix-unit work, and the dot tiles pile up in registers
+            asm volatile("" : "+v"(acc[i][j]));
+            if constexpr (DUMP) {
+                const int nn = n0 + brow0 + 32 * j;
+                // Q8_0 / Q4_K: block 2p + h; Q6_K: group h of block p
+                const int kb = (k0 >> 5) + (QT == kQ6_K ? p : 2 * p + h);
+                const int G = QT == kQ6_K ? 2 * KB : KB;
+                const int gi = QT == kQ6_K ? 2 * kb + h : kb;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int m = m0 + 64 * wm + 32 * i + acc_row(v, g);
+                    if (m < M && nn < N && kb < KB) dots[(int64_t(m) * N + nn) * G + gi] = D[v];
+                }
+            }
+        };
+        // Q4_K min term of tile (i, j) for the step's 4 blocks:
+        // acc += sum_b (dx S)[m][b] * mw[n][b], two blocks per MFMA
+        auto min_term = [&](int i, int j) {
             if constexpr (QT == kQ4_K) {
-                // min term: acc += sum_b txs[b][m] * mws[b][n] over the step's 4 blocks, 2 per MFMA
+                const int ar = arow0 + 32 * i, br = brow0 + 32 * j;
 #pragma unroll
-                for (int p = 0; p < NB / 2; ++p) {
-                    float to[2], mo[2];
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        to[i] = txs[2 * p + g][64 * wm + 32 * i + r32];
-                        mo[i] = mws[2 * p + g][64 * wn + 32 * i + r32];
-                    }
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(to[i], mo[j], acc[i][j], 0, 0, 0);
+                for (int q = 0; q < 2; ++q) {
+                    const float to = sm.dx[buf][2 * q + g][ar] * float(sm.sx[buf][2 * q + g][ar]);
+                    const float mo = sm.mw[buf][2 * q + g][br];
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(to, mo, acc[i][j], 0, 0, 0);
                 }
             }
-        } else {
+        };
+
+        // Each product is cut into scheduling regions (sched_barrier) so that the matrix-unit
+        // work of product k+1 sits between the two halves of product k's vector work.
+        frag(0);
+        scales(S[0]);
+        dot0();
+        dot1();
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                // block b as two 16-value groups 2b, 2b+1 with their own sub-scales
-                long alo[2], ahi[2], blo[2], bhi[2];
-                float dxe[2], dwo[2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int8_t* ap = As + (64 * wm + 32 * i + r32) * LDA + 32 * b + 8 * g;
-                    alo[i] = *reinterpret_cast<const long*>(ap);
-                    ahi[i] = *reinterpret_cast<const long*>(ap + 16);
-                    const int8_t* bp = Bs + (64 * wn + 32 * i + r32) * LDA + 32 * b + 8 * g;
-                    blo[i] = *reinterpret_cast<const long*>(bp);
-                    bhi[i] = *reinterpret_cast<const long*>(bp + 16);
-                    dxe[i] = dxs[b][64 * wm + 32 * i + r32];
-                    dwo[i] = dws[2 * b + g][64 * wn + 32 * i + r32];
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const v32f z32 = {};
-                        const v16i zi = {};
-                        // element scales of group 2b (S[0..15]) and 2b+1 (S[16..31]): one dx, own d*s
-                        const v32f S = __builtin_amdgcn_mfma_f32_32x32x1f32(dxe[i], dwo[j], z32, 0, 0, 0);
-                        const v16i Dl = __builtin_amdgcn_mfma_i32_32x32x16_i8(alo[i], blo[j], zi, 0, 0, 0);
-                        const v16i Dh = __builtin_amdgcn_mfma_i32_32x32x16_i8(ahi[i], bhi[j], zi, 0, 0, 0);
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            acc[i][j][v] = fmaf(float(Dl[v]), S[v], acc[i][j][v]);
-                            acc[i][j][v] = fmaf(float(Dh[v]), S[16 + v], acc[i][j][v]);
-                        }
-                        if constexpr (DUMP) {
-                            const int nn = n0 + 64 * wn + 32 * j + r32;
-                            const int kb = (k0 >> 5) + b;
-#pragma unroll
-                            for (int v = 0; v < 16; ++v) {
-                                const int m = m0 + 64 * wm + 32 * i + acc_row(v, g);
-                                if (m < M && nn < N && kb < KB) {
-                                    const int64_t o = (int64_t(m) * N + nn) * (2 * KB) + 2 * kb;
-                                    dots[o] = Dl[v];
-                                    dots[o + 1] = Dh[v];
-                                }
-                            }
-                        }
-                    }
+        for (int k = 0; k < kProducts; ++k) {
+            const int cur = k & 1;
+            const bool more = k + 1 < kProducts;
+            if (more) frag(k + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(k, S[cur], D0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) {
+                scales(S[cur ^ 1]);
+                dot0();
             }
+            __builtin_amdgcn_sched_barrier(0);
+            consume(k, S[cur], D1, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) dot1();
+            __builtin_amdgcn_sched_barrier(0);
+            if (QT == kQ4_K && (k >> 2) == 1) min_term((k >> 1) & 1, k & 1);
         }
+        // next step: its weight registers and LDS-direct loads were issued a step ago
+        if (k0 + KS < kend) {
+            wait_vm_all();
+            wr.store(sm, buf ^ 1, k0 + KS);
+        }
+        __syncthreads();   // buffer `buf` is free, buffer `buf ^ 1` is complete
+        if (k0 + 2 * KS < kend) {
+            wr.load(W, row_bytes, n0, N, k0 + 2 * KS, K);
+            act.issue(sm, buf, k0 + 2 * KS);
+        }
+    };
+    for (int k0 = kbeg;;) {
+        step(std::integral_constant<int, 0>{}, k0);
+        if ((k0 += KS) >= kend) break;
+        step(std::integral_constant<int, 1>{}, k0);
+        if ((k0 += KS) >= kend) break;
     }
 
     // Y store: for a fixed accumulator element the 32 lanes of a group write 32 consecutive n.
+    // A split tile stores its partial tile whole (the reduce applies the M, N bounds).
     // The block-dot export variant stores only the dots.
     if constexpr (DUMP) return;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int n = n0 + 64 * wn + 32 * j + r32;
+            const int nl = 64 * wn + 32 * j + r32;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int m = m0 + 64 * wm + 32 * i + acc_row(v, g);
-                if (m < M && n < N) Y[int64_t(m) * N + n] = acc[i][j][v];
+                const int ml = 64 * wm + 32 * i + acc_row(v, g);
+                if (!whole) {
+                    Pt[ml * BN + nl] = acc[i][j][v];
+                } else if (m0 + ml < M && n0 + nl < N) {
+                    Y[int64_t(m0 + ml) * N + n0 + nl] = acc[i][j][v];
+                }
             }
         }
 }
 
-// Sum of the split-K partials P[splits][count] in split order (deterministic).
+// Sum of the partial tiles P[splits][split_tiles][BM x BN] of the split tiles, in split
+// order (deterministic), into Y.  Split tile t is tile full + t.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, float* __restrict__ Y,
-                                                            int64_t count, int splits) {
-    const int64_t stride = int64_t(gridDim.x) * 256;
-    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < count; i += stride) {
-        float acc = P[i];
-        for (int s = 1; s < splits; ++s) acc += P[int64_t(s) * count + i];
-        Y[i] = acc;
+                                                            int M, int N, int tiles_m, int full, int split_tiles,
+                                                            int splits) {
+    const int t = blockIdx.y;
+    const int tile = full + t;
+    const int m0 = (tile % tiles_m) * BM, n0 = (tile / tiles_m) * BN;
+    const int64_t slot = int64_t(BM) * BN;
+    for (int e = blockIdx.x * 256 + threadIdx.x; e < BM * BN; e += gridDim.x * 256) {
+        const int m = m0 + e / BN, n = n0 + e % BN;
+        if (m >= M || n >= N) continue;
+        float acc = P[int64_t(t) * slot + e];
+        for (int sp = 1; sp < splits; ++sp) acc += P[(int64_t(sp) * split_tiles + t) * slot + e];
+        Y[int64_t(m) * N + n] = acc;
     }
 }
 
@@ -456,46 +535,52 @@ hipError_t launch_typed(const uint8_t* W, const int8_t* codes, const float* xs, 
                         int64_t row_bytes, hipStream_t s) {
     const MmqPlan plan = mmq_plan(QT, M, N, K);
     const int tiles_m = int((M + BM - 1) / BM);
-    const int tiles_n = int((N + BN - 1) / BN);
-    const int total = tiles_m * tiles_n * plan.splits;
+    const int total = plan.full + plan.split_tiles * plan.splits;
     if (dots) {
         hipLaunchKernelGGL((mmq_kernel<QT, true>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, Y, dots,
-                           int(M), int(N), int(K), row_bytes, tiles_m, tiles_n, plan.splits, plan.steps);
+                           partial, int(M), int(N), int(K), row_bytes, tiles_m, plan.full, plan.split_tiles,
+                           plan.splits, plan.steps);
         return hipGetLastError();
     }
-    float* out = plan.splits > 1 ? partial : Y;
-    hipLaunchKernelGGL((mmq_kernel<QT, false>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, out, dots,
-                       int(M), int(N), int(K), row_bytes, tiles_m, tiles_n, plan.splits, plan.steps);
+    hipLaunchKernelGGL((mmq_kernel<QT, false>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, Y, dots, partial,
+                       int(M), int(N), int(K), row_bytes, tiles_m, plan.full, plan.split_tiles, plan.splits,
+                       plan.steps);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || plan.splits == 1) return e;
-    const int64_t count = M * N;
-    const int64_t blocks = std::min<int64_t>((count + 255) / 256, 4096);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, partial, Y, count,
-                       plan.splits);
+    if (e != hipSuccess || plan.split_tiles == 0) return e;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(BM * BN / 256, plan.split_tiles), dim3(256), 0, s, partial, Y, int(M),
+                       int(N), tiles_m, plan.full, plan.split_tiles, plan.splits);
     return hipGetLastError();
 }
 
 }  // namespace
 
 MmqPlan mmq_plan(int /*type*/, int64_t M, int64_t N, int64_t K) {
-    // Enough workgroups to fill the chip: when the output has fewer tiles than about
-    // 3/4 of kTargetWorkgroups, K is split so that tiles x splits comes near it, with at
-    // least kMinStepsPerSplit K-steps per split.  A function of the shape alone, so the
-    // result does not depend on the device.
+    // kTargetWorkgroups workgroups fill the chip.  Tiles are dealt whole while they fill it;
+    // the tiles of a last, less than half full round (or all tiles, when there are fewer
+    // than half a round of them) are cut into K ranges of at least kMinStepsPerSplit steps,
+    // enough of them to fill that round.  A function of the shape alone, so the result does
+    // not depend on the device.
     MmqPlan p;
     p.steps = int((K + KS - 1) / KS);
-    p.splits = 1;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    if (tiles * 4 < int64_t(kTargetWorkgroups) * 3) {
-        const int64_t want = kTargetWorkgroups / tiles;
-        p.splits = int(std::max<int64_t>(1, std::min<int64_t>(want, p.steps / kMinStepsPerSplit)));
+    const int64_t rem = tiles % kTargetWorkgroups;
+    p.full = int(tiles);
+    p.split_tiles = 0;
+    p.splits = 1;
+    if (rem > 0 && rem * 2 <= kTargetWorkgroups) {
+        const int64_t splits = std::min<int64_t>(kTargetWorkgroups / rem, p.steps / kMinStepsPerSplit);
+        if (splits >= 2) {
+            p.full = int(tiles - rem);
+            p.split_tiles = int(rem);
+            p.splits = int(splits);
+        }
     }
     return p;
 }
 
 size_t mmq_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
     const MmqPlan p = mmq_plan(type, M, N, K);
-    return p.splits > 1 ? size_t(p.splits) * size_t(M) * size_t(N) * sizeof(float) : 0;
+    return size_t(p.split_tiles) * size_t(p.splits) * BM * BN * sizeof(float);
 }
 
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* codes, const float* xs, const int32_t* xsum,

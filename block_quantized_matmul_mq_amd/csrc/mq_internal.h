@@ -33,9 +33,12 @@ int gemv_tile_units(int type, int64_t K, size_t lds_limit);
 hipError_t gemv_set_attributes(size_t lds_limit);
 hipError_t launch_gemv(int type, const uint8_t* W, const float* x, float* y, int64_t N, int64_t K,
                        hipStream_t s, const char** kernel_name);
-// MMQ work split: K is cut into `splits` ranges of whole K-steps when the output has
-// too few tiles to fill the chip; the partials then need mmq_scratch_bytes of scratch.
+// MMQ work split over 128 x 128 output tiles: the first `full` tiles are computed whole;
+// each of the remaining `split_tiles` is cut into `splits` ranges of whole 128-value
+// K-steps, whose f32 partial tiles (mmq_scratch_bytes of scratch) a second launch sums.
 struct MmqPlan {
+    int full;
+    int split_tiles;
     int splits;
     int steps;
 };

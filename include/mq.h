@@ -120,11 +120,14 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
 
 /*
  * mq_gemm_scratch_bytes -- device scratch that mq_gemm needs for (type, M, N,
- * K); 0 when the chosen kernel needs none, and 0 for a shape mq_gemm refuses.
- * When the output has too few 128 x 128 tiles to fill the device, mq_gemm cuts
- * K into S ranges of whole 128-value steps and sums the S partial products in a
- * second launch, in range order (deterministic); the scratch then holds
- * S x M x N f32.  S depends on the shape only, never on the device.
+ * K); 0 when the chosen work split needs none, and 0 for a shape mq_gemm
+ * refuses.  mq_gemm computes Y in 128 x 128 tiles, sized for 512 resident
+ * workgroups: tiles are computed whole while they fill rounds of 512; the tiles
+ * of a last round that is at most half full (or all tiles, when there are at
+ * most 256) are cut into S ranges of whole 128-value K-steps, and a second
+ * launch sums their S f32 partial tiles in range order (deterministic).  The
+ * scratch then holds S x (number of cut tiles) x 128 x 128 f32.  The split
+ * depends on the shape only, never on the device.
  */
 size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
 

@@ -92,12 +92,17 @@ def test_gemm_refusals():
 
 
 def test_gemm_scratch_is_sized_by_the_split_plan():
-    # many output tiles: no split, no scratch
-    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 18944, 3584) == 0
-    # 16 tiles of 128 x 128 over 28 K-steps of 128: 14 splits of 2 steps, f32 partials
-    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 512, 3584) == 14 * 512 * 512 * 4
-    # 112 tiles: 4 splits
-    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 3584, 3584) == 4 * 512 * 3584 * 4
+    tile = 128 * 128 * 4
+    # 512 tiles of 128 x 128 fill one round of 512 workgroups: no split, no scratch
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 16384, 3584) == 0
+    # 592 tiles: 512 whole, the last 80 cut into 6 K ranges (28 steps of 128)
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 18944, 3584) == 6 * 80 * tile
+    # a last round more than half full is not cut
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512 * 3, 128 * 200, 3584) == 0
+    # 16 tiles over 28 K-steps: 14 ranges of 2 steps (at least 2 steps per range)
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 512, 3584) == 14 * 16 * tile
+    # 112 tiles: 4 ranges
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 3584, 3584) == 4 * 112 * tile
     # invalid shapes report 0 (the call itself refuses them)
     assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 512, 100) == 0
     assert mq.gemm_scratch_bytes(99, 512, 512, 3584) == 0

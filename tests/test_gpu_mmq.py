@@ -95,6 +95,20 @@ def test_split_k_uneven_ranges(qtype):
 
 
 @pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
+def test_whole_tiles_plus_split_tail(qtype):
+    # 520 output tiles: 512 computed whole, the last 8 cut into K ranges and summed by the
+    # second launch; columns are sampled from both kinds of tile (the last 8 tiles are the
+    # last 1024 columns).
+    M, N, K = 100, 128 * 520, 512
+    assert mq.gemm_scratch_bytes(qtype, M, N, K) == 2 * 8 * 128 * 128 * 4
+    raw = weights(qtype, N, K, "quantized", 80)
+    X = synth.activations(M, K, config_index=12, tensor_index=31)
+    rng = np.random.default_rng(5)
+    cols = np.sort(np.concatenate([rng.choice(N - 1024, 200, replace=False), np.arange(N - 1024, N)]))
+    check_gemm(raw, qtype, X, N, K, cols=cols, what="whole + split tiles")
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
 @pytest.mark.parametrize("kind", ["quantized", "random"])
 def test_gemm_small_ragged(qtype, kind):
     for i, (M, N, K) in enumerate(small_cases(qtype)):

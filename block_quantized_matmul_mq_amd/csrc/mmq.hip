@@ -30,7 +30,12 @@
 //     of blocks: the f32 scale of every element of both blocks;
 //   * the vector ALU accumulates acc += float(D) * scale;
 //   * for Q4_K the min term sum_b (dx S)[m][b] * mw[n][b] is a small GEMM over
-//     blocks, accumulated straight into acc by v_mfma_f32_32x32x2_f32.
+//     the step's 4 blocks, accumulated straight into acc by one
+//     v_mfma_f32_32x32x16_bf16 per tile: both factors are split into two bf16
+//     terms (hi + lo, together 16 significant bits) and the three products
+//     hi*hi + hi*lo + lo*hi are summed in f32, so the term keeps a relative
+//     error below 2^-16.  (An f32 MFMA here would not overlap the vector ALU of
+//     the other wave on the SIMD; bf16 and int8 MFMAs do.)
 // The tile products of a step are software-pipelined: the matrix-unit work of
 // product k+1 is issued before the vector work of product k, so the two units
 // run side by side within a wave.
@@ -53,6 +58,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 128;
 constexpr int BN = 128;
@@ -79,6 +85,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kBufferWord3);
 }
 
+// x as two bf16 terms, hi = bf16(x) and lo = bf16(x - hi) (round to nearest even), packed as
+// hi | lo << 16; hi + lo carries 16 significant bits of x.
+__device__ __forceinline__ uint32_t bf16_hilo(float x) {
+    const __bf16 hi = static_cast<__bf16>(x);
+    const __bf16 lo = static_cast<__bf16>(x - static_cast<float>(hi));
+    return uint32_t(__builtin_bit_cast(uint16_t, hi)) | (uint32_t(__builtin_bit_cast(uint16_t, lo)) << 16);
+}
+
 // Wait for every outstanding vector-memory operation of this wave (LDS-direct loads included).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -87,9 +101,9 @@ struct Smem {
     int8_t A[2][BM * KS];                               // activation codes
     int8_t B[2][BN * KS];                               // weight codes
     float dx[2][NB][BM];                                // activation block scales
-    int32_t sx[2][QT == kQ4_K ? NB : 1][BM];            // activation block code sums (Q4_K)
+    uint32_t tx[2][QT == kQ4_K ? NB : 1][BM];           // Q4_K: bf16_hilo(dx * code sum) per block
     float dw[2][Groups<QT>::per_step][BN];              // weight scale per block (per group, Q6_K)
-    float mw[2][QT == kQ4_K ? NB : 1][BN];              // -dmin * m per block (Q4_K)
+    uint32_t mw[2][QT == kQ4_K ? NB : 1][BN];           // Q4_K: bf16_hilo(-dmin * m) per block
 };
 
 // ------------------------------------------------------------------ weight staging
@@ -98,66 +112,66 @@ struct Smem {
 template <int QT> struct WeightRegs;
 
 template <> struct WeightRegs<kQ4_K> {
-    // Thread t owns pieces u = t and t + 256: row u/4, 16-byte code chunk 4*half + u%4
-    // of the super-block (half = which 128 values of it this step covers), and the
-    // 16-byte header (d, dmin, packed scales) of that row's super-block.
-    uint4 q[2], hd[2];
+    // Thread t owns row t % 128 and, of the 4 16-byte code chunks that hold this step's
+    // 128 values (half = which half of the super-block the step covers), chunks p0 and
+    // p0 + 2 with p0 = t / 128; and the row's 16-byte header (d, dmin, packed scales).
+    // Chunk p holds the low nibbles (values 16p' ..) of sub-block 2c and the high nibbles
+    // of sub-block 2c + 1, c = 2 half + p / 2.  A wave writes one chunk of 64 consecutive
+    // rows at a time: 1 KB of contiguous LDS, no bank conflicts.
+    uint4 q[2], hd;
     __device__ void load(const uint8_t* W, int64_t rb, int n0, int N, int k0, int) {
         const int t = threadIdx.x, sb = k0 >> 8, half = (k0 >> 7) & 1;
+        const int n = min(n0 + (t & (BN - 1)), N - 1);
+        const uint8_t* blk = W + int64_t(n) * rb + 144 * sb;
+        const int p0 = t >> 7;
 #pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int u = t + 256 * it, row = u >> 2, p = 4 * half + (u & 3);
-            const int n = min(n0 + row, N - 1);
-            const uint8_t* blk = W + int64_t(n) * rb + 144 * sb;
-            q[it] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * p);
-            hd[it] = *reinterpret_cast<const uint4*>(blk);
-        }
+        for (int it = 0; it < 2; ++it)
+            q[it] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (4 * half + p0 + 2 * it));
+        hd = *reinterpret_cast<const uint4*>(blk);
     }
     __device__ void store(Smem<kQ4_K>& sm, int buf, int k0) const {
         const int t = threadIdx.x, half = (k0 >> 7) & 1;
+        const int row = t & (BN - 1), p0 = t >> 7;
         int8_t* Bs = sm.B[buf];
+        const float d = half_bits_to_float(hd.x & 0xFFFFu);
+        const float dmin = half_bits_to_float(hd.x >> 16);
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
-            const int u = t + 256 * it, row = u >> 2, p = 4 * half + (u & 3);
-            const int c = p >> 1, h = p & 1;
+            const int p = p0 + 2 * it;          // chunk within the step's 64 code bytes
+            const int c = p >> 1, h = p & 1;    // 64-value group c of the step, piece h of it
             const uint4 v = q[it];
             const uint4 lo = make_uint4(v.x & 0x0F0F0F0Fu, v.y & 0x0F0F0F0Fu, v.z & 0x0F0F0F0Fu, v.w & 0x0F0F0F0Fu);
             const uint4 hi = make_uint4((v.x >> 4) & 0x0F0F0F0Fu, (v.y >> 4) & 0x0F0F0F0Fu,
                                         (v.z >> 4) & 0x0F0F0F0Fu, (v.w >> 4) & 0x0F0F0F0Fu);
-            // code chunk c holds values 64c..64c+63: low nibbles the first 32, high nibbles the next
-            // 32; piece h of it is 16 bytes, i.e. 16-value chunk 4c + h (low) and 4c + h + 2 (high)
-            const int cl = 4 * c + h - 8 * half;   // 16-value chunk within this step
-            *reinterpret_cast<uint4*>(Bs + chk(row, cl)) = lo;
-            *reinterpret_cast<uint4*>(Bs + chk(row, cl + 2)) = hi;
-            if (h == 0) {
-                const float d = half_bits_to_float(hd[it].x & 0xFFFFu);
-                const float dmin = half_bits_to_float(hd[it].x >> 16);
-                const int jb = 2 * c - 4 * half;   // step-local block of sub-block 2c
-                uint32_t sc, mn;
-                q4k_scale_min(hd[it].y, hd[it].z, hd[it].w, 2 * c, sc, mn);
-                sm.dw[buf][jb][row] = d * float(sc);
-                sm.mw[buf][jb][row] = -(dmin * float(mn));
-                q4k_scale_min(hd[it].y, hd[it].z, hd[it].w, 2 * c + 1, sc, mn);
-                sm.dw[buf][jb + 1][row] = d * float(sc);
-                sm.mw[buf][jb + 1][row] = -(dmin * float(mn));
-            }
+            // group c holds values 64c..64c+63 of the step: low nibbles the first 32, high nibbles
+            // the next 32; piece h is 16 bytes, i.e. 16-value chunks 4c + h (low) and 4c + h + 2 (high)
+            *reinterpret_cast<uint4*>(Bs + chk(row, 4 * c + h)) = lo;
+            *reinterpret_cast<uint4*>(Bs + chk(row, 4 * c + h + 2)) = hi;
+            // this thread also decodes step block jb = 2c + h (sub-block 4 half + jb of the
+            // super-block); the branch inside is uniform (it depends on half only)
+            const int jb = 2 * c + h;
+            uint32_t sc, mn;
+            q4k_scale_min(hd.y, hd.z, hd.w, 4 * half + jb, sc, mn);
+            sm.dw[buf][jb][row] = d * float(sc);
+            sm.mw[buf][jb][row] = bf16_hilo(-(dmin * float(mn)));
         }
     }
 };
 
 template <> struct WeightRegs<kQ8_0> {
-    // Thread t owns pieces u = t and t + 256: block u%4 of this step in row u/4, read as
-    // the 9 naturally aligned dwords that cover its 34 bytes (every one of them holds
-    // bytes of the block, so nothing past the payload is touched).
+    // Thread t owns row t % 128 and blocks b0 and b0 + 2 of this step, b0 = t / 128, each
+    // read as the 9 naturally aligned dwords that cover its 34 bytes (every one of them
+    // holds bytes of the block, so nothing past the payload is touched).  A wave writes
+    // one chunk of 64 consecutive rows at a time.
     uint32_t w[2][9];
     bool odd[2], live[2];
     __device__ void load(const uint8_t* W, int64_t rb, int n0, int N, int k0, int K) {
         const int t = threadIdx.x;
+        const int n = min(n0 + (t & (BN - 1)), N - 1);
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
-            const int u = t + 256 * it, row = u >> 2, kb = (k0 >> 5) + (u & 3);
+            const int kb = (k0 >> 5) + (t >> 7) + 2 * it;
             live[it] = kb < (K >> 5);
-            const int n = min(n0 + row, N - 1);
             const uintptr_t a = reinterpret_cast<uintptr_t>(W + int64_t(n) * rb + 34 * int64_t(live[it] ? kb : 0));
             odd[it] = (a & 2) != 0;
             const uint32_t* p = reinterpret_cast<const uint32_t*>(a & ~uintptr_t(3));
@@ -167,10 +181,11 @@ template <> struct WeightRegs<kQ8_0> {
     }
     __device__ void store(Smem<kQ8_0>& sm, int buf, int) const {
         const int t = threadIdx.x;
+        const int row = t & (BN - 1);
         int8_t* Bs = sm.B[buf];
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
-            const int u = t + 256 * it, row = u >> 2, bi = u & 3;
+            const int bi = (t >> 7) + 2 * it;
             // block at 4-byte offset 2 (odd): d in the high half of dword 0, codes in dwords 1..8;
             // at offset 0: d in the low half, codes start at byte 2
             uint32_t c[8];
@@ -240,15 +255,19 @@ template <> struct WeightRegs<kQ6_K> {
 };
 
 // ------------------------------------------------------------------ activation staging
-// Activation codes and block scales (and Q4_K code sums) of one K-step, loaded by
-// each wave straight into LDS.  One buffer_load ... lds instruction writes 64 lanes x
-// 16 (or 4) consecutive LDS bytes; each lane picks the global bytes that belong at its
-// LDS slot.  Loads past the tile's last row return zeros (buffer range check).
+// Activation codes and block scales of one K-step, loaded by each wave straight into
+// LDS.  One buffer_load ... lds instruction writes 64 lanes x 16 (or 4) consecutive LDS
+// bytes; each lane picks the global bytes that belong at its LDS slot.  Loads past the
+// tile's last row return zeros (buffer range check).  Wave w loads the scales of block w
+// of the step (all 128 rows); for Q4_K it also loads that block's code sums into
+// registers, and after its loads have landed forms the min-term factor dx * sum of the
+// rows itself (its own loads are complete after its own wait, before any barrier).
 template <int QT>
 struct ActDirect {
     __amdgpu_buffer_rsrc_t rc, rs, ru;
     uint32_t voff_a[4];   // codes: lane's byte offset for each of the wave's 4 instructions
-    uint32_t voff_s[2];   // scales / sums: lane's byte offset for each of the wave's 2 instructions
+    uint32_t voff_s[2];   // scales / sums of rows lane and lane + 64, block `wave`
+    int32_t sums[2];      // Q4_K: code sums of rows lane and lane + 64, block `wave`
 
     __device__ void init(const int8_t* codes, const float* xscale, const int32_t* xsum, int m0, int M, int K) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -266,15 +285,10 @@ struct ActDirect {
             voff_a[i] = uint32_t(row * K + 16 * (ins >> 1));
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            // instruction j of wave w fills dword slots 64(2w+j) .. +63 of the [block][row] array
-            const int slot = 64 * (2 * wave + j) + lane;
-            const int b = slot >> 7, row = slot & (BM - 1);
-            voff_s[j] = uint32_t((row * KB + b) * 4);
-        }
+        for (int j = 0; j < 2; ++j) voff_s[j] = uint32_t(((lane + 64 * j) * KB + wave) * 4);
     }
 
-    __device__ void issue(Smem<QT>& sm, int buf, int k0) const {
+    __device__ void issue(Smem<QT>& sm, int buf, int k0) {
         const int wave = threadIdx.x >> 6;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -282,11 +296,22 @@ struct ActDirect {
                                                      voff_a[i], uint32_t(k0), 0, 0);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(&sm.dx[buf][0][0] + 64 * (2 * wave + j)), 4,
-                                                     voff_s[j], uint32_t(k0 >> 3), 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(&sm.dx[buf][wave][64 * j]), 4, voff_s[j],
+                                                     uint32_t(k0 >> 3), 0, 0);
             if constexpr (QT == kQ4_K)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (lds_void*)(&sm.sx[buf][0][0] + 64 * (2 * wave + j)),
-                                                         4, voff_s[j], uint32_t(k0 >> 3), 0, 0);
+                sums[j] = __builtin_amdgcn_raw_buffer_load_b32(ru, voff_s[j], uint32_t(k0 >> 3), 0);
+        }
+    }
+
+    // after this wave's loads of the step in `buf` have landed
+    __device__ void finish(Smem<QT>& sm, int buf) const {
+        if constexpr (QT == kQ4_K) {
+            const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int row = lane + 64 * j;
+                sm.tx[buf][wave][row] = bf16_hilo(sm.dx[buf][wave][row] * float(sums[j]));
+            }
         }
     }
 };
@@ -350,6 +375,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
     act.issue(sm, 0, kbeg);
     wait_vm_all();
     wr.store(sm, 0, kbeg);
+    act.finish(sm, 0);
     __syncthreads();
     if (kbeg + KS < kend) {
         wr.load(W, row_bytes, n0, N, kbeg + KS, K);
@@ -433,17 +459,19 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
                 }
             }
         };
-        // Q4_K min term of tile (i, j) for the step's 4 blocks:
-        // acc += sum_b (dx S)[m][b] * mw[n][b], two blocks per MFMA
+        // Q4_K min term of tile (i, j) for the step's 4 blocks, acc += sum_b tx[m][b] * mw[n][b]:
+        // one bf16 MFMA with K = 16 = 4 blocks x 4 slots; lane group g feeds blocks 2g, 2g+1,
+        // slots (hi*hi, hi*lo, lo*hi, 0) from the hi | lo << 16 packs.
         auto min_term = [&](int i, int j) {
             if constexpr (QT == kQ4_K) {
                 const int ar = arow0 + 32 * i, br = brow0 + 32 * j;
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const float to = sm.dx[buf][2 * q + g][ar] * float(sm.sx[buf][2 * q + g][ar]);
-                    const float mo = sm.mw[buf][2 * q + g][br];
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(to, mo, acc[i][j], 0, 0, 0);
-                }
+                const uint32_t t0 = sm.tx[buf][2 * g][ar], t1 = sm.tx[buf][2 * g + 1][ar];
+                const uint32_t w0 = sm.mw[buf][2 * g][br], w1 = sm.mw[buf][2 * g + 1][br];
+                const v4i a = {int((t0 & 0xFFFFu) | (t0 << 16)), int(t0 >> 16), int((t1 & 0xFFFFu) | (t1 << 16)),
+                               int(t1 >> 16)};
+                const v4i b = {int(w0), int(w0 & 0xFFFFu), int(w1), int(w1 & 0xFFFFu)};
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a),
+                                                                    __builtin_bit_cast(v8bf, b), acc[i][j], 0, 0, 0);
             }
         };
 
@@ -476,6 +504,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
         if (k0 + KS < kend) {
             wait_vm_all();
             wr.store(sm, buf ^ 1, k0 + KS);
+            act.finish(sm, buf ^ 1);
         }
         __syncthreads();   // buffer `buf` is free, buffer `buf ^ 1` is complete
         if (k0 + 2 * KS < kend) {

@@ -315,15 +315,17 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
         }
     };
 
-    // Every slot load is issued unconditionally (a slot past the end of the tile
-    // re-reads the tile's first unit, which is valid and cached), so the number
-    // of loads in flight is static and the compiler can wait for exactly the
-    // slot it needs (loads complete in issue order) instead of for all of them.
+    // A tile takes `iters` rounds of kThreads units (the last round partly dead).  The
+    // steady part of the loop issues every slot load unconditionally (a dead lane of the
+    // last round re-reads the tile's first unit, valid and cached), so the number of
+    // loads in flight is static and the compiler waits for exactly the slot it needs
+    // (loads complete in issue order); only the drain at the end of a tile, which issues
+    // no loads past the tile, waits for all.
     Unit buf[kSlots];
     Cursor ld, cp;
     int t0 = r_begin;
     const uint8_t* tile = W + int64_t(t0) * row_bytes;
-    int units = 0;
+    int units = 0, iters = 0;
     auto load_next = [&](int j) {
         const bool live = ld.f < units;
         buf[j].load(live ? ld.row : tile, live ? ld.u : 0);
@@ -331,6 +333,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
     };
     auto prime = [&](int tfirst) {
         units = min(rows_per_tile, r_end - tfirst) * U;
+        iters = (units + kThreads - 1) / kThreads;
         tile = W + int64_t(tfirst) * row_bytes;
         start(ld, tile);
         start(cp, tile);
@@ -408,12 +411,22 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
     for (; t0 < r_end; t0 += rows_per_tile) {
         const int rows = min(rows_per_tile, r_end - t0);
 
-        for (int base = 0; base < units; base += kSlots * kThreads) {
+        int it0 = 0;
+        for (; it0 + 2 * kSlots <= iters; it0 += kSlots) {
 #pragma unroll
             for (int j = 0; j < kSlots; ++j) {
                 if (cp.f < units) part[cp.f] = buf[j].dot(st, cp.u, cp.u);
                 advance(cp);
-                load_next(j);
+                load_next(j);   // round it0 + j + kSlots < iters: always a round of this tile
+            }
+        }
+        // drain: the last rounds, loading only rounds that exist (the conditions are uniform)
+#pragma unroll
+        for (int j = 0; j < 2 * kSlots; ++j) {
+            if (it0 + j < iters) {
+                if (cp.f < units) part[cp.f] = buf[j % kSlots].dot(st, cp.u, cp.u);
+                advance(cp);
+                if (it0 + j + kSlots < iters) load_next(j % kSlots);
             }
         }
         // Issue the next tile's first loads before summing this one.

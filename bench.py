@@ -307,6 +307,15 @@ def main():
         yh = torch.empty(152064, dtype=torch.float32, device=dev)
         us = timer.per_launch_us([lambda W=W: mq.gemv(W, Q6_K, xh, 152064, 3584, y=yh) for W in hcop], reps)
         sec["gemv_q6_K_head_152064x3584"] = {"us": round(us, 3), "GBps": round(hb / us / 1e3, 1)}
+        # small-M product on the head: M = 8 rows (a speculative-verify batch), q8 activations
+        Xh = torch.from_numpy(synth.activations(8, 3584, 2, tensor_index=5)).to(dev)
+        Xhq = mq.quantize_act(Xh)
+        Yh = torch.empty((8, 152064), dtype=torch.float32, device=dev)
+        sch = torch.empty(max(mq.gemm_scratch_bytes(Q6_K, 8, 152064, 3584), 256), dtype=torch.uint8, device=dev)
+        us = timer.per_launch_us([lambda W=W: mq.gemm(W, Q6_K, Xhq, 8, 152064, 3584, Y=Yh, scratch=sch)
+                                  for W in hcop], reps)
+        sec["mmq_q6_K_head_M8_152064x3584"] = {"us": round(us, 3), "weight_GBps": round(hb / us / 1e3, 1),
+                                               "TOPS": round(2 * 8 * 152064 * 3584 / us / 1e6, 2)}
         del hcop
         for N, K, tag in [(18944, 3584, "7B_ffn_up_shape"), (4864, 896, "0.5B_ffn_up")]:
             w8 = synth.quantized_weight(Q8_0, N, K, 0, 0)

@@ -60,23 +60,36 @@ typedef float v32f __attribute__((ext_vector_type(32)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-constexpr int BM = 128;
-constexpr int BN = 128;
+constexpr int BN = 128;         // output tile columns (weight rows)
 constexpr int KS = 128;        // K values per step (bytes per LDS row)
 constexpr int NB = KS / 32;    // 32-blocks per step
 constexpr int kXcds = 8;
 constexpr int kTargetWorkgroups = 512;   // two resident 256-thread workgroups on each of 256 CUs
 constexpr int kMinStepsPerSplit = 2;
+constexpr int kSmallM = 32;              // M up to this uses 32-row output tiles
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource: 32-bit data format, no swizzle
 
 template <int QT> struct Groups { static constexpr int per_step = NB; };
 template <> struct Groups<kQ6_K> { static constexpr int per_step = 2 * NB; };
 
+// Output tile rows: 128 for prefill-sized M, 32 for small M (at most 32 activation
+// rows), where a 128-row tile would be mostly padding.  Waves: WM x WN, each owning
+// TI x TJ MFMA tiles of 32 x 32.
+template <int BM_>
+struct TileShape {
+    static constexpr int BM = BM_;
+    static constexpr int WM = BM_ == 128 ? 2 : 1;
+    static constexpr int WN = 4 / WM;
+    static constexpr int TI = BM_ / (32 * WM);
+    static constexpr int TJ = BN / (32 * WN);
+};
+
 // LDS tiles are chunk-major: 16-byte chunk c (values 16c..16c+15 of the step) of row r
-// sits at c * 2048 + r * 16.  A fragment read (32 consecutive rows, one chunk) is then
-// 512 contiguous bytes, free of bank conflicts, and every address is a per-lane base
-// plus a compile-time offset.
-__device__ __forceinline__ int chk(int r, int c) { return c * (BM * 16) + r * 16; }
+// sits at c * 16 * rows + r * 16.  A fragment read (32 consecutive rows, one chunk) is
+// then 512 contiguous bytes, free of bank conflicts, and every address is a per-lane
+// base plus a compile-time offset.
+template <int ROWS>
+__device__ __forceinline__ int chk(int r, int c) { return c * (ROWS * 16) + r * 16; }
 
 // Row index (within a 32-row MFMA tile) of accumulator element v for lane group g = lane / 32.
 __device__ __forceinline__ int acc_row(int v, int g) { return 8 * (v >> 2) + 4 * g + (v & 3); }
@@ -96,7 +109,7 @@ __device__ __forceinline__ uint32_t bf16_hilo(float x) {
 // Wait for every outstanding vector-memory operation of this wave (LDS-direct loads included).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int QT>
+template <int QT, int BM>
 struct Smem {
     int8_t A[2][BM * KS];                               // activation codes
     int8_t B[2][BN * KS];                               // weight codes
@@ -129,7 +142,8 @@ template <> struct WeightRegs<kQ4_K> {
             q[it] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (4 * half + p0 + 2 * it));
         hd = *reinterpret_cast<const uint4*>(blk);
     }
-    __device__ void store(Smem<kQ4_K>& sm, int buf, int k0) const {
+    template <int BM>
+    __device__ void store(Smem<kQ4_K, BM>& sm, int buf, int k0) const {
         const int t = threadIdx.x, half = (k0 >> 7) & 1;
         const int row = t & (BN - 1), p0 = t >> 7;
         int8_t* Bs = sm.B[buf];
@@ -145,8 +159,8 @@ template <> struct WeightRegs<kQ4_K> {
                                         (v.z >> 4) & 0x0F0F0F0Fu, (v.w >> 4) & 0x0F0F0F0Fu);
             // group c holds values 64c..64c+63 of the step: low nibbles the first 32, high nibbles
             // the next 32; piece h is 16 bytes, i.e. 16-value chunks 4c + h (low) and 4c + h + 2 (high)
-            *reinterpret_cast<uint4*>(Bs + chk(row, 4 * c + h)) = lo;
-            *reinterpret_cast<uint4*>(Bs + chk(row, 4 * c + h + 2)) = hi;
+            *reinterpret_cast<uint4*>(Bs + chk<BN>(row, 4 * c + h)) = lo;
+            *reinterpret_cast<uint4*>(Bs + chk<BN>(row, 4 * c + h + 2)) = hi;
             // this thread also decodes step block jb = 2c + h (sub-block 4 half + jb of the
             // super-block); the branch inside is uniform (it depends on half only)
             const int jb = 2 * c + h;
@@ -179,7 +193,8 @@ template <> struct WeightRegs<kQ8_0> {
             for (int i = 0; i < 9; ++i) w[it][i] = p[i];
         }
     }
-    __device__ void store(Smem<kQ8_0>& sm, int buf, int) const {
+    template <int BM>
+    __device__ void store(Smem<kQ8_0, BM>& sm, int buf, int) const {
         const int t = threadIdx.x;
         const int row = t & (BN - 1);
         int8_t* Bs = sm.B[buf];
@@ -193,9 +208,9 @@ template <> struct WeightRegs<kQ8_0> {
             for (int i = 0; i < 8; ++i) c[i] = odd[it] ? w[it][i + 1] : align_byte(w[it][i + 1], w[it][i], 2);
             const float d = half_bits_to_float(odd[it] ? (w[it][0] >> 16) : (w[it][0] & 0xFFFFu));
             const uint32_t keep = live[it] ? 0xFFFFFFFFu : 0u;   // blocks past K contribute nothing
-            *reinterpret_cast<uint4*>(Bs + chk(row, 2 * bi)) =
+            *reinterpret_cast<uint4*>(Bs + chk<BN>(row, 2 * bi)) =
                 make_uint4(c[0] & keep, c[1] & keep, c[2] & keep, c[3] & keep);
-            *reinterpret_cast<uint4*>(Bs + chk(row, 2 * bi + 1)) =
+            *reinterpret_cast<uint4*>(Bs + chk<BN>(row, 2 * bi + 1)) =
                 make_uint4(c[4] & keep, c[5] & keep, c[6] & keep, c[7] & keep);
             sm.dw[buf][bi][row] = live[it] ? d : 0.f;
         }
@@ -225,7 +240,8 @@ template <> struct WeightRegs<kQ6_K> {
         s1 = load_u32_a2(blk + 192 + 8 * h + 4);
         dbits = load_u16(blk + 208);
     }
-    __device__ void store(Smem<kQ6_K>& sm, int buf, int) const {
+    template <int BM>
+    __device__ void store(Smem<kQ6_K, BM>& sm, int buf, int) const {
         const int t = threadIdx.x;
         int8_t* Bs = sm.B[buf];
 #pragma unroll
@@ -240,7 +256,7 @@ template <> struct WeightRegs<kQ6_K> {
                 // per byte: code - 32 as int8 ((c + 128) - 32, then flip the sign bit back)
                 code = ((code | 0x80808080u) - 0x20202020u) ^ 0x80808080u;
                 // values 32tt + 4p .. +3 of the step: chunk 2tt + p/4, bytes 4(p%4)..
-                *reinterpret_cast<uint32_t*>(Bs + chk(row, 2 * tt + (p >> 2)) + 4 * (p & 3)) = code;
+                *reinterpret_cast<uint32_t*>(Bs + chk<BN>(row, 2 * tt + (p >> 2)) + 4 * (p & 3)) = code;
             }
         }
         if (t < BN) {
@@ -258,16 +274,19 @@ template <> struct WeightRegs<kQ6_K> {
 // Activation codes and block scales of one K-step, loaded by each wave straight into
 // LDS.  One buffer_load ... lds instruction writes 64 lanes x 16 (or 4) consecutive LDS
 // bytes; each lane picks the global bytes that belong at its LDS slot.  Loads past the
-// tile's last row return zeros (buffer range check).  Wave w loads the scales of block w
-// of the step (all 128 rows); for Q4_K it also loads that block's code sums into
-// registers, and after its loads have landed forms the min-term factor dx * sum of the
-// rows itself (its own loads are complete after its own wait, before any barrier).
-template <int QT>
+// tile's last row return zeros (buffer range check).  The scales of the step form NB x BM
+// dword slots, 64 per instruction: wave w issues instructions 2w and 2w+1 (those that
+// exist); for Q4_K it also loads the matching code sums into registers, and after its
+// loads have landed forms the min-term factor dx * sum of those slots itself (its own
+// loads are complete after its own wait, before any barrier).
+template <int QT, int BM>
 struct ActDirect {
+    static constexpr int kCodeIns = BM / 32;           // 1 KB code instructions per wave
+    static constexpr int kScaleIns = NB * BM / 64;     // 64-dword scale instructions in all
     __amdgpu_buffer_rsrc_t rc, rs, ru;
-    uint32_t voff_a[4];   // codes: lane's byte offset for each of the wave's 4 instructions
-    uint32_t voff_s[2];   // scales / sums of rows lane and lane + 64, block `wave`
-    int32_t sums[2];      // Q4_K: code sums of rows lane and lane + 64, block `wave`
+    uint32_t voff_a[kCodeIns];   // codes: lane's byte offset per instruction
+    uint32_t voff_s[2];          // scales / sums: lane's byte offset per instruction
+    int32_t sums[2];             // Q4_K: code sums of the lane's two scale slots
 
     __device__ void init(const int8_t* codes, const float* xscale, const int32_t* xsum, int m0, int M, int K) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -277,47 +296,54 @@ struct ActDirect {
         rs = make_rsrc(xscale + int64_t(m0) * KB, int64_t(rows) * KB * 4);
         ru = make_rsrc(xsum + int64_t(m0) * KB, int64_t(rows) * KB * 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // instruction i of wave w fills LDS bytes 1024(4w+i) .. +1023: chunk (4w+i)/2 of
-            // rows 64((4w+i)%2) .. +63, one row per lane
-            const int ins = 4 * wave + i;
-            const int row = 64 * (ins & 1) + lane;
-            voff_a[i] = uint32_t(row * K + 16 * (ins >> 1));
+        for (int i = 0; i < kCodeIns; ++i) {
+            // instruction i of wave w fills LDS bytes 1024 (kCodeIns w + i) .. +1023 of the
+            // chunk-major tile: chunk o / (16 BM), row (o % (16 BM)) / 16 for byte o
+            const int o = 1024 * (kCodeIns * wave + i) + 16 * lane;
+            const int c = o / (16 * BM), row = (o % (16 * BM)) / 16;
+            voff_a[i] = uint32_t(row * K + 16 * c);
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) voff_s[j] = uint32_t(((lane + 64 * j) * KB + wave) * 4);
+        for (int j = 0; j < 2; ++j) {
+            const int slot = 64 * (2 * wave + j) + lane;   // block slot / BM, row slot % BM
+            voff_s[j] = uint32_t(((slot % BM) * KB + slot / BM) * 4);
+        }
     }
 
-    __device__ void issue(Smem<QT>& sm, int buf, int k0) {
+    __device__ void issue(Smem<QT, BM>& sm, int buf, int k0) {
         const int wave = threadIdx.x >> 6;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void*)(sm.A[buf] + 1024 * (4 * wave + i)), 16,
+        for (int i = 0; i < kCodeIns; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void*)(sm.A[buf] + 1024 * (kCodeIns * wave + i)), 16,
                                                      voff_a[i], uint32_t(k0), 0, 0);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(&sm.dx[buf][wave][64 * j]), 4, voff_s[j],
-                                                     uint32_t(k0 >> 3), 0, 0);
-            if constexpr (QT == kQ4_K)
-                sums[j] = __builtin_amdgcn_raw_buffer_load_b32(ru, voff_s[j], uint32_t(k0 >> 3), 0);
+            if (2 * wave + j < kScaleIns) {   // uniform
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(&sm.dx[buf][0][0] + 64 * (2 * wave + j)), 4,
+                                                         voff_s[j], uint32_t(k0 >> 3), 0, 0);
+                if constexpr (QT == kQ4_K)
+                    sums[j] = __builtin_amdgcn_raw_buffer_load_b32(ru, voff_s[j], uint32_t(k0 >> 3), 0);
+            }
         }
     }
 
     // after this wave's loads of the step in `buf` have landed
-    __device__ void finish(Smem<QT>& sm, int buf) const {
+    __device__ void finish(Smem<QT, BM>& sm, int buf) const {
         if constexpr (QT == kQ4_K) {
             const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const int row = lane + 64 * j;
-                sm.tx[buf][wave][row] = bf16_hilo(sm.dx[buf][wave][row] * float(sums[j]));
+                if (2 * wave + j < kScaleIns) {
+                    const int slot = 64 * (2 * wave + j) + lane;
+                    (&sm.tx[buf][0][0])[slot] = bf16_hilo((&sm.dx[buf][0][0])[slot] * float(sums[j]));
+                }
             }
         }
     }
 };
 
 // ------------------------------------------------------------------ kernel
-template <int QT, bool DUMP>
+template <int QT, int BM, bool DUMP>
 __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__ W,
                                                      const int8_t* __restrict__ codes,
                                                      const float* __restrict__ xscale,
@@ -326,7 +352,9 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
                                                      float* __restrict__ partial, int M, int N, int K,
                                                      int64_t row_bytes, int tiles_m, int full, int split_tiles,
                                                      int splits, int total_steps) {
-    __shared__ __attribute__((aligned(16))) Smem<QT> sm;
+    using T = TileShape<BM>;
+    constexpr int TI = T::TI, TJ = T::TJ;
+    __shared__ __attribute__((aligned(16))) Smem<QT, BM> sm;
 
     // Work split (MmqPlan): workgroups [0, full) own whole tiles 0..full-1; the remaining
     // split_tiles tiles are each cut into `splits` K ranges, one workgroup per range, whose
@@ -347,26 +375,26 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
     // K range: steps [s0, s1) of KS values
     const int kbeg = int(int64_t(split) * total_steps / nsplit) * KS;
     const int kend = min(int(int64_t(split + 1) * total_steps / nsplit) * KS, K);
-    // a split tile's partial goes to its own 128 x 128 slot of the partial buffer
+    // a split tile's partial goes to its own BM x BN slot of the partial buffer
     float* Pt = whole ? nullptr : partial + (int64_t(split) * split_tiles + (tile - full)) * (BM * BN);
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / T::WN, wn = wave % T::WN;
     const int g = lane >> 5;   // lane group: which half of a block's K this lane feeds
     const int r32 = lane & 31;
     const int KB = K >> 5;
 
-    v16f acc[2][2];
+    v16f acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    ActDirect<QT> act;
+    ActDirect<QT, BM> act;
     act.init(codes, xscale, xsum, m0, M, K);
     WeightRegs<QT> wr;
 
@@ -388,16 +416,17 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
         constexpr int buf = decltype(buf_c)::value;
         const int8_t* As = sm.A[buf];
         const int8_t* Bs = sm.B[buf];
-        const int arow0 = 64 * wm + r32;   // + 32 i
-        const int brow0 = 64 * wn + r32;   // + 32 j
+        const int arow0 = 32 * TI * wm + r32;   // + 32 i
+        const int brow0 = 32 * TJ * wn + r32;   // + 32 j
 
-        // Tile products of the step, k = 4p + 2i + j (block pair p, or block p for Q6_K's two
-        // 16-value groups; tiles i, j).  Product k needs: S (the scale outer product, 32
+        // Tile products of the step, k = (TI TJ) p + TJ i + j (block pair p, or block p for
+        // Q6_K's two 16-value groups; tiles i, j).  Product k needs: S (the scale outer product, 32
         // regs) and two int32 dot tiles D0, D1 (16 regs each).  Pipeline: S of product k+1
         // is issued when product k starts; D0 of product k+1 as soon as product k has used
         // its D0, D1 likewise, so every matrix-unit result has a half product of vector work
         // to arrive in.
-        constexpr int kProducts = QT == kQ6_K ? 16 : 8;
+        constexpr int kTiles = TI * TJ;
+        constexpr int kProducts = (QT == kQ6_K ? 4 : 2) * kTiles;
         v32f S[2];
         v16i D0, D1;
         // operands of the next product's dot tiles
@@ -405,19 +434,19 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
         long la0, la1, lb0, lb1;  // 8-byte fragments (Q6_K)
         float sdx, sdw;           // the next product's scale-outer-product operands
         auto frag = [&](int k) {
-            const int p = k >> 2, i = (k >> 1) & 1, j = k & 1;
+            const int p = k / kTiles, i = (k / TJ) % TI, j = k % TJ;
             const int ar = arow0 + 32 * i, br = brow0 + 32 * j;
             if constexpr (QT != kQ6_K) {
-                na0 = *reinterpret_cast<const v4i*>(As + chk(ar, 4 * p + g));
-                na1 = *reinterpret_cast<const v4i*>(As + chk(ar, 4 * p + 2 + g));
-                nb0 = *reinterpret_cast<const v4i*>(Bs + chk(br, 4 * p + g));
-                nb1 = *reinterpret_cast<const v4i*>(Bs + chk(br, 4 * p + 2 + g));
+                na0 = *reinterpret_cast<const v4i*>(As + chk<BM>(ar, 4 * p + g));
+                na1 = *reinterpret_cast<const v4i*>(As + chk<BM>(ar, 4 * p + 2 + g));
+                nb0 = *reinterpret_cast<const v4i*>(Bs + chk<BN>(br, 4 * p + g));
+                nb1 = *reinterpret_cast<const v4i*>(Bs + chk<BN>(br, 4 * p + 2 + g));
                 sdx = sm.dx[buf][2 * p + g][ar];   // block 2p + g (lane group g feeds block g of the pair)
             } else {
-                la0 = *reinterpret_cast<const long*>(As + chk(ar, 2 * p) + 8 * g);
-                la1 = *reinterpret_cast<const long*>(As + chk(ar, 2 * p + 1) + 8 * g);
-                lb0 = *reinterpret_cast<const long*>(Bs + chk(br, 2 * p) + 8 * g);
-                lb1 = *reinterpret_cast<const long*>(Bs + chk(br, 2 * p + 1) + 8 * g);
+                la0 = *reinterpret_cast<const long*>(As + chk<BM>(ar, 2 * p) + 8 * g);
+                la1 = *reinterpret_cast<const long*>(As + chk<BM>(ar, 2 * p + 1) + 8 * g);
+                lb0 = *reinterpret_cast<const long*>(Bs + chk<BN>(br, 2 * p) + 8 * g);
+                lb1 = *reinterpret_cast<const long*>(Bs + chk<BN>(br, 2 * p + 1) + 8 * g);
                 sdx = sm.dx[buf][p][ar];           // one block scale for both groups
             }
             sdw = sm.dw[buf][2 * p + g][br];
@@ -440,7 +469,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
         };
         // acc += float(D) * S-half h, and the block-dot export
         auto consume = [&](int k, const v32f& Sk, const v16i& D, int h) {
-            const int p = k >> 2, i = (k >> 1) & 1, j = k & 1;
+            const int p = k / kTiles, i = (k / TJ) % TI, j = k % TJ;
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = fmaf(float(D[v]), Sk[16 * h + v], acc[i][j][v]);
             // pin the accumulation here: without it the compiler sinks all vector work of
@@ -454,7 +483,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
                 const int gi = QT == kQ6_K ? 2 * kb + h : kb;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int m = m0 + 64 * wm + 32 * i + acc_row(v, g);
+                    const int m = m0 + 32 * TI * wm + 32 * i + acc_row(v, g);
                     if (m < M && nn < N && kb < KB) dots[(int64_t(m) * N + nn) * G + gi] = D[v];
                 }
             }
@@ -498,7 +527,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
             __builtin_amdgcn_sched_barrier(0);
             if (more) dot1();
             __builtin_amdgcn_sched_barrier(0);
-            if (QT == kQ4_K && (k >> 2) == 1) min_term((k >> 1) & 1, k & 1);
+            if (QT == kQ4_K && k / kTiles == 1) min_term((k / TJ) % TI, k % TJ);
         }
         // next step: its weight registers and LDS-direct loads were issued a step ago
         if (k0 + KS < kend) {
@@ -524,13 +553,13 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
     // The block-dot export variant stores only the dots.
     if constexpr (DUMP) return;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int nl = 64 * wn + 32 * j + r32;
+        for (int j = 0; j < TJ; ++j) {
+            const int nl = 32 * TJ * wn + 32 * j + r32;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int ml = 64 * wm + 32 * i + acc_row(v, g);
+                const int ml = 32 * TI * wm + 32 * i + acc_row(v, g);
                 if (!whole) {
                     Pt[ml * BN + nl] = acc[i][j][v];
                 } else if (m0 + ml < M && n0 + nl < N) {
@@ -540,16 +569,16 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
         }
 }
 
-// Sum of the partial tiles P[splits][split_tiles][BM x BN] of the split tiles, in split
+// Sum of the partial tiles P[splits][split_tiles][bm x BN] of the split tiles, in split
 // order (deterministic), into Y.  Split tile t is tile full + t.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, float* __restrict__ Y,
-                                                            int M, int N, int tiles_m, int full, int split_tiles,
-                                                            int splits) {
+                                                            int M, int N, int bm, int tiles_m, int full,
+                                                            int split_tiles, int splits) {
     const int t = blockIdx.y;
     const int tile = full + t;
-    const int m0 = (tile % tiles_m) * BM, n0 = (tile / tiles_m) * BN;
-    const int64_t slot = int64_t(BM) * BN;
-    for (int e = blockIdx.x * 256 + threadIdx.x; e < BM * BN; e += gridDim.x * 256) {
+    const int m0 = (tile % tiles_m) * bm, n0 = (tile / tiles_m) * BN;
+    const int64_t slot = int64_t(bm) * BN;
+    for (int e = blockIdx.x * 256 + threadIdx.x; e < bm * BN; e += gridDim.x * 256) {
         const int m = m0 + e / BN, n = n0 + e % BN;
         if (m >= M || n >= N) continue;
         float acc = P[int64_t(t) * slot + e];
@@ -558,27 +587,57 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
+// Explicit instantiations: the host-side launch stubs of these kernels are otherwise not
+// emitted by this compiler when they are only named inside launch_shaped below.
+#define MQ_MMQ_INSTANCE(QT, BM, DUMP)                                                                        \
+    template __global__ void mmq_kernel<QT, BM, DUMP>(const uint8_t* __restrict__, const int8_t* __restrict__, \
+                                                      const float* __restrict__, const int32_t* __restrict__,  \
+                                                      float* __restrict__, int32_t* __restrict__,              \
+                                                      float* __restrict__, int, int, int, int64_t, int, int, int, \
+                                                      int, int);
+MQ_MMQ_INSTANCE(kQ8_0, 32, false)
+MQ_MMQ_INSTANCE(kQ8_0, 128, false)
+MQ_MMQ_INSTANCE(kQ4_K, 32, false)
+MQ_MMQ_INSTANCE(kQ4_K, 128, false)
+MQ_MMQ_INSTANCE(kQ6_K, 32, false)
+MQ_MMQ_INSTANCE(kQ6_K, 128, false)
+MQ_MMQ_INSTANCE(kQ8_0, 32, true)
+MQ_MMQ_INSTANCE(kQ8_0, 128, true)
+MQ_MMQ_INSTANCE(kQ4_K, 32, true)
+MQ_MMQ_INSTANCE(kQ4_K, 128, true)
+MQ_MMQ_INSTANCE(kQ6_K, 32, true)
+MQ_MMQ_INSTANCE(kQ6_K, 128, true)
+#undef MQ_MMQ_INSTANCE
+
+template <int QT, int BM>
+hipError_t launch_shaped(const uint8_t* W, const int8_t* codes, const float* xs, const int32_t* xsum, float* Y,
+                         int32_t* dots, float* partial, int64_t M, int64_t N, int64_t K, int64_t row_bytes,
+                         const MmqPlan& plan, hipStream_t s) {
+    const int tiles_m = int((M + BM - 1) / BM);
+    const int total = plan.full + plan.split_tiles * plan.splits;
+    if (dots) {
+        hipLaunchKernelGGL((mmq_kernel<QT, BM, true>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, Y, dots,
+                           partial, int(M), int(N), int(K), row_bytes, tiles_m, plan.full, plan.split_tiles,
+                           plan.splits, plan.steps);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((mmq_kernel<QT, BM, false>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, Y, dots,
+                       partial, int(M), int(N), int(K), row_bytes, tiles_m, plan.full, plan.split_tiles, plan.splits,
+                       plan.steps);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || plan.split_tiles == 0) return e;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(BM * BN / 256, plan.split_tiles), dim3(256), 0, s, partial, Y,
+                       int(M), int(N), BM, tiles_m, plan.full, plan.split_tiles, plan.splits);
+    return hipGetLastError();
+}
+
 template <int QT>
 hipError_t launch_typed(const uint8_t* W, const int8_t* codes, const float* xs, const int32_t* xsum,
                         float* Y, int32_t* dots, float* partial, int64_t M, int64_t N, int64_t K,
                         int64_t row_bytes, hipStream_t s) {
     const MmqPlan plan = mmq_plan(QT, M, N, K);
-    const int tiles_m = int((M + BM - 1) / BM);
-    const int total = plan.full + plan.split_tiles * plan.splits;
-    if (dots) {
-        hipLaunchKernelGGL((mmq_kernel<QT, true>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, Y, dots,
-                           partial, int(M), int(N), int(K), row_bytes, tiles_m, plan.full, plan.split_tiles,
-                           plan.splits, plan.steps);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL((mmq_kernel<QT, false>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, Y, dots, partial,
-                       int(M), int(N), int(K), row_bytes, tiles_m, plan.full, plan.split_tiles, plan.splits,
-                       plan.steps);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || plan.split_tiles == 0) return e;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(BM * BN / 256, plan.split_tiles), dim3(256), 0, s, partial, Y, int(M),
-                       int(N), tiles_m, plan.full, plan.split_tiles, plan.splits);
-    return hipGetLastError();
+    if (plan.bm == 32) return launch_shaped<QT, 32>(W, codes, xs, xsum, Y, dots, partial, M, N, K, row_bytes, plan, s);
+    return launch_shaped<QT, 128>(W, codes, xs, xsum, Y, dots, partial, M, N, K, row_bytes, plan, s);
 }
 
 }  // namespace
@@ -590,8 +649,9 @@ MmqPlan mmq_plan(int /*type*/, int64_t M, int64_t N, int64_t K) {
     // enough of them to fill that round.  A function of the shape alone, so the result does
     // not depend on the device.
     MmqPlan p;
+    p.bm = M <= kSmallM ? 32 : 128;
     p.steps = int((K + KS - 1) / KS);
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + BN - 1) / BN);
     const int64_t rem = tiles % kTargetWorkgroups;
     p.full = int(tiles);
     p.split_tiles = 0;
@@ -609,7 +669,7 @@ MmqPlan mmq_plan(int /*type*/, int64_t M, int64_t N, int64_t K) {
 
 size_t mmq_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
     const MmqPlan p = mmq_plan(type, M, N, K);
-    return size_t(p.split_tiles) * size_t(p.splits) * BM * BN * sizeof(float);
+    return size_t(p.split_tiles) * size_t(p.splits) * size_t(p.bm) * BN * sizeof(float);
 }
 
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* codes, const float* xs, const int32_t* xsum,

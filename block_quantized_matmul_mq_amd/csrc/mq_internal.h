@@ -33,10 +33,11 @@ int gemv_tile_units(int type, int64_t K, size_t lds_limit);
 hipError_t gemv_set_attributes(size_t lds_limit);
 hipError_t launch_gemv(int type, const uint8_t* W, const float* x, float* y, int64_t N, int64_t K,
                        hipStream_t s, const char** kernel_name);
-// MMQ work split over 128 x 128 output tiles: the first `full` tiles are computed whole;
+// MMQ work split over bm x 128 output tiles: the first `full` tiles are computed whole;
 // each of the remaining `split_tiles` is cut into `splits` ranges of whole 128-value
 // K-steps, whose f32 partial tiles (mmq_scratch_bytes of scratch) a second launch sums.
 struct MmqPlan {
+    int bm;            // output tile rows: 32 (M <= 32) or 128
     int full;
     int split_tiles;
     int splits;

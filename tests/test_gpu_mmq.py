@@ -95,6 +95,18 @@ def test_split_k_uneven_ranges(qtype):
 
 
 @pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
+def test_small_m_tiles_at_the_switch(qtype):
+    # M <= 32 uses 32-row output tiles, M = 33 the 128-row ones; both with a ragged N.
+    K = 2 * BLOCK[qtype] + 256
+    for i, M in enumerate([32, 33]):
+        N = 200
+        raw = weights(qtype, N, K, "random", 90 + i)
+        X = synth.activations(M, K, config_index=12, tensor_index=40 + i)
+        check_blockdots(raw, qtype, X, N, K, f"M={M}")
+        check_gemm(raw, qtype, X, N, K, what=f"M={M}")
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
 def test_whole_tiles_plus_split_tail(qtype):
     # 520 output tiles: 512 computed whole, the last 8 cut into K ranges and summed by the
     # second launch; columns are sampled from both kinds of tile (the last 8 tiles are the

@@ -285,9 +285,10 @@ def main():
         "mmq_dtype": "i8 x i8 -> i32 block dots, f32 scales",
         "roofline": {"bound": "hbm", "achieved": round(gemv_alg_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gemv_alg_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": recorded_traffic("gemv_q4k_7b_ffn_hbm_traffic.txt", ["gemv.hip", "mq_device.h"]),
+                     "traffic": recorded_traffic("gemv_q4k_7b_ffn_hbm_traffic.txt",
+                                                 ["gemv.hip", "gemv_mfma.hip", "mq_device.h"]),
                      "algorithmic_bytes_per_launch": gemv_alg_bytes,
-                     "kernel": "gemv<q4_K> (ffn_up + ffn_down)",
+                     "kernel": f"{kernel_names['gemv_ffn_up']} (ffn_up) + {kernel_names['gemv_ffn_down']} (ffn_down)",
                      "ffn_up_GBps": round(up_gbps, 1), "ffn_down_GBps": round(down_gbps, 1)},
         "roofline_mmq": {"bound": "mfma", "achieved": round(mmq_up_tops, 2), "peak": INT8_PEAK_TOPS,
                          "unit": "TOP/s", "frac": round(mmq_up_tops / INT8_PEAK_TOPS, 4),

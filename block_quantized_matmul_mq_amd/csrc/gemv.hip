@@ -521,6 +521,17 @@ Config chosen_config(int type) {
     return default_config(type);
 }
 
+// Wide Q4_K matrices go to the matrix-core kernel unless MQ_GEMV_MFMA=0 (read once;
+// bench A/B only).
+bool use_mfma() {
+    static int v = -1;
+    if (v < 0) {
+        const char* e = getenv("MQ_GEMV_MFMA");
+        v = (e && e[0] == '0') ? 0 : 1;
+    }
+    return v == 1;
+}
+
 }  // namespace
 
 // Largest tile (in units) that fits next to the staged x; 0 if not even one row fits.
@@ -550,6 +561,8 @@ hipError_t launch_gemv(int type, const uint8_t* W, const float* x, float* y, int
                        hipStream_t s, const char** name) {
     const DeviceInfo* info = device_info();
     if (!info) return hipErrorInvalidDevice;
+    if (use_mfma() && gemv_mfma_applies(type, N, K, info->cu_count))
+        return launch_gemv_mfma(W, x, y, N, K, info->cu_count, s, name);
     int tile = gemv_tile_units(type, K, info->lds_per_block);
     if (tile <= 0) return hipErrorInvalidValue;
     const int vals = type == kQ8_0 ? 32 : 64;

@@ -1,0 +1,312 @@
+// mq_gemv for wide Q4_K matrices: y = deq(W) x for one f32 activation row (the decode
+// product of "minfer CUDA Backend Design", 4.4 Execution dispatch), with the integer
+// dot products on int8 matrix cores and the weights streamed through LDS.
+//
+// Work split.  The matrix is cut into tiles of 16 rows, dealt round-robin to the
+// workgroups (one per CU): tile t goes to workgroup t % G, so at any moment the GPU reads
+// one window of consecutive tiles (faster on HBM than one separate stream per CU).
+// Inside a workgroup, wave w owns super-block w of every row (rows of up to 16
+// super-blocks, K <= 4096): its work item for a tile is that super-block of the tile's
+// 16 rows, 16 x 144 bytes.  Each wave streams its own items into its own LDS ring of NB
+// slots with buffer_load ... lds (16 consecutive bytes per lane, 9 lanes per 144-byte
+// block) and waits only for its own loads, so the main loop has no workgroup barrier:
+// a wave computes an item as soon as its bytes have landed, with NB - 1 items in flight.
+//
+// Activation.  x is staged once per workgroup in an exact integer form: per 32-value
+// block b, x = 2^e_b * v with v = rint(x * 2^-e_b) of at most 21 bits (e_b puts the block
+// maximum in [2^20, 2^21)); v is kept as three signed byte planes v = 65536 d2 + 256 d1 +
+// d0.  Since a wave always sees the same super-block, it keeps that super-block's digits
+// (the MFMA A operands), exponents and block sums in registers.
+//
+// Products.  v_mfma_i32_16x16x64_i8 on one item:
+//   B (64 x 16): column n = row n of the tile; lane group q (lanes 16q .. 16q + 15) holds
+//                16 codes of unit q (values 64q .. 64q + 63 of the super-block);
+//   A (16 x 64): row 4q + p (p < 3) = digit plane p of the same 16 values in lane group q
+//                and zero in the other groups; rows 4q + 3 are zero too.
+// So C[4q + p][n] = exact sum over unit q's 16 values of code * d_p, and lane (n, q) gets
+// exactly its own unit's three plane sums (C rows 4q .. 4q + 2 of column n).  Two MFMAs
+// cover a 32-value sub-block (low nibbles: sub-block 2q, high nibbles: 2q + 1), four an
+// item.  Each lane then applies its two sub-blocks' 6-bit scales and mins:
+//   y[n] += d * sc * 2^e * sum(code * v) - dmin * m * sum(x)      (per sub-block).
+// The four lanes of a row are summed with two lane swaps; each wave leaves one partial
+// per row and tile in LDS, and the partials of a row are summed in wave order at the end
+// (deterministic).
+#include <utility>
+
+#include "mq_device.h"
+#include "mq_internal.h"
+
+namespace mq {
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kTileRows = 16;
+constexpr int kMaxSB = kWaves;                     // super-blocks per row: one per wave
+constexpr int kMinSB = 12;                         // fewer leaves too many waves idle
+constexpr int kItemBytes = kTileRows * 144;        // 2304: one super-block of 16 rows
+constexpr int kFracBits = 21;
+constexpr int kBufferWord3 = 0x00020000;           // raw buffer resource: 32-bit data format, no swizzle
+constexpr int kStageBytes = 16384;                 // x staging, later the row partials
+constexpr int kMaxTilesPerGroup = kStageBytes / (kTileRows * kWaves * 4);
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, n - 1>)
+template <class F, int... i>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, i...>) {
+    (f(std::integral_constant<int, i>{}), ...);
+}
+template <int n, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, n>{});
+}
+
+// Wait until at most n vector memory operations of this wave are outstanding and its
+// LDS operations are done, then a workgroup barrier.  (__syncthreads would also wait for
+// every load in flight: its workgroup fence covers global memory.)  The "memory" clobber
+// keeps the compiler from moving LDS accesses across it.
+template <int n>
+__device__ __forceinline__ void wait_barrier() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(n) : "memory");
+}
+
+// Byte k of four dwords -> one dword (a 4 x 4 byte transpose, three planes).
+__device__ __forceinline__ void transpose3(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3, uint32_t& p0,
+                                           uint32_t& p1, uint32_t& p2) {
+    const uint32_t t01 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);   // r0.b0 r1.b0 r0.b1 r1.b1
+    const uint32_t t23 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
+    p0 = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+    p1 = __builtin_amdgcn_perm(t23, t01, 0x07060302u);
+    const uint32_t u01 = __builtin_amdgcn_perm(r1, r0, 0x00000602u);   // r0.b2 r1.b2
+    const uint32_t u23 = __builtin_amdgcn_perm(r3, r2, 0x00000602u);
+    p2 = __builtin_amdgcn_perm(u23, u01, 0x05040100u);
+}
+
+// Signed digits of v = rint(x * 2^k) (|v| <= 2^21) in bytes 0..2:
+// (v + 0x808080) has unsigned bytes b_i = d_i + 128, and b_i ^ 0x80 is d_i as int8.
+__device__ __forceinline__ uint32_t digits3(float x, int k) {
+    const float f = ldexpf(x, k) + 12582912.0f;   // 1.5 * 2^23: the low mantissa bits are rint(x*2^k)
+    return (__float_as_uint(f) - 0x4ABF7F80u) ^ 0x00808080u;
+}
+
+__device__ __forceinline__ int combine3(const v4i c) {
+    return (((c[2] << 8) + c[1]) << 8) + c[0];   // exact: |sum code * v| <= 32 * 15 * 2^21 < 2^31
+}
+
+// Sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (v_permlane16_swap, v_permlane32_swap).
+__device__ __forceinline__ float sum_lane_groups(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// NB: LDS ring slots per wave (items in flight + the one being computed).
+template <int NB>
+__global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_kernel(const uint8_t* __restrict__ W,
+                                                                 const float* __restrict__ x,
+                                                                 float* __restrict__ y, int N, int K,
+                                                                 int row_bytes) {
+    // One static array per ring slot: with compile-time slot numbers the compiler knows
+    // which slot a read touches and waits for that slot's loads only.
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[kWaves * kItemBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[kWaves * kItemBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t ring2[NB > 2 ? kWaves * kItemBytes : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t ring3[NB > 3 ? kWaves * kItemBytes : 16];
+    // x staging (digit planes [3][K], block exponents, block sums), then row partials
+    // [tile][row][wave]: a barrier separates the last read of the one from the first
+    // write of the other.
+    __shared__ __attribute__((aligned(16))) uint8_t stage_lds[kStageBytes];
+    auto slot = [&](auto b) -> uint8_t* {
+        constexpr int B = decltype(b)::value;
+        if constexpr (B == 0) return ring0;
+        else if constexpr (B == 1) return ring1;
+        else if constexpr (B == 2) return ring2;
+        else return ring3;
+    };
+    int8_t* xp = reinterpret_cast<int8_t*>(stage_lds);
+    int* ex = reinterpret_cast<int*>(stage_lds + 3 * 256 * kMaxSB);
+    float* sums = reinterpret_cast<float*>(ex + 8 * kMaxSB);
+    float* part = reinterpret_cast<float*>(stage_lds);
+
+    const int SB = K >> 8;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = gridDim.x, w0 = blockIdx.x;
+    const int T = (N + kTileRows - 1) / kTileRows;
+    const int tiles = (T - w0 + G - 1) / G;   // this workgroup's: global tiles w0 + k G
+    const int TB = kTileRows * row_bytes;
+    const bool active = wave < SB;            // uniform: waves past the row's super-blocks only stage x
+
+    // x first: loads complete in issue order, so x is requested before the weights.
+    const int nquads = K >> 2;
+    float4 xe = {};
+    if (tid < nquads) xe = reinterpret_cast<const float4*>(x)[tid];
+
+    // The matrix as one buffer: rows past the last (the last tile's tail, tiles past the
+    // end) read as zeros through the buffer range check.
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W), 0, N * row_bytes, kBufferWord3);
+    // This wave's item of a tile: 144 16-byte chunks c (row c / 9, bytes 16 (c % 9) of the
+    // row's super-block), to slot bytes 16 c: chunks 0..63 and 64..127 with 16-byte lanes,
+    // chunks 128..143 with 4-byte lanes.
+    // Idle waves issue the same loads (so that every wave runs the same load sequence and
+    // the compiler's wait counts stay exact), all past the end of the buffer: they move no
+    // data (offsets from 2^31 on; every real offset is below 2^31).
+    auto chunk_offset = [&](int c) {
+        return active ? uint32_t((c / 9) * row_bytes + wave * 144 + 16 * (c % 9)) : 0x80000000u;
+    };
+    const uint32_t vo0 = chunk_offset(lane);
+    const uint32_t vo1 = chunk_offset(64 + lane);
+    const uint32_t vo2 = chunk_offset(128 + (lane >> 2)) + 4 * (lane & 3);
+    auto issue = [&](auto b, int k) {
+        uint8_t* dst = slot(b) + wave * kItemBytes;
+        const uint32_t base = uint32_t((w0 + k * G) * TB);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)dst, 16, base + vo0, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(dst + 1024), 16, base + vo1, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(dst + 2048), 4, base + vo2, 0, 0, 0);
+    };
+    // Every wave requests its x before any wave requests weights: a CU returns loads in
+    // order, and x queued behind the weight stream would arrive microseconds late.
+    asm volatile("s_barrier" ::: "memory");
+    static_for<NB - 1>([&](auto b) { issue(b, decltype(b)::value); });
+
+    // Stage x: 8 lanes per 32-block, 4 values (one float4) per lane; plane-major digits.
+    if (tid < nquads) {   // uniform per wave: K is a multiple of 256
+        const float4 v = xe;
+        float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        a = fmaxf(a, __shfl_xor(a, 1, 64));
+        a = fmaxf(a, __shfl_xor(a, 2, 64));
+        a = fmaxf(a, __shfl_xor(a, 4, 64));
+        // amax = m * 2^E, m in [0.5, 1): scale by 2^(21 - E) puts the block in [2^20, 2^21)
+        const int k = kFracBits - __builtin_amdgcn_frexp_expf(a);
+        uint32_t d0, d1, d2;
+        transpose3(digits3(v.x, k), digits3(v.y, k), digits3(v.z, k), digits3(v.w, k), d0, d1, d2);
+        *reinterpret_cast<uint32_t*>(xp + 4 * tid) = d0;
+        *reinterpret_cast<uint32_t*>(xp + K + 4 * tid) = d1;
+        *reinterpret_cast<uint32_t*>(xp + 2 * K + 4 * tid) = d2;
+        float sm = (v.x + v.y) + (v.z + v.w);
+        sm += __shfl_xor(sm, 1, 64);
+        sm += __shfl_xor(sm, 2, 64);
+        sm += __shfl_xor(sm, 4, 64);
+        if ((tid & 7) == 0) {
+            sums[tid >> 3] = sm;
+            ex[tid >> 3] = -k;
+        }
+    }
+    wait_barrier<(NB - 1) * 3>();   // x staged; the weight loads stay in flight
+
+    // Lane roles: B column n (row n of the tile) with unit q of this wave's super-block;
+    // A row n of lane group q is digit plane n & 3 of unit q's values when n / 4 == q and
+    // n & 3 < 3, else zero.
+    const int n = lane & 15, q = lane >> 4;
+    const int sb = active ? wave : 0;
+    v4i a0 = {0, 0, 0, 0}, a1 = a0, a2 = a0, a3 = a0;
+    if ((n >> 2) == q && (n & 3) < 3) {
+        const int8_t* ap = xp + (n & 3) * K + 256 * sb + 64 * q;
+        a0 = *reinterpret_cast<const v4i*>(ap);
+        a1 = *reinterpret_cast<const v4i*>(ap + 16);
+        a2 = *reinterpret_cast<const v4i*>(ap + 32);
+        a3 = *reinterpret_cast<const v4i*>(ap + 48);
+    }
+    const int2 e2 = *reinterpret_cast<const int2*>(ex + 8 * sb + 2 * q);        // sub-blocks 2q, 2q + 1
+    const float2 s2 = *reinterpret_cast<const float2*>(sums + 8 * sb + 2 * q);
+    // (scale, min) bytes of sub-blocks 2q, 2q + 1 from the packed 12-byte field (per-lane q)
+    const uint32_t sc_shift = 16u * uint32_t(q & 1);
+    wait_barrier<(NB - 1) * 3>();   // x no longer read: its LDS now takes the partials
+
+    auto compute = [&](const uint8_t* it, int k) {
+        const uint8_t* blk = it + n * 144;
+        const uint4 hd = *reinterpret_cast<const uint4*>(blk);
+        const v4i c0 = *reinterpret_cast<const v4i*>(blk + 16 + 32 * q);
+        const v4i c1 = *reinterpret_cast<const v4i*>(blk + 32 + 32 * q);
+        const v4i z = {0, 0, 0, 0};
+        v4i clo = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, c0 & 0x0F0F0F0F, z, 0, 0, 0);
+        clo = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, c1 & 0x0F0F0F0F, clo, 0, 0, 0);
+        v4i chi = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, (c0 >> 4) & 0x0F0F0F0F, z, 0, 0, 0);
+        chi = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, (c1 >> 4) & 0x0F0F0F0F, chi, 0, 0, 0);
+        const int ilo = combine3(clo), ihi = combine3(chi);
+        const uint32_t t0 = hd.y >> sc_shift, t1 = hd.z >> sc_shift, t2 = hd.w >> sc_shift;
+        const uint32_t sc_hi = (t2 & 0x0F0Fu) | ((t0 >> 2) & 0x3030u);
+        const uint32_t mn_hi = ((t2 >> 4) & 0x0F0Fu) | ((t1 >> 2) & 0x3030u);
+        const uint32_t scp = q >= 2 ? sc_hi : (t0 & 0x3F3Fu);
+        const uint32_t mnp = q >= 2 ? mn_hi : (t1 & 0x3F3Fu);
+        const float d = half_bits_to_float(hd.x & 0xFFFFu);
+        const float dmin = half_bits_to_float(hd.x >> 16);
+        const float codes = ldexpf(ubyte_f<0>(scp) * float(ilo), e2.x) + ldexpf(ubyte_f<1>(scp) * float(ihi), e2.y);
+        const float mins = fmaf(ubyte_f<0>(mnp), s2.x, ubyte_f<1>(mnp) * s2.y);
+        const float r = sum_lane_groups(fmaf(d, codes, -dmin * mins));
+        if (q == 0) part[(k * kTileRows + n) * kWaves + wave] = r;
+    };
+
+    // Item k sits in slot k % NB.  Whole ring periods, then the tail: with no condition
+    // inside the loop the compiler counts the loads in flight exactly.
+    constexpr int kInFlight = (NB - 1) * 3;   // loads of the NB - 1 items after item k
+    static_assert(kInFlight < 16, "vmcnt immediate");
+    auto step = [&](auto b, int k) {
+        constexpr int B = decltype(b)::value;
+        issue(std::integral_constant<int, (B + NB - 1) % NB>{}, k + NB - 1);   // the slot of item k - 1
+        __builtin_amdgcn_s_waitcnt(kInFlight | 0x0F70);                       // item k has landed
+        compute(slot(b) + wave * kItemBytes, k);
+    };
+    if (active) {
+        int k0 = 0;
+        for (; k0 + NB <= tiles; k0 += NB) static_for<NB>([&](auto b) { step(b, k0 + decltype(b)::value); });
+        static_for<NB>([&](auto b) {
+            if (k0 + decltype(b)::value < tiles) step(b, k0 + decltype(b)::value);
+        });
+    }
+    wait_barrier<0>();   // every partial written (and the loads past the end have landed)
+
+    const int wl = SB < kWaves ? SB : kWaves;
+    for (int r = tid; r < tiles * kTileRows; r += kThreads) {
+        const int row = (w0 + (r / kTileRows) * G) * kTileRows + r % kTileRows;
+        float s = 0.f;
+        for (int w = 0; w < wl; ++w) s += part[r * kWaves + w];
+        if (row < N) y[row] = s;
+    }
+}
+
+constexpr int kRing = 4;
+
+struct Plan {
+    int grid = 0;
+};
+
+Plan plan(int64_t N, int64_t K, int cu_count) {
+    Plan p;
+    if (N <= 0 || K % 256 || K / 256 < kMinSB || K / 256 > kMaxSB || cu_count <= 0) return p;
+    const int64_t T = (N + kTileRows - 1) / kTileRows;
+    const int64_t grid = T < cu_count ? T : cu_count;
+    const int64_t row_bytes = (K / 256) * 144;
+    // 32-bit buffer offsets: the last prefetch reaches kRing rounds of tiles past the end
+    if ((T + grid - 1) / grid > kMaxTilesPerGroup ||
+        (T + (kRing + 1) * grid) * kTileRows * row_bytes >= (int64_t(1) << 31))
+        return p;
+    p.grid = int(grid);
+    return p;
+}
+
+}  // namespace
+
+bool gemv_mfma_applies(int type, int64_t N, int64_t K, int cu_count) {
+    // Wide matrices only: at least two 16-row tiles per CU.
+    return type == kQ4_K && N >= 2 * kTileRows * int64_t(cu_count) && plan(N, K, cu_count).grid > 0;
+}
+
+hipError_t launch_gemv_mfma(const uint8_t* W, const float* x, float* y, int64_t N, int64_t K, int cu_count,
+                            hipStream_t s, const char** name) {
+    const Plan p = plan(N, K, cu_count);
+    if (p.grid <= 0) return hipErrorInvalidValue;
+    *name = "gemv_mfma<q4_K>";
+    int n = int(N), k = int(K), row_bytes = int((K / 256) * 144);
+    void* args[] = {&W, &x, &y, &n, &k, &row_bytes};
+    return hipLaunchKernel(reinterpret_cast<const void*>(gemv_mfma_q4k_kernel<kRing>), dim3(p.grid),
+                           dim3(kThreads), args, 0, s);
+}
+
+}  // namespace mq

@@ -33,6 +33,11 @@ int gemv_tile_units(int type, int64_t K, size_t lds_limit);
 hipError_t gemv_set_attributes(size_t lds_limit);
 hipError_t launch_gemv(int type, const uint8_t* W, const float* x, float* y, int64_t N, int64_t K,
                        hipStream_t s, const char** kernel_name);
+// Q4_K GEMV with the dot products on int8 matrix cores and the weights streamed through
+// LDS, for wide matrices (gemv_mfma.hip).
+bool gemv_mfma_applies(int type, int64_t N, int64_t K, int cu_count);
+hipError_t launch_gemv_mfma(const uint8_t* W, const float* x, float* y, int64_t N, int64_t K, int cu_count,
+                            hipStream_t s, const char** kernel_name);
 // MMQ work split over bm x 128 output tiles: the first `full` tiles are computed whole;
 // each of the remaining `split_tiles` is cut into `splits` ranges of whole 128-value
 // K-steps, whose f32 partial tiles (mmq_scratch_bytes of scratch) a second launch sums.

@@ -95,3 +95,27 @@ def test_gemv_config5_14b(qtype, N, K, tensor):
     x = synth.activations(1, K, config_index=4, tensor_index=tensor)[0]
     rows = None if N * K <= 5120 * 5120 else np.random.default_rng(1).choice(N, 2048, replace=False)
     run_gemv(raw, qtype, x, N, K, rows=rows, what="14B")
+
+
+@pytest.mark.parametrize("N,K,kind,sampled", [(16384 + 77, 3072, "random", False),
+                                              (20000, 3584, "quantized", False),
+                                              (2 * 16384 + 5, 4096, "random", False),
+                                              (8192, 3584, "quantized", False),
+                                              (65536 - 3, 3584, "random", True)],
+                         ids=["ragged_K3072", "K3584", "K4096_ring_wraps", "two_tiles_per_cu",
+                              "sixteen_tiles_per_cu"])
+def test_gemv_q4_k_wide_matrix_core_path(N, K, kind, sampled):
+    """Wide Q4_K matrices (at least two 16-row tiles per CU, 12 to 16 super-blocks per row)
+    take the int8 matrix-core kernel: a ragged last tile, idle waves (K < 4096), tiles per
+    workgroup below the prefetch depth, ring wrap-around with a tail, the largest tile
+    count per workgroup, and an x with all-zero and tiny blocks."""
+    raw = weights(mq.Q4_K, N, K, kind, 7)
+    x = synth.activations(1, K, config_index=10, tensor_index=N % 97)[0]
+    x[32:64] = 0.0
+    x[96:128] *= 1e-30
+    rows = None
+    if sampled:
+        rng = np.random.default_rng(N)
+        rows = np.unique(np.concatenate([rng.integers(0, N, 3000), np.arange(32), np.arange(N - 32, N)]))
+    run_gemv(raw, mq.Q4_K, x, N, K, rows=rows, what=f"{kind} matrix-core")
+    assert "mfma" in mq.last_kernel()

@@ -79,7 +79,7 @@ struct UnitQ4K {
     static constexpr int kChunks = 4;
     uint4 hd, q0, q1;
 
-    __device__ void load(const uint8_t* __restrict__ row, int u) {
+    __device__ void load(const uint8_t* __restrict__ row, int u, int, int) {
         const uint8_t* blk = row + 144 * (u >> 2);
         hd = *reinterpret_cast<const uint4*>(blk);
         const uint4* qs = reinterpret_cast<const uint4*>(blk + 16 + 32 * (u & 3));
@@ -133,8 +133,9 @@ struct UnitQ4K {
 // staged chunk t of the unit holds exactly those 16 values.
 // Low 4 bits: ql[64h + l] (t = 0 low nibble, t = 2 high nibble) and
 // ql[64h + 32 + l] (t = 1, 3); high 2 bits: bits 2t..2t+1 of qh[32h + l].
-// Blocks are 210 bytes, so a block starts on a 2-byte boundary: every segment
-// is read as naturally aligned dwords and realigned with v_alignbyte.
+// GGUF blocks are 210 bytes, so a block starts on a 2-byte boundary: every segment
+// is read as naturally aligned dwords and realigned with v_alignbyte (a no-op on the
+// 16-byte-aligned 224-byte slots of the repacked layout).
 struct UnitQ6K {
     static constexpr int kValues = 64;
     static constexpr int kChunks = 4;
@@ -142,8 +143,8 @@ struct UnitQ6K {
     uint32_t dbits;
     uint32_t shift;
 
-    __device__ void load(const uint8_t* __restrict__ row, int u) {
-        const uint8_t* blk = row + 210 * (u >> 2);
+    __device__ void load(const uint8_t* __restrict__ row, int u, int stride, int off) {
+        const uint8_t* blk = row + stride * (u >> 2) + off;
         const int h = (u >> 1) & 1, l0 = 16 * (u & 1);
         const uintptr_t base = reinterpret_cast<uintptr_t>(blk);
         shift = uint32_t(base & 3);
@@ -202,16 +203,17 @@ struct UnitQ6K {
 };
 
 // ---------------------------------------------------------------- Q8_0
-// Unit u = block u (34 bytes: f16 d, 32 int8 codes), 2-byte aligned; staged
-// chunks 0,1 hold its 32 values.
+// Unit u = block u (34 bytes: f16 d, 32 int8 codes), 2-byte aligned in the GGUF
+// payload (at offset 2 of a 36-byte slot in the repacked layout, so that its codes
+// are 4-byte aligned); staged chunks 0,1 hold its 32 values.
 struct UnitQ80 {
     static constexpr int kValues = 32;
     static constexpr int kChunks = 2;
     uint32_t w[9];
     uint32_t odd;
 
-    __device__ void load(const uint8_t* __restrict__ row, int u) {
-        const uintptr_t base = reinterpret_cast<uintptr_t>(row + 34 * u);
+    __device__ void load(const uint8_t* __restrict__ row, int u, int stride, int off) {
+        const uintptr_t base = reinterpret_cast<uintptr_t>(row + stride * u + off);
         odd = uint32_t(base & 2);
         const uint32_t* p = reinterpret_cast<const uint32_t*>(base & ~uintptr_t(3));
         // 9 naturally aligned dwords cover the block; each holds a byte of it
@@ -269,7 +271,8 @@ template <int QT, int kThreads, int kSlots>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restrict__ W,
                                                         const float* __restrict__ x,
                                                         float* __restrict__ y, int N, int K,
-                                                        int64_t row_bytes, int tile_units) {
+                                                        int64_t row_bytes, int tile_units, int blk_stride,
+                                                        int blk_off) {
     using Unit = typename UnitOf<QT>::T;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int U = K / Unit::kValues;
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
     int units = 0, iters = 0;
     auto load_next = [&](int j) {
         const bool live = ld.f < units;
-        buf[j].load(live ? ld.row : tile, live ? ld.u : 0);
+        buf[j].load(live ? ld.row : tile, live ? ld.u : 0, blk_stride, blk_off);
         advance(ld);
     };
     auto prime = [&](int tfirst) {
@@ -557,11 +560,11 @@ hipError_t gemv_set_attributes(size_t lds_limit) {
     return hipSuccess;
 }
 
-hipError_t launch_gemv(int type, const uint8_t* W, const float* x, float* y, int64_t N, int64_t K,
-                       hipStream_t s, const char** name) {
+hipError_t launch_gemv(int type, BlockLayout layout, const uint8_t* W, const float* x, float* y, int64_t N,
+                       int64_t K, hipStream_t s, const char** name) {
     const DeviceInfo* info = device_info();
     if (!info) return hipErrorInvalidDevice;
-    if (use_mfma() && gemv_mfma_applies(type, N, K, info->cu_count))
+    if (use_mfma() && type == kQ4_K && gemv_mfma_applies(type, N, K, info->cu_count))
         return launch_gemv_mfma(W, x, y, N, K, info->cu_count, s, name);
     int tile = gemv_tile_units(type, K, info->lds_per_block);
     if (tile <= 0) return hipErrorInvalidValue;
@@ -577,15 +580,16 @@ hipError_t launch_gemv(int type, const uint8_t* W, const float* x, float* y, int
     const size_t shmem = fixed_lds_bytes(type, K) + size_t(tile) * 4;
     const Config c = chosen_config(type);
     const void* kern = kernel_for(type, c);
-    int64_t row_bytes = 0;
+    const bool repacked = layout.off != 0 || (type == kQ6_K && layout.stride != 210);
     switch (type) {
-        case kQ8_0: *name = "gemv<q8_0>"; row_bytes = (K / 32) * 34; break;
-        case kQ4_K: *name = "gemv<q4_K>"; row_bytes = (K / 256) * 144; break;
-        case kQ6_K: *name = "gemv<q6_K>"; row_bytes = (K / 256) * 210; break;
+        case kQ8_0: *name = repacked ? "gemv<q8_0 repacked>" : "gemv<q8_0>"; break;
+        case kQ4_K: *name = "gemv<q4_K>"; break;
+        case kQ6_K: *name = repacked ? "gemv<q6_K repacked>" : "gemv<q6_K>"; break;
         default: return hipErrorInvalidValue;
     }
-    int n = int(N), k = int(K);
-    void* args[] = {&W, &x, &y, &n, &k, &row_bytes, &tile};
+    int64_t row_bytes = (K / (type == kQ8_0 ? 32 : 256)) * layout.stride;
+    int n = int(N), k = int(K), stride = layout.stride, off = layout.off;
+    void* args[] = {&W, &x, &y, &n, &k, &row_bytes, &tile, &stride, &off};
     return hipLaunchKernel(kern, dim3(grid), dim3(c.threads), args, shmem, s);
 }
 

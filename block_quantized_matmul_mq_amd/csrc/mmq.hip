@@ -132,7 +132,7 @@ template <> struct WeightRegs<kQ4_K> {
     // of sub-block 2c + 1, c = 2 half + p / 2.  A wave writes one chunk of 64 consecutive
     // rows at a time: 1 KB of contiguous LDS, no bank conflicts.
     uint4 q[2], hd;
-    __device__ void load(const uint8_t* W, int64_t rb, int n0, int N, int k0, int) {
+    __device__ void load(const uint8_t* W, int64_t rb, int n0, int N, int k0, int, int bs, int bo) {
         const int t = threadIdx.x, sb = k0 >> 8, half = (k0 >> 7) & 1;
         const int n = min(n0 + (t & (BN - 1)), N - 1);
         const uint8_t* blk = W + int64_t(n) * rb + 144 * sb;
@@ -179,14 +179,15 @@ template <> struct WeightRegs<kQ8_0> {
     // one chunk of 64 consecutive rows at a time.
     uint32_t w[2][9];
     bool odd[2], live[2];
-    __device__ void load(const uint8_t* W, int64_t rb, int n0, int N, int k0, int K) {
+    __device__ void load(const uint8_t* W, int64_t rb, int n0, int N, int k0, int K, int bs, int bo) {
         const int t = threadIdx.x;
         const int n = min(n0 + (t & (BN - 1)), N - 1);
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             const int kb = (k0 >> 5) + (t >> 7) + 2 * it;
             live[it] = kb < (K >> 5);
-            const uintptr_t a = reinterpret_cast<uintptr_t>(W + int64_t(n) * rb + 34 * int64_t(live[it] ? kb : 0));
+            const uintptr_t a =
+                reinterpret_cast<uintptr_t>(W + int64_t(n) * rb + int64_t(bs) * (live[it] ? kb : 0) + bo);
             odd[it] = (a & 2) != 0;
             const uint32_t* p = reinterpret_cast<const uint32_t*>(a & ~uintptr_t(3));
 #pragma unroll
@@ -223,19 +224,19 @@ template <> struct WeightRegs<kQ6_K> {
     // t < 128 also owns row t's 8 sub-scales of this half and d.
     uint32_t ql0[4], ql1[4], qh[4];
     uint32_t s0, s1, dbits;
-    __device__ void load(const uint8_t* W, int64_t rb, int n0, int N, int k0, int) {
+    __device__ void load(const uint8_t* W, int64_t rb, int n0, int N, int k0, int, int bs, int bo) {
         const int t = threadIdx.x, sb = k0 >> 8, h = (k0 >> 7) & 1;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int u = t + 256 * it, row = u >> 3, p = u & 7;
             const int n = min(n0 + row, N - 1);
-            const uint8_t* blk = W + int64_t(n) * rb + 210 * sb;
+            const uint8_t* blk = W + int64_t(n) * rb + bs * sb + bo;
             ql0[it] = load_u32_a2(blk + 64 * h + 4 * p);
             ql1[it] = load_u32_a2(blk + 64 * h + 32 + 4 * p);
             qh[it] = load_u32_a2(blk + 128 + 32 * h + 4 * p);
         }
         const int n = min(n0 + (t & (BN - 1)), N - 1);
-        const uint8_t* blk = W + int64_t(n) * rb + 210 * sb;
+        const uint8_t* blk = W + int64_t(n) * rb + bs * sb + bo;
         s0 = load_u32_a2(blk + 192 + 8 * h);
         s1 = load_u32_a2(blk + 192 + 8 * h + 4);
         dbits = load_u16(blk + 208);
@@ -350,8 +351,8 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
                                                      const int32_t* __restrict__ xsum,
                                                      float* __restrict__ Y, int32_t* __restrict__ dots,
                                                      float* __restrict__ partial, int M, int N, int K,
-                                                     int64_t row_bytes, int tiles_m, int full, int split_tiles,
-                                                     int splits, int total_steps) {
+                                                     int64_t row_bytes, int blk_stride, int blk_off, int tiles_m,
+                                                     int full, int split_tiles, int splits, int total_steps) {
     using T = TileShape<BM>;
     constexpr int TI = T::TI, TJ = T::TJ;
     __shared__ __attribute__((aligned(16))) Smem<QT, BM> sm;
@@ -399,14 +400,14 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
     WeightRegs<QT> wr;
 
     // prologue: step kbeg into buffer 0, step kbeg + KS in flight
-    wr.load(W, row_bytes, n0, N, kbeg, K);
+    wr.load(W, row_bytes, n0, N, kbeg, K, blk_stride, blk_off);
     act.issue(sm, 0, kbeg);
     wait_vm_all();
     wr.store(sm, 0, kbeg);
     act.finish(sm, 0);
     __syncthreads();
     if (kbeg + KS < kend) {
-        wr.load(W, row_bytes, n0, N, kbeg + KS, K);
+        wr.load(W, row_bytes, n0, N, kbeg + KS, K, blk_stride, blk_off);
         act.issue(sm, 1, kbeg + KS);
     }
 
@@ -537,7 +538,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
         }
         __syncthreads();   // buffer `buf` is free, buffer `buf ^ 1` is complete
         if (k0 + 2 * KS < kend) {
-            wr.load(W, row_bytes, n0, N, k0 + 2 * KS, K);
+            wr.load(W, row_bytes, n0, N, k0 + 2 * KS, K, blk_stride, blk_off);
             act.issue(sm, buf, k0 + 2 * KS);
         }
     };
@@ -594,7 +595,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                       const float* __restrict__, const int32_t* __restrict__,  \
                                                       float* __restrict__, int32_t* __restrict__,              \
                                                       float* __restrict__, int, int, int, int64_t, int, int, int, \
-                                                      int, int);
+                                                      int, int, int, int);
 MQ_MMQ_INSTANCE(kQ8_0, 32, false)
 MQ_MMQ_INSTANCE(kQ8_0, 128, false)
 MQ_MMQ_INSTANCE(kQ4_K, 32, false)
@@ -611,19 +612,20 @@ MQ_MMQ_INSTANCE(kQ6_K, 128, true)
 
 template <int QT, int BM>
 hipError_t launch_shaped(const uint8_t* W, const int8_t* codes, const float* xs, const int32_t* xsum, float* Y,
-                         int32_t* dots, float* partial, int64_t M, int64_t N, int64_t K, int64_t row_bytes,
+                         int32_t* dots, float* partial, int64_t M, int64_t N, int64_t K, BlockLayout lay,
                          const MmqPlan& plan, hipStream_t s) {
     const int tiles_m = int((M + BM - 1) / BM);
     const int total = plan.full + plan.split_tiles * plan.splits;
+    const int64_t row_bytes = (K / (QT == kQ8_0 ? 32 : 256)) * lay.stride;
     if (dots) {
         hipLaunchKernelGGL((mmq_kernel<QT, BM, true>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, Y, dots,
-                           partial, int(M), int(N), int(K), row_bytes, tiles_m, plan.full, plan.split_tiles,
-                           plan.splits, plan.steps);
+                           partial, int(M), int(N), int(K), row_bytes, lay.stride, lay.off, tiles_m, plan.full,
+                           plan.split_tiles, plan.splits, plan.steps);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((mmq_kernel<QT, BM, false>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, Y, dots,
-                       partial, int(M), int(N), int(K), row_bytes, tiles_m, plan.full, plan.split_tiles, plan.splits,
-                       plan.steps);
+                       partial, int(M), int(N), int(K), row_bytes, lay.stride, lay.off, tiles_m, plan.full,
+                       plan.split_tiles, plan.splits, plan.steps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.split_tiles == 0) return e;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(BM * BN / 256, plan.split_tiles), dim3(256), 0, s, partial, Y,
@@ -634,10 +636,10 @@ hipError_t launch_shaped(const uint8_t* W, const int8_t* codes, const float* xs,
 template <int QT>
 hipError_t launch_typed(const uint8_t* W, const int8_t* codes, const float* xs, const int32_t* xsum,
                         float* Y, int32_t* dots, float* partial, int64_t M, int64_t N, int64_t K,
-                        int64_t row_bytes, hipStream_t s) {
+                        BlockLayout lay, hipStream_t s) {
     const MmqPlan plan = mmq_plan(QT, M, N, K);
-    if (plan.bm == 32) return launch_shaped<QT, 32>(W, codes, xs, xsum, Y, dots, partial, M, N, K, row_bytes, plan, s);
-    return launch_shaped<QT, 128>(W, codes, xs, xsum, Y, dots, partial, M, N, K, row_bytes, plan, s);
+    if (plan.bm == 32) return launch_shaped<QT, 32>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, plan, s);
+    return launch_shaped<QT, 128>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, plan, s);
 }
 
 }  // namespace
@@ -672,19 +674,20 @@ size_t mmq_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
     return size_t(p.split_tiles) * size_t(p.splits) * size_t(p.bm) * BN * sizeof(float);
 }
 
-hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* codes, const float* xs, const int32_t* xsum,
-                      float* Y, int32_t* dots, float* partial, int64_t M, int64_t N, int64_t K, hipStream_t s,
-                      const char** name) {
+hipError_t launch_mmq(int type, BlockLayout lay, const uint8_t* W, const int8_t* codes, const float* xs,
+                      const int32_t* xsum, float* Y, int32_t* dots, float* partial, int64_t M, int64_t N, int64_t K,
+                      hipStream_t s, const char** name) {
+    const bool repacked = lay.off != 0 || (type == kQ6_K && lay.stride != 210);
     switch (type) {
         case kQ8_0:
-            *name = "mmq<q8_0>";
-            return launch_typed<kQ8_0>(W, codes, xs, xsum, Y, dots, partial, M, N, K, (K / 32) * 34, s);
+            *name = repacked ? "mmq<q8_0 repacked>" : "mmq<q8_0>";
+            return launch_typed<kQ8_0>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
         case kQ4_K:
             *name = "mmq<q4_K>";
-            return launch_typed<kQ4_K>(W, codes, xs, xsum, Y, dots, partial, M, N, K, (K / 256) * 144, s);
+            return launch_typed<kQ4_K>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
         case kQ6_K:
-            *name = "mmq<q6_K>";
-            return launch_typed<kQ6_K>(W, codes, xs, xsum, Y, dots, partial, M, N, K, (K / 256) * 210, s);
+            *name = repacked ? "mmq<q6_K repacked>" : "mmq<q6_K>";
+            return launch_typed<kQ6_K>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -53,9 +53,35 @@ int block_bytes(int type) {
     }
 }
 
+// The slot a block takes in the layout mq_repack writes, and the block's offset in it:
+// Q8_0 36 bytes with the block at 2 (its 32 codes then start 4-byte aligned), Q6_K 224
+// bytes with the block at 0 (16-byte aligned slots).  Q4_K blocks are 144 bytes, already
+// 16-byte aligned: it has no repacked layout.
+BlockLayout repacked_layout(int base) {
+    switch (base) {
+        case MQ_Q8_0: return {36, 2};
+        case MQ_Q6_K: return {224, 0};
+        default: return {0, 0};
+    }
+}
+
+// A type id is a GGUF type, optionally OR-ed with MQ_REPACKED for the layout mq_repack
+// writes.  Returns the GGUF type (0 for an unknown id or a type with no repacked layout)
+// and the layout of its blocks.
+int parse_type(int type, BlockLayout& lay) {
+    const int base = type & ~MQ_REPACKED;
+    if (block_values(base) == 0) return 0;
+    if (type & MQ_REPACKED) {
+        lay = repacked_layout(base);
+        return lay.stride ? base : 0;
+    }
+    lay = BlockLayout{block_bytes(base), 0};
+    return base;
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Shape/type checks shared by the weight-consuming calls.
+// Shape/type checks shared by the weight-consuming calls (`type` without the repack flag).
 int check_weight_shape(const char* fn, int type, int64_t N, int64_t K) {
     if (block_values(type) == 0) return fail(MQ_ERR_TYPE, "%s: unsupported weight type %d", fn, type);
     if (N <= 0 || K <= 0) return fail(MQ_ERR_ARG, "%s: N=%lld K=%lld must be positive", fn, (long long)N, (long long)K);
@@ -143,9 +169,17 @@ int mq_init(int device) {
 }
 
 size_t mq_weight_bytes(int type, int64_t N, int64_t K) {
-    const int bv = block_values(type);
-    if (bv == 0 || N <= 0 || K <= 0 || K % bv != 0) return 0;
-    return size_t(N) * size_t(K / bv) * size_t(block_bytes(type));
+    BlockLayout lay;
+    const int base = parse_type(type, lay);
+    if (base == 0) return 0;
+    const int bv = block_values(base);
+    if (N <= 0 || K <= 0 || K % bv != 0) return 0;
+    return size_t(N) * size_t(K / bv) * size_t(lay.stride);
+}
+
+size_t mq_repack_bytes(int type, int64_t N, int64_t K) {
+    if (type & MQ_REPACKED) return 0;
+    return mq_weight_bytes(type | MQ_REPACKED, N, K);
 }
 
 size_t mq_act_bytes(int64_t M, int64_t K) {
@@ -164,6 +198,8 @@ size_t mq_act_sum_offset(int64_t M, int64_t K) {
 }
 
 size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
+    BlockLayout lay;
+    type = parse_type(type, lay);
     if (type != MQ_Q8_0 && type != MQ_Q4_K && type != MQ_Q6_K) return 0;
     if (M <= 0 || N <= 0 || K <= 0 || M > MQ_MAX_M || N > MQ_MAX_N || K > MQ_MAX_K) return 0;
     if (K % (type == MQ_Q8_0 ? 32 : 256) != 0) return 0;
@@ -192,6 +228,10 @@ int mq_quantize_act(const float* X, void* Xq, int64_t M, int64_t K, void* stream
 int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_t K, void* stream) {
     const char* fn = "mq_gemv";
     if (!W || !x || !y) return fail(MQ_ERR_ARG, "%s: null pointer (W=%p x=%p y=%p)", fn, W, (const void*)x, (void*)y);
+    BlockLayout lay;
+    const int base = parse_type(type, lay);
+    if (base == 0) return fail(MQ_ERR_TYPE, "%s: unsupported weight type %d", fn, type);
+    type = base;
     int rc = check_weight_shape(fn, type, N, K);
     if (rc) return rc;
     if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4))
@@ -203,8 +243,8 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
         return fail(MQ_ERR_SHAPE, "%s: K=%lld does not fit the %zu-byte LDS of this device", fn, (long long)K,
                     device_info()->lds_per_block);
     const char* kernel = "gemv";
-    hipError_t e = launch_gemv(type, static_cast<const uint8_t*>(W), x, y, N, K, static_cast<hipStream_t>(stream),
-                               &kernel);
+    hipError_t e = launch_gemv(type, lay, static_cast<const uint8_t*>(W), x, y, N, K,
+                               static_cast<hipStream_t>(stream), &kernel);
     return launch_status(fn, e, kernel);
 }
 
@@ -212,6 +252,10 @@ static int gemm_common(const char* fn, const void* W, int type, const void* Xq, 
                        float* partial, int64_t M, int64_t N, int64_t K, void* stream) {
     if (!W || !Xq || (!Y && !D))
         return fail(MQ_ERR_ARG, "%s: null pointer (W=%p Xq=%p out=%p)", fn, W, Xq, Y ? (void*)Y : (void*)D);
+    BlockLayout lay;
+    const int base = parse_type(type, lay);
+    if (base == 0) return fail(MQ_ERR_TYPE, "%s: unsupported weight type %d", fn, type);
+    type = base;
     int rc = check_weight_shape(fn, type, N, K);
     if (rc) return rc;
     if (M <= 0) return fail(MQ_ERR_ARG, "%s: M=%lld must be positive", fn, (long long)M);
@@ -224,12 +268,12 @@ static int gemm_common(const char* fn, const void* W, int type, const void* Xq, 
         return fail(MQ_ERR_ALIGN, "%s: W 16-byte, Xq 256-byte, outputs 4-byte alignment required", fn);
     rc = check_ready(fn);
     if (rc) return rc;
-    const uint8_t* base = static_cast<const uint8_t*>(Xq);
+    const uint8_t* xq = static_cast<const uint8_t*>(Xq);
     const char* kernel = "mmq";
     float* Yout = Y;
-    hipError_t e = launch_mmq(type, static_cast<const uint8_t*>(W), reinterpret_cast<const int8_t*>(base),
-                              reinterpret_cast<const float*>(base + act_scale_offset(M, K)),
-                              reinterpret_cast<const int32_t*>(base + act_sum_offset(M, K)), Yout, D, partial, M, N, K,
+    hipError_t e = launch_mmq(type, lay, static_cast<const uint8_t*>(W), reinterpret_cast<const int8_t*>(xq),
+                              reinterpret_cast<const float*>(xq + act_scale_offset(M, K)),
+                              reinterpret_cast<const int32_t*>(xq + act_sum_offset(M, K)), Yout, D, partial, M, N, K,
                               static_cast<hipStream_t>(stream), &kernel);
     return launch_status(fn, e, kernel);
 }
@@ -252,6 +296,36 @@ int mq_debug_gemm_blockdots(const void* W, int type, const void* Xq, int32_t* D,
     const char* fn = "mq_debug_gemm_blockdots";
     if (!D) return fail(MQ_ERR_ARG, "%s: null D", fn);
     return gemm_common(fn, W, type, Xq, nullptr, D, nullptr, M, N, K, stream);
+}
+
+int mq_repack(const void* W, int type, int64_t N, int64_t K, size_t nbytes, void* Wr, size_t wr_bytes,
+              void* stream) {
+    const char* fn = "mq_repack";
+    if (!W || !Wr) return fail(MQ_ERR_ARG, "%s: null pointer (W=%p Wr=%p)", fn, W, Wr);
+    if (type & MQ_REPACKED) return fail(MQ_ERR_TYPE, "%s: type %d is already the repacked layout", fn, type);
+    if (block_values(type) != 0 && repacked_layout(type).stride == 0)
+        return fail(MQ_ERR_TYPE, "%s: type %d has no repacked layout (its blocks are already 16-byte aligned)", fn,
+                    type);
+    int rc = check_weight_shape(fn, type, N, K);
+    if (rc) return rc;
+    const size_t in_bytes = mq_weight_bytes(type, N, K), out_bytes = mq_repack_bytes(type, N, K);
+    if (nbytes != in_bytes)
+        return fail(MQ_ERR_SIZE, "%s: payload of %zu bytes, a %lld x %lld type-%d matrix is exactly %zu", fn, nbytes,
+                    (long long)N, (long long)K, type, in_bytes);
+    if (wr_bytes < out_bytes)
+        return fail(MQ_ERR_SIZE, "%s: output of %zu bytes, %zu required", fn, wr_bytes, out_bytes);
+    if (!aligned(W, 16) || !aligned(Wr, 16))
+        return fail(MQ_ERR_ALIGN, "%s: W and Wr must be 16-byte aligned (W=%p Wr=%p)", fn, W, Wr);
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(W), a1 = a0 + in_bytes;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(Wr), b1 = b0 + out_bytes;
+    if (a0 < b1 && b0 < a1) return fail(MQ_ERR_ARG, "%s: W and Wr overlap", fn);
+    rc = check_ready(fn);
+    if (rc) return rc;
+    const BlockLayout lay = repacked_layout(type);
+    const int64_t blocks = N * (K / block_values(type));
+    hipError_t e = launch_repack(static_cast<const uint8_t*>(W), static_cast<uint8_t*>(Wr), blocks, block_bytes(type),
+                                 lay.stride, lay.off, static_cast<hipStream_t>(stream));
+    return launch_status(fn, e, "repack");
 }
 
 }  // extern "C"

@@ -25,14 +25,22 @@ struct DeviceInfo {
 };
 const DeviceInfo* device_info();  // null if mq_init has not succeeded on the current device
 
+// How weight blocks are stored: bytes per block slot and the offset of the GGUF block in
+// its slot.  The GGUF payload itself is {34, 0} (Q8_0), {144, 0} (Q4_K), {210, 0} (Q6_K);
+// mq_repack writes Q8_0 as {36, 2} and Q6_K as {224, 0}.
+struct BlockLayout {
+    int stride = 0;
+    int off = 0;
+};
+
 // Kernel launchers: they enqueue on `s` and return the launch status (hipGetLastError read
 // right after the launch).  Arguments are validated by the callers in mq_api.hip.
 hipError_t launch_quantize_act(const float* X, int8_t* codes, float* scales, int32_t* sums,
                                int64_t M, int64_t K, hipStream_t s);
 int gemv_tile_units(int type, int64_t K, size_t lds_limit);
 hipError_t gemv_set_attributes(size_t lds_limit);
-hipError_t launch_gemv(int type, const uint8_t* W, const float* x, float* y, int64_t N, int64_t K,
-                       hipStream_t s, const char** kernel_name);
+hipError_t launch_gemv(int type, BlockLayout layout, const uint8_t* W, const float* x, float* y, int64_t N,
+                       int64_t K, hipStream_t s, const char** kernel_name);
 // Q4_K GEMV with the dot products on int8 matrix cores and the weights streamed through
 // LDS, for wide matrices (gemv_mfma.hip).
 bool gemv_mfma_applies(int type, int64_t N, int64_t K, int cu_count);
@@ -52,8 +60,12 @@ MmqPlan mmq_plan(int type, int64_t M, int64_t N, int64_t K);
 size_t mmq_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
 // Y: the product (null for the block-dot export); dots: the export (null for the product);
 // partial: at least mmq_scratch_bytes of device memory when the plan has splits > 1.
-hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* codes, const float* scales,
+hipError_t launch_mmq(int type, BlockLayout layout, const uint8_t* W, const int8_t* codes, const float* scales,
                       const int32_t* sums, float* Y, int32_t* dots, float* partial, int64_t M, int64_t N,
                       int64_t K, hipStream_t s, const char** kernel_name);
+// mq_repack: every `in_bytes`-byte block of W into a `slot_bytes`-byte slot of Wr at offset
+// `off`, the rest of the slot zero (repack.hip).
+hipError_t launch_repack(const uint8_t* W, uint8_t* Wr, int64_t blocks, int in_bytes, int slot_bytes, int off,
+                         hipStream_t s);
 
 }  // namespace mq

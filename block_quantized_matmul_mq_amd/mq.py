@@ -13,6 +13,7 @@ import os
 Q8_0 = 8
 Q4_K = 12
 Q6_K = 14
+REPACKED = 0x100   # OR-ed into Q8_0 / Q6_K: weights in the layout mq_repack writes
 
 MQ_OK = 0
 ERRORS = {
@@ -40,6 +41,9 @@ _SIGNATURES = {
     "mq_debug_gemm_blockdots": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                                ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                                ctypes.c_int64, ctypes.c_void_p]),
+    "mq_repack_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]),
+    "mq_repack": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_size_t,
+                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "mq_device_lds_bytes": (ctypes.c_int, []),
     "mq_last_error": (ctypes.c_char_p, []),
     "mq_last_kernel": (ctypes.c_char_p, []),
@@ -98,6 +102,20 @@ def init(device=0):
 
 def weight_bytes(qtype, N, K):
     return load().mq_weight_bytes(qtype, N, K)
+
+
+def repack_bytes(qtype, N, K):
+    return load().mq_repack_bytes(qtype, N, K)
+
+
+def repack(W, qtype, N, K, Wr=None, stream=None):
+    """The repacked layout of a GGUF payload W (uint8 CUDA tensor); use with qtype | REPACKED."""
+    import torch
+    if Wr is None:
+        Wr = torch.empty(repack_bytes(qtype, N, K), dtype=torch.uint8, device=W.device)
+    _check(load().mq_repack(ctypes.c_void_p(W.data_ptr()), qtype, N, K, W.numel() * W.element_size(),
+                            ctypes.c_void_p(Wr.data_ptr()), Wr.numel() * Wr.element_size(), _stream(stream)))
+    return Wr
 
 
 def act_bytes(M, K):
@@ -164,7 +182,7 @@ def gemm(W, qtype, Xq, M, N, K, Y=None, scratch=None, stream=None):
 def gemm_blockdots(W, qtype, Xq, M, N, K, D=None, stream=None):
     """Exact int32 block dots [M, N, G] of the MMQ kernel (G = K/32, or K/16 for Q6_K)."""
     import torch
-    G = K // 16 if qtype == Q6_K else K // 32
+    G = K // 16 if (qtype & ~REPACKED) == Q6_K else K // 32
     if D is None:
         D = torch.empty((M, N, G), dtype=torch.int32, device=Xq.device)
     _check(load().mq_debug_gemm_blockdots(ctypes.c_void_p(W.data_ptr()), qtype, ctypes.c_void_p(Xq.data_ptr()),

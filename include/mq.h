@@ -64,6 +64,9 @@ extern "C" {
 #define MQ_Q8_0 8
 #define MQ_Q4_K 12
 #define MQ_Q6_K 14
+/* OR-ed into MQ_Q8_0 or MQ_Q6_K: the weights are in the layout mq_repack writes
+ * (every call that takes a weight type accepts it). */
+#define MQ_REPACKED 0x100
 
 /* Status codes. */
 #define MQ_OK 0
@@ -90,9 +93,31 @@ extern "C" {
  */
 int mq_init(int device);
 
-/* Exact byte size of a GGUF payload of N x K weights of `type` [BD2.3];
- * 0 for an unsupported type or a K that is not a whole number of blocks. */
+/* Exact byte size of a GGUF payload of N x K weights of `type` [BD2.3] (of
+ * the repacked layout for type | MQ_REPACKED); 0 for an unsupported type or a
+ * K that is not a whole number of blocks. */
 size_t mq_weight_bytes(int type, int64_t N, int64_t K);
+
+/*
+ * mq_repack_bytes / mq_repack -- the one-time device-layout transform of a
+ * weight matrix [BD2.3: Q6_K is repacked into 16-byte-aligned 224-byte slots;
+ * a derived plane is admitted only with an exact-length payload].  Each block
+ * of the GGUF payload W (device, nbytes bytes, which must equal
+ * mq_weight_bytes(type, N, K) exactly, else MQ_ERR_SIZE) is copied into its own
+ * slot of Wr (device, at least mq_repack_bytes(type, N, K) bytes), rows and
+ * blocks in the same order, the other slot bytes zero:
+ *   MQ_Q6_K: 224-byte slots, the 210-byte block at offset 0 (16-byte aligned);
+ *   MQ_Q8_0: 36-byte slots, the 34-byte block at offset 2 (its 32 codes start
+ *            4-byte aligned).
+ * Pass type | MQ_REPACKED with Wr to mq_gemv / mq_gemm: the results are the
+ * same as with W.  MQ_Q4_K (blocks already 16-byte aligned) has no repacked
+ * layout: MQ_ERR_TYPE, and mq_repack_bytes returns 0.  W and Wr must be 16-byte
+ * aligned and must not overlap (MQ_ERR_ARG).  Runs on `stream`; W may be freed
+ * once the stream has passed the call.
+ */
+size_t mq_repack_bytes(int type, int64_t N, int64_t K);
+int mq_repack(const void* W, int type, int64_t N, int64_t K, size_t nbytes, void* Wr, size_t wr_bytes,
+              void* stream);
 
 /* Bytes of the quantized activation plane for M x K, and the offsets of its
  * scale and sum arrays (both 256-byte aligned).  0 if K % 32 != 0. */
@@ -121,13 +146,14 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
 /*
  * mq_gemm_scratch_bytes -- device scratch that mq_gemm needs for (type, M, N,
  * K); 0 when the chosen work split needs none, and 0 for a shape mq_gemm
- * refuses.  mq_gemm computes Y in 128 x 128 tiles, sized for 512 resident
- * workgroups: tiles are computed whole while they fill rounds of 512; the tiles
- * of a last round that is at most half full (or all tiles, when there are at
- * most 256) are cut into S ranges of whole 128-value K-steps, and a second
- * launch sums their S f32 partial tiles in range order (deterministic).  The
- * scratch then holds S x (number of cut tiles) x 128 x 128 f32.  The split
- * depends on the shape only, never on the device.
+ * refuses.  mq_gemm computes Y in BM x 128 tiles (BM = 32 for M <= 32, else
+ * 128), sized for 512 resident workgroups: tiles are computed whole while they
+ * fill rounds of 512; the tiles of a last round that is at most half full (or
+ * all tiles, when there are at most 256) are cut into S ranges of whole
+ * 128-value K-steps, and a second launch sums their S f32 partial tiles in
+ * range order (deterministic).  The scratch then holds S x (number of cut
+ * tiles) x BM x 128 f32.  The split depends on the shape only, never on the
+ * device.
  */
 size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
 

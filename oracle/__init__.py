@@ -11,6 +11,7 @@ What is here:
                        path computes: block decoders, the activation
                        quantizer, the GEMV, the int block dots and the MMQ
                        product.
+  ``repack`` / ``unpack_repacked`` define the repacked weight layout.
 * ``bitwise_decode`` -- a second, independently written per-block decoder that
                        assembles every field bit by bit; it exists only to
                        cross-check ``mq_oracle``'s vectorised decoders.
@@ -30,4 +31,5 @@ from .mq_oracle import (  # noqa: F401
     f16_bits_to_f64, row_bytes,
     q8_0_fields, q4_k_fields, q6_k_fields, decode,
     gemv, quantize_act, block_dots, mmq, mmq_from_block_dots,
+    REPACK_SLOT, repack, unpack_repacked,
 )

@@ -40,6 +40,13 @@ Readings where the pages are silent (each also listed in the design doc):
 * R7  Block dots are exact integers: per 32-value block for Q8_0 and Q4_K
       (Q4_K codes in [0, 15], unsigned), per 16-value group for Q6_K with the
       signed code (c - 32).
+* R12 The repacked layout (the one-time device-layout transform): the pages
+      repack a Q6_K block into a 16-byte-aligned 224-byte slot ("minfer CUDA
+      Backend Design", 2.3); the block sits at the start of its slot and the
+      14 trailing bytes are zero.  A Q8_0 block goes to a 36-byte slot at
+      offset 2, the first 2 bytes zero, so that its 32 codes start 4-byte
+      aligned (the pages name no Q8_0 repack: this layout is a reading).
+      Rows and blocks keep their order.
 """
 
 import numpy as np
@@ -80,6 +87,42 @@ def f16_bits_to_f64(lo_byte, hi_byte):
     normal = sign * (1.0 + frac / 1024.0) * np.exp2(exp.astype(np.float64) - 15.0)
     subnormal = sign * frac * 2.0 ** -24
     return np.where(exp == 0, subnormal, normal)
+
+
+# R12: slot bytes and the block's offset inside its slot, per repackable type.
+REPACK_SLOT = {Q8_0: (36, 2), Q6_K: (224, 0)}
+
+
+def repack(raw, qtype, N, K):
+    """R12: the repacked bytes (uint8, N * K/bv slots) of a GGUF payload.
+
+    Block b of row n goes to slot b of row n at the slot's offset; every other
+    byte of the slot is zero.  Pinned by the page's 224-byte Q6_K slot
+    (tests/golden/block_sizes.txt), the alignment each slot is for, and a
+    per-block brute force.
+    """
+    slot, off = REPACK_SLOT[qtype]
+    b = _blocks(raw, qtype, N, K)
+    out = np.zeros((N, b.shape[1], slot), dtype=np.uint8)
+    out[:, :, off:off + BLOCK_BYTES[qtype]] = b
+    return out.reshape(-1)
+
+
+def unpack_repacked(rep, qtype, N, K):
+    """Inverse of repack: the GGUF payload back from the repacked bytes.
+
+    Raises ValueError when the size is not exact or a padding byte is nonzero.
+    """
+    slot, off = REPACK_SLOT[qtype]
+    nb = K // BLOCK_VALUES[qtype]
+    rep = np.ascontiguousarray(rep, dtype=np.uint8).reshape(-1)
+    if rep.size != N * nb * slot:
+        raise ValueError(f"repacked payload is {rep.size} bytes, expected exactly {N * nb * slot}")
+    r = rep.reshape(N, nb, slot)
+    pad = np.concatenate([r[:, :, :off], r[:, :, off + BLOCK_BYTES[qtype]:]], axis=-1)
+    if np.any(pad):
+        raise ValueError("nonzero padding byte in a repacked slot")
+    return np.ascontiguousarray(r[:, :, off:off + BLOCK_BYTES[qtype]]).reshape(-1)
 
 
 def _blocks(raw, qtype, N, K):

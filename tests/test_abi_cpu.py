@@ -116,6 +116,38 @@ def test_gemm_scratch_is_sized_by_the_split_plan():
     assert lib.mq_gemm(FAKE, mq.Q4_K, FAKE, FAKE, 512, 512, 3584, FAKE + 4, need, None) == -5
 
 
+def test_repacked_sizes_and_type_flag():
+    R = mq.REPACKED
+    assert mq.repack_bytes(mq.Q6_K, 152064, 3584) == 152064 * 14 * 224
+    assert mq.repack_bytes(mq.Q8_0, 4864, 896) == 4864 * 28 * 36
+    assert mq.weight_bytes(mq.Q6_K | R, 10, 512) == 10 * 2 * 224
+    assert mq.weight_bytes(mq.Q8_0 | R, 10, 64) == 10 * 2 * 36
+    assert mq.repack_bytes(mq.Q4_K, 10, 256) == 0          # already 16-byte aligned: no layout
+    assert mq.weight_bytes(mq.Q4_K | R, 10, 256) == 0
+    assert mq.repack_bytes(mq.Q6_K | R, 10, 256) == 0
+    assert mq.repack_bytes(mq.Q6_K, 10, 100) == 0
+    assert mq.gemm_scratch_bytes(mq.Q6_K | R, 8, 152064, 3584) == mq.gemm_scratch_bytes(mq.Q6_K, 8, 152064, 3584)
+
+
+def test_repack_refusals():
+    lib = mq.load()
+    nb6 = mq.weight_bytes(mq.Q6_K, 8, 512)
+    rb6 = mq.repack_bytes(mq.Q6_K, 8, 512)
+    far = FAKE + (1 << 24)
+    assert lib.mq_repack(None, mq.Q6_K, 8, 512, nb6, far, rb6, None) == -1
+    assert lib.mq_repack(FAKE, mq.Q4_K, 8, 512, mq.weight_bytes(mq.Q4_K, 8, 512), far, 1 << 20, None) == -3
+    assert "no repacked layout" in mq.last_error()
+    assert lib.mq_repack(FAKE, mq.Q6_K | mq.REPACKED, 8, 512, nb6, far, rb6, None) == -3
+    assert lib.mq_repack(FAKE, mq.Q6_K, 8, 500, nb6, far, rb6, None) == -2
+    assert lib.mq_repack(FAKE, mq.Q6_K, 8, 512, nb6 + 1, far, rb6, None) == -4      # exact length only
+    assert "exactly" in mq.last_error()
+    assert lib.mq_repack(FAKE, mq.Q6_K, 8, 512, nb6, far, rb6 - 1, None) == -4
+    assert lib.mq_repack(FAKE + 2, mq.Q6_K, 8, 512, nb6, far, rb6, None) == -5
+    assert lib.mq_repack(FAKE, mq.Q6_K, 8, 512, nb6, FAKE + 16, rb6, None) == -1    # overlap
+    assert "overlap" in mq.last_error()
+    assert lib.mq_gemv(FAKE, mq.Q4_K | mq.REPACKED, FAKE, FAKE, 8, 256, None) == -3
+
+
 def test_calls_without_init_are_refused_not_run():
     # Valid arguments but mq_init has not succeeded (and there may be no device
     # at all): the call must return an error code, never launch.

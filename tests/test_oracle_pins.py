@@ -99,6 +99,41 @@ def test_block_sizes_match_the_pages():
     assert oracle.row_bytes(Q8_0, 896) == 28 * 34
 
 
+def test_repacked_slots_follow_the_pages_and_their_alignment():
+    sizes = read_sizes()
+    slot6, off6 = oracle.REPACK_SLOT[Q6_K]
+    # the page's Q6_K slot, and what it is for: every slot starts 16-byte aligned
+    assert slot6 == sizes["Q6_K_PADDED_SLOT"][1] and slot6 % 16 == 0
+    assert off6 + oracle.BLOCK_BYTES[Q6_K] <= slot6
+    slot8, off8 = oracle.REPACK_SLOT[Q8_0]
+    # the Q8_0 codes follow the 2-byte scale: they must start 4-byte aligned
+    assert slot8 % 4 == 0 and (off8 + 2) % 4 == 0 and off8 + oracle.BLOCK_BYTES[Q8_0] <= slot8
+
+
+@pytest.mark.parametrize("qtype", [Q8_0, Q6_K], ids=["q8_0", "q6_K"])
+def test_repack_brute_force_and_round_trip(qtype):
+    rng = np.random.default_rng(qtype)
+    bv, bb = oracle.BLOCK_VALUES[qtype], oracle.BLOCK_BYTES[qtype]
+    N, nb = 3, 2
+    K = nb * bv
+    raw = rng.integers(0, 256, N * nb * bb, dtype=np.uint8)
+    rep = oracle.repack(raw, qtype, N, K)
+    slot, off = oracle.REPACK_SLOT[qtype]
+    assert rep.size == N * nb * slot
+    for n in range(N):              # byte by byte: slot (n, b) holds block (n, b) at off, zeros elsewhere
+        for b in range(nb):
+            for j in range(slot):
+                want = raw[(n * nb + b) * bb + j - off] if off <= j < off + bb else 0
+                assert rep[(n * nb + b) * slot + j] == want
+    assert np.array_equal(oracle.unpack_repacked(rep, qtype, N, K), raw)
+    bad = rep.copy()
+    bad[slot - 1 if off == 0 else 0] = 1     # a padding byte
+    with pytest.raises(ValueError):
+        oracle.unpack_repacked(bad, qtype, N, K)
+    with pytest.raises(ValueError):
+        oracle.unpack_repacked(rep[:-1], qtype, N, K)
+
+
 def test_payload_length_must_be_exact():
     raw = np.zeros(2 * 144, dtype=np.uint8)
     oracle.decode(raw, Q4_K, 2, 256)

@@ -316,8 +316,22 @@ def main():
         us = timer.per_launch_us([lambda W=W: mq.gemm(W, Q6_K, Xhq, 8, 152064, 3584, Y=Yh, scratch=sch)
                                   for W in hcop], reps)
         sec["mmq_q6_K_head_M8_152064x3584"] = {"us": round(us, 3), "weight_GBps": round(hb / us / 1e3, 1),
-                                               "TOPS": round(2 * 8 * 152064 * 3584 / us / 1e6, 2)}
+                                               "TOPS": round(2 * 8 * 152064 * 3584 / us / 1e6, 2),
+                                               "kernel": mq.last_kernel()}
+        # the same head in the repacked layout (224-byte slots): bytes read are the slots
+        rb = mq.repack_bytes(Q6_K, 152064, 3584)
+        rcop = [mq.repack(W, Q6_K, 152064, 3584) for W in hcop]
         del hcop
+        torch.cuda.synchronize()
+        us = timer.per_launch_us([lambda W=W: mq.gemv(W, Q6_K | mq.REPACKED, xh, 152064, 3584, y=yh)
+                                  for W in rcop], reps)
+        sec["gemv_q6_K_head_repacked_152064x3584"] = {"us": round(us, 3), "GBps": round(rb / us / 1e3, 1),
+                                                      "kernel": mq.last_kernel()}
+        us = timer.per_launch_us([lambda W=W: mq.gemm(W, Q6_K | mq.REPACKED, Xhq, 8, 152064, 3584, Y=Yh,
+                                                      scratch=sch) for W in rcop], reps)
+        sec["mmq_q6_K_head_M8_repacked_152064x3584"] = {"us": round(us, 3), "weight_GBps": round(rb / us / 1e3, 1),
+                                                        "kernel": mq.last_kernel()}
+        del rcop
         for N, K, tag in [(18944, 3584, "7B_ffn_up_shape"), (4864, 896, "0.5B_ffn_up")]:
             w8 = synth.quantized_weight(Q8_0, N, K, 0, 0)
             nb = mq.weight_bytes(Q8_0, N, K)

@@ -24,6 +24,7 @@
 
 #include "mq_device.h"
 #include "mq_internal.h"
+#include "weight_units.h"
 
 namespace mq {
 
@@ -69,23 +70,10 @@ __device__ __forceinline__ void dot16(const uint32_t* c, const uint4& a, const u
 }
 
 // ---------------------------------------------------------------- Q4_K
-// Unit u of a row: super-block u/4, 64-value group c = u%4 (sub-blocks 2c and
-// 2c+1).  Bytes: 16-byte header (d, dmin, packed scales) and the 32 code bytes
-// at 16 + 32c; byte i holds the code of value 64c+i (low nibble) and of value
-// 64c+32+i (high nibble).  Staged chunks 0,1 hold values 64u..64u+31 (the low
-// nibbles), chunks 2,3 values 64u+32..64u+63.
-struct UnitQ4K {
-    static constexpr int kValues = 64;
+// Staged chunks 0,1 hold values 64u..64u+31 (the low nibbles), chunks 2,3 values
+// 64u+32..64u+63.
+struct UnitQ4K : RawQ4K {
     static constexpr int kChunks = 4;
-    uint4 hd, q0, q1;
-
-    __device__ void load(const uint8_t* __restrict__ row, int u, int, int) {
-        const uint8_t* blk = row + 144 * (u >> 2);
-        hd = *reinterpret_cast<const uint4*>(blk);
-        const uint4* qs = reinterpret_cast<const uint4*>(blk + 16 + 32 * (u & 3));
-        q0 = qs[0];
-        q1 = qs[1];
-    }
 
     // exact sum of code * v over a 32-value run: int32 (|s2| <= 32 * 15 * 32)
     __device__ static int run_dot(const uint32_t (&c)[8], const Stage& st, int k0, int uu) {
@@ -99,79 +87,28 @@ struct UnitQ4K {
     }
 
     __device__ float dot(const Stage& st, int uu, int u) const {
-        const int c = u & 3;
         uint32_t lo[8], hi[8];
-        const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            lo[k] = w[k] & 0x0F0F0F0Fu;
-            hi[k] = (w[k] >> 4) & 0x0F0F0F0Fu;
-        }
+        codes(lo, hi);
         const int ilo = run_dot(lo, st, 0, uu);
         const int ihi = run_dot(hi, st, 2, uu);
-        // 6-bit (scale, min) of sub-blocks 2c, 2c+1, two per halfword, no branches:
-        // c < 2 reads bytes 2c,2c+1 of the first two dwords; c >= 2 assembles from all three.
-        const uint32_t sh = 16u * uint32_t(c & 1);
-        const uint32_t t0 = hd.y >> sh, t1 = hd.z >> sh, t2 = hd.w >> sh;
-        const uint32_t sc_hi = (t2 & 0x0F0Fu) | ((t0 >> 2) & 0x3030u);
-        const uint32_t mn_hi = ((t2 >> 4) & 0x0F0Fu) | ((t1 >> 2) & 0x3030u);
-        const uint32_t scp = c >= 2 ? sc_hi : (t0 & 0x3F3Fu);
-        const uint32_t mnp = c >= 2 ? mn_hi : (t1 & 0x3F3Fu);
-        const float d = half_bits_to_float(hd.x & 0xFFFFu);
-        const float dmin = half_bits_to_float(hd.x >> 16);
+        uint32_t scp, mnp;
+        scale_min(u & 3, scp, mnp);
         const int2 e2 = *reinterpret_cast<const int2*>(st.ex + 2 * uu);
         const float2 s2 = *reinterpret_cast<const float2*>(st.sums + 2 * uu);
-        const float codes = ldexpf(ubyte_f<0>(scp) * float(ilo), e2.x) + ldexpf(ubyte_f<1>(scp) * float(ihi), e2.y);
+        const float codes_term = ldexpf(ubyte_f<0>(scp) * float(ilo), e2.x) + ldexpf(ubyte_f<1>(scp) * float(ihi), e2.y);
         const float mins = fmaf(ubyte_f<0>(mnp), s2.x, ubyte_f<1>(mnp) * s2.y);
-        return fmaf(d, codes, -dmin * mins);
+        return fmaf(d(), codes_term, -dmin() * mins);
     }
 };
 
 // ---------------------------------------------------------------- Q6_K
-// Unit u: super-block u/4, half h = (u/2)%2, lane run l in [l0, l0+16) with
-// l0 = 16*(u%2): values 128h + 32t + l for t < 4 (16 each, one sub-scale each);
-// staged chunk t of the unit holds exactly those 16 values.
-// Low 4 bits: ql[64h + l] (t = 0 low nibble, t = 2 high nibble) and
-// ql[64h + 32 + l] (t = 1, 3); high 2 bits: bits 2t..2t+1 of qh[32h + l].
-// GGUF blocks are 210 bytes, so a block starts on a 2-byte boundary: every segment
-// is read as naturally aligned dwords and realigned with v_alignbyte (a no-op on the
-// 16-byte-aligned 224-byte slots of the repacked layout).
-struct UnitQ6K {
-    static constexpr int kValues = 64;
+// Staged chunk t of the unit holds exactly the 16 values of run t.
+struct UnitQ6K : RawQ6K {
     static constexpr int kChunks = 4;
-    uint32_t a[5], b[5], hq[5], s[3];
-    uint32_t dbits;
-    uint32_t shift;
-
-    __device__ void load(const uint8_t* __restrict__ row, int u, int stride, int off) {
-        const uint8_t* blk = row + stride * (u >> 2) + off;
-        const int h = (u >> 1) & 1, l0 = 16 * (u & 1);
-        const uintptr_t base = reinterpret_cast<uintptr_t>(blk);
-        shift = uint32_t(base & 3);
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(base & ~uintptr_t(3));
-        // Every dword read holds at least one byte of this block, so none can
-        // fault: segments end at most 196 bytes in, the scales end at 210.
-        const uint32_t* pa = p + (64 * h + l0) / 4;
-        const uint32_t* pb = p + (64 * h + 32 + l0) / 4;
-        const uint32_t* ph = p + (128 + 32 * h + l0) / 4;
-        const uint32_t* ps = p + (192 + 8 * h) / 4;
-#pragma unroll
-        for (int i = 0; i < 5; ++i) { a[i] = pa[i]; b[i] = pb[i]; hq[i] = ph[i]; }
-#pragma unroll
-        for (int i = 0; i < 3; ++i) s[i] = ps[i];
-        dbits = load_u16(blk + 208);
-    }
 
     __device__ float dot(const Stage& st, int uu, int u) const {
-        const int hi16 = u & 1;
-        uint32_t A[4], B[4], H[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            A[i] = align_byte(a[i + 1], a[i], shift);
-            B[i] = align_byte(b[i + 1], b[i], shift);
-            H[i] = align_byte(hq[i + 1], hq[i], shift);
-        }
-        const uint32_t s0 = align_byte(s[1], s[0], shift), s1 = align_byte(s[2], s[1], shift);
+        uint32_t A[4], B[4], H[4], s0, s1;
+        realign(A, B, H, s0, s1);
         const int4 e4 = *reinterpret_cast<const int4*>(st.ex + 4 * uu);
         const float4 m4 = *reinterpret_cast<const float4*>(st.sums + 4 * uu);
         const int ev[4] = {e4.x, e4.y, e4.z, e4.w};
@@ -180,59 +117,34 @@ struct UnitQ6K {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             uint32_t code[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t ql = (t & 1) ? B[i] : A[i];
-                const uint32_t lo = (t < 2) ? ql : (ql >> 4);
-                const uint32_t hb = (H[i] >> (2 * t)) & 0x03030303u;
-                code[i] = (lo & 0x0F0F0F0Fu) | (hb << 4);   // bytes: codes 0..63
-            }
+            run_codes(t, A, B, H, code);
             uint4 xa, xb, xc;
             st.chunk(t, uu, xa, xb, xc);
             int d0 = 0, d1 = 0, d2 = 0;
             dot16(code, xa, xb, xc, d0, d1, d2);
             // sum((c - 32) * x) = 2^e * sum(c * v) - 32 * sum(x)
             const float cv = ldexpf(combine3(d2, d1, d0), ev[t]);
-            const int g = 2 * t + hi16;                  // sub-scale byte within this half
-            const uint32_t word = g < 4 ? s0 : s1;
-            const float sc = float(int32_t(word << (24 - 8 * (g & 3))) >> 24);
-            acc = fmaf(sc, fmaf(-32.0f, sv[t], cv), acc);
+            acc = fmaf(subscale(t, u, s0, s1), fmaf(-32.0f, sv[t], cv), acc);
         }
-        return half_bits_to_float(dbits) * acc;
+        return d() * acc;
     }
 };
 
 // ---------------------------------------------------------------- Q8_0
-// Unit u = block u (34 bytes: f16 d, 32 int8 codes), 2-byte aligned in the GGUF
-// payload (at offset 2 of a 36-byte slot in the repacked layout, so that its codes
-// are 4-byte aligned); staged chunks 0,1 hold its 32 values.
-struct UnitQ80 {
-    static constexpr int kValues = 32;
+// Staged chunks 0,1 hold the block's 32 values.
+struct UnitQ80 : RawQ80 {
     static constexpr int kChunks = 2;
-    uint32_t w[9];
-    uint32_t odd;
 
-    __device__ void load(const uint8_t* __restrict__ row, int u, int stride, int off) {
-        const uintptr_t base = reinterpret_cast<uintptr_t>(row + stride * u + off);
-        odd = uint32_t(base & 2);
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(base & ~uintptr_t(3));
-        // 9 naturally aligned dwords cover the block; each holds a byte of it
-#pragma unroll
-        for (int i = 0; i < 9; ++i) w[i] = p[i];
-    }
-
-    __device__ float dot(const Stage& st, int uu, int u) const {
-        const float d = half_bits_to_float(odd ? (w[0] >> 16) : (w[0] & 0xFFFFu));
+    __device__ float dot(const Stage& st, int uu, int) const {
         uint32_t c[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = odd ? w[i + 1] : align_byte(w[i + 1], w[i], 2);
+        codes(c);
         int s0 = 0, s1 = 0, s2 = 0;
         uint4 a, b, e;
         st.chunk(0, uu, a, b, e);
         dot16(c, a, b, e, s0, s1, s2);
         st.chunk(1, uu, a, b, e);
         dot16(c + 4, a, b, e, s0, s1, s2);
-        return d * ldexpf(combine3(s2, s1, s0), st.ex[uu]);
+        return d() * ldexpf(combine3(s2, s1, s0), st.ex[uu]);
     }
 };
 

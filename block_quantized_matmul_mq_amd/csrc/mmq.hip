@@ -670,6 +670,7 @@ MmqPlan mmq_plan(int /*type*/, int64_t M, int64_t N, int64_t K) {
 }
 
 size_t mmq_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
+    if (gemv_q8_applies(type, M, K)) return 0;
     const MmqPlan p = mmq_plan(type, M, N, K);
     return size_t(p.split_tiles) * size_t(p.splits) * size_t(p.bm) * BN * sizeof(float);
 }
@@ -677,6 +678,7 @@ size_t mmq_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
 hipError_t launch_mmq(int type, BlockLayout lay, const uint8_t* W, const int8_t* codes, const float* xs,
                       const int32_t* xsum, float* Y, int32_t* dots, float* partial, int64_t M, int64_t N, int64_t K,
                       hipStream_t s, const char** name) {
+    if (gemv_q8_applies(type, M, K)) return launch_gemv_q8(type, lay, W, codes, xs, xsum, Y, dots, M, N, K, s, name);
     const bool repacked = lay.off != 0 || (type == kQ6_K && lay.stride != 210);
     switch (type) {
         case kQ8_0:

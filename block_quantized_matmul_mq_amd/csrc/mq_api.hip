@@ -161,6 +161,7 @@ int mq_init(int device) {
     info.lds_per_block = lds;
     // Kernel attributes are set here, once, so that no call ever sets one inside a stream capture.
     e = gemv_set_attributes(lds);
+    if (e == hipSuccess) e = gemv_q8_set_attributes(lds);
     if (e != hipSuccess)
         return fail(MQ_ERR_DEVICE, "mq_init: setting the GEMV LDS limit to %zu bytes failed: %s", lds,
                     hipGetErrorName(e));

@@ -63,6 +63,15 @@ size_t mmq_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
 hipError_t launch_mmq(int type, BlockLayout layout, const uint8_t* W, const int8_t* codes, const float* scales,
                       const int32_t* sums, float* Y, int32_t* dots, float* partial, int64_t M, int64_t N,
                       int64_t K, hipStream_t s, const char** kernel_name);
+// mq_gemm for M <= kGemvQ8MaxRows: a multi-row GEMV over the quantized activation plane
+// (gemv_q8.hip), taken by launch_mmq whenever gemv_q8_applies; it needs no scratch.
+constexpr int kGemvQ8MaxRows = 8;
+constexpr size_t kGfx950LdsBytes = 160 * 1024;
+bool gemv_q8_applies(int type, int64_t M, int64_t K);
+hipError_t gemv_q8_set_attributes(size_t lds_limit);
+hipError_t launch_gemv_q8(int type, BlockLayout lay, const uint8_t* W, const int8_t* codes, const float* scales,
+                          const int32_t* sums, float* Y, int32_t* dots, int64_t M, int64_t N, int64_t K,
+                          hipStream_t s, const char** kernel_name);
 // mq_repack: every `in_bytes`-byte block of W into a `slot_bytes`-byte slot of Wr at offset
 // `off`, the rest of the slot zero (repack.hip).
 hipError_t launch_repack(const uint8_t* W, uint8_t* Wr, int64_t blocks, int in_bytes, int slot_bytes, int off,

@@ -103,8 +103,11 @@ def test_gemm_scratch_is_sized_by_the_split_plan():
     assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 512, 3584) == 14 * 16 * tile
     # 112 tiles: 4 ranges
     assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 3584, 3584) == 4 * 112 * tile
-    # M <= 32: 32 x 128 tiles; the vocab head at M = 8 has 1188 of them, the last 164 cut in 3
-    assert mq.gemm_scratch_bytes(mq.Q6_K, 8, 152064, 3584) == 3 * 164 * 32 * 128 * 4
+    # 8 < M <= 32: 32 x 128 tiles; the vocab head at M = 9 has 1188 of them, the last 164 cut in 3
+    assert mq.gemm_scratch_bytes(mq.Q6_K, 9, 152064, 3584) == 3 * 164 * 32 * 128 * 4
+    # M <= 8: the multi-row GEMV, no scratch -- unless the rows do not fit its LDS
+    assert mq.gemm_scratch_bytes(mq.Q6_K, 8, 152064, 3584) == 0
+    assert mq.gemm_scratch_bytes(mq.Q6_K, 8, 260, 32768) > 0
     # invalid shapes report 0 (the call itself refuses them)
     assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 512, 100) == 0
     assert mq.gemm_scratch_bytes(99, 512, 512, 3584) == 0
@@ -126,7 +129,7 @@ def test_repacked_sizes_and_type_flag():
     assert mq.weight_bytes(mq.Q4_K | R, 10, 256) == 0
     assert mq.repack_bytes(mq.Q6_K | R, 10, 256) == 0
     assert mq.repack_bytes(mq.Q6_K, 10, 100) == 0
-    assert mq.gemm_scratch_bytes(mq.Q6_K | R, 8, 152064, 3584) == mq.gemm_scratch_bytes(mq.Q6_K, 8, 152064, 3584)
+    assert mq.gemm_scratch_bytes(mq.Q6_K | R, 9, 152064, 3584) == mq.gemm_scratch_bytes(mq.Q6_K, 9, 152064, 3584)
 
 
 def test_repack_refusals():

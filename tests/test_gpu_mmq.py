@@ -42,7 +42,7 @@ def check_blockdots(raw, qtype, X, N, K, what):
     Xq = quantized_plane(X, dev)
     D = mq.gemm_blockdots(to_dev(raw.reshape(-1), dev), qtype, Xq, M, N, K)
     torch.cuda.synchronize()
-    assert mq.last_kernel().startswith("mmq")
+    assert mq.last_kernel().startswith(("mmq", "gemv_q8"))
     D = D.cpu().numpy()
     q, _, _ = oracle.quantize_act(X)
     ref = oracle.block_dots(raw, qtype, q, N, K)
@@ -57,7 +57,7 @@ def check_gemm(raw, qtype, X, N, K, cols=None, what=""):
     Xq = quantized_plane(X, dev)
     Y = mq.gemm(to_dev(raw.reshape(-1), dev), qtype, Xq, M, N, K)
     torch.cuda.synchronize()
-    assert mq.last_kernel().startswith("mmq")
+    assert mq.last_kernel().startswith(("mmq", "gemv_q8"))
     Y = Y.cpu().numpy()
     cols = np.arange(N) if cols is None else cols
     xn, q, d = x_hat_norms(X)
@@ -92,6 +92,34 @@ def test_split_k_uneven_ranges(qtype):
     X = synth.activations(M, K, config_index=12, tensor_index=30)
     check_blockdots(raw, qtype, X, N, K, "split-K")
     check_gemm(raw, qtype, X, N, K, what="split-K")
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
+def test_small_m_multirow_gemv(qtype):
+    # M <= 8 runs the multi-row GEMV over the quantized plane (rows padded to 1, 2, 4 or 8
+    # in the kernel), ragged N and a K of several units; its block dots are exported by
+    # the same kernel template.
+    K = 2 * BLOCK[qtype] + 512
+    for i, M in enumerate([1, 2, 3, 5, 8]):
+        N = 300 + 7 * i
+        raw = weights(qtype, N, K, "random", 110 + i)
+        X = synth.activations(M, K, config_index=12, tensor_index=60 + i)
+        check_blockdots(raw, qtype, X, N, K, f"M={M}")
+        assert mq.last_kernel().startswith("gemv_q8")
+        check_gemm(raw, qtype, X, N, K, what=f"M={M}")
+        assert mq.last_kernel().startswith("gemv_q8")
+        assert mq.gemm_scratch_bytes(qtype, M, N, K) == 0
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
+def test_small_m_long_rows(qtype):
+    # A long row still fits the multi-row GEMV's LDS at M = 4; at M = 8 and K = 32768 it
+    # does not, and the product runs on the MMQ kernel with 32-row tiles.
+    for M, K, N, path in [(4, 18944, 700, "gemv_q8"), (8, 32768, 260, "mmq")]:
+        raw = weights(qtype, N, K, "random", 120 + M)
+        X = synth.activations(M, K, config_index=12, tensor_index=70 + M)
+        check_gemm(raw, qtype, X, N, K, what=f"M={M} K={K}")
+        assert mq.last_kernel().startswith(path), mq.last_kernel()
 
 
 @pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])

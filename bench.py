@@ -286,7 +286,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gemv_alg_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gemv_alg_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": recorded_traffic("gemv_q4k_7b_ffn_hbm_traffic.txt",
-                                                 ["gemv.hip", "gemv_mfma.hip", "mq_device.h"]),
+                                                 ["gemv.hip", "gemv_mfma.hip", "weight_units.h", "mq_device.h"]),
                      "algorithmic_bytes_per_launch": gemv_alg_bytes,
                      "kernel": f"{kernel_names['gemv_ffn_up']} (ffn_up) + {kernel_names['gemv_ffn_down']} (ffn_down)",
                      "ffn_up_GBps": round(up_gbps, 1), "ffn_down_GBps": round(down_gbps, 1)},

@@ -103,6 +103,8 @@ def test_gemm_scratch_is_sized_by_the_split_plan():
     assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 512, 3584) == 14 * 16 * tile
     # 112 tiles: 4 ranges
     assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 3584, 3584) == 4 * 112 * tile
+    # Q8_0 splits the same way (28 K-steps of 128 at K = 3584)
+    assert mq.gemm_scratch_bytes(mq.Q8_0, 512, 512, 3584) == 14 * 16 * tile
     # 8 < M <= 32: 32 x 128 tiles; the vocab head at M = 9 has 1188 of them, the last 164 cut in 3
     assert mq.gemm_scratch_bytes(mq.Q6_K, 9, 152064, 3584) == 3 * 164 * 32 * 128 * 4
     # M <= 8: the multi-row GEMV, no scratch -- unless the rows do not fit its LDS

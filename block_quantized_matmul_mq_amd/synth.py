@@ -4,7 +4,8 @@ This module makes the inputs that both the HIP library and the CPU checks
 consume.  It holds none of the matmul's arithmetic (no decode, no dot
 product, no activation quantizer); it only draws seeded f32 tensors and
 packs them into the GGUF block byte layouts Q8_0 (34 B / 32 values),
-Q4_K (144 B / 256) and Q6_K (210 B / 256).  Sizes follow "minfer CUDA
+Q4_0 / Q4_1 / Q5_0 / Q5_1 (18 / 20 / 22 / 24 B / 32), Q4_K (144 B / 256),
+Q5_K (176 B / 256) and Q6_K (210 B / 256).  Sizes follow "minfer CUDA
 Backend Design", 2.3 Weight residency and registry; the field layouts are the
 public GGUF ones.
 
@@ -22,18 +23,30 @@ readings used to make test weights, each with an exact error bound):
 * Q6_K: step_g = amax_g / 31 per 16-value group; d = f16_up(max_g step_g / 127);
   s_g = ceil(step_g / d) <= 127; code - 32 = rne(w / (d*s_g)) in [-31, 31];
   |w - d*s_g*(code - 32)| <= d*s_g / 2.
+* Q4_0 / Q5_0 (symmetric, codes offset by 8 / 16): d = f16_up(amax / 7) or
+  f16_up(amax / 15); q = rne(w / d) (|q| <= 7 or 15); |w - d*q| <= d/2.
+* Q4_1 / Q5_1 (affine): m = f16_down(min w); d = f16_up((max w - m) / 15 or
+  31); code = clamp(rne((w - m) / d), 0, 15 or 31); the grid covers
+  [min w, max w], so |w - (d*code + m)| <= d/2 (a block of equal values has
+  d = 0 and is off by at most its f16 rounding of m).
+* Q5_K: the Q4_K quantizer with 31 code steps instead of 15.
 
 Seeds: numpy ``default_rng(SeedSequence([0, config_index, tensor_index]))``.
 """
 
 import numpy as np
 
+Q4_0 = 2
+Q4_1 = 3
+Q5_0 = 6
+Q5_1 = 7
 Q8_0 = 8
 Q4_K = 12
+Q5_K = 13
 Q6_K = 14
 
-BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q6_K: 210}
+BLOCK_VALUES = {Q4_0: 32, Q4_1: 32, Q5_0: 32, Q5_1: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q5_0: 22, Q5_1: 24, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
 _ROW_CHUNK = 2048
 
@@ -63,6 +76,17 @@ def f16_round_up(v):
     h = np.where(low, np.nextafter(h, np.float16(np.inf)), h).astype(np.float16)
     if not np.all(np.isfinite(h)):
         raise ValueError("scale overflows binary16")
+    return h
+
+
+def f16_round_down(v):
+    """Largest IEEE binary16 value <= v (finite), as a float16 array."""
+    v = np.asarray(v, dtype=np.float64)
+    h = v.astype(np.float16)
+    high = h.astype(np.float64) > v
+    h = np.where(high, np.nextafter(h, np.float16(-np.inf)), h).astype(np.float16)
+    if not np.all(np.isfinite(h)):
+        raise ValueError("value overflows binary16")
     return h
 
 
@@ -133,6 +157,97 @@ def encode_q4_k(W):
     return out.reshape(N, nb * 144)
 
 
+def _k_quant_header_codes(wb, steps):
+    """The Q4_K covering quantizer with `steps` code steps (15 for Q4_K, 31 for Q5_K).
+
+    wb: f64 [.., nb, 8, 32].  Returns d, dmin (f16 [.., nb]), sc, mn (int [.., nb, 8]) and
+    codes (int [.., nb, 256]).
+    """
+    lo = np.minimum(0.0, wb.min(axis=-1))
+    hi = wb.max(axis=-1)
+    mprime = -lo + 0.0
+    dmin = f16_round_up(mprime.max(axis=-1) / 63.0)
+    dmin64 = dmin.astype(np.float64)[..., None]
+    mn = np.where(dmin64 > 0, np.minimum(63, np.ceil(mprime / np.where(dmin64 > 0, dmin64, 1.0))), 0)
+    offset = dmin64 * mn
+    span = hi + offset
+    d = f16_round_up(span.max(axis=-1) / (steps * 63.0))
+    d64 = d.astype(np.float64)[..., None]
+    sc = np.where(d64 > 0, np.minimum(63, np.ceil(span / (steps * np.where(d64 > 0, d64, 1.0)))), 0)
+    step = (d64 * sc)[..., None]
+    codes = np.where(step > 0, np.clip(np.rint((wb + offset[..., None]) / np.where(step > 0, step, 1.0)), 0, steps), 0)
+    shape = wb.shape[:-2]
+    return d, dmin, sc.astype(np.int64), mn.astype(np.int64), codes.reshape(shape + (256,)).astype(np.int64)
+
+
+def encode_q5_k(W):
+    W = np.asarray(W, dtype=np.float32)
+    N, K = W.shape
+    nb = K // 256
+    out = np.empty((N, nb, 176), dtype=np.uint8)
+    for r0 in range(0, N, _ROW_CHUNK):
+        r1 = min(N, r0 + _ROW_CHUNK)
+        wb = W[r0:r1].reshape(r1 - r0, nb, 8, 32).astype(np.float64)
+        d, dmin, sc, mn, codes = _k_quant_header_codes(wb, 31)
+        out[r0:r1] = _pack_q5_k(d, dmin, sc, mn, codes)
+    return out.reshape(N, nb * 176)
+
+
+def _pack_q5_k(d, dmin, sc, mn, codes):
+    """176-byte blocks: the Q4_K header and nibbles around 32 bytes of high bits."""
+    q4 = _pack_q4_k(d, dmin, sc, mn, codes & 15)
+    out = np.zeros(d.shape + (176,), dtype=np.uint8)
+    out[..., 0:16] = q4[..., 0:16]
+    out[..., 48:176] = q4[..., 16:144]
+    high = (codes >> 4).astype(np.uint8)
+    for j in range(8):
+        out[..., 16:48] |= high[..., 32 * j:32 * j + 32] << j
+    return out
+
+
+def _pack_legacy(qtype, d, m, codes):
+    """Blocks of the 32-value types: f16 d, [f16 m], [qh], 16 nibble bytes; codes [.., 32]."""
+    nbytes = BLOCK_BYTES[qtype]
+    out = np.zeros(d.shape + (nbytes,), dtype=np.uint8)
+    out[..., 0:2] = _f16_bytes(d)
+    pos = 2
+    if qtype in (Q4_1, Q5_1):
+        out[..., 2:4] = _f16_bytes(m)
+        pos = 4
+    codes = codes.astype(np.int64)
+    if qtype in (Q5_0, Q5_1):
+        bits = np.zeros(d.shape, dtype=np.int64)
+        for i in range(32):
+            bits |= ((codes[..., i] >> 4) & 1) << i
+        for k in range(4):
+            out[..., pos + k] = (bits >> (8 * k)) & 0xFF
+        pos += 4
+    out[..., pos:pos + 16] = ((codes[..., 0:16] & 15) | ((codes[..., 16:32] & 15) << 4)).astype(np.uint8)
+    return out
+
+
+def _encode_legacy(qtype, W):
+    W = np.asarray(W, dtype=np.float32)
+    N, K = W.shape
+    nb = K // 32
+    wb = W.reshape(N, nb, 32).astype(np.float64)
+    top = 15 if qtype in (Q4_0, Q4_1) else 31
+    if qtype in (Q4_0, Q5_0):
+        qmax, off = (7, 8) if qtype == Q4_0 else (15, 16)
+        d = f16_round_up(np.max(np.abs(wb), axis=-1) / qmax)
+        d64 = d.astype(np.float64)[..., None]
+        q = np.where(d64 > 0, np.clip(np.rint(wb / np.where(d64 > 0, d64, 1.0)), -qmax, qmax), 0)
+        codes = q + off
+        m = np.zeros_like(d)
+    else:
+        m = f16_round_down(wb.min(axis=-1))
+        m64 = m.astype(np.float64)[..., None]
+        d = f16_round_up((wb.max(axis=-1) - m.astype(np.float64)) / top)
+        d64 = d.astype(np.float64)[..., None]
+        codes = np.where(d64 > 0, np.clip(np.rint((wb - m64) / np.where(d64 > 0, d64, 1.0)), 0, top), 0)
+    return _pack_legacy(qtype, d, m, codes).reshape(N, nb * BLOCK_BYTES[qtype])
+
+
 def _pack_q6_k(d, scales, codes):
     """Pack fields into 210-byte blocks.  scales [.., 16] int8; codes [.., 256] in [0, 63]."""
     shape = d.shape
@@ -167,7 +282,9 @@ def encode_q6_k(W):
     return out.reshape(N, nb * 210)
 
 
-ENCODERS = {Q8_0: encode_q8_0, Q4_K: encode_q4_k, Q6_K: encode_q6_k}
+ENCODERS = {Q8_0: encode_q8_0, Q4_K: encode_q4_k, Q6_K: encode_q6_k, Q5_K: encode_q5_k,
+            Q4_0: lambda W: _encode_legacy(Q4_0, W), Q4_1: lambda W: _encode_legacy(Q4_1, W),
+            Q5_0: lambda W: _encode_legacy(Q5_0, W), Q5_1: lambda W: _encode_legacy(Q5_1, W)}
 
 
 def weights_f32(N, K, config_index, tensor_index, sigma=0.02, rows=None):
@@ -223,9 +340,11 @@ def random_blocks(qtype, N, K, rng, exp_lo=-14, exp_hi=-4):
     if qtype == Q8_0:
         raw[..., 0:2] = _f16_bytes(_random_f16(rng, (N, nb), exp_lo, exp_hi))
         # -128 is not a code the quantizer emits but it is a valid int8: keep it.
-    elif qtype == Q4_K:
+    elif qtype in (Q4_K, Q5_K, Q4_1, Q5_1):
         raw[..., 0:2] = _f16_bytes(_random_f16(rng, (N, nb), exp_lo, exp_hi))
         raw[..., 2:4] = _f16_bytes(_random_f16(rng, (N, nb), exp_lo, exp_hi))
+    elif qtype in (Q4_0, Q5_0):
+        raw[..., 0:2] = _f16_bytes(_random_f16(rng, (N, nb), exp_lo, exp_hi))
     elif qtype == Q6_K:
         raw[..., 208:210] = _f16_bytes(_random_f16(rng, (N, nb), exp_lo, exp_hi))
     return raw.reshape(N, nb * BLOCK_BYTES[qtype])

@@ -21,15 +21,15 @@ Pinning status (each function's docstring repeats it):
 * The arithmetic of every function is pinned by tests that do not retype it:
   hand-worked blocks with closed-form values, a brute-force product in exact
   rationals, closed forms, invariants and planted-mistake (mutation) checks.
-* The *bit layouts* of Q4_K and Q6_K are the public GGUF layouts; the pages
-  state only the block byte sizes.  Agreement with real GGUF files is
+* The *bit layouts* of every type are the public GGUF layouts; the pages state
+  only block byte sizes (Q8_0, Q4_K, Q4_0, Q5_K) and the list of types.  Agreement with real GGUF files is
   **parity unpinned**: no GGUF file exists in this environment to pin it.
 """
 
 from .mq_oracle import (  # noqa: F401
-    Q8_0, Q4_K, Q6_K, BLOCK_VALUES, BLOCK_BYTES,
+    Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q4_K, Q5_K, Q6_K, BLOCK_VALUES, BLOCK_BYTES, LEGACY,
     f16_bits_to_f64, row_bytes,
-    q8_0_fields, q4_k_fields, q6_k_fields, decode,
+    q8_0_fields, q4_k_fields, q5_k_fields, q6_k_fields, legacy_fields, decode,
     gemv, quantize_act, block_dots, mmq, mmq_from_block_dots,
     REPACK_SLOT, repack, unpack_repacked,
 )

@@ -6,9 +6,11 @@ library's IEEE half codec (``struct`` format 'e').  It shares no code with
 ``mq_oracle`` so that a slip in either (a swapped nibble, a wrong scale index,
 a shifted qh pair) shows up as a disagreement on random bytes.
 
-The layouts it reads are the public GGUF ones (Q8_0 34 B, Q4_K 144 B,
-Q6_K 210 B per block); only the sizes are on the pages ("minfer CUDA Backend
-Design", 2.3 Weight residency and registry).  GGUF interop: parity unpinned.
+The layouts it reads are the public GGUF ones (Q8_0 34 B, Q4_0 18 B, Q4_1
+20 B, Q5_0 22 B, Q5_1 24 B per 32 values; Q4_K 144 B, Q5_K 176 B, Q6_K 210 B
+per 256); only some sizes are on the pages ("minfer CUDA Backend Design", 2.3
+Weight residency and registry; "GPU Safety (Metal + CUDA Backends)", 3. Audit
+findings).  GGUF interop: parity unpinned.
 """
 
 import struct
@@ -93,4 +95,65 @@ def decode_q6_k_block(block):
         su = block[192 + e // 16]
         scale = su - 256 if su >= 128 else su
         out.append(d * scale * (code - 32))
+    return out
+
+
+def _legacy(block, nbytes, has_min, has_high, offset):
+    """Shared walk of the 32-value types: f16 d, [f16 m], [qh: 32 bits], 16 nibble bytes."""
+    block = bytes(bytearray(int(b) for b in block))
+    assert len(block) == nbytes
+    d = _half(block, 0)
+    m = _half(block, 2) if has_min else 0.0
+    qh_at = 4 if has_min else 2
+    qs_at = qh_at + (4 if has_high else 0)
+    out = []
+    for i in range(32):
+        byte_index = qs_at + (i % 16)
+        first_bit = 0 if i < 16 else 4
+        positions = [(byte_index, first_bit + k) for k in range(4)]
+        if has_high:
+            positions.append((qh_at + i // 8, i % 8))
+        code = _field(block, positions)
+        out.append(d * (code - offset) + m)
+    return out
+
+
+def decode_q4_0_block(block):
+    """18 bytes -> 32 floats: d * (code - 8)."""
+    return _legacy(block, 18, False, False, 8)
+
+
+def decode_q4_1_block(block):
+    """20 bytes -> 32 floats: d * code + m."""
+    return _legacy(block, 20, True, False, 0)
+
+
+def decode_q5_0_block(block):
+    """22 bytes -> 32 floats: d * (code - 16), 5-bit codes."""
+    return _legacy(block, 22, False, True, 16)
+
+
+def decode_q5_1_block(block):
+    """24 bytes -> 32 floats: d * code + m, 5-bit codes."""
+    return _legacy(block, 24, True, True, 0)
+
+
+def decode_q5_k_block(block):
+    """176 bytes -> 256 floats (Q4_K header, 32 bytes qh at 16, nibbles at 48)."""
+    block = bytes(bytearray(int(b) for b in block))
+    assert len(block) == 176
+    d = _half(block, 0)
+    dmin = _half(block, 2)
+    out = []
+    for e in range(256):
+        j = e // 32
+        sc_pos, mn_pos = _q4_k_scale_min_positions(j)
+        sc = _field(block, sc_pos)
+        mn = _field(block, mn_pos)
+        chunk, r = divmod(e, 64)
+        byte_index = 48 + 32 * chunk + (r % 32)
+        first_bit = 0 if r < 32 else 4
+        positions = [(byte_index, first_bit + k) for k in range(4)] + [(16 + e % 32, j)]
+        code = _field(block, positions)
+        out.append(d * sc * code - dmin * mn)
     return out

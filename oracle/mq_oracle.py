@@ -40,6 +40,25 @@ Readings where the pages are silent (each also listed in the design doc):
 * R7  Block dots are exact integers: per 32-value block for Q8_0 and Q4_K
       (Q4_K codes in [0, 15], unsigned), per 16-value group for Q6_K with the
       signed code (c - 32).
+* R14 The 32-value types Q4_0 / Q4_1 / Q5_0 / Q5_1 (named by the matmul type
+      whitelist, "minfer CUDA Backend Design", 4.3 Eligibility; Q4_0's 18 bytes
+      per 32 values by the bytes-per-element ratio it shares with Q4_K, same
+      page, 2.3) use the public GGUF layouts: f16 d, then (Q4_1, Q5_1) f16 m,
+      then (Q5_0, Q5_1) 4 bytes of high bits qh, then 16 bytes of nibbles.
+      Value i < 16 is the low nibble of byte i, value 16 + i its high nibble;
+      bit i of the little-endian 32-bit qh is bit 4 of value i's code.
+      Q4_0: d * (code - 8); Q5_0: d * (code - 16); Q4_1, Q5_1: d * code + m.
+      Sizes 18, 20, 22, 24 bytes.
+* R15 Q5_K (176 bytes per 256 values, the block size "GPU Safety (Metal + CUDA
+      Backends)", 3. Audit findings, names as the bound of the kernel's qh/qs
+      reads): Q4_K's
+      header (f16 d, f16 dmin, the same 12 packed bytes of 6-bit scales and
+      mins), then 32 bytes qh, then Q4_K's 128 bytes of nibbles; bit j of
+      qh[e % 32] is bit 4 of the code of value e, j = e // 32 its sub-block.
+      value_e = d * scale_j * code_e - dmin * min_j, codes in [0, 31].
+* R16 Block dots of the new types are per 32-value block: the signed code
+      (code - 8 or code - 16) for Q4_0 / Q5_0, the unsigned code for Q4_1,
+      Q5_1 and Q5_K (whose min term rides on the activation block's code sum).
 * R12 The repacked layout (the one-time device-layout transform): the pages
       repack a Q6_K block into a 16-byte-aligned 224-byte slot ("minfer CUDA
       Backend Design", 2.3); the block sits at the start of its slot and the
@@ -52,12 +71,20 @@ Readings where the pages are silent (each also listed in the design doc):
 import numpy as np
 
 # GGUF tensor-type ids.
+Q4_0 = 2
+Q4_1 = 3
+Q5_0 = 6
+Q5_1 = 7
 Q8_0 = 8
 Q4_K = 12
+Q5_K = 13
 Q6_K = 14
 
-BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q6_K: 210}
+BLOCK_VALUES = {Q4_0: 32, Q4_1: 32, Q5_0: 32, Q5_1: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q5_0: 22, Q5_1: 24, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
+
+# R14: the 32-value types -- (has a min m, has high bits qh, code offset of the _0 types)
+LEGACY = {Q4_0: (False, False, 8), Q4_1: (True, False, 0), Q5_0: (False, True, 16), Q5_1: (True, True, 0)}
 
 ACT_BLOCK = 32
 
@@ -163,6 +190,13 @@ def q4_k_fields(raw, N, K):
     value_e = d * scale_j * code_e - dmin * min_j, with j = e // 32.
     """
     b = _blocks(raw, Q4_K, N, K)
+    d, dmin, sc, mn = _k_header(b)
+    codes = _k_nibbles(b[..., 16:144].astype(np.int64))
+    return d, dmin, sc, mn, codes
+
+
+def _k_header(b):
+    """d, dmin and the eight 6-bit (scale, min) pairs of a Q4_K / Q5_K block header."""
     d = f16_bits_to_f64(b[..., 0], b[..., 1])
     dmin = f16_bits_to_f64(b[..., 2], b[..., 3])
     s = b[..., 4:16].astype(np.int64)
@@ -174,13 +208,62 @@ def q4_k_fields(raw, N, K):
     for j in range(4, 8):
         sc[..., j] = (s[..., j + 4] & 15) | ((s[..., j - 4] >> 6) << 4)
         mn[..., j] = (s[..., j + 4] >> 4) | ((s[..., j] >> 6) << 4)
-    qs = b[..., 16:144].astype(np.int64)
-    codes = np.empty(b.shape[:-1] + (256,), dtype=np.int64)
+    return d, dmin, sc, mn
+
+
+def _k_nibbles(qs):
+    """The 256 4-bit codes of 128 K-quant code bytes (chunk c: low nibbles, then high)."""
+    codes = np.empty(qs.shape[:-1] + (256,), dtype=np.int64)
     for c in range(4):
         chunk = qs[..., 32 * c:32 * c + 32]
         codes[..., 64 * c:64 * c + 32] = chunk & 15
         codes[..., 64 * c + 32:64 * c + 64] = chunk >> 4
-    return d, dmin, sc, mn, codes
+    return codes
+
+
+def q5_k_fields(raw, N, K):
+    """Q5_K fields (R15): d, dmin f64 [N, nb]; sc, m int64 [N, nb, 8]; codes int64 [N, nb, 256] in [0, 31].
+
+    Block (176 bytes): Q4_K's 16-byte header (bytes 0-15), qh (16-47), then
+    the 128 nibble bytes (48-175) read as in Q4_K; bit j = e // 32 of
+    qh[e % 32] is bit 4 of the code of value e.
+    value_e = d * scale_j * code_e - dmin * min_j.
+    """
+    b = _blocks(raw, Q5_K, N, K)
+    d, dmin, sc, mn = _k_header(b)
+    qh = b[..., 16:48].astype(np.int64)
+    low = _k_nibbles(b[..., 48:176].astype(np.int64))
+    high = np.empty_like(low)
+    for j in range(8):
+        high[..., 32 * j:32 * j + 32] = (qh >> j) & 1
+    return d, dmin, sc, mn, low | (high << 4)
+
+
+def legacy_fields(raw, qtype, N, K):
+    """Q4_0 / Q4_1 / Q5_0 / Q5_1 fields (R14): d, m f64 [N, nb]; codes int64 [N, nb, 32].
+
+    m is 0 for Q4_0 / Q5_0.  Returns (d, m, codes, offset) with
+    value_i = d * (code_i - offset) + m (offset 8 for Q4_0, 16 for Q5_0, else 0).
+    """
+    has_min, has_high, offset = LEGACY[qtype]
+    b = _blocks(raw, qtype, N, K)
+    d = f16_bits_to_f64(b[..., 0], b[..., 1])
+    pos = 2
+    m = np.zeros_like(d)
+    if has_min:
+        m = f16_bits_to_f64(b[..., 2], b[..., 3])
+        pos = 4
+    codes = np.zeros(b.shape[:-1] + (32,), dtype=np.int64)
+    if has_high:
+        qh = b[..., pos:pos + 4].astype(np.int64)
+        bits = qh[..., 0] | (qh[..., 1] << 8) | (qh[..., 2] << 16) | (qh[..., 3] << 24)
+        for i in range(32):
+            codes[..., i] = ((bits >> i) & 1) << 4
+        pos += 4
+    qs = b[..., pos:pos + 16].astype(np.int64)
+    codes[..., 0:16] |= qs & 15
+    codes[..., 16:32] |= qs >> 4
+    return d, m, codes, offset
 
 
 def q6_k_fields(raw, N, K):
@@ -223,6 +306,14 @@ def decode(raw, qtype, N, K):
         d, scales, codes = q6_k_fields(raw, N, K)
         group_scale = np.repeat(d[..., None] * scales, 16, axis=-1)
         w = group_scale * (codes - 32)
+    elif qtype == Q5_K:
+        d, dmin, sc, mn, codes = q5_k_fields(raw, N, K)
+        sub_scale = np.repeat(d[..., None] * sc, 32, axis=-1)
+        sub_min = np.repeat(dmin[..., None] * mn, 32, axis=-1)
+        w = sub_scale * codes - sub_min
+    elif qtype in LEGACY:
+        d, m, codes, offset = legacy_fields(raw, qtype, N, K)
+        w = d[..., None] * (codes - offset) + m[..., None]
     else:
         raise ValueError(f"unsupported type {qtype}")
     return w.reshape(N, K)
@@ -270,6 +361,8 @@ def block_dots(raw, qtype, q, N, K):
     * Q8_0: D[m, n, b] = sum_{i<32} qw[n, 32b+i] * qx[m, 32b+i]
     * Q4_K: D[m, n, b] = sum_{i<32} code[n, 32b+i] * qx[m, 32b+i]   (codes 0..15)
     * Q6_K: D[m, n, g] = sum_{i<16} (code[n, 16g+i] - 32) * qx[m, 16g+i]
+    * Q4_0, Q5_0: per 32-block, the signed code (code - 8, code - 16)
+    * Q4_1, Q5_1, Q5_K: per 32-block, the unsigned code (R16)
     """
     q = np.asarray(q, dtype=np.int8).astype(np.int64)
     M = q.shape[0]
@@ -282,6 +375,13 @@ def block_dots(raw, qtype, q, N, K):
     elif qtype == Q6_K:
         wq = q6_k_fields(raw, N, K)[2] - 32
         grp = 16
+    elif qtype == Q5_K:
+        wq = q5_k_fields(raw, N, K)[4]
+        grp = 32
+    elif qtype in LEGACY:
+        _, _, codes, offset = legacy_fields(raw, qtype, N, K)
+        wq = codes - offset
+        grp = 32
     else:
         raise ValueError(f"unsupported type {qtype}")
     wq = wq.reshape(N, K // grp, grp)
@@ -307,6 +407,9 @@ def mmq_from_block_dots(raw, qtype, q, d, S, N, K):
     * Q8_0: Y = sum_b dx[m,b] * d[n,b] * D[m,n,b]
     * Q4_K: Y = sum_j dx[m,j] * (d*sc_j * D[m,n,j] - dmin*m_j * S[m,j])
     * Q6_K: Y = sum_g dx[m,g//2] * d*s_g * D[m,n,g]
+    * Q5_K: as Q4_K (5-bit codes)
+    * Q4_0, Q5_0: Y = sum_b dx[m,b] * d[n,b] * D[m,n,b]   (signed codes)
+    * Q4_1, Q5_1: Y = sum_b dx[m,b] * (d[n,b] * D[m,n,b] + m[n,b] * S[m,b])
     Tests check that this equals ``mmq`` to ~1e-15 relative.
     """
     D = block_dots(raw, qtype, q, N, K).astype(np.float64)
@@ -314,8 +417,8 @@ def mmq_from_block_dots(raw, qtype, q, d, S, N, K):
     if qtype == Q8_0:
         dw, _ = q8_0_fields(raw, N, K)
         return np.einsum("mb,nb,mnb->mn", dx, dw.reshape(N, K // 32), D)
-    if qtype == Q4_K:
-        dd, dmin, sc, mn, _ = q4_k_fields(raw, N, K)
+    if qtype in (Q4_K, Q5_K):
+        dd, dmin, sc, mn, _ = (q4_k_fields if qtype == Q4_K else q5_k_fields)(raw, N, K)
         wscale = (dd[..., None] * sc).reshape(N, K // 32)
         wmin = (dmin[..., None] * mn).reshape(N, K // 32)
         S = np.asarray(S, dtype=np.int64).astype(np.float64)
@@ -327,4 +430,9 @@ def mmq_from_block_dots(raw, qtype, q, d, S, N, K):
         gscale = (dd[..., None] * scales).reshape(N, K // 16)
         dxg = np.repeat(dx, 2, axis=-1)
         return np.einsum("mg,ng,mng->mn", dxg, gscale, D)
+    if qtype in LEGACY:
+        dw, mw, _, _ = legacy_fields(raw, qtype, N, K)
+        S = np.asarray(S, dtype=np.int64).astype(np.float64)
+        main = np.einsum("mb,nb,mnb->mn", dx, dw, D)
+        return main + np.einsum("mb,nb,mb->mn", dx, mw, S)
     raise ValueError(f"unsupported type {qtype}")

@@ -17,8 +17,9 @@
 // kept as three signed bytes (v = 65536 d2 + 256 d1 + d0) in three byte planes,
 // which lets the weight codes meet x in v_dot4_i32_i8: three dot4 per four
 // codes, exact int32 sums, one conversion to f32 per run of codes that shares a
-// scale.  Q4_K also needs the f32 sum of x over each 32-block (min term); Q6_K
-// the sum over each 16-value run (code offset 32).
+// scale.  Q4_K, Q5_K and the 32-value types also need the f32 sum of x over each
+// 32-block (their min term or code offset); Q6_K the sum over each 16-value run
+// (code offset 32).
 #include <cstdio>
 #include <cstdlib>
 
@@ -101,6 +102,49 @@ struct UnitQ4K : RawQ4K {
     }
 };
 
+// ---------------------------------------------------------------- Q5_K
+// As Q4_K, with 5-bit codes (|sum code * v| <= 32 * 31 * 2^21 < 2^31 over a run).
+struct UnitQ5K : RawQ5K {
+    static constexpr int kChunks = 4;
+
+    __device__ float dot(const Stage& st, int uu, int u) const {
+        uint32_t lo[8], hi[8];
+        codes(u, lo, hi);
+        const int ilo = UnitQ4K::run_dot(lo, st, 0, uu);
+        const int ihi = UnitQ4K::run_dot(hi, st, 2, uu);
+        uint32_t scp, mnp;
+        scale_min(u & 3, scp, mnp);
+        const int2 e2 = *reinterpret_cast<const int2*>(st.ex + 2 * uu);
+        const float2 s2 = *reinterpret_cast<const float2*>(st.sums + 2 * uu);
+        const float codes_term = ldexpf(ubyte_f<0>(scp) * float(ilo), e2.x) + ldexpf(ubyte_f<1>(scp) * float(ihi), e2.y);
+        const float mins = fmaf(ubyte_f<0>(mnp), s2.x, ubyte_f<1>(mnp) * s2.y);
+        return fmaf(d(), codes_term, -dmin() * mins);
+    }
+};
+
+// ---------------------------------------------------------------- Q4_0 / Q4_1 / Q5_0 / Q5_1
+// Staged chunks 0,1 hold the block's 32 values.  sum((code - offset) * x) =
+// 2^e * sum(code * v) - offset * sum(x); the min of Q4_1 / Q5_1 adds m * sum(x).
+template <int QT>
+struct UnitLegacy : RawLegacy<QT> {
+    static constexpr int kChunks = 2;
+
+    __device__ float dot(const Stage& st, int uu, int) const {
+        uint32_t c[8];
+        this->codes(c);
+        int s0 = 0, s1 = 0, s2 = 0;
+        uint4 a, b, e;
+        st.chunk(0, uu, a, b, e);
+        dot16(c, a, b, e, s0, s1, s2);
+        st.chunk(1, uu, a, b, e);
+        dot16(c + 4, a, b, e, s0, s1, s2);
+        const float cv = ldexpf(combine3(s2, s1, s0), st.ex[uu]);
+        const float sx = st.sums[uu];
+        if constexpr (Legacy<QT>::kMin) return fmaf(this->d(), cv, this->m() * sx);
+        return this->d() * fmaf(-float(Legacy<QT>::kOffset), sx, cv);
+    }
+};
+
 // ---------------------------------------------------------------- Q6_K
 // Staged chunk t of the unit holds exactly the 16 values of run t.
 struct UnitQ6K : RawQ6K {
@@ -152,6 +196,11 @@ template <int QT> struct UnitOf;
 template <> struct UnitOf<kQ4_K> { using T = UnitQ4K; };
 template <> struct UnitOf<kQ6_K> { using T = UnitQ6K; };
 template <> struct UnitOf<kQ8_0> { using T = UnitQ80; };
+template <> struct UnitOf<kQ5_K> { using T = UnitQ5K; };
+template <> struct UnitOf<kQ4_0> { using T = UnitLegacy<kQ4_0>; };
+template <> struct UnitOf<kQ4_1> { using T = UnitLegacy<kQ4_1>; };
+template <> struct UnitOf<kQ5_0> { using T = UnitLegacy<kQ5_0>; };
+template <> struct UnitOf<kQ5_1> { using T = UnitLegacy<kQ5_1>; };
 
 __device__ __forceinline__ float group_sum(float v, int width) {
     for (int off = width >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -196,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
     int* ex = reinterpret_cast<int*>(p2 + plane);
     const int nex = (QT == kQ6_K) ? 4 * U : (K >> 5);
     float* sums = reinterpret_cast<float*>(ex + nex);
-    const int nsum = (QT == kQ6_K) ? 4 * U : (QT == kQ4_K ? (K >> 5) : 0);
+    const int nsum = (QT == kQ6_K) ? 4 * U : (QT == kQ8_0 ? 0 : (K >> 5));
     float* part = sums + nsum;
 
     const int tid = threadIdx.x;
@@ -284,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
         if constexpr (QT == kQ6_K) {
             uu = ((val >> 8) << 2) | (((val >> 7) & 1) << 1) | ((val >> 4) & 1);
             kc = (val >> 5) & 3;
-        } else if constexpr (QT == kQ4_K) {
+        } else if constexpr (QT == kQ4_K || QT == kQ5_K) {
             uu = val >> 6;
             kc = (val >> 4) & 3;
         } else {
@@ -304,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
                 ex[4 * uu + kc] = -k;
             }
         } else {
-            if constexpr (QT == kQ4_K) {
+            if constexpr (QT != kQ8_0) {
                 sm += __shfl_xor(sm, 4, 64);
                 if ((i & 7) == 0) sums[i >> 3] = sm;
             }
@@ -369,13 +418,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
 }
 
 size_t fixed_lds_bytes(int type, int64_t K) {
-    const int64_t vals = type == kQ8_0 ? 32 : 64;
-    const int64_t chunks = type == kQ8_0 ? 2 : 4;
+    const int64_t vals = unit_values(type);
+    const int64_t chunks = vals / 16;
     const int64_t U = K / vals;
     size_t b = 3 * size_t(chunks * (U + 1) * 16);            // digit planes
     b += size_t(type == kQ6_K ? 4 * U : K / 32) * 4;         // exponents
-    if (type == kQ4_K) b += size_t(K / 32) * 4;              // sums per 32-block
     if (type == kQ6_K) b += size_t(4 * U) * 4;               // sums per (unit, 16-run)
+    else if (type != kQ8_0) b += size_t(K / 32) * 4;         // sums per 32-block
     return b;
 }
 
@@ -405,8 +454,13 @@ const void* pick_kernel(Config c) {
 const void* kernel_for(int type, Config c) {
     switch (type) {
         case kQ4_K: return pick_kernel<kQ4_K>(c);
+        case kQ5_K: return pick_kernel<kQ5_K>(c);
         case kQ6_K: return pick_kernel<kQ6_K>(c);
         case kQ8_0: return pick_kernel<kQ8_0>(c);
+        case kQ4_0: return pick_kernel<kQ4_0>(c);
+        case kQ4_1: return pick_kernel<kQ4_1>(c);
+        case kQ5_0: return pick_kernel<kQ5_0>(c);
+        case kQ5_1: return pick_kernel<kQ5_1>(c);
         default: return nullptr;
     }
 }
@@ -452,7 +506,7 @@ bool use_mfma() {
 // Largest tile (in units) that fits next to the staged x; 0 if not even one row fits.
 int gemv_tile_units(int type, int64_t K, size_t lds_limit) {
     const size_t fixed = fixed_lds_bytes(type, K);
-    const int vals = type == kQ8_0 ? 32 : 64;
+    const int vals = unit_values(type);
     const int64_t U = K / vals;
     if (lds_limit <= fixed) return 0;
     int64_t units = int64_t((lds_limit - fixed) / 4);
@@ -462,7 +516,7 @@ int gemv_tile_units(int type, int64_t K, size_t lds_limit) {
 }
 
 hipError_t gemv_set_attributes(size_t lds_limit) {
-    for (int type : {kQ4_K, kQ6_K, kQ8_0}) {
+    for (int type : {kQ4_K, kQ5_K, kQ6_K, kQ8_0, kQ4_0, kQ4_1, kQ5_0, kQ5_1}) {
         for (const Config& c : kConfigs) {
             hipError_t e = hipFuncSetAttribute(kernel_for(type, c), hipFuncAttributeMaxDynamicSharedMemorySize,
                                                int(lds_limit));
@@ -480,7 +534,7 @@ hipError_t launch_gemv(int type, BlockLayout layout, const uint8_t* W, const flo
         return launch_gemv_mfma(W, x, y, N, K, info->cu_count, s, name);
     int tile = gemv_tile_units(type, K, info->lds_per_block);
     if (tile <= 0) return hipErrorInvalidValue;
-    const int vals = type == kQ8_0 ? 32 : 64;
+    const int vals = unit_values(type);
     const int U = int(K / vals);
     // Rows of one workgroup; shrink the tile so a workgroup's rows split into equal tiles.
     const int grid = int(N < info->cu_count ? N : info->cu_count);
@@ -496,10 +550,15 @@ hipError_t launch_gemv(int type, BlockLayout layout, const uint8_t* W, const flo
     switch (type) {
         case kQ8_0: *name = repacked ? "gemv<q8_0 repacked>" : "gemv<q8_0>"; break;
         case kQ4_K: *name = "gemv<q4_K>"; break;
+        case kQ5_K: *name = "gemv<q5_K>"; break;
         case kQ6_K: *name = repacked ? "gemv<q6_K repacked>" : "gemv<q6_K>"; break;
+        case kQ4_0: *name = "gemv<q4_0>"; break;
+        case kQ4_1: *name = "gemv<q4_1>"; break;
+        case kQ5_0: *name = "gemv<q5_0>"; break;
+        case kQ5_1: *name = "gemv<q5_1>"; break;
         default: return hipErrorInvalidValue;
     }
-    int64_t row_bytes = (K / (type == kQ8_0 ? 32 : 256)) * layout.stride;
+    int64_t row_bytes = (K / block_values_of(type)) * layout.stride;
     int n = int(N), k = int(K), stride = layout.stride, off = layout.off;
     void* args[] = {&W, &x, &y, &n, &k, &row_bytes, &tile, &stride, &off};
     return hipLaunchKernel(kern, dim3(grid), dim3(c.threads), args, shmem, s);

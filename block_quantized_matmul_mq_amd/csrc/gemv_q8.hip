@@ -53,6 +53,24 @@ template <int QT> struct Shape;
 template <> struct Shape<kQ4_K> { static constexpr int kValues = 64, kChunks = 4; };
 template <> struct Shape<kQ6_K> { static constexpr int kValues = 64, kChunks = 4; };
 template <> struct Shape<kQ8_0> { static constexpr int kValues = 32, kChunks = 2; };
+template <> struct Shape<kQ5_K> { static constexpr int kValues = 64, kChunks = 4; };
+template <> struct Shape<kQ4_0> { static constexpr int kValues = 32, kChunks = 2; };
+template <> struct Shape<kQ4_1> { static constexpr int kValues = 32, kChunks = 2; };
+template <> struct Shape<kQ5_0> { static constexpr int kValues = 32, kChunks = 2; };
+template <> struct Shape<kQ5_1> { static constexpr int kValues = 32, kChunks = 2; };
+
+template <int QT> struct UnitT { using T = RawLegacy<QT>; };
+template <> struct UnitT<kQ4_K> { using T = RawQ4K; };
+template <> struct UnitT<kQ5_K> { using T = RawQ5K; };
+template <> struct UnitT<kQ6_K> { using T = RawQ6K; };
+template <> struct UnitT<kQ8_0> { using T = RawQ80; };
+
+// Per-(row, unit) activation factors: the 32-value types keep the block scale and the
+// block's code sum (their offset or min term needs it exactly).
+struct ScaleSum {
+    float dx;
+    int32_t S;
+};
 
 // unit and chunk of the 16 values starting at `val` (a multiple of 16) -- the layouts of
 // the units in weight_units.h
@@ -61,7 +79,7 @@ __device__ __forceinline__ void unit_chunk(int val, int& uu, int& kc) {
     if constexpr (QT == kQ6_K) {
         uu = ((val >> 8) << 2) | (((val >> 7) & 1) << 1) | ((val >> 4) & 1);
         kc = (val >> 5) & 3;
-    } else if constexpr (QT == kQ4_K) {
+    } else if constexpr (QT == kQ4_K || QT == kQ5_K) {
         uu = val >> 6;
         kc = (val >> 4) & 3;
     } else {
@@ -71,11 +89,14 @@ __device__ __forceinline__ void unit_chunk(int val, int& uu, int& kc) {
 }
 
 // LDS (dynamic): MR code planes of kChunks * S * 16 bytes (S = U + 1) | per-row factors
-// (Q4_K: float4 [MR][U]; Q6_K: float4 [MR][U] then int4 [MR][U]; Q8_0: float [MR][U]) |
-// partials f32 [tile_units][MR].
+// (Q4_K, Q5_K: float4 [MR][U]; Q6_K: float4 [MR][U] then int4 [MR][U]; Q8_0: float [MR][U];
+// the 32-value types: ScaleSum [MR][U]) | partials f32 [tile_units][MR].
+__host__ __device__ constexpr size_t factor_unit_bytes(int type) {
+    return (type == kQ4_K || type == kQ5_K) ? 16 : (type == kQ6_K ? 32 : (type == kQ8_0 ? 4 : 8));
+}
 template <int QT, int MR>
 __host__ __device__ constexpr size_t factor_bytes(int U) {
-    return QT == kQ4_K ? size_t(MR) * U * 16 : (QT == kQ6_K ? size_t(MR) * U * 32 : size_t(MR) * U * 4);
+    return size_t(MR) * U * factor_unit_bytes(QT);
 }
 
 template <int QT, int MR, bool DUMP>
@@ -101,8 +122,7 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_kernel(const uint8_t* __rest
     const int r_end = int((int64_t(blockIdx.x + 1) * N) / gridDim.x);
     const int rows_per_tile = max(1, tile_units / U);
 
-    using Unit = typename std::conditional<QT == kQ4_K, RawQ4K,
-                                           typename std::conditional<QT == kQ6_K, RawQ6K, RawQ80>::type>::type;
+    using Unit = typename UnitT<QT>::T;
     // A lane handles flat unit indices f = tid, tid + kThreads, ... of a tile; two cursors
     // (next load, next compute) step by kThreads units without multiplies or divisions.
     const int dq = kThreads / U, dr = kThreads - dq * U;
@@ -174,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_kernel(const uint8_t* __rest
         const int m = i / U, uu = i - m * U;
         const bool live = m < M;
         const float* xs = xscale + int64_t(m) * KB;
-        if constexpr (QT == kQ4_K) {
+        if constexpr (QT == kQ4_K || QT == kQ5_K) {
             float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
             if (live) {
                 const int32_t* su = xsum + int64_t(m) * KB;
@@ -190,8 +210,10 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_kernel(const uint8_t* __rest
                 f = make_float4(xs[b0], xs[b0 + 1], xs[b0 + 2], xs[b0 + 3]);
             }
             reinterpret_cast<float4*>(fac)[i] = f;
-        } else {
+        } else if constexpr (QT == kQ8_0) {
             reinterpret_cast<float*>(fac)[i] = live ? xs[uu] : 0.f;
+        } else {
+            reinterpret_cast<ScaleSum*>(fac)[i] = live ? ScaleSum{xs[uu], xsum[int64_t(m) * KB + uu]} : ScaleSum{0.f, 0};
         }
     }
     __syncthreads();
@@ -201,9 +223,10 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_kernel(const uint8_t* __rest
         auto chunk = [&](int m, int kc) {
             return *reinterpret_cast<const uint4*>(planes + m * plane + (kc * S + uu) * 16);
         };
-        if constexpr (QT == kQ4_K) {
+        if constexpr (QT == kQ4_K || QT == kQ5_K) {
             uint32_t lo[8], hi[8], scp, mnp;
-            w.codes(lo, hi);
+            if constexpr (QT == kQ4_K) w.codes(lo, hi);
+            else w.codes(uu, lo, hi);
             w.scale_min(uu & 3, scp, mnp);
             const float d = w.d(), dmin = w.dmin();
             const float a0 = d * ubyte_f<0>(scp), a1 = d * ubyte_f<1>(scp);
@@ -251,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_kernel(const uint8_t* __rest
                 }
                 r[m] = acc;
             }
-        } else {
+        } else if constexpr (QT == kQ8_0) {
             uint32_t c[8];
             w.codes(c);
             const float d = w.d();
@@ -261,6 +284,27 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_kernel(const uint8_t* __rest
                 r[m] = d * reinterpret_cast<const float*>(fac)[m * U + uu] * float(D);
                 if constexpr (DUMP) {
                     if (m < M) dots[(int64_t(m) * N + row) * KB + uu] = D;
+                }
+            }
+        } else {
+            // Q4_0 / Q5_0: the block dot of (code - offset), exact: D - offset * S.
+            // Q4_1 / Q5_1: d * dx * D + m * dx * S.
+            uint32_t c[8];
+            w.codes(c);
+            const float d = w.d();
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const int D = dot16(c + 4, chunk(m, 1), dot16(c, chunk(m, 0), 0));
+                const ScaleSum f = reinterpret_cast<const ScaleSum*>(fac)[m * U + uu];
+                int E = D;
+                if constexpr (Legacy<QT>::kMin) {
+                    r[m] = fmaf(d * f.dx, float(D), w.m() * (f.dx * float(f.S)));
+                } else {
+                    E = D - Legacy<QT>::kOffset * f.S;
+                    r[m] = d * f.dx * float(E);
+                }
+                if constexpr (DUMP) {
+                    if (m < M) dots[(int64_t(m) * N + row) * KB + uu] = E;
                 }
             }
         }
@@ -314,11 +358,10 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_kernel(const uint8_t* __rest
 }
 
 size_t fixed_bytes(int type, int MR, int64_t K) {
-    const int vals = type == kQ8_0 ? 32 : 64, chunks = type == kQ8_0 ? 2 : 4;
+    const int vals = unit_values(type), chunks = vals / 16;
     const int U = int(K / vals);
     const size_t planes = size_t(MR) * chunks * (U + 1) * 16;
-    const size_t fac = type == kQ4_K ? size_t(MR) * U * 16 : (type == kQ6_K ? size_t(MR) * U * 32 : size_t(MR) * U * 4);
-    return planes + fac;
+    return planes + size_t(MR) * U * factor_unit_bytes(type);
 }
 
 int rows_for(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8)); }
@@ -342,8 +385,13 @@ const void* kernel_for_type(int mr, bool dump) {
 const void* kernel_for(int type, int mr, bool dump) {
     switch (type) {
         case kQ4_K: return kernel_for_type<kQ4_K>(mr, dump);
+        case kQ5_K: return kernel_for_type<kQ5_K>(mr, dump);
         case kQ6_K: return kernel_for_type<kQ6_K>(mr, dump);
         case kQ8_0: return kernel_for_type<kQ8_0>(mr, dump);
+        case kQ4_0: return kernel_for_type<kQ4_0>(mr, dump);
+        case kQ4_1: return kernel_for_type<kQ4_1>(mr, dump);
+        case kQ5_0: return kernel_for_type<kQ5_0>(mr, dump);
+        case kQ5_1: return kernel_for_type<kQ5_1>(mr, dump);
         default: return nullptr;
     }
 }
@@ -354,13 +402,13 @@ bool gemv_q8_applies(int type, int64_t M, int64_t K) {
     // a function of the shape alone (the code planes, the factor arrays and the partials of
     // one row must fit the 160 KB of LDS a gfx950 workgroup may use), so that the scratch
     // sizing of mq_gemm does not depend on the device
-    if (M < 1 || M > kGemvQ8MaxRows || (type != kQ4_K && type != kQ6_K && type != kQ8_0)) return false;
+    if (M < 1 || M > kGemvQ8MaxRows || !kernel_for(type, 1, false)) return false;
     const int mr = rows_for(M);
-    return fixed_bytes(type, mr, K) + size_t(K / (type == kQ8_0 ? 32 : 64)) * mr * 4 <= kGfx950LdsBytes;
+    return fixed_bytes(type, mr, K) + size_t(K / unit_values(type)) * mr * 4 <= kGfx950LdsBytes;
 }
 
 hipError_t gemv_q8_set_attributes(size_t lds_limit) {
-    for (int type : {kQ4_K, kQ6_K, kQ8_0})
+    for (int type : {kQ4_K, kQ5_K, kQ6_K, kQ8_0, kQ4_0, kQ4_1, kQ5_0, kQ5_1})
         for (int mr : {1, 2, 4, 8})
             for (bool dump : {false, true}) {
                 hipError_t e = hipFuncSetAttribute(kernel_for(type, mr, dump),
@@ -376,7 +424,7 @@ hipError_t launch_gemv_q8(int type, BlockLayout lay, const uint8_t* W, const int
     const DeviceInfo* info = device_info();
     if (!info) return hipErrorInvalidDevice;
     const int mr = rows_for(M);
-    const int vals = type == kQ8_0 ? 32 : 64;
+    const int vals = unit_values(type);
     const int U = int(K / vals);
     const size_t fixed = fixed_bytes(type, mr, K);
     if (fixed >= info->lds_per_block) return hipErrorInvalidValue;
@@ -395,10 +443,15 @@ hipError_t launch_gemv_q8(int type, BlockLayout lay, const uint8_t* W, const int
     switch (type) {
         case kQ8_0: *name = repacked ? "gemv_q8<q8_0 repacked>" : "gemv_q8<q8_0>"; break;
         case kQ4_K: *name = "gemv_q8<q4_K>"; break;
+        case kQ5_K: *name = "gemv_q8<q5_K>"; break;
         case kQ6_K: *name = repacked ? "gemv_q8<q6_K repacked>" : "gemv_q8<q6_K>"; break;
+        case kQ4_0: *name = "gemv_q8<q4_0>"; break;
+        case kQ4_1: *name = "gemv_q8<q4_1>"; break;
+        case kQ5_0: *name = "gemv_q8<q5_0>"; break;
+        case kQ5_1: *name = "gemv_q8<q5_1>"; break;
         default: return hipErrorInvalidValue;
     }
-    int64_t row_bytes = (K / (type == kQ8_0 ? 32 : 256)) * lay.stride;
+    int64_t row_bytes = (K / block_values_of(type)) * lay.stride;
     int m = int(M), n = int(N), k = int(K), stride = lay.stride, off = lay.off;
     void* args[] = {&W, &codes, &xs, &xsum, &Y, &dots, &m, &n, &k, &row_bytes, &tile_units, &stride, &off};
     return hipLaunchKernel(kernel_for(type, mr, dots != nullptr), dim3(grid), dim3(kThreads), args, shmem, s);

@@ -48,6 +48,7 @@
 
 #include "mq_device.h"
 #include "mq_internal.h"
+#include "weight_units.h"
 
 namespace mq {
 
@@ -114,9 +115,9 @@ struct Smem {
     int8_t A[2][BM * KS];                               // activation codes
     int8_t B[2][BN * KS];                               // weight codes
     float dx[2][NB][BM];                                // activation block scales
-    uint32_t tx[2][QT == kQ4_K ? NB : 1][BM];           // Q4_K: bf16_hilo(dx * code sum) per block
+    uint32_t tx[2][has_min_term<QT>() ? NB : 1][BM];    // min types: bf16_hilo(dx * code sum) per block
     float dw[2][Groups<QT>::per_step][BN];              // weight scale per block (per group, Q6_K)
-    uint32_t mw[2][QT == kQ4_K ? NB : 1][BN];           // Q4_K: bf16_hilo(-dmin * m) per block
+    uint32_t mw[2][has_min_term<QT>() ? NB : 1][BN];    // bf16_hilo(-dmin * m) (K-quants) or m per block
 };
 
 // ------------------------------------------------------------------ weight staging
@@ -217,6 +218,100 @@ template <> struct WeightRegs<kQ8_0> {
         }
     }
 };
+
+template <> struct WeightRegs<kQ5_K> {
+    // As Q4_K (chunks p0 and p0 + 2 of the step's 64 code bytes, and the row's header),
+    // plus the 16 high-bit bytes qh[16 (p0 % 2) ..]: chunk p covers byte l of its 64-value
+    // group c, whose two sub-blocks take bits 2c and 2c + 1 of qh[l].
+    uint4 q[2], hd, qh;
+    __device__ void load(const uint8_t* W, int64_t rb, int n0, int N, int k0, int, int, int) {
+        const int t = threadIdx.x, sb = k0 >> 8, half = (k0 >> 7) & 1;
+        const int n = min(n0 + (t & (BN - 1)), N - 1);
+        const uint8_t* blk = W + int64_t(n) * rb + 176 * sb;
+        const int p0 = t >> 7;
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+            q[it] = *reinterpret_cast<const uint4*>(blk + 48 + 16 * (4 * half + p0 + 2 * it));
+        hd = *reinterpret_cast<const uint4*>(blk);
+        qh = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (p0 & 1));
+    }
+    template <int BM>
+    __device__ void store(Smem<kQ5_K, BM>& sm, int buf, int k0) const {
+        const int t = threadIdx.x, half = (k0 >> 7) & 1;
+        const int row = t & (BN - 1), p0 = t >> 7;
+        int8_t* Bs = sm.B[buf];
+        const float d = half_bits_to_float(hd.x & 0xFFFFu);
+        const float dmin = half_bits_to_float(hd.x >> 16);
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int p = p0 + 2 * it;
+            const int c = p >> 1, h = p & 1;
+            const uint32_t s = 2u * uint32_t(2 * half + c);   // qh bit of the group's first sub-block
+            const uint4 v = q[it];
+            auto hb = [&](uint32_t w, uint32_t b) { return ((w >> b) & 0x01010101u) << 4; };
+            const uint4 lo = make_uint4((v.x & 0x0F0F0F0Fu) | hb(qh.x, s), (v.y & 0x0F0F0F0Fu) | hb(qh.y, s),
+                                        (v.z & 0x0F0F0F0Fu) | hb(qh.z, s), (v.w & 0x0F0F0F0Fu) | hb(qh.w, s));
+            const uint4 hi = make_uint4(((v.x >> 4) & 0x0F0F0F0Fu) | hb(qh.x, s + 1),
+                                        ((v.y >> 4) & 0x0F0F0F0Fu) | hb(qh.y, s + 1),
+                                        ((v.z >> 4) & 0x0F0F0F0Fu) | hb(qh.z, s + 1),
+                                        ((v.w >> 4) & 0x0F0F0F0Fu) | hb(qh.w, s + 1));
+            *reinterpret_cast<uint4*>(Bs + chk<BN>(row, 4 * c + h)) = lo;
+            *reinterpret_cast<uint4*>(Bs + chk<BN>(row, 4 * c + h + 2)) = hi;
+            const int jb = 2 * c + h;
+            uint32_t sc, mn;
+            q4k_scale_min(hd.y, hd.z, hd.w, 4 * half + jb, sc, mn);
+            sm.dw[buf][jb][row] = d * float(sc);
+            sm.mw[buf][jb][row] = bf16_hilo(-(dmin * float(mn)));
+        }
+    }
+};
+
+// Q4_0 / Q4_1 / Q5_0 / Q5_1: thread t owns row t % 128 and blocks b0 and b0 + 2 of this
+// step, b0 = t / 128 (as Q8_0), read through the 32-value unit loader.  The codes go to LDS
+// as int8: code - offset for Q4_0 / Q5_0 (signed), the code itself for Q4_1 / Q5_1 (whose
+// min m rides on the activation block's code sum).  Blocks past K contribute nothing.
+template <int QT>
+struct LegacyRegs {
+    RawLegacy<QT> blk[2];
+    bool live[2];
+    __device__ void load(const uint8_t* W, int64_t rb, int n0, int N, int k0, int K, int, int) {
+        const int t = threadIdx.x;
+        const int n = min(n0 + (t & (BN - 1)), N - 1);
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int kb = (k0 >> 5) + (t >> 7) + 2 * it;
+            live[it] = kb < (K >> 5);
+            blk[it].load(W + int64_t(n) * rb, live[it] ? kb : 0, 0, 0);
+        }
+    }
+    template <int BM>
+    __device__ void store(Smem<QT, BM>& sm, int buf, int) const {
+        const int t = threadIdx.x;
+        const int row = t & (BN - 1);
+        int8_t* Bs = sm.B[buf];
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int bi = (t >> 7) + 2 * it;
+            uint32_t c[8];
+            blk[it].codes(c);
+            const uint32_t keep = live[it] ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if constexpr (Legacy<QT>::kOffset != 0)   // per byte: (c + 128 - offset) with the sign bit flipped back
+                    c[i] = ((c[i] | 0x80808080u) - 0x01010101u * uint32_t(Legacy<QT>::kOffset)) ^ 0x80808080u;
+                c[i] &= keep;
+            }
+            *reinterpret_cast<uint4*>(Bs + chk<BN>(row, 2 * bi)) = make_uint4(c[0], c[1], c[2], c[3]);
+            *reinterpret_cast<uint4*>(Bs + chk<BN>(row, 2 * bi + 1)) = make_uint4(c[4], c[5], c[6], c[7]);
+            sm.dw[buf][bi][row] = live[it] ? blk[it].d() : 0.f;
+            if constexpr (Legacy<QT>::kMin) sm.mw[buf][bi][row] = live[it] ? bf16_hilo(blk[it].m()) : 0u;
+        }
+    }
+};
+template <> struct WeightRegs<kQ4_0> : LegacyRegs<kQ4_0> {};
+template <> struct WeightRegs<kQ4_1> : LegacyRegs<kQ4_1> {};
+template <> struct WeightRegs<kQ5_0> : LegacyRegs<kQ5_0> {};
+template <> struct WeightRegs<kQ5_1> : LegacyRegs<kQ5_1> {};
 
 template <> struct WeightRegs<kQ6_K> {
     // Thread t owns pieces u = t + 256 i (i < 4): row u/8, part p = u%8, which holds the
@@ -322,7 +417,7 @@ struct ActDirect {
             if (2 * wave + j < kScaleIns) {   // uniform
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(&sm.dx[buf][0][0] + 64 * (2 * wave + j)), 4,
                                                          voff_s[j], uint32_t(k0 >> 3), 0, 0);
-                if constexpr (QT == kQ4_K)
+                if constexpr (has_min_term<QT>())
                     sums[j] = __builtin_amdgcn_raw_buffer_load_b32(ru, voff_s[j], uint32_t(k0 >> 3), 0);
             }
         }
@@ -330,7 +425,7 @@ struct ActDirect {
 
     // after this wave's loads of the step in `buf` have landed
     __device__ void finish(Smem<QT, BM>& sm, int buf) const {
-        if constexpr (QT == kQ4_K) {
+        if constexpr (has_min_term<QT>()) {
             const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -493,7 +588,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
         // one bf16 MFMA with K = 16 = 4 blocks x 4 slots; lane group g feeds blocks 2g, 2g+1,
         // slots (hi*hi, hi*lo, lo*hi, 0) from the hi | lo << 16 packs.
         auto min_term = [&](int i, int j) {
-            if constexpr (QT == kQ4_K) {
+            if constexpr (has_min_term<QT>()) {
                 const int ar = arow0 + 32 * i, br = brow0 + 32 * j;
                 const uint32_t t0 = sm.tx[buf][2 * g][ar], t1 = sm.tx[buf][2 * g + 1][ar];
                 const uint32_t w0 = sm.mw[buf][2 * g][br], w1 = sm.mw[buf][2 * g + 1][br];
@@ -528,7 +623,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
             __builtin_amdgcn_sched_barrier(0);
             if (more) dot1();
             __builtin_amdgcn_sched_barrier(0);
-            if (QT == kQ4_K && k / kTiles == 1) min_term((k / TJ) % TI, k % TJ);
+            if (has_min_term<QT>() && k / kTiles == 1) min_term((k / TJ) % TI, k % TJ);
         }
         // next step: its weight registers and LDS-direct loads were issued a step ago
         if (k0 + KS < kend) {
@@ -596,6 +691,26 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                       float* __restrict__, int32_t* __restrict__,              \
                                                       float* __restrict__, int, int, int, int64_t, int, int, int, \
                                                       int, int, int, int);
+MQ_MMQ_INSTANCE(kQ5_K, 32, false)
+MQ_MMQ_INSTANCE(kQ5_K, 128, false)
+MQ_MMQ_INSTANCE(kQ5_K, 32, true)
+MQ_MMQ_INSTANCE(kQ5_K, 128, true)
+MQ_MMQ_INSTANCE(kQ4_0, 32, false)
+MQ_MMQ_INSTANCE(kQ4_0, 128, false)
+MQ_MMQ_INSTANCE(kQ4_0, 32, true)
+MQ_MMQ_INSTANCE(kQ4_0, 128, true)
+MQ_MMQ_INSTANCE(kQ4_1, 32, false)
+MQ_MMQ_INSTANCE(kQ4_1, 128, false)
+MQ_MMQ_INSTANCE(kQ4_1, 32, true)
+MQ_MMQ_INSTANCE(kQ4_1, 128, true)
+MQ_MMQ_INSTANCE(kQ5_0, 32, false)
+MQ_MMQ_INSTANCE(kQ5_0, 128, false)
+MQ_MMQ_INSTANCE(kQ5_0, 32, true)
+MQ_MMQ_INSTANCE(kQ5_0, 128, true)
+MQ_MMQ_INSTANCE(kQ5_1, 32, false)
+MQ_MMQ_INSTANCE(kQ5_1, 128, false)
+MQ_MMQ_INSTANCE(kQ5_1, 32, true)
+MQ_MMQ_INSTANCE(kQ5_1, 128, true)
 MQ_MMQ_INSTANCE(kQ8_0, 32, false)
 MQ_MMQ_INSTANCE(kQ8_0, 128, false)
 MQ_MMQ_INSTANCE(kQ4_K, 32, false)
@@ -616,7 +731,7 @@ hipError_t launch_shaped(const uint8_t* W, const int8_t* codes, const float* xs,
                          const MmqPlan& plan, hipStream_t s) {
     const int tiles_m = int((M + BM - 1) / BM);
     const int total = plan.full + plan.split_tiles * plan.splits;
-    const int64_t row_bytes = (K / (QT == kQ8_0 ? 32 : 256)) * lay.stride;
+    const int64_t row_bytes = (K / block_values_of(QT)) * lay.stride;
     if (dots) {
         hipLaunchKernelGGL((mmq_kernel<QT, BM, true>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, Y, dots,
                            partial, int(M), int(N), int(K), row_bytes, lay.stride, lay.off, tiles_m, plan.full,
@@ -690,6 +805,21 @@ hipError_t launch_mmq(int type, BlockLayout lay, const uint8_t* W, const int8_t*
         case kQ6_K:
             *name = repacked ? "mmq<q6_K repacked>" : "mmq<q6_K>";
             return launch_typed<kQ6_K>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
+        case kQ5_K:
+            *name = "mmq<q5_K>";
+            return launch_typed<kQ5_K>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
+        case kQ4_0:
+            *name = "mmq<q4_0>";
+            return launch_typed<kQ4_0>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
+        case kQ4_1:
+            *name = "mmq<q4_1>";
+            return launch_typed<kQ4_1>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
+        case kQ5_0:
+            *name = "mmq<q5_0>";
+            return launch_typed<kQ5_0>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
+        case kQ5_1:
+            *name = "mmq<q5_1>";
+            return launch_typed<kQ5_1>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -37,17 +37,21 @@ int fail(int code, const char* fmt, ...) {
 
 int block_values(int type) {
     switch (type) {
-        case MQ_Q8_0: return 32;
-        case MQ_Q4_K: return 256;
-        case MQ_Q6_K: return 256;
+        case MQ_Q4_0: case MQ_Q4_1: case MQ_Q5_0: case MQ_Q5_1: case MQ_Q8_0: return 32;
+        case MQ_Q4_K: case MQ_Q5_K: case MQ_Q6_K: return 256;
         default: return 0;
     }
 }
 
 int block_bytes(int type) {
     switch (type) {
+        case MQ_Q4_0: return 18;
+        case MQ_Q4_1: return 20;
+        case MQ_Q5_0: return 22;
+        case MQ_Q5_1: return 24;
         case MQ_Q8_0: return 34;
         case MQ_Q4_K: return 144;
+        case MQ_Q5_K: return 176;
         case MQ_Q6_K: return 210;
         default: return 0;
     }
@@ -201,9 +205,9 @@ size_t mq_act_sum_offset(int64_t M, int64_t K) {
 size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
     BlockLayout lay;
     type = parse_type(type, lay);
-    if (type != MQ_Q8_0 && type != MQ_Q4_K && type != MQ_Q6_K) return 0;
+    if (type == 0) return 0;
     if (M <= 0 || N <= 0 || K <= 0 || M > MQ_MAX_M || N > MQ_MAX_N || K > MQ_MAX_K) return 0;
-    if (K % (type == MQ_Q8_0 ? 32 : 256) != 0) return 0;
+    if (K % block_values(type) != 0) return 0;
     return mmq_scratch_bytes(type, M, N, K);
 }
 

@@ -1,9 +1,15 @@
 // Device-side helpers shared by the libmq kernels (gfx950, wave64).
 //
-// Block layouts read here ("minfer CUDA Backend Design", 2.3 fixes the sizes;
-// the field layouts are the public GGUF ones):
+// Block layouts read here ("minfer CUDA Backend Design", 2.3 fixes some sizes and
+// 4.3 lists the types; the field layouts are the public GGUF ones):
 //   Q8_0  34 B / 32 values : f16 d | int8 q[32]
+//   Q4_0  18 B / 32 values : f16 d | 16 B nibbles (value i low, value 16 + i high nibble of byte i)
+//   Q4_1  20 B / 32 values : f16 d | f16 m | 16 B nibbles
+//   Q5_0  22 B / 32 values : f16 d | 4 B high bits (bit i = bit 4 of value i) | 16 B nibbles
+//   Q5_1  24 B / 32 values : f16 d | f16 m | 4 B high bits | 16 B nibbles
 //   Q4_K 144 B / 256 values: f16 d | f16 dmin | 12 B packed 6-bit (scale,min) x 8 | 128 B 4-bit codes
+//   Q5_K 176 B / 256 values: Q4_K's 16-byte header | 32 B high bits (bit j of byte l = bit 4 of
+//                            value 32 j + l) | Q4_K's 128 B of 4-bit codes
 //   Q6_K 210 B / 256 values: 128 B low nibbles | 64 B high 2-bit pairs | int8 scales[16] | f16 d
 #pragma once
 
@@ -12,9 +18,30 @@
 
 namespace mq {
 
+constexpr int kQ4_0 = 2;
+constexpr int kQ4_1 = 3;
+constexpr int kQ5_0 = 6;
+constexpr int kQ5_1 = 7;
 constexpr int kQ8_0 = 8;
 constexpr int kQ4_K = 12;
+constexpr int kQ5_K = 13;
 constexpr int kQ6_K = 14;
+
+// The 32-value types Q4_0 / Q4_1 / Q5_0 / Q5_1: block bytes, code offset (value =
+// d * (code - offset) for Q4_0 / Q5_0), whether a f16 min m follows d (value =
+// d * code + m) and whether 4 bytes of high bits (5-bit codes) precede the nibbles.
+template <int QT> struct Legacy { static constexpr bool kIs = false; };
+template <> struct Legacy<kQ4_0> { static constexpr bool kIs = true, kMin = false, kHigh = false; static constexpr int kBytes = 18, kOffset = 8; };
+template <> struct Legacy<kQ4_1> { static constexpr bool kIs = true, kMin = true, kHigh = false; static constexpr int kBytes = 20, kOffset = 0; };
+template <> struct Legacy<kQ5_0> { static constexpr bool kIs = true, kMin = false, kHigh = true; static constexpr int kBytes = 22, kOffset = 16; };
+template <> struct Legacy<kQ5_1> { static constexpr bool kIs = true, kMin = true, kHigh = true; static constexpr int kBytes = 24, kOffset = 0; };
+
+// Types whose value has a subtracted or added per-block minimum, carried through the
+// activation block's code sum: Q4_K, Q5_K (- dmin * min_j), Q4_1, Q5_1 (+ m).
+template <int QT>
+constexpr bool has_min_term() {
+    return QT == kQ4_K || QT == kQ5_K || QT == kQ4_1 || QT == kQ5_1;
+}
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
     // v_cvt_f32_f16: exact, subnormal halves included (f16 denormals are not flushed).

@@ -5,7 +5,16 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "mq_device.h"
+
 namespace mq {
+
+// Values per block, and per "unit" of the GEMV kernels (64 for the 256-value K-quants,
+// one block for the 32-value types).
+inline bool is_kquant(int type) { return type == kQ4_K || type == kQ5_K || type == kQ6_K; }
+inline int block_values_of(int type) { return is_kquant(type) ? 256 : 32; }
+inline int unit_values(int type) { return is_kquant(type) ? 64 : 32; }
+inline bool is_legacy(int type) { return type == kQ4_0 || type == kQ4_1 || type == kQ5_0 || type == kQ5_1; }
 
 // Activation plane layout (see include/mq.h): codes [M][K] | scales [M][K/32] | sums [M][K/32],
 // each array starting on a 256-byte boundary.

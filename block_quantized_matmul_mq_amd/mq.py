@@ -10,8 +10,13 @@ first.
 import ctypes
 import os
 
+Q4_0 = 2
+Q4_1 = 3
+Q5_0 = 6
+Q5_1 = 7
 Q8_0 = 8
 Q4_K = 12
+Q5_K = 13
 Q6_K = 14
 REPACKED = 0x100   # OR-ed into Q8_0 / Q6_K: weights in the layout mq_repack writes
 

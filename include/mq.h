@@ -1,6 +1,7 @@
 /*
  * mq.h -- C ABI of libmq: matrix products of GGUF block-quantized weights
- * (Q8_0, Q4_K, Q6_K) with f32 activations on AMD Instinct MI355X (gfx950).
+ * (Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q4_K, Q5_K, Q6_K) with f32 activations on AMD
+ * Instinct MI355X (gfx950).
  *
  * Sources (page title, section):
  *   [BD2.3] "minfer CUDA Backend Design", 2.3 Weight residency and registry:
@@ -9,7 +10,10 @@
  *           a derived plane is admitted by a type gate plus an exact-length
  *           payload gate ("equality, not a lower bound").
  *   [BD4.3] same page, 4.3 Eligibility: a quantized matmul needs id % 32 == 0;
+ *           the matmul weight types are Q4_0/Q4_1/Q5_0/Q5_1/Q8_0/Q4_K/Q5_K/Q6_K;
  *           an invariant violation is an error, never a silent fallback.
+ *   [GS3]   "GPU Safety (Metal + CUDA Backends)", 3. Audit findings: the Q5_K
+ *           block is 176 bytes.
  *   [BD4.4] same page, 4.4 Execution dispatch: decode (one token) runs a
  *           matrix-vector product; prefill runs the int8 "MMQ" GEMM over an
  *           activation plane quantized to q8 blocks, which is computed once and
@@ -23,11 +27,17 @@
  *
  * Layouts (all little-endian):
  *   W  : N rows (outputs) x K columns (inputs), row-major; each row is K / bv
- *        consecutive blocks (bv = 32 for Q8_0, 256 for Q4_K and Q6_K).  Block
- *        bytes: Q8_0 34 (f16 d, int8 q[32]); Q4_K 144 (f16 d, f16 dmin,
- *        12 bytes of 6-bit scale/min pairs, 128 bytes of 4-bit codes); Q6_K 210
- *        (128 bytes low 4 bits, 64 bytes high 2 bits, 16 int8 sub-scales, f16 d).
- *        These are the public GGUF layouts; the pages fix only the sizes.
+ *        consecutive blocks (bv = 32 for Q4_0/Q4_1/Q5_0/Q5_1/Q8_0, 256 for
+ *        Q4_K/Q5_K/Q6_K).  Block bytes: Q8_0 34 (f16 d, int8 q[32]); Q4_0 18
+ *        (f16 d, 16 bytes of 4-bit codes, value i in the low and value 16 + i in
+ *        the high nibble of byte i; value d (code - 8)); Q4_1 20 (f16 d, f16 m,
+ *        the codes; value d code + m); Q5_0 22 (f16 d, 32 high bits, the low
+ *        nibbles; value d (code - 16)); Q5_1 24 (f16 d, f16 m, high bits, low
+ *        nibbles; value d code + m); Q4_K 144 (f16 d, f16 dmin, 12 bytes of
+ *        6-bit scale/min pairs, 128 bytes of 4-bit codes); Q5_K 176 (Q4_K's
+ *        header, 32 bytes of high bits, Q4_K's codes); Q6_K 210 (128 bytes low
+ *        4 bits, 64 bytes high 2 bits, 16 int8 sub-scales, f16 d).  These are
+ *        the public GGUF layouts; the pages fix only some sizes and the types.
  *   x  : K f32.   y : N f32.   X : M x K f32 row-major.   Y : M x N f32 row-major.
  *   Xq : the quantized activation plane written by mq_quantize_act, three
  *        arrays in one buffer of mq_act_bytes(M, K) bytes:
@@ -61,8 +71,13 @@ extern "C" {
 #endif
 
 /* Weight type ids: the GGUF tensor-type ids. */
+#define MQ_Q4_0 2
+#define MQ_Q4_1 3
+#define MQ_Q5_0 6
+#define MQ_Q5_1 7
 #define MQ_Q8_0 8
 #define MQ_Q4_K 12
+#define MQ_Q5_K 13
 #define MQ_Q6_K 14
 /* OR-ed into MQ_Q8_0 or MQ_Q6_K: the weights are in the layout mq_repack writes
  * (every call that takes a weight type accepts it). */
@@ -164,7 +179,7 @@ size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
  * several weights that share the input).  Per 32-value block the kernel forms
  * exact int32 dot products of weight codes and activation codes on int8 MFMA
  * (per 16-value group for Q6_K) and applies the block scales in f32 (and, for
- * Q4_K, the min term through the block's code sum).  Y: M x N f32 (device,
+ * Q4_K, Q5_K, Q4_1 and Q5_1, the min term through the block's code sum).  Y: M x N f32 (device,
  * overwritten).  scratch / scratch_bytes: device memory of at least
  * mq_gemm_scratch_bytes(type, M, N, K) bytes, 16-byte aligned (may be NULL/0
  * when that is 0); its contents are overwritten, and calls that share one
@@ -177,8 +192,10 @@ int mq_gemm(const void* W, int type, const void* Xq, float* Y, int64_t M, int64_
 /*
  * mq_debug_gemm_blockdots -- test export: the exact int32 block dot products
  * the mq_gemm kernel forms, written to D (device) as int32 [M][N][G] with
- * G = K / 32 for Q8_0 and Q4_K (code dot per 32-value block, Q4_K codes 0..15)
- * and G = K / 16 for Q6_K (dot of (code - 32) per 16-value group).  Runs the
+ * G = K / 16 for Q6_K (dot of (code - 32) per 16-value group) and G = K / 32
+ * for every other type (dot per 32-value block of: the signed q of Q8_0;
+ * code - 8 of Q4_0; code - 16 of Q5_0; the unsigned code of Q4_1, Q5_1, Q4_K
+ * (0..15) and Q5_K (0..31)).  Runs the
  * same kernel template as mq_gemm with its store of block dots switched on.
  * D must hold M * N * G int32.
  */

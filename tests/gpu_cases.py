@@ -15,8 +15,13 @@ from block_quantized_matmul_mq_amd import mq, synth
 
 TOL = 2e-4
 
-BLOCK = {mq.Q8_0: 32, mq.Q4_K: 256, mq.Q6_K: 256}
-NAMES = {mq.Q8_0: "q8_0", mq.Q4_K: "q4_K", mq.Q6_K: "q6_K"}
+BLOCK = {mq.Q8_0: 32, mq.Q4_K: 256, mq.Q6_K: 256,
+         mq.Q4_0: 32, mq.Q4_1: 32, mq.Q5_0: 32, mq.Q5_1: 32, mq.Q5_K: 256}
+NAMES = {mq.Q8_0: "q8_0", mq.Q4_K: "q4_K", mq.Q6_K: "q6_K",
+         mq.Q4_0: "q4_0", mq.Q4_1: "q4_1", mq.Q5_0: "q5_0", mq.Q5_1: "q5_1", mq.Q5_K: "q5_K"}
+# every served weight type: the three of the measured workloads first, then the other
+# types of the eligibility list
+ALL_TYPES = [mq.Q8_0, mq.Q4_K, mq.Q6_K, mq.Q4_0, mq.Q4_1, mq.Q5_0, mq.Q5_1, mq.Q5_K]
 
 
 def say(msg):

@@ -41,6 +41,17 @@ def test_weight_bytes_are_exact_payload_sizes():
     assert mq.weight_bytes(mq.Q4_K, 10, 100) == 0      # K not a whole super-block
     assert mq.weight_bytes(99, 10, 256) == 0           # unknown type
     assert mq.weight_bytes(mq.Q8_0, 0, 32) == 0
+    # the 32-value types and Q5_K (block bytes 18, 20, 22, 24 per 32 values and 176 per 256)
+    assert mq.weight_bytes(mq.Q4_0, 4864, 896) == 4864 * 28 * 18
+    assert mq.weight_bytes(mq.Q4_1, 4864, 896) == 4864 * 28 * 20
+    assert mq.weight_bytes(mq.Q5_0, 4864, 896) == 4864 * 28 * 22
+    assert mq.weight_bytes(mq.Q5_1, 4864, 896) == 4864 * 28 * 24
+    assert mq.weight_bytes(mq.Q5_K, 18944, 3584) == 18944 * 14 * 176
+    assert mq.weight_bytes(mq.Q5_K, 10, 100) == 0
+    assert mq.weight_bytes(mq.Q4_0, 10, 48) == 0       # K not a whole 32-value block
+    # no repacked layout for them
+    for t in (mq.Q4_0, mq.Q4_1, mq.Q5_0, mq.Q5_1, mq.Q5_K):
+        assert mq.weight_bytes(t | mq.REPACKED, 10, 256) == 0
 
 
 def test_activation_plane_layout():
@@ -70,8 +81,8 @@ def test_quantize_act_refusals():
 def test_gemv_refusals():
     lib = mq.load()
     assert lib.mq_gemv(None, mq.Q4_K, FAKE, FAKE, 8, 256, None) == -1
-    assert lib.mq_gemv(FAKE, 2, FAKE, FAKE, 8, 256, None) == -3        # q4_0 is not served here
-    assert "unsupported weight type 2" in mq.last_error()
+    assert lib.mq_gemv(FAKE, 10, FAKE, FAKE, 8, 256, None) == -3       # q2_K is not served here
+    assert "unsupported weight type 10" in mq.last_error()
     assert lib.mq_gemv(FAKE, mq.Q4_K, FAKE, FAKE, 8, 128, None) == -2  # K % 256
     assert "K=128" in mq.last_error()
     assert lib.mq_gemv(FAKE, mq.Q8_0, FAKE, FAKE, 8, 48, None) == -2   # K % 32
@@ -86,7 +97,7 @@ def test_gemm_refusals():
     assert lib.mq_gemm(FAKE, mq.Q4_K, FAKE, None, 4, 8, 256, None, 0, None) == -1
     assert lib.mq_gemm(FAKE, mq.Q4_K, FAKE, FAKE, 0, 8, 256, None, 0, None) == -1
     assert lib.mq_gemm(FAKE, mq.Q6_K, FAKE, FAKE, 4, 8, 96, None, 0, None) == -2
-    assert lib.mq_gemm(FAKE, 7, FAKE, FAKE, 4, 8, 256, None, 0, None) == -3
+    assert lib.mq_gemm(FAKE, 11, FAKE, FAKE, 4, 8, 256, None, 0, None) == -3   # q3_K
     assert lib.mq_gemm(FAKE, mq.Q4_K, FAKE + 16, FAKE, 4, 8, 256, None, 0, None) == -5
     assert lib.mq_debug_gemm_blockdots(FAKE, mq.Q4_K, FAKE, None, 4, 8, 256, None) == -1
 
@@ -103,8 +114,9 @@ def test_gemm_scratch_is_sized_by_the_split_plan():
     assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 512, 3584) == 14 * 16 * tile
     # 112 tiles: 4 ranges
     assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 3584, 3584) == 4 * 112 * tile
-    # Q8_0 splits the same way (28 K-steps of 128 at K = 3584)
-    assert mq.gemm_scratch_bytes(mq.Q8_0, 512, 512, 3584) == 14 * 16 * tile
+    # every other type splits the same way (28 K-steps of 128 at K = 3584)
+    for t in (mq.Q8_0, mq.Q6_K, mq.Q5_K, mq.Q4_0, mq.Q4_1, mq.Q5_0, mq.Q5_1):
+        assert mq.gemm_scratch_bytes(t, 512, 512, 3584) == 14 * 16 * tile
     # 8 < M <= 32: 32 x 128 tiles; the vocab head at M = 9 has 1188 of them, the last 164 cut in 3
     assert mq.gemm_scratch_bytes(mq.Q6_K, 9, 152064, 3584) == 3 * 164 * 32 * 128 * 4
     # M <= 8: the multi-row GEMV, no scratch -- unless the rows do not fit its LDS

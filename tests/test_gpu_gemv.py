@@ -6,11 +6,11 @@ import pytest
 import oracle
 from block_quantized_matmul_mq_amd import mq, synth
 
-from gpu_cases import BLOCK, NAMES, check_normalized, device, row_norms, say, to_dev, weights
+from gpu_cases import ALL_TYPES, BLOCK, NAMES, check_normalized, device, row_norms, say, to_dev, weights
 
 pytestmark = pytest.mark.gpu
 
-TYPES = [mq.Q8_0, mq.Q4_K, mq.Q6_K]
+TYPES = ALL_TYPES
 
 
 def run_gemv(raw, qtype, x, N, K, rows=None, what=""):

@@ -12,11 +12,11 @@ import pytest
 import oracle
 from block_quantized_matmul_mq_amd import mq, synth
 
-from gpu_cases import BLOCK, NAMES, check_normalized, device, row_norms, say, to_dev, weights
+from gpu_cases import ALL_TYPES, BLOCK, NAMES, check_normalized, device, row_norms, say, to_dev, weights
 
 pytestmark = pytest.mark.gpu
 
-TYPES = [mq.Q8_0, mq.Q4_K, mq.Q6_K]
+TYPES = ALL_TYPES
 
 
 def quantized_plane(X, dev):
@@ -86,7 +86,7 @@ def test_split_k_uneven_ranges(qtype):
     # One output tile and a long K: the kernel splits K into many ranges of whole
     # 128-value steps (uneven lengths; for Q8_0 the last step is cut by K) and sums
     # the partials in a second launch.
-    M, N, K = 40, 100, (4128 if qtype == mq.Q8_0 else 8192)
+    M, N, K = 40, 100, (4128 if BLOCK[qtype] == 32 else 8192)
     assert mq.gemm_scratch_bytes(qtype, M, N, K) >= 8 * M * N * 4, "shape must take the split-K path"
     raw = weights(qtype, N, K, "random", 70)
     X = synth.activations(M, K, config_index=12, tensor_index=30)

@@ -341,6 +341,54 @@ def main():
             us = timer.per_launch_us([lambda W=W: mq.gemv(W, Q8_0, x8, N, K, y=y8) for W in wc], reps)
             sec[f"gemv_q8_0_{tag}_{N}x{K}"] = {"us": round(us, 3), "GBps": round(nb / us / 1e3, 1)}
             del wc
+        # the other types of the eligibility list on the 7B ffn_up shape: GEMV at M = 1 (weights
+        # rotated past the last-level cache) and the prefill product at M = 512
+        N7, K7 = 18944, 3584
+        for qt, tag in [(mq.Q5_K, "q5_K"), (mq.Q4_0, "q4_0"), (mq.Q4_1, "q4_1"), (mq.Q5_0, "q5_0"),
+                        (mq.Q5_1, "q5_1")]:
+            wt = synth.quantized_weight(qt, N7, K7, 1, 50 + qt)
+            nb = mq.weight_bytes(qt, N7, K7)
+            wc = [to_dev(wt) for _ in range(copies_for(nb))]
+            del wt
+            xt = x_dev["ffn_up"]
+            yt = torch.empty(N7, dtype=torch.float32, device=dev)
+            us = timer.per_launch_us([lambda W=W: mq.gemv(W, qt, xt, N7, K7, y=yt) for W in wc], reps)
+            gk = mq.last_kernel()
+            Yt = torch.empty((PREFILL_M, N7), dtype=torch.float32, device=dev)
+            sct = torch.empty(max(mq.gemm_scratch_bytes(qt, PREFILL_M, N7, K7), 256), dtype=torch.uint8, device=dev)
+            us_m = timer.per_launch_us([lambda W=W: mq.gemm(W, qt, Xq, PREFILL_M, N7, K7, Y=Yt, scratch=sct)
+                                        for W in wc[:4]], reps)
+            sec[f"{tag}_7B_ffn_up_{N7}x{K7}"] = {
+                "gemv_us": round(us, 3), "gemv_GBps": round(nb / us / 1e3, 1), "gemv_kernel": gk,
+                "mmq_M512_us": round(us_m, 3), "mmq_M512_TOPS": round(2 * PREFILL_M * N7 * K7 / us_m / 1e6, 2),
+                "mmq_kernel": mq.last_kernel()}
+            del wc, Yt, sct
+        # gate and up (18944 x 3584 Q4_K each) as two products, or as one 37888-row product
+        gate = copies["ffn_up"][0]
+        upw = to_dev(synth.quantized_weight(Q4_K, N7, K7, 1, 60))
+        gu = torch.cat([gate, upw])
+        ncg = copies_for(2 * mq.weight_bytes(Q4_K, N7, K7))
+        gus = [gu] + [gu.clone() for _ in range(ncg - 1)]
+        pairs = [(gate, upw)] + [(g[:gate.numel()], g[gate.numel():]) for g in gus[1:]]
+        ygu = torch.empty(2 * N7, dtype=torch.float32, device=dev)
+        xg = x_dev["ffn_up"]
+        us_sep = timer.per_launch_us([lambda a=a, b=b: (mq.gemv(a, Q4_K, xg, N7, K7, y=ygu[:N7]),
+                                                        mq.gemv(b, Q4_K, xg, N7, K7, y=ygu[N7:])) for a, b in pairs],
+                                     reps)
+        us_cat = timer.per_launch_us([lambda g=g: mq.gemv(g, Q4_K, xg, 2 * N7, K7, y=ygu) for g in gus], reps)
+        Ygu = torch.empty((PREFILL_M, 2 * N7), dtype=torch.float32, device=dev)
+        Yg, Yu = (torch.empty((PREFILL_M, N7), dtype=torch.float32, device=dev) for _ in range(2))
+        scg = torch.empty(max(mq.gemm_scratch_bytes(Q4_K, PREFILL_M, 2 * N7, K7),
+                              mq.gemm_scratch_bytes(Q4_K, PREFILL_M, N7, K7), 256), dtype=torch.uint8, device=dev)
+        mm_sep = timer.per_launch_us([lambda: (mq.gemm(gate, Q4_K, Xq, PREFILL_M, N7, K7, Y=Yg, scratch=scg),
+                                               mq.gemm(upw, Q4_K, Xq, PREFILL_M, N7, K7, Y=Yu, scratch=scg))] * 2,
+                                     reps)
+        mm_cat = timer.per_launch_us([lambda: mq.gemm(gu, Q4_K, Xq, PREFILL_M, 2 * N7, K7, Y=Ygu, scratch=scg)] * 2,
+                                     reps)
+        sec["q4_K_gate_up_7B"] = {"gemv_two_launches_us": round(us_sep, 3), "gemv_one_37888_row_launch_us": round(us_cat, 3),
+                                  "mmq_M512_two_launches_us": round(mm_sep, 3),
+                                  "mmq_M512_one_37888_row_launch_us": round(mm_cat, 3)}
+        del gus, pairs, gu, upw
         qa_bytes = PREFILL_M * 3584 * 4
         sec["quantize_act_512x3584"] = {"us": round(avg_us["quantize_act"], 3),
                                         "GBps_in": round(qa_bytes / avg_us["quantize_act"] / 1e3, 1)}

@@ -5,6 +5,8 @@
 // Work split.  The matrix is cut into tiles of 16 rows, dealt round-robin to the
 // workgroups (one per CU): tile t goes to workgroup t % G, so at any moment the GPU reads
 // one window of consecutive tiles (faster on HBM than one separate stream per CU).
+// (Sharing the rows of the last, partial round out evenly, a partial tile per
+// workgroup, was measured slower: a workgroup's time follows its item count.)
 // Inside a workgroup, wave w owns super-block w of every row (rows of up to 16
 // super-blocks, K <= 4096): its work item for a tile is that super-block of the tile's
 // 16 rows, 16 x 144 bytes.  Each wave streams its own items into its own LDS ring of NB
@@ -29,8 +31,8 @@
 // item.  Each lane then applies its two sub-blocks' 6-bit scales and mins:
 //   y[n] += d * sc * 2^e * sum(code * v) - dmin * m * sum(x)      (per sub-block).
 // The four lanes of a row are summed with two lane swaps; each wave leaves one partial
-// per row and tile in LDS, and the partials of a row are summed in wave order at the end
-// (deterministic).
+// per row and tile in LDS, and at the end four lanes per row each add four of the row's
+// wave partials and two lane swaps combine them (a fixed order: deterministic).
 #include <utility>
 
 #include "mq_device.h"
@@ -53,6 +55,7 @@ constexpr int kFracBits = 21;
 constexpr int kBufferWord3 = 0x00020000;           // raw buffer resource: 32-bit data format, no swizzle
 constexpr int kStageBytes = 16384;                 // x staging, later the row partials
 constexpr int kMaxTilesPerGroup = kStageBytes / (kTileRows * kWaves * 4);
+static_assert(kMaxTilesPerGroup * kTileRows * 4 <= kThreads, "one pass of the row sums");
 
 // f(integral_constant<int, 0>), ..., f(integral_constant<int, n - 1>)
 template <class F, int... i>
@@ -137,9 +140,9 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_kernel(const uint8_t* 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = gridDim.x, w0 = blockIdx.x;
+    const int TB = kTileRows * row_bytes;
     const int T = (N + kTileRows - 1) / kTileRows;
     const int tiles = (T - w0 + G - 1) / G;   // this workgroup's: global tiles w0 + k G
-    const int TB = kTileRows * row_bytes;
     const bool active = wave < SB;            // uniform: waves past the row's super-blocks only stage x
 
     // x first: loads complete in issue order, so x is requested before the weights.
@@ -262,11 +265,21 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_kernel(const uint8_t* 
     }
     wait_barrier<0>();   // every partial written (and the loads past the end have landed)
 
+    // Row sums: lane j of the four lanes of row r adds the partials of waves 4j .. 4j + 3
+    // (one 16-byte LDS read; waves past the row's super-blocks wrote none and count zero).
+    // tiles * 16 rows * 4 lanes <= kThreads (kMaxTilesPerGroup).
     const int wl = SB < kWaves ? SB : kWaves;
-    for (int r = tid; r < tiles * kTileRows; r += kThreads) {
+    const int r = tid >> 2, j = tid & 3;
+    float s = 0.f;
+    if (r < tiles * kTileRows) {
+        const float4 v = *reinterpret_cast<const float4*>(part + r * kWaves + 4 * j);
+        s = ((4 * j < wl ? v.x : 0.f) + (4 * j + 1 < wl ? v.y : 0.f)) +
+            ((4 * j + 2 < wl ? v.z : 0.f) + (4 * j + 3 < wl ? v.w : 0.f));
+    }
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    if (j == 0 && r < tiles * kTileRows) {
         const int row = (w0 + (r / kTileRows) * G) * kTileRows + r % kTileRows;
-        float s = 0.f;
-        for (int w = 0; w < wl; ++w) s += part[r * kWaves + w];
         if (row < N) y[row] = s;
     }
 }

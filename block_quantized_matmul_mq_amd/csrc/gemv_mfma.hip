@@ -1,6 +1,8 @@
-// mq_gemv for wide Q4_K matrices: y = deq(W) x for one f32 activation row (the decode
-// product of "minfer CUDA Backend Design", 4.4 Execution dispatch), with the integer
-// dot products on int8 matrix cores and the weights streamed through LDS.
+// mq_gemv for wide Q4_K matrices and for Q4_K matrices with long rows: y = deq(W) x for
+// one f32 activation row (the decode product of "minfer CUDA Backend Design", 4.4
+// Execution dispatch), with the integer dot products on int8 matrix cores and the weights
+// streamed through LDS.  The wide-matrix kernel is described first; the long-row kernel
+// (more than 16 super-blocks per row, few rows per CU) further down.
 //
 // Work split.  The matrix is cut into tiles of 16 rows, dealt round-robin to the
 // workgroups (one per CU): tile t goes to workgroup t % G, so at any moment the GPU reads
@@ -284,6 +286,171 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_kernel(const uint8_t* 
     }
 }
 
+
+// ------------------------------------------------------------------ long rows
+// More than 16 super-blocks per row (e.g. the 7B ffn_down 3584 x 18944, 74 super-blocks)
+// and at most 16 rows per CU: each workgroup owns one tile of TR <= 16 consecutive rows,
+// TR = ceil(N / G), so that the G workgroups split N evenly, and its 16 waves share the
+// tile's super-blocks: wave w takes super-blocks w, w + 16, w + 32, ...  (At any moment
+// the GPU then reads 16 consecutive super-blocks, 2304 contiguous bytes, of every row.)
+// An item is one super-block of the tile's rows (TR x 144 bytes; the lanes of rows past
+// TR read past the end of the buffer: zeros, no traffic), streamed into the wave's LDS
+// ring as in the kernel above, together with that super-block's 256 x values (one float4
+// per lane, into registers).  When the item has landed the wave turns its x into the
+// exact digit form of the kernel above in its own 832 bytes of LDS (no workgroup
+// barrier: a wave reads back only what it wrote, and one wave's LDS operations complete
+// in order), then runs the same four MFMAs.  A lane accumulates its unit's share of its
+// row over the wave's items, in item order; the four lanes of a row, then the 16 waves,
+// are summed at the end in a fixed order (deterministic).  One item in flight per wave
+// (a ring of two slots): rings of three and four slots measured slower (more rows'
+// fragments in flight at once), and so did staggering the item order across CUs.
+constexpr int kLongRing = 2;
+constexpr uint32_t kPastEnd = 0x7FFF0000u;   // a buffer offset past the end of any matrix this kernel takes
+
+template <int NB>
+__global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_long_kernel(const uint8_t* __restrict__ W,
+                                                                       const float* __restrict__ x,
+                                                                       float* __restrict__ y, int N, int K,
+                                                                       int row_bytes, int TR) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[kWaves * kItemBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[kWaves * kItemBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t ring2[NB > 2 ? kWaves * kItemBytes : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t ring3[NB > 3 ? kWaves * kItemBytes : 16];
+    __shared__ __attribute__((aligned(16))) int8_t xs[kWaves * 768];   // per wave: 3 digit planes of 256 values
+    __shared__ __attribute__((aligned(16))) int xex[kWaves * 8];       // per wave: 8 block exponents
+    __shared__ __attribute__((aligned(16))) float xsum[kWaves * 8];    // per wave: 8 block sums
+    __shared__ __attribute__((aligned(16))) float part[kTileRows * kWaves];
+    auto slot = [&](auto b) -> uint8_t* {
+        constexpr int B = decltype(b)::value;
+        if constexpr (B == 0) return ring0;
+        else if constexpr (B == 1) return ring1;
+        else if constexpr (B == 2) return ring2;
+        else return ring3;
+    };
+
+    const int SB = K >> 8;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r0 = blockIdx.x * TR;
+    const int rows = min(TR, N - r0);
+    const int items = (SB - wave + kWaves - 1) / kWaves;   // super-blocks wave, wave + 16, ... (>= 1: SB > 16)
+
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W), 0, N * row_bytes, kBufferWord3);
+    auto chunk_offset = [&](int c) { return uint32_t((c / 9) * row_bytes + 16 * (c % 9)); };
+    const int c0 = lane, c1 = 64 + lane, c2 = 128 + (lane >> 2);
+    const bool live0 = c0 / 9 < rows, live1 = c1 / 9 < rows, live2 = c2 / 9 < rows;
+    const uint32_t vo0 = chunk_offset(c0), vo1 = chunk_offset(c1), vo2 = chunk_offset(c2) + 4 * (lane & 3);
+    const uint32_t tile0 = uint32_t(r0) * uint32_t(row_bytes);
+    float4 xr[NB];
+    // Item i: x of super-block wave + 16 i (a float4 per lane, into registers), then the
+    // super-block's TR rows (into the slot).  Items past the wave's last read x of its
+    // last super-block and move no weight bytes.
+    auto issue = [&](auto b, int i) {
+        constexpr int B = decltype(b)::value;
+        uint8_t* dst = slot(b) + wave * kItemBytes;
+        const bool in = i < items;
+        const int sb = wave + kWaves * (in ? i : items - 1);
+        xr[B] = reinterpret_cast<const float4*>(x + 256 * sb)[lane];
+        const uint32_t base = tile0 + uint32_t(sb) * 144u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)dst, 16, in && live0 ? base + vo0 : kPastEnd, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(dst + 1024), 16, in && live1 ? base + vo1 : kPastEnd, 0,
+                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(dst + 2048), 4, in && live2 ? base + vo2 : kPastEnd, 0,
+                                                 0, 0);
+    };
+    static_for<NB - 1>([&](auto b) { issue(b, decltype(b)::value); });
+
+    const int n = lane & 15, q = lane >> 4;
+    const bool a_lane = (n >> 2) == q && (n & 3) < 3;
+    const uint32_t sc_shift = 16u * uint32_t(q & 1);
+    int8_t* my_xs = xs + wave * 768;
+    int* my_ex = xex + wave * 8;
+    float* my_sum = xsum + wave * 8;
+    float acc = 0.f;
+
+    auto compute = [&](const uint8_t* it, const float4 v) {
+        // Stage this super-block's x: lane l holds values 4l .. 4l + 3, 8 lanes per 32-block.
+        float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        a = fmaxf(a, __shfl_xor(a, 1, 64));
+        a = fmaxf(a, __shfl_xor(a, 2, 64));
+        a = fmaxf(a, __shfl_xor(a, 4, 64));
+        const int k = kFracBits - __builtin_amdgcn_frexp_expf(a);
+        uint32_t d0, d1, d2;
+        transpose3(digits3(v.x, k), digits3(v.y, k), digits3(v.z, k), digits3(v.w, k), d0, d1, d2);
+        *reinterpret_cast<uint32_t*>(my_xs + 4 * lane) = d0;
+        *reinterpret_cast<uint32_t*>(my_xs + 256 + 4 * lane) = d1;
+        *reinterpret_cast<uint32_t*>(my_xs + 512 + 4 * lane) = d2;
+        float sm = (v.x + v.y) + (v.z + v.w);
+        sm += __shfl_xor(sm, 1, 64);
+        sm += __shfl_xor(sm, 2, 64);
+        sm += __shfl_xor(sm, 4, 64);
+        if ((lane & 7) == 0) {
+            my_sum[lane >> 3] = sm;
+            my_ex[lane >> 3] = -k;
+        }
+        // (LDS operations of one wave complete in order: the reads below see the writes.)
+        v4i a0 = {0, 0, 0, 0}, a1 = a0, a2 = a0, a3 = a0;
+        if (a_lane) {
+            const int8_t* ap = my_xs + (n & 3) * 256 + 64 * q;
+            a0 = *reinterpret_cast<const v4i*>(ap);
+            a1 = *reinterpret_cast<const v4i*>(ap + 16);
+            a2 = *reinterpret_cast<const v4i*>(ap + 32);
+            a3 = *reinterpret_cast<const v4i*>(ap + 48);
+        }
+        const int2 e2 = *reinterpret_cast<const int2*>(my_ex + 2 * q);
+        const float2 s2 = *reinterpret_cast<const float2*>(my_sum + 2 * q);
+        const uint8_t* blk = it + n * 144;
+        const uint4 hd = *reinterpret_cast<const uint4*>(blk);
+        const v4i c0w = *reinterpret_cast<const v4i*>(blk + 16 + 32 * q);
+        const v4i c1w = *reinterpret_cast<const v4i*>(blk + 32 + 32 * q);
+        const v4i z = {0, 0, 0, 0};
+        v4i clo = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, c0w & 0x0F0F0F0F, z, 0, 0, 0);
+        clo = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, c1w & 0x0F0F0F0F, clo, 0, 0, 0);
+        v4i chi = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, (c0w >> 4) & 0x0F0F0F0F, z, 0, 0, 0);
+        chi = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, (c1w >> 4) & 0x0F0F0F0F, chi, 0, 0, 0);
+        const int ilo = combine3(clo), ihi = combine3(chi);
+        const uint32_t t0 = hd.y >> sc_shift, t1 = hd.z >> sc_shift, t2 = hd.w >> sc_shift;
+        const uint32_t sc_hi = (t2 & 0x0F0Fu) | ((t0 >> 2) & 0x3030u);
+        const uint32_t mn_hi = ((t2 >> 4) & 0x0F0Fu) | ((t1 >> 2) & 0x3030u);
+        const uint32_t scp = q >= 2 ? sc_hi : (t0 & 0x3F3Fu);
+        const uint32_t mnp = q >= 2 ? mn_hi : (t1 & 0x3F3Fu);
+        const float d = half_bits_to_float(hd.x & 0xFFFFu);
+        const float dmin = half_bits_to_float(hd.x >> 16);
+        const float codes = ldexpf(ubyte_f<0>(scp) * float(ilo), e2.x) + ldexpf(ubyte_f<1>(scp) * float(ihi), e2.y);
+        const float mins = fmaf(ubyte_f<0>(mnp), s2.x, ubyte_f<1>(mnp) * s2.y);
+        acc += fmaf(d, codes, -dmin * mins);
+    };
+
+    constexpr int kInFlight = (NB - 1) * 4;   // x and weight loads of the NB - 1 items after item i
+    static_assert(kInFlight < 16, "vmcnt immediate");
+    auto step = [&](auto b, int i) {
+        constexpr int B = decltype(b)::value;
+        issue(std::integral_constant<int, (B + NB - 1) % NB>{}, i + NB - 1);   // the slot of item i - 1
+        __builtin_amdgcn_s_waitcnt(kInFlight | 0x0F70);                       // item i has landed
+        compute(slot(b) + wave * kItemBytes, xr[B]);
+    };
+    int i0 = 0;
+    for (; i0 + NB <= items; i0 += NB) static_for<NB>([&](auto b) { step(b, i0 + decltype(b)::value); });
+    static_for<NB>([&](auto b) {
+        if (i0 + decltype(b)::value < items) step(b, i0 + decltype(b)::value);
+    });
+
+    const float r = sum_lane_groups(acc);
+    if (q == 0) part[n * kWaves + wave] = r;
+    wait_barrier<0>();   // every partial written (and the loads past the end have landed)
+
+    const int rr = tid >> 2, j = tid & 3;
+    float sum = 0.f;
+    if (rr < kTileRows) {
+        const float4 v = *reinterpret_cast<const float4*>(part + rr * kWaves + 4 * j);
+        sum = (v.x + v.y) + (v.z + v.w);
+    }
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    if (j == 0 && rr < rows) y[r0 + rr] = sum;
+}
+
 constexpr int kRing = 4;
 
 struct Plan {
@@ -304,15 +471,34 @@ Plan plan(int64_t N, int64_t K, int cu_count) {
     return p;
 }
 
+// Long rows: more than 16 super-blocks and between 8 and 16 rows per CU (one tile of TR rows
+// per workgroup).
+int long_tile_rows(int64_t N, int64_t K, int cu_count) {
+    if (N <= 0 || K % 256 || K / 256 <= kMaxSB || cu_count <= 0) return 0;
+    const int64_t tr = (N + cu_count - 1) / cu_count;
+    if (tr < 8 || tr > kTileRows) return 0;
+    if (N * ((K / 256) * 144) > int64_t(kPastEnd)) return 0;
+    return int(tr);
+}
+
 }  // namespace
 
 bool gemv_mfma_applies(int type, int64_t N, int64_t K, int cu_count) {
-    // Wide matrices only: at least two 16-row tiles per CU.
-    return type == kQ4_K && N >= 2 * kTileRows * int64_t(cu_count) && plan(N, K, cu_count).grid > 0;
+    // Wide matrices: at least two 16-row tiles per CU; or long rows at 8..16 rows per CU.
+    if (type != kQ4_K) return false;
+    if (long_tile_rows(N, K, cu_count) > 0) return true;
+    return N >= 2 * kTileRows * int64_t(cu_count) && plan(N, K, cu_count).grid > 0;
 }
 
 hipError_t launch_gemv_mfma(const uint8_t* W, const float* x, float* y, int64_t N, int64_t K, int cu_count,
                             hipStream_t s, const char** name) {
+    if (const int tr = long_tile_rows(N, K, cu_count)) {
+        *name = "gemv_mfma_long<q4_K>";
+        int n = int(N), k = int(K), row_bytes = int((K / 256) * 144), t = tr;
+        void* args[] = {&W, &x, &y, &n, &k, &row_bytes, &t};
+        return hipLaunchKernel(reinterpret_cast<const void*>(gemv_mfma_q4k_long_kernel<kLongRing>),
+                               dim3(unsigned((N + tr - 1) / tr)), dim3(kThreads), args, 0, s);
+    }
     const Plan p = plan(N, K, cu_count);
     if (p.grid <= 0) return hipErrorInvalidValue;
     *name = "gemv_mfma<q4_K>";

@@ -119,3 +119,23 @@ def test_gemv_q4_k_wide_matrix_core_path(N, K, kind, sampled):
         rows = np.unique(np.concatenate([rng.integers(0, N, 3000), np.arange(32), np.arange(N - 32, N)]))
     run_gemv(raw, mq.Q4_K, x, N, K, rows=rows, what=f"{kind} matrix-core")
     assert "mfma" in mq.last_kernel()
+
+
+@pytest.mark.parametrize("N,K,kind", [(3584 - 5, 18944, "random"),
+                                      (2048 + 3, 13824, "quantized"),
+                                      (4096, 14336, "random"),
+                                      (3000, 256 * 17, "quantized"),
+                                      (2304, 24576, "random")],
+                         ids=["ragged_7b_down", "nine_row_tiles", "sixteen_row_tiles", "seventeen_super_blocks",
+                              "longest_rows"])
+def test_gemv_q4_k_long_row_matrix_core_path(N, K, kind):
+    """Long Q4_K rows (more than 16 super-blocks) at 8 to 16 rows per CU take the
+    long-row matrix-core kernel: a short last tile, tiles of 9 and 16 rows, waves with
+    one and two items (17 super-blocks), the largest K the kernel stages, and an x with
+    all-zero and tiny blocks."""
+    raw = weights(mq.Q4_K, N, K, kind, 8)
+    x = synth.activations(1, K, config_index=10, tensor_index=N % 89)[0]
+    x[32:64] = 0.0
+    x[K - 96:K - 64] *= 1e-30
+    run_gemv(raw, mq.Q4_K, x, N, K, what=f"{kind} long-row matrix-core")
+    assert "mfma_long" in mq.last_kernel()

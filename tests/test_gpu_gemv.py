@@ -139,3 +139,34 @@ def test_gemv_q4_k_long_row_matrix_core_path(N, K, kind):
     x[K - 96:K - 64] *= 1e-30
     run_gemv(raw, mq.Q4_K, x, N, K, what=f"{kind} long-row matrix-core")
     assert "mfma_long" in mq.last_kernel()
+
+
+@pytest.mark.parametrize("N,K,kind,sampled", [(16 * 512 + 4, 3584, "random", False),
+                                              (9000, 3072, "quantized", False),
+                                              (8192 + 16 * 37, 4096, "random", False),
+                                              (152064, 3584, "quantized", True)],
+                         ids=["ragged_tile_K3584", "twelve_super_blocks", "sixteen_super_blocks", "vocab_head"])
+def test_gemv_q6_k_matrix_core_path(N, K, kind, sampled):
+    """Wide Q6_K matrices in the GGUF layout (at least two 16-row tiles per CU, 12 to 16
+    super-blocks per row, the matrix ending on a 16-byte boundary) take the whole-tile
+    matrix-core kernel: a ragged last tile, idle waves (K = 3072), every wave busy
+    (K = 4096), the vocab head, and an x with all-zero and tiny blocks and runs."""
+    raw = weights(mq.Q6_K, N, K, kind, 9)
+    x = synth.activations(1, K, config_index=10, tensor_index=N % 83)[0]
+    x[32:64] = 0.0
+    x[112:128] *= 1e-30
+    rows = None
+    if sampled:
+        rng = np.random.default_rng(N)
+        rows = np.unique(np.concatenate([rng.integers(0, N, 3000), np.arange(32), np.arange(N - 32, N)]))
+    run_gemv(raw, mq.Q6_K, x, N, K, rows=rows, what=f"{kind} matrix-core")
+    assert mq.last_kernel() == "gemv_mfma<q6_K>"
+
+
+def test_gemv_q6_k_unaligned_end_takes_the_vector_kernel():
+    # 8193 rows of 2940 bytes do not end on a 16-byte boundary: the vector kernel runs
+    N, K = 8193, 3584
+    raw = weights(mq.Q6_K, N, K, "quantized", 10)
+    x = synth.activations(1, K, config_index=10, tensor_index=3)[0]
+    run_gemv(raw, mq.Q6_K, x, N, K, what="unaligned end")
+    assert mq.last_kernel() == "gemv<q6_K>"

@@ -490,7 +490,7 @@ Config chosen_config(int type) {
     return default_config(type);
 }
 
-// Wide Q4_K and Q6_K matrices go to the matrix-core kernels unless MQ_GEMV_MFMA=0 (read once;
+// Wide matrices go to the matrix-core kernels unless MQ_GEMV_MFMA=0 (read once;
 // bench A/B only).
 bool use_mfma() {
     static int v = -1;
@@ -532,8 +532,8 @@ hipError_t launch_gemv(int type, BlockLayout layout, const uint8_t* W, const flo
     if (!info) return hipErrorInvalidDevice;
     if (use_mfma() && type == kQ4_K && gemv_mfma_applies(type, N, K, info->cu_count))
         return launch_gemv_mfma(W, x, y, N, K, info->cu_count, s, name);
-    if (use_mfma() && type == kQ6_K && gemv_mfma_q6k_applies(layout, W, N, K, info->cu_count))
-        return launch_gemv_mfma_q6k(W, x, y, N, K, info->cu_count, s, name);
+    if (use_mfma() && gemv_tiled_applies(type, layout, W, N, K, info->cu_count))
+        return launch_gemv_tiled(type, W, x, y, N, K, info->cu_count, s, name);
     int tile = gemv_tile_units(type, K, info->lds_per_block);
     if (tile <= 0) return hipErrorInvalidValue;
     const int vals = unit_values(type);

@@ -452,28 +452,32 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_long_kernel(const uint
 }
 
 
-// ------------------------------------------------------------------ Q6_K, whole tiles
+// ------------------------------------------------------------------ whole tiles
 // Q6_K blocks are 210 bytes: neither the blocks nor the rows sit on 16-byte boundaries,
 // but a tile of 16 consecutive rows is 16 x row_bytes, a whole number of 16-byte chunks.
-// So the workgroup streams whole tiles: lane i reads chunks i, i + 1024, ... of the
-// tile into registers (16-byte loads, consecutive lanes on consecutive bytes), D tiles
-// ahead, and writes them to one of two LDS slots, so a tile is one contiguous copy of
-// its bytes in LDS.  A workgroup barrier per tile separates the slot being written from
-// the one being read.  Tiles are dealt round-robin as above (tile t to workgroup t % G).
+// So the workgroup streams whole tiles: lane i reads chunks i, i + 1024, ... of the tile
+// into registers (16-byte loads, consecutive lanes on consecutive bytes), D tiles ahead,
+// and writes them to one of two LDS slots, so a tile is one contiguous copy of its bytes
+// in LDS.  A workgroup barrier per tile separates the slot being written from the one
+// being read.  Tiles are dealt round-robin as above (tile t to workgroup t % G).
 //
 // Wave w computes super-block w of the tile's 16 rows with four v_mfma_i32_16x16x64_i8,
 // one per quarter t of the super-block's 16 runs of 16 values: lane group q takes run
-// g = 4t + q, whose codes are 16 consecutive ql bytes (one nibble) and 16 consecutive qh
-// bytes (two bits); A row 4q + p holds digit plane p of the same 16 x values.  So lane
-// (n, q) receives the exact sums over run g of code * v per plane, for each t, and
-// applies the run's signed sub-scale and the code offset 32 through the run's x sum:
+// g = 4t + q, A row 4q + p holds digit plane p of the run's x values and B column n the
+// run's 16 codes of row n (16 consecutive ql bytes, one nibble, and 16 consecutive qh
+// bytes, two bits).  So lane (n, q) receives the exact sums over run g of code * v per
+// plane, and applies the run's signed sub-scale and the code offset 32 through the run's
+// f32 sum of x:
 //   y[n] += d * sum_t sc[4t + q] * (2^e * sum(code * v) - 32 * sum(x)).
-// A block starts at an even byte offset in LDS; each 16-byte field is read as the five
+// Blocks start at even byte offsets in LDS; each 16-byte field is read as the five
 // aligned dwords that cover it and realigned with v_alignbyte.
-constexpr int kQ6Block = 210;
-constexpr int kQ6SlotBytes = kTileRows * kMaxSB * kQ6Block;           // 53760: a tile of 16-super-block rows
-constexpr int kQ6ChunksPerLane = (kQ6SlotBytes / 16 + kThreads - 1) / kThreads;   // 4
-constexpr uint32_t kQ6PastEnd = 0x80000000u;   // a buffer offset past the end of any matrix this kernel takes
+//
+// The kernel is written for any block type through TiledItem (bytes per 256 values and
+// the lane's share of a super-chunk).  Q8_0, Q4_0, Q4_1, Q5_0, Q5_1 and Q5_K were built
+// this way, passed the parity tests and measured slower than the vector kernel on the
+// 7B ffn_up shape (their decode is light, and the per-tile barrier and realignment cost
+// more than they save), so only Q6_K is routed here.
+constexpr uint32_t kTiledPastEnd = 0x80000000u;   // a buffer offset past the end of any matrix this kernel takes
 
 // 16 bytes at an even LDS address: the five aligned dwords that cover them, realigned
 __device__ __forceinline__ uint4 lds_seg16(const uint8_t* p) {
@@ -484,19 +488,67 @@ __device__ __forceinline__ uint4 lds_seg16(const uint8_t* p) {
     return make_uint4(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh),
                       __builtin_amdgcn_alignbyte(w3, w2, sh), __builtin_amdgcn_alignbyte(w4, w3, sh));
 }
+__device__ __forceinline__ float lds_f16(const uint8_t* p) {
+    return half_bits_to_float(uint32_t(*reinterpret_cast<const uint16_t*>(p)));
+}
+// signed byte k (0..3) of a dword
+__device__ __forceinline__ float sbyte_f(uint32_t v, int k) { return float(int32_t(v << (24 - 8 * k)) >> 24); }
+
+
+// Per type: bytes per 256 values, and the lane's share of one super-chunk of its row.
+// row: the row's bytes in LDS; sc: super-chunk index; q: lane group; a, e, sx: the
+// lane's x digits, exponents and f32 x sums for runs 4t + q.
+template <int QT> struct TiledItem;
+
+template <> struct TiledItem<kQ6_K> {
+    static constexpr int kSBBytes = 210;
+    __device__ static float run(const uint8_t* row, int sc, int q, const v4i (&a)[4], const int (&e)[4],
+                                const float (&sx)[4]) {
+        const uint8_t* blk = row + sc * kSBBytes;
+        const uint4 scw = lds_seg16(blk + 192);
+        const uint32_t sc4[4] = {scw.x, scw.y, scw.z, scw.w};
+        const uint32_t s_lo = 2u * uint32_t(q >> 1);   // qh bit pair of the low-nibble runs (t even)
+        float acc = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // runs 8h + q (low nibbles) and 8h + 4 + q (high nibbles) share 16 ql and 16 qh bytes
+            const uint4 ql = lds_seg16(blk + 64 * h + 16 * q);
+            const uint4 qh = lds_seg16(blk + 128 + 32 * h + 16 * (q & 1));
+            const uint32_t L[4] = {ql.x, ql.y, ql.z, ql.w}, H[4] = {qh.x, qh.y, qh.z, qh.w};
+            v4i clo, chi;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                clo[i] = int((L[i] & 0x0F0F0F0Fu) | (((H[i] >> s_lo) & 0x03030303u) << 4));
+                chi[i] = int(((L[i] >> 4) & 0x0F0F0F0Fu) | (((H[i] >> (s_lo + 4)) & 0x03030303u) << 4));
+            }
+            const v4i z = {0, 0, 0, 0};
+            const v4i rlo = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[2 * h], clo, z, 0, 0, 0);
+            const v4i rhi = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[2 * h + 1], chi, z, 0, 0, 0);
+            acc = fmaf(sbyte_f(sc4[2 * h], q), fmaf(-32.0f, sx[2 * h], ldexpf(float(combine3(rlo)), e[2 * h])), acc);
+            acc = fmaf(sbyte_f(sc4[2 * h + 1], q),
+                       fmaf(-32.0f, sx[2 * h + 1], ldexpf(float(combine3(rhi)), e[2 * h + 1])), acc);
+        }
+        return lds_f16(blk + 208) * acc;
+    }
+};
+
+template <int QT>
+constexpr int tiled_slot_bytes() { return kTileRows * kMaxSB * TiledItem<QT>::kSBBytes; }
 
 // D: tiles in flight (register ring; two measured faster than three or four); CPL: 16-byte
 // chunks per lane and tile.  The loop is unrolled over lcm(D, 2) tiles so that every ring
 // and slot index is a compile-time constant.
-template <int D, int CPL>
-__global__ __launch_bounds__(kThreads) void gemv_mfma_q6k_kernel(const uint8_t* __restrict__ W,
-                                                                 const float* __restrict__ x,
-                                                                 float* __restrict__ y, int N, int K,
-                                                                 int row_bytes) {
+template <int QT, int D, int CPL>
+__global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(const uint8_t* __restrict__ W,
+                                                              const float* __restrict__ x,
+                                                              float* __restrict__ y, int N, int K,
+                                                              int row_bytes) {
+    using Item = TiledItem<QT>;
+    constexpr int kSlot = tiled_slot_bytes<QT>();
     // (16 bytes past a full slot: the aligned dwords read around a row's last block may
     // reach 2 bytes past its end)
-    __shared__ __attribute__((aligned(16))) uint8_t slot0[kQ6SlotBytes + 16];
-    __shared__ __attribute__((aligned(16))) uint8_t slot1[kQ6SlotBytes + 16];
+    __shared__ __attribute__((aligned(16))) uint8_t slot0[kSlot + 16];
+    __shared__ __attribute__((aligned(16))) uint8_t slot1[kSlot + 16];
     __shared__ __attribute__((aligned(16))) int8_t xp[3 * 256 * kMaxSB];   // digit planes [3][K]
     __shared__ __attribute__((aligned(16))) int ex[8 * kMaxSB];             // per 32-block
     __shared__ __attribute__((aligned(16))) float sums[16 * kMaxSB];        // per 16-run
@@ -522,15 +574,14 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q6k_kernel(const uint8_t* 
     // The matrix as one buffer: rows past the last read as zeros.
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W), 0, N * row_bytes, kBufferWord3);
-    static_assert(CPL <= kQ6ChunksPerLane, "chunks per lane");
     uint4 R[D][CPL];
     auto issue = [&](auto r, int k) {
         constexpr int J = decltype(r)::value;
-        const uint32_t base = k < tiles ? uint32_t(w0 + k * G) * TB : kQ6PastEnd;
+        const uint32_t base = k < tiles ? uint32_t(w0 + k * G) * TB : kTiledPastEnd;
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = tid + j * kThreads;
-            const uint32_t off = c < chunks ? base + 16u * uint32_t(c) : kQ6PastEnd;
+            const uint32_t off = c < chunks ? base + 16u * uint32_t(c) : kTiledPastEnd;
             const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
             R[J][j] = make_uint4(v[0], v[1], v[2], v[3]);
         }
@@ -541,8 +592,8 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q6k_kernel(const uint8_t* 
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = tid + j * kThreads;
-            // every lane has chunks 0 and 1 (a tile holds at least 12 x 210 chunks)
-            if (j < 2 || c < chunks) *reinterpret_cast<uint4*>(dst + 16 * c) = R[J][j];
+            // CPL = ceil(chunks / 1024): only the last round of chunks is partial
+            if (j < CPL - 1 || c < chunks) *reinterpret_cast<uint4*>(dst + 16 * c) = R[J][j];
         }
     };
     asm volatile("s_barrier" ::: "memory");   // every wave's x requested before any weights
@@ -552,11 +603,11 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q6k_kernel(const uint8_t* 
     // of every 16-value run (four lanes).
     if (tid < nquads) {   // uniform per wave: K is a multiple of 256
         const float4 v = xe;
-        float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-        a = fmaxf(a, __shfl_xor(a, 1, 64));
-        a = fmaxf(a, __shfl_xor(a, 2, 64));
-        a = fmaxf(a, __shfl_xor(a, 4, 64));
-        const int k = kFracBits - __builtin_amdgcn_frexp_expf(a);
+        float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        am = fmaxf(am, __shfl_xor(am, 1, 64));
+        am = fmaxf(am, __shfl_xor(am, 2, 64));
+        am = fmaxf(am, __shfl_xor(am, 4, 64));
+        const int k = kFracBits - __builtin_amdgcn_frexp_expf(am);
         uint32_t d0, d1, d2;
         transpose3(digits3(v.x, k), digits3(v.y, k), digits3(v.z, k), digits3(v.w, k), d0, d1, d2);
         *reinterpret_cast<uint32_t*>(xp + 4 * tid) = d0;
@@ -571,52 +622,24 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q6k_kernel(const uint8_t* 
     __syncthreads();
 
     // Lane roles as in the Q4_K kernel: column n = row n of the tile, lane group q = run
-    // 4t + q of this wave's super-block in MFMA t.
+    // 4t + q of this wave's super-chunk in MFMA t.
     const bool active = wave < SB;   // uniform
-    const int sb = active ? wave : 0;
+    const int sc = active ? wave : 0;
     const int n = lane & 15, q = lane >> 4;
     v4i a[4];
+    int e[4];
+    float sx[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         a[t] = v4i{0, 0, 0, 0};
-        if ((n >> 2) == q && (n & 3) < 3) a[t] = *reinterpret_cast<const v4i*>(xp + (n & 3) * K + 256 * sb + 64 * t + 16 * q);
+        if ((n >> 2) == q && (n & 3) < 3)
+            a[t] = *reinterpret_cast<const v4i*>(xp + (n & 3) * K + 256 * sc + 64 * t + 16 * q);
+        e[t] = ex[8 * sc + 2 * t + (q >> 1)];
+        sx[t] = sums[16 * sc + 4 * t + q];
     }
-    int e[4];
-    float moff[4];   // -32 * sum(x) over run 4t + q
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        e[t] = ex[8 * sb + 2 * t + (q >> 1)];
-        moff[t] = -32.0f * sums[16 * sb + 4 * t + q];
-    }
-    const uint32_t s_lo = 2u * uint32_t(q >> 1);   // qh bit pair of the low-nibble runs (t even)
 
     auto compute = [&](const uint8_t* tile, float* pt) {
-        const uint8_t* blk = tile + n * row_bytes + sb * kQ6Block;
-        const uint4 scw = lds_seg16(blk + 192);
-        const uint32_t sc4[4] = {scw.x, scw.y, scw.z, scw.w};
-        const float d = half_bits_to_float(uint32_t(*reinterpret_cast<const uint16_t*>(blk + 208)));
-        float acc = 0.f;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint4 ql = lds_seg16(blk + 64 * h + 16 * q);
-            const uint4 qh = lds_seg16(blk + 128 + 32 * h + 16 * (q & 1));
-            const uint32_t L[4] = {ql.x, ql.y, ql.z, ql.w}, H[4] = {qh.x, qh.y, qh.z, qh.w};
-            v4i clo, chi;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                clo[i] = int((L[i] & 0x0F0F0F0Fu) | (((H[i] >> s_lo) & 0x03030303u) << 4));
-                chi[i] = int(((L[i] >> 4) & 0x0F0F0F0Fu) | (((H[i] >> (s_lo + 4)) & 0x03030303u) << 4));
-            }
-            const v4i z = {0, 0, 0, 0};
-            const v4i rlo = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[2 * h], clo, z, 0, 0, 0);
-            const v4i rhi = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[2 * h + 1], chi, z, 0, 0, 0);
-            // signed sub-scales: byte q of dwords 2h and 2h + 1 (arithmetic shift keeps the sign)
-            const float sclo = float(int32_t(sc4[2 * h] << (24 - 8 * q)) >> 24);
-            const float schi = float(int32_t(sc4[2 * h + 1] << (24 - 8 * q)) >> 24);
-            acc = fmaf(sclo, ldexpf(float(combine3(rlo)), e[2 * h]) + moff[2 * h], acc);
-            acc = fmaf(schi, ldexpf(float(combine3(rhi)), e[2 * h + 1]) + moff[2 * h + 1], acc);
-        }
-        const float r = sum_lane_groups(d * acc);
+        const float r = sum_lane_groups(Item::run(tile + n * row_bytes, sc, q, a, e, sx));
         if (q == 0) pt[n * kWaves + wave] = r;
     };
     // Row sums of a tile's partials (wave kWaves - 1, idle in compute when SB < 16):
@@ -690,31 +713,56 @@ int long_tile_rows(int64_t N, int64_t K, int cu_count) {
     return int(tr);
 }
 
-constexpr int kQ6Depth = 2;
+constexpr int kTiledDepth = 2;
+
+int tiled_sb_bytes(int type) { return type == kQ6_K ? TiledItem<kQ6_K>::kSBBytes : 0; }
+
+// Instances for the chunks per lane that rows of kMinSB .. kMaxSB super-chunks need.
+template <int QT, int CPL>
+const void* tiled_instance() {
+    constexpr int lo = (kMinSB * TiledItem<QT>::kSBBytes + kThreads - 1) / kThreads;
+    constexpr int hi = (kMaxSB * TiledItem<QT>::kSBBytes + kThreads - 1) / kThreads;
+    if constexpr (CPL >= lo && CPL <= hi) return reinterpret_cast<const void*>(gemv_tiled_kernel<QT, kTiledDepth, CPL>);
+    return nullptr;
+}
+
+template <int QT>
+const void* tiled_kernel(int cpl) {
+    switch (cpl) {
+        case 2: return tiled_instance<QT, 2>();
+        case 3: return tiled_instance<QT, 3>();
+        case 4: return tiled_instance<QT, 4>();
+        case 5: return tiled_instance<QT, 5>();
+        default: return nullptr;
+    }
+}
+
+const void* tiled_kernel_for(int type, int cpl) { return type == kQ6_K ? tiled_kernel<kQ6_K>(cpl) : nullptr; }
 
 }  // namespace
 
-bool gemv_mfma_q6k_applies(BlockLayout layout, const uint8_t* W, int64_t N, int64_t K, int cu_count) {
+bool gemv_tiled_applies(int type, BlockLayout layout, const uint8_t* W, int64_t N, int64_t K, int cu_count) {
     // GGUF layout, 16-byte aligned matrix, at least two 16-row tiles per CU, 12 to 16
-    // super-blocks per row, and 32-bit buffer offsets.
-    if (layout.stride != kQ6Block || layout.off != 0 || (reinterpret_cast<uintptr_t>(W) & 15)) return false;
+    // super-chunks per row, the matrix ending on a 16-byte boundary (the last chunk is
+    // read whole), and 32-bit buffer offsets.
+    const int sbb = tiled_sb_bytes(type);
+    if (sbb == 0 || layout.stride != sbb * block_values_of(type) / 256 || layout.off != 0) return false;
+    if (reinterpret_cast<uintptr_t>(W) & 15) return false;
     if (N <= 0 || K % 256 || K / 256 < kMinSB || K / 256 > kMaxSB || cu_count <= 0) return false;
     if (N < 2 * kTileRows * int64_t(cu_count)) return false;
-    // The matrix must end on a 16-byte chunk boundary: the last chunk is read whole.
-    const int64_t bytes = N * (K / 256) * kQ6Block;
-    return bytes % 16 == 0 && bytes < int64_t(kQ6PastEnd) - int64_t(kQ6SlotBytes);
+    const int64_t bytes = N * (K / 256) * sbb;
+    return bytes % 16 == 0 && bytes < int64_t(kTiledPastEnd) - int64_t(kTileRows) * kMaxSB * sbb;
 }
 
-hipError_t launch_gemv_mfma_q6k(const uint8_t* W, const float* x, float* y, int64_t N, int64_t K, int cu_count,
-                                hipStream_t s, const char** name) {
+hipError_t launch_gemv_tiled(int type, const uint8_t* W, const float* x, float* y, int64_t N, int64_t K,
+                             int cu_count, hipStream_t s, const char** name) {
     const int64_t T = (N + kTileRows - 1) / kTileRows;
     const int grid = int(T < cu_count ? T : cu_count);
+    int n = int(N), k = int(K), row_bytes = int((K / 256) * tiled_sb_bytes(type));
+    const void* f = tiled_kernel_for(type, (row_bytes + kThreads - 1) / kThreads);   // chunks per lane
+    if (!f) return hipErrorInvalidValue;
     *name = "gemv_mfma<q6_K>";
-    int n = int(N), k = int(K), row_bytes = int((K / 256) * kQ6Block);
     void* args[] = {&W, &x, &y, &n, &k, &row_bytes};
-    // chunks per lane: row_bytes (the tile's 16-byte chunks) over 1024 lanes
-    const void* f = row_bytes > 3 * kThreads ? reinterpret_cast<const void*>(gemv_mfma_q6k_kernel<kQ6Depth, 4>)
-                                             : reinterpret_cast<const void*>(gemv_mfma_q6k_kernel<kQ6Depth, 3>);
     return hipLaunchKernel(f, dim3(grid), dim3(kThreads), args, 0, s);
 }
 

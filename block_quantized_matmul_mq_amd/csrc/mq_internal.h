@@ -55,11 +55,11 @@ hipError_t launch_gemv(int type, BlockLayout layout, const uint8_t* W, const flo
 bool gemv_mfma_applies(int type, int64_t N, int64_t K, int cu_count);
 hipError_t launch_gemv_mfma(const uint8_t* W, const float* x, float* y, int64_t N, int64_t K, int cu_count,
                             hipStream_t s, const char** kernel_name);
-// Q6_K GEMV on int8 matrix cores, whole 16-row tiles streamed through LDS, for wide
-// matrices in the GGUF layout (gemv_mfma.hip).
-bool gemv_mfma_q6k_applies(BlockLayout layout, const uint8_t* W, int64_t N, int64_t K, int cu_count);
-hipError_t launch_gemv_mfma_q6k(const uint8_t* W, const float* x, float* y, int64_t N, int64_t K, int cu_count,
-                                hipStream_t s, const char** kernel_name);
+// GEMV on int8 matrix cores with whole 16-row tiles streamed through LDS, for wide
+// matrices of the other block types in the GGUF layout (gemv_mfma.hip).
+bool gemv_tiled_applies(int type, BlockLayout layout, const uint8_t* W, int64_t N, int64_t K, int cu_count);
+hipError_t launch_gemv_tiled(int type, const uint8_t* W, const float* x, float* y, int64_t N, int64_t K,
+                             int cu_count, hipStream_t s, const char** kernel_name);
 // MMQ work split over bm x 128 output tiles: the first `full` tiles are computed whole;
 // each of the remaining `split_tiles` is cut into `splits` ranges of whole 128-value
 // K-steps, whose f32 partial tiles (mmq_scratch_bytes of scratch) a second launch sums.

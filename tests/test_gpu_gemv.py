@@ -170,3 +170,4 @@ def test_gemv_q6_k_unaligned_end_takes_the_vector_kernel():
     x = synth.activations(1, K, config_index=10, tensor_index=3)[0]
     run_gemv(raw, mq.Q6_K, x, N, K, what="unaligned end")
     assert mq.last_kernel() == "gemv<q6_K>"
+

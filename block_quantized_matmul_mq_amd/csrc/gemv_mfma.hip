@@ -683,6 +683,214 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(const uint8_t* __r
     if (tiles > 0) row_sums(part[(tiles - 1) % 2], tiles - 1);
 }
 
+
+// ------------------------------------------------------------------ Q6_K, a few q8 rows
+// The product of mq_gemm for M <= 8 activation rows already quantized to q8 blocks, on the
+// whole-tile stream above: the weight bytes are read once for all rows.  A is now the
+// rows' int8 codes themselves: lane (i, q) holds, for i / 4 == q, the 16 codes of run
+// 4t + q of activation row i % 4 (+ 4 in the second MFMA of a quarter, for M > 4), so
+// lane (n, q) receives the exact int32 dots of that run with weight row n for four
+// activation rows.  Each result is the run's block dot sum((c - 32) q) directly: for
+// four rows a first MFMA of the same A with B = -32 in every byte seeds the accumulator
+// with -32 sum(q); for eight rows (whose registers are short) B holds the codes minus 32
+// as signed bytes instead.  And
+//   Y[m][n] = sum over runs of d * sc_g * dx[m][block] * dot.
+// Row m's arithmetic does not depend on the other rows or on M: the product of M <= 8
+// rows equals, row by row, the product of each row alone, bit for bit.
+template <int MR, bool DUMP, int CPL>
+__global__ __launch_bounds__(kThreads) void gemv_q8_q6k_kernel(const uint8_t* __restrict__ W,
+                                                               const int8_t* __restrict__ codes,
+                                                               const float* __restrict__ xscale,
+                                                               float* __restrict__ Y, int32_t* __restrict__ dots,
+                                                               int M, int N, int K, int row_bytes) {
+    constexpr int kSlot = tiled_slot_bytes<kQ6_K>();
+    constexpr int H = MR / 4;   // MFMAs per quarter
+    constexpr int kStage = MR * 256 * kMaxSB;
+    static_assert(MR == 4 || MR == 8, "row groups of four");
+    __shared__ __attribute__((aligned(16))) uint8_t slot0[kSlot + 16];
+    __shared__ __attribute__((aligned(16))) uint8_t slot1[kSlot + 16];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kStage];                       // codes [MR][K], rows M.. zero
+    __shared__ __attribute__((aligned(16))) float dxT[8 * kMaxSB][MR];                    // block scales [block][row]
+    __shared__ __attribute__((aligned(16))) float part[2][MR * kTileRows * kWaves];       // [m][row][wave]
+    auto slot = [&](auto b) -> uint8_t* {
+        if constexpr (decltype(b)::value == 0) return slot0;
+        else return slot1;
+    };
+
+    const int SB = K >> 8, KB = K >> 5;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = gridDim.x, w0 = blockIdx.x;
+    const int T = (N + kTileRows - 1) / kTileRows;
+    const int tiles = (T - w0 + G - 1) / G;
+    const uint32_t TB = uint32_t(kTileRows) * uint32_t(row_bytes);
+    const int chunks = row_bytes;
+
+    // The rows' codes and block scales first (loads complete in issue order).
+    constexpr int kCodeLoads = kStage / 16 / kThreads;   // 16-byte chunks per lane
+    uint4 xc[kCodeLoads];
+    const int rowchunks = K >> 4;
+#pragma unroll
+    for (int j = 0; j < kCodeLoads; ++j) {
+        const int c = tid + j * kThreads, r = c / rowchunks;
+        xc[j] = make_uint4(0, 0, 0, 0);
+        if (r < M) xc[j] = reinterpret_cast<const uint4*>(codes)[c];   // rows are contiguous: chunk c of the plane
+    }
+    float dxv = 0.f;
+    const int br = tid / MR, rr = tid % MR;   // dxT entry [br][rr]
+    if (br < KB && rr < M) dxv = xscale[int64_t(rr) * KB + br];
+
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W), 0, N * row_bytes, kBufferWord3);
+    uint4 R[2][CPL];
+    auto issue = [&](auto r, int k) {
+        constexpr int J = decltype(r)::value;
+        const uint32_t base = k < tiles ? uint32_t(w0 + k * G) * TB : kTiledPastEnd;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = tid + j * kThreads;
+            const uint32_t off = c < chunks ? base + 16u * uint32_t(c) : kTiledPastEnd;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
+            R[J][j] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+    };
+    auto store = [&](auto r, auto b) {
+        constexpr int J = decltype(r)::value;
+        uint8_t* dst = slot(b);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = tid + j * kThreads;
+            if (j < CPL - 1 || c < chunks) *reinterpret_cast<uint4*>(dst + 16 * c) = R[J][j];
+        }
+    };
+    asm volatile("s_barrier" ::: "memory");   // every wave's activations requested before any weights
+    issue(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 1>{}, 1);
+
+#pragma unroll
+    for (int j = 0; j < kCodeLoads; ++j) *reinterpret_cast<uint4*>(stage + 16 * (tid + j * kThreads)) = xc[j];
+    if (br < KB) dxT[br][rr] = dxv;
+    __syncthreads();
+
+    const bool active = wave < SB;   // uniform
+    const int sc = active ? wave : 0;
+    const int n = lane & 15, q = lane >> 4;
+    // A operands (read per item: registers are short): lanes with n / 4 == q read row
+    // n % 4 + 4h of the staged codes, the others hold zeros
+    const bool a_lane = (n >> 2) == q;
+    const uint8_t* a_src = stage + (n & 3) * K + 256 * sc + 16 * q;
+
+    auto compute = [&](const uint8_t* tile, float* pt, int k) __attribute__((always_inline)) {
+        const uint8_t* blk = tile + n * row_bytes + sc * TiledItem<kQ6_K>::kSBBytes;
+        const uint4 scw = lds_seg16(blk + 192);
+        const uint32_t sc4[4] = {scw.x, scw.y, scw.z, scw.w};
+        const float d = lds_f16(blk + 208);
+        const uint32_t s_lo = 2u * uint32_t(q >> 1);
+        const int row = (w0 + k * G) * kTileRows + n;
+        float acc[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            // (one half at a time: hoisting the second half's reads over the first would
+            // run out of registers)
+            __builtin_amdgcn_sched_barrier(0);
+            const uint4 ql = lds_seg16(blk + 64 * hh + 16 * q);
+            const uint4 qh = lds_seg16(blk + 128 + 32 * hh + 16 * (q & 1));
+            const uint32_t L[4] = {ql.x, ql.y, ql.z, ql.w}, Hb[4] = {qh.x, qh.y, qh.z, qh.w};
+#pragma unroll
+            for (int part_t = 0; part_t < 2; ++part_t) {
+                __builtin_amdgcn_sched_barrier(0);
+                const int t = 2 * hh + part_t;   // low nibbles, then high nibbles
+                v4i c;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t code = ((L[i] >> (4 * part_t)) & 0x0F0F0F0Fu) |
+                                          (((Hb[i] >> (s_lo + 4 * part_t)) & 0x03030303u) << 4);
+                    if constexpr (MR == 4) {
+                        c[i] = int(code);
+                    } else {
+                        // code - 32 as signed bytes: flip bit 5; a set bit 5 (code < 32) marks
+                        // a negative result, whose bits 6 and 7 are then set as well
+                        const uint32_t u = code ^ 0x20202020u, neg = u & 0x20202020u;
+                        c[i] = int(u | (neg << 1) | (neg << 2));
+                    }
+                }
+                const float f = d * sbyte_f(sc4[t], q);
+                const float* dxb = dxT[8 * sc + 2 * t + (q >> 1)];
+#pragma unroll
+                for (int h = 0; h < H; ++h) {
+                    v4i av = {0, 0, 0, 0};
+                    if (a_lane) av = *reinterpret_cast<const v4i*>(a_src + 4 * h * K + 64 * t);
+                    v4i off = {0, 0, 0, 0};
+                    if constexpr (MR == 4) {
+                        const v4i m32 = {int(0xE0E0E0E0u), int(0xE0E0E0E0u), int(0xE0E0E0E0u), int(0xE0E0E0E0u)};
+                        off = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, m32, off, 0, 0, 0);
+                    }
+                    const v4i C = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, c, off, 0, 0, 0);
+                    const float4 dx4 = *reinterpret_cast<const float4*>(dxb + 4 * h);
+                    const float dxr[4] = {dx4.x, dx4.y, dx4.z, dx4.w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        acc[4 * h + r] = fmaf(f * dxr[r], float(C[r]), acc[4 * h + r]);
+                        if constexpr (DUMP) {
+                            const int m = 4 * h + r;
+                            if (m < M && row < N) dots[(int64_t(m) * N + row) * (K >> 4) + 16 * sc + 4 * t + q] = C[r];
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            const float r = sum_lane_groups(acc[m]);
+            if (q == 0) pt[(m * kTileRows + n) * kWaves + wave] = r;
+        }
+    };
+    // Outputs of a tile (wave kWaves - 1): output o = (m, row r) sums its 16 wave partials.
+    // The block-dot export (DUMP) passes no Y: it writes only the dots.
+    auto row_sums = [&](const float* pt, int k) __attribute__((always_inline)) {
+        if constexpr (DUMP) return;
+        if (wave != kWaves - 1) return;
+#pragma unroll
+        for (int o = lane; o < MR * kTileRows; o += 64) {
+            const int m = o / kTileRows, r = o % kTileRows;
+            const float4* p = reinterpret_cast<const float4*>(pt + o * kWaves);
+            float s4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 v = p[j];
+                s4[j] = ((4 * j < SB ? v.x : 0.f) + (4 * j + 1 < SB ? v.y : 0.f)) +
+                        ((4 * j + 2 < SB ? v.z : 0.f) + (4 * j + 3 < SB ? v.w : 0.f));
+            }
+            const int row = (w0 + k * G) * kTileRows + r;
+            if (m < M && row < N) Y[int64_t(m) * N + row] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        }
+    };
+
+    if (tiles > 0) {
+        store(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+        issue(std::integral_constant<int, 0>{}, 2);
+    }
+    __syncthreads();   // tile 0 stored
+    auto body = [&](auto i_c, int k) __attribute__((always_inline)) {
+        constexpr int I = decltype(i_c)::value;   // k % 2
+        if (active) compute(slot(std::integral_constant<int, I>{}), part[I], k);
+        __builtin_amdgcn_sched_barrier(0);   // keep the phases apart: registers are short
+        if (k > 0) row_sums(part[I ^ 1], k - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + 1 < tiles) {
+            store(std::integral_constant<int, I ^ 1>{}, std::integral_constant<int, I ^ 1>{});
+            issue(std::integral_constant<int, I ^ 1>{}, k + 3);
+        }
+        __syncthreads();
+    };
+    int k0 = 0;
+    for (; k0 + 2 <= tiles; k0 += 2) static_for<2>([&](auto i) { body(i, k0 + decltype(i)::value); });
+    if (k0 < tiles) body(std::integral_constant<int, 0>{}, k0);
+    if (tiles > 0) row_sums(part[(tiles - 1) & 1], tiles - 1);
+}
+
 constexpr int kRing = 4;
 
 struct Plan {
@@ -739,6 +947,15 @@ const void* tiled_kernel(int cpl) {
 
 const void* tiled_kernel_for(int type, int cpl) { return type == kQ6_K ? tiled_kernel<kQ6_K>(cpl) : nullptr; }
 
+template <int MR, bool DUMP>
+const void* q8_q6k_kernel(int cpl) {
+    switch (cpl) {
+        case 3: return reinterpret_cast<const void*>(gemv_q8_q6k_kernel<MR, DUMP, 3>);
+        case 4: return reinterpret_cast<const void*>(gemv_q8_q6k_kernel<MR, DUMP, 4>);
+        default: return nullptr;
+    }
+}
+
 }  // namespace
 
 bool gemv_tiled_applies(int type, BlockLayout layout, const uint8_t* W, int64_t N, int64_t K, int cu_count) {
@@ -765,6 +982,30 @@ hipError_t launch_gemv_tiled(int type, const uint8_t* W, const float* x, float* 
     void* args[] = {&W, &x, &y, &n, &k, &row_bytes};
     return hipLaunchKernel(f, dim3(grid), dim3(kThreads), args, 0, s);
 }
+
+bool gemv_q8_tiled_applies(int type, BlockLayout layout, const uint8_t* W, const int8_t* codes, int64_t M,
+                           int64_t N, int64_t K, int cu_count) {
+    return type == kQ6_K && M >= 1 && M <= 8 && !(reinterpret_cast<uintptr_t>(codes) & 15) &&
+           gemv_tiled_applies(type, layout, W, N, K, cu_count);
+}
+
+hipError_t launch_gemv_q8_tiled(int type, const uint8_t* W, const int8_t* codes, const float* xs, float* Y,
+                                int32_t* dots, int64_t M, int64_t N, int64_t K, int cu_count, hipStream_t s,
+                                const char** name) {
+    if (type != kQ6_K) return hipErrorInvalidValue;
+    const int64_t T = (N + kTileRows - 1) / kTileRows;
+    const int grid = int(T < cu_count ? T : cu_count);
+    int m = int(M), n = int(N), k = int(K), row_bytes = int((K / 256) * TiledItem<kQ6_K>::kSBBytes);
+    const int cpl = (row_bytes + kThreads - 1) / kThreads;
+    const bool dump = dots != nullptr;
+    const void* f = M <= 4 ? (dump ? q8_q6k_kernel<4, true>(cpl) : q8_q6k_kernel<4, false>(cpl))
+                           : (dump ? q8_q6k_kernel<8, true>(cpl) : q8_q6k_kernel<8, false>(cpl));
+    if (!f) return hipErrorInvalidValue;
+    *name = "gemv_q8_mfma<q6_K>";
+    void* args[] = {&W, &codes, &xs, &Y, &dots, &m, &n, &k, &row_bytes};
+    return hipLaunchKernel(f, dim3(grid), dim3(kThreads), args, 0, s);
+}
+
 
 bool gemv_mfma_applies(int type, int64_t N, int64_t K, int cu_count) {
     // Wide matrices: at least two 16-row tiles per CU; or long rows at 8..16 rows per CU.

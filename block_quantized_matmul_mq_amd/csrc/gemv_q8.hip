@@ -423,6 +423,8 @@ hipError_t launch_gemv_q8(int type, BlockLayout lay, const uint8_t* W, const int
                           hipStream_t s, const char** name) {
     const DeviceInfo* info = device_info();
     if (!info) return hipErrorInvalidDevice;
+    if (gemv_q8_tiled_applies(type, lay, W, codes, M, N, K, info->cu_count))
+        return launch_gemv_q8_tiled(type, W, codes, xs, Y, dots, M, N, K, info->cu_count, s, name);
     const int mr = rows_for(M);
     const int vals = unit_values(type);
     const int U = int(K / vals);

@@ -60,6 +60,12 @@ hipError_t launch_gemv_mfma(const uint8_t* W, const float* x, float* y, int64_t 
 bool gemv_tiled_applies(int type, BlockLayout layout, const uint8_t* W, int64_t N, int64_t K, int cu_count);
 hipError_t launch_gemv_tiled(int type, const uint8_t* W, const float* x, float* y, int64_t N, int64_t K,
                              int cu_count, hipStream_t s, const char** kernel_name);
+// mq_gemm for M <= 8 q8 rows on the same whole-tile stream (Q6_K, wide, GGUF layout).
+bool gemv_q8_tiled_applies(int type, BlockLayout layout, const uint8_t* W, const int8_t* codes, int64_t M,
+                           int64_t N, int64_t K, int cu_count);
+hipError_t launch_gemv_q8_tiled(int type, const uint8_t* W, const int8_t* codes, const float* xs, float* Y,
+                                int32_t* dots, int64_t M, int64_t N, int64_t K, int cu_count, hipStream_t s,
+                                const char** kernel_name);
 // MMQ work split over bm x 128 output tiles: the first `full` tiles are computed whole;
 // each of the remaining `split_tiles` is cut into `splits` ranges of whole 128-value
 // K-steps, whose f32 partial tiles (mmq_scratch_bytes of scratch) a second launch sums.

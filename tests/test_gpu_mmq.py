@@ -225,3 +225,21 @@ def test_gemm_config5_m2048_sampled(qtype, N, K, tensor):
     X = synth.activations(2048, K, config_index=4, tensor_index=10 + (K == 13824))
     cols = np.random.default_rng(4).choice(N, 384, replace=False)
     check_gemm(raw, qtype, X, N, K, cols=cols, what="14B prefill M=2048 (sampled cols)")
+
+
+@pytest.mark.parametrize("N,K,kind", [(8192 + 4 * 37, 3584, "random"), (8192 + 16 * 9, 3072, "quantized"),
+                                      (8192 + 16 * 5, 4096, "random")],
+                         ids=["ragged_tile_K3584", "twelve_super_blocks", "sixteen_super_blocks"])
+def test_small_m_q6_k_matrix_core_path(N, K, kind):
+    """Wide Q6_K at M <= 8 takes the whole-tile matrix-core kernel over the q8 rows (one
+    group of four rows for M <= 4, two above): bitwise block dots (the dot of code - 32
+    with the q8 codes per 16-value group) and f32 parity, for M = 1, 3, 4, 5, 8, with a
+    ragged last tile, idle waves (K = 3072) and every wave busy (K = 4096)."""
+    raw = weights(mq.Q6_K, N, K, kind, 130)
+    for i, M in enumerate([1, 3, 4, 5, 8]):
+        X = synth.activations(M, K, config_index=12, tensor_index=80 + i)
+        X[:, 32:64] = 0.0
+        check_blockdots(raw, mq.Q6_K, X, N, K, f"M={M} {kind}")
+        assert mq.last_kernel() == "gemv_q8_mfma<q6_K>", mq.last_kernel()
+        check_gemm(raw, mq.Q6_K, X, N, K, what=f"M={M} {kind}")
+        assert mq.last_kernel() == "gemv_q8_mfma<q6_K>", mq.last_kernel()

@@ -72,6 +72,14 @@ def load():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m block_quantized_matmul_mq_amd.build`")
+        # torch first: its bundled HIP runtime then also serves libmq (libmq's dependency
+        # on libamdhip64.so.7 resolves to the copy already loaded).  Loaded the other way
+        # round, the process would hold two HIP runtimes, and the second one to open the
+        # device finds none.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(lib, name)

@@ -670,16 +670,45 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, float* __restrict__ Y,
                                                             int M, int N, int bm, int tiles_m, int full,
                                                             int split_tiles, int splits) {
+    // Four consecutive elements of one output row per thread (BN is a multiple of 4), the
+    // partials of eight splits loaded before any is added (independent loads in flight),
+    // then added in split order: the same sums, in the same order, as one split at a time.
     const int t = blockIdx.y;
     const int tile = full + t;
     const int m0 = (tile % tiles_m) * bm, n0 = (tile / tiles_m) * BN;
     const int64_t slot = int64_t(bm) * BN;
-    for (int e = blockIdx.x * 256 + threadIdx.x; e < bm * BN; e += gridDim.x * 256) {
+    const int64_t step = int64_t(split_tiles) * slot / 4;   // one split further, in float4
+    for (int e4 = blockIdx.x * 256 + threadIdx.x; e4 < bm * BN / 4; e4 += gridDim.x * 256) {
+        const int e = 4 * e4;
         const int m = m0 + e / BN, n = n0 + e % BN;
         if (m >= M || n >= N) continue;
-        float acc = P[int64_t(t) * slot + e];
-        for (int sp = 1; sp < splits; ++sp) acc += P[(int64_t(sp) * split_tiles + t) * slot + e];
-        Y[int64_t(m) * N + n] = acc;
+        const float4* p = reinterpret_cast<const float4*>(P + int64_t(t) * slot + e);
+        float4 acc = p[0];
+        int sp = 1;
+        for (; sp + 8 <= splits; sp += 8) {
+            float4 v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = p[(sp + j) * step];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                acc.x += v[j].x;
+                acc.y += v[j].y;
+                acc.z += v[j].z;
+                acc.w += v[j].w;
+            }
+        }
+        for (; sp < splits; ++sp) {
+            const float4 v = p[sp * step];
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        float* y = Y + int64_t(m) * N + n;
+        y[0] = acc.x;
+        if (n + 1 < N) y[1] = acc.y;
+        if (n + 2 < N) y[2] = acc.z;
+        if (n + 3 < N) y[3] = acc.w;
     }
 }
 
@@ -743,7 +772,7 @@ hipError_t launch_shaped(const uint8_t* W, const int8_t* codes, const float* xs,
                        plan.split_tiles, plan.splits, plan.steps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.split_tiles == 0) return e;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(BM * BN / 256, plan.split_tiles), dim3(256), 0, s, partial, Y,
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(BM * BN / 1024, plan.split_tiles), dim3(256), 0, s, partial, Y,
                        int(M), int(N), BM, tiles_m, plan.full, plan.split_tiles, plan.splits);
     return hipGetLastError();
 }

@@ -534,6 +534,8 @@ hipError_t launch_gemv(int type, BlockLayout layout, const uint8_t* W, const flo
         return launch_gemv_mfma(W, x, y, N, K, info->cu_count, s, name);
     if (use_mfma() && gemv_tiled_applies(type, layout, W, N, K, info->cu_count))
         return launch_gemv_tiled(type, W, x, y, N, K, info->cu_count, s, name);
+    if (use_mfma() && gemv_wide_applies(type, layout, W, N, K, info->cu_count))
+        return launch_gemv_wide(type, W, x, y, N, K, info->cu_count, s, name);
     int tile = gemv_tile_units(type, K, info->lds_per_block);
     if (tile <= 0) return hipErrorInvalidValue;
     const int vals = unit_values(type);

@@ -39,6 +39,7 @@
 
 #include "mq_device.h"
 #include "mq_internal.h"
+#include "weight_units.h"
 
 namespace mq {
 
@@ -491,6 +492,19 @@ __device__ __forceinline__ uint4 lds_seg16(const uint8_t* p) {
 __device__ __forceinline__ float lds_f16(const uint8_t* p) {
     return half_bits_to_float(uint32_t(*reinterpret_cast<const uint16_t*>(p)));
 }
+// 4 bytes at an even LDS address
+__device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) {
+    const uint32_t a = uint32_t(reinterpret_cast<uintptr_t>(p));
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p - (a & 3));
+    return __builtin_amdgcn_alignbyte(q[1], q[0], a & 3);
+}
+__device__ __forceinline__ v4i as_v4i(uint4 v) { return v4i{int(v.x), int(v.y), int(v.z), int(v.w)}; }
+// the low (hi = 0) or high (hi = 1) nibbles of 16 bytes, one per byte
+__device__ __forceinline__ uint4 nib4(uint4 v, int hi) {
+    const int s = 4 * hi;
+    return make_uint4((v.x >> s) & 0x0F0F0F0Fu, (v.y >> s) & 0x0F0F0F0Fu, (v.z >> s) & 0x0F0F0F0Fu,
+                      (v.w >> s) & 0x0F0F0F0Fu);
+}
 // signed byte k (0..3) of a dword
 __device__ __forceinline__ float sbyte_f(uint32_t v, int k) { return float(int32_t(v << (24 - 8 * k)) >> 24); }
 
@@ -531,6 +545,55 @@ template <> struct TiledItem<kQ6_K> {
         return lds_f16(blk + 208) * acc;
     }
 };
+
+template <> struct TiledItem<kQ8_0> {
+    static constexpr int kSBBytes = 8 * 34;
+    __device__ static float run(const uint8_t* row, int sc, int q, const v4i (&a)[4], const int (&e)[4],
+                                const float (&)[4]) {
+        float acc = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint8_t* blk = row + (8 * sc + 2 * t + (q >> 1)) * 34;   // block of run 4t + q
+            const v4i c = as_v4i(lds_seg16(blk + 2 + 16 * (q & 1)));
+            const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], c, v4i{0, 0, 0, 0}, 0, 0, 0);
+            acc = fmaf(lds_f16(blk), ldexpf(float(combine3(r)), e[t]), acc);
+        }
+        return acc;
+    }
+};
+
+// The 32-value types (Q4_0 routed; written for Q4_1, Q5_0 and Q5_1 as well): run 4t + q is
+// half q % 2 of block 2t + q / 2 of the super-chunk: values 16h + i take the low (h = 0) or
+// high (h = 1) nibble of qs[i] and bit 16h + i of qh.
+template <int QT>
+struct TiledLegacy {
+    using L = Legacy<QT>;
+    static constexpr int kSBBytes = 8 * L::kBytes;
+    __device__ static float run(const uint8_t* row, int sc, int q, const v4i (&a)[4], const int (&e)[4],
+                                const float (&sx)[4]) {
+        constexpr int kQs = 2 + (L::kMin ? 2 : 0) + (L::kHigh ? 4 : 0);   // offset of the code bytes
+        const int h = q & 1;
+        float acc = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint8_t* blk = row + (8 * sc + 2 * t + (q >> 1)) * L::kBytes;
+            uint4 c = nib4(lds_seg16(blk + kQs), h);
+            if constexpr (L::kHigh) {
+                const uint32_t bits = lds_u32(blk + (L::kMin ? 4 : 2)) >> (16 * h);
+                c.x |= spread4(bits & 15u) << 4;
+                c.y |= spread4((bits >> 4) & 15u) << 4;
+                c.z |= spread4((bits >> 8) & 15u) << 4;
+                c.w |= spread4((bits >> 12) & 15u) << 4;
+            }
+            const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], as_v4i(c), v4i{0, 0, 0, 0}, 0, 0, 0);
+            const float cx = ldexpf(float(combine3(r)), e[t]);
+            if constexpr (L::kMin) acc = fmaf(lds_f16(blk + 2), sx[t], fmaf(lds_f16(blk), cx, acc));
+            else acc = fmaf(lds_f16(blk), fmaf(-float(L::kOffset), sx[t], cx), acc);
+        }
+        return acc;
+    }
+};
+template <> struct TiledItem<kQ4_0> : TiledLegacy<kQ4_0> {};
 
 template <int QT>
 constexpr int tiled_slot_bytes() { return kTileRows * kMaxSB * TiledItem<QT>::kSBBytes; }
@@ -891,6 +954,202 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_q6k_kernel(const uint8_t* __
     if (tiles > 0) row_sums(part[(tiles - 1) & 1], tiles - 1);
 }
 
+
+// ------------------------------------------------------------------ wide, per-wave items, Q8_0 and Q4_0
+// The scheme of the Q4_K kernel above for Q8_0 and Q4_0, whose 256-value super-chunks are
+// 272 and 144 bytes, whole numbers of 16-byte chunks: wave w streams super-chunk w of every
+// tile's 16 rows into its own LDS ring with buffer_load ... lds and computes it with the
+// TiledItem of its type (four v_mfma_i32_16x16x64_i8, one per quarter of the
+// super-chunk's 16-value runs).  An item's chunk c is row c / (bytes / 16), bytes
+// 16 (c % (bytes / 16)) of the row's super-chunk, to slot bytes 16 c: 16-byte lanes for
+// whole groups of 64 chunks, then 4-byte lanes (16 chunks per load) for the rest.
+// The same kernel with items for Q4_1, Q5_0, Q5_1 and Q5_K passed the parity tests and ran
+// no faster than the vector kernel (their 160- and 192-byte rows put several of an
+// MFMA's 16 rows on one LDS bank, and Q5_K's unpacking is heavier), so they stay there.
+template <int QT>
+struct WideItem {
+    static constexpr int kSCB = TiledItem<QT>::kSBBytes;   // bytes of one row's super-chunk
+    static constexpr int kCR = kSCB / 16;                   // its 16-byte chunks
+    static constexpr int kChunks = kTileRows * kCR;         // chunks of an item
+    static constexpr int kFull = kChunks / 64;              // 16-byte-lane loads
+    static constexpr int kTail = (kChunks % 64) / 16;       // 4-byte-lane loads
+    static constexpr int kLoads = kFull + kTail;
+    static constexpr int kBytes = kTileRows * kSCB;
+    static_assert(kSCB % 16 == 0 && kChunks % 16 == 0, "whole chunks");
+};
+
+template <int QT, int NB>
+__global__ __launch_bounds__(kThreads) void gemv_wide_kernel(const uint8_t* __restrict__ W,
+                                                             const float* __restrict__ x,
+                                                             float* __restrict__ y, int N, int K,
+                                                             int row_bytes) {
+    using WI = WideItem<QT>;
+    constexpr int kIB = WI::kBytes;
+    // (16 bytes past each ring: a field read as the aligned dwords around it may reach 4
+    // bytes past the last wave's item)
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[kWaves * kIB + 16];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[kWaves * kIB + 16];
+    __shared__ __attribute__((aligned(16))) uint8_t ring2[NB > 2 ? kWaves * kIB + 16 : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t ring3[NB > 3 ? kWaves * kIB + 16 : 16];
+    // x staging (digit planes [3][K], exponents per 32-block, sums per 16-run), then row
+    // partials [tile][row][wave]
+    __shared__ __attribute__((aligned(16))) uint8_t stage_lds[kStageBytes];
+    auto slot = [&](auto b) -> uint8_t* {
+        constexpr int B = decltype(b)::value;
+        if constexpr (B == 0) return ring0;
+        else if constexpr (B == 1) return ring1;
+        else if constexpr (B == 2) return ring2;
+        else return ring3;
+    };
+    int8_t* xp = reinterpret_cast<int8_t*>(stage_lds);
+    int* ex = reinterpret_cast<int*>(stage_lds + 3 * 256 * kMaxSB);
+    float* sums = reinterpret_cast<float*>(ex + 8 * kMaxSB);
+    float* part = reinterpret_cast<float*>(stage_lds);
+    static_assert(3 * 256 * kMaxSB + 8 * kMaxSB * 4 + 16 * kMaxSB * 4 <= kStageBytes, "x staging");
+
+    const int SB = K >> 8;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = gridDim.x, w0 = blockIdx.x;
+    const int TB = kTileRows * row_bytes;
+    const int T = (N + kTileRows - 1) / kTileRows;
+    const int tiles = (T - w0 + G - 1) / G;
+    const bool active = wave < SB;
+
+    const int nquads = K >> 2;
+    float4 xe = {};
+    if (tid < nquads) xe = reinterpret_cast<const float4*>(x)[tid];
+
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W), 0, N * row_bytes, kBufferWord3);
+    // Idle waves issue the same loads, all past the end of the buffer (no data moves).
+    auto chunk_offset = [&](int c) {
+        return active ? uint32_t((c / WI::kCR) * row_bytes + wave * WI::kSCB + 16 * (c % WI::kCR)) : 0x80000000u;
+    };
+    // Load j of an item (at most five): 16-byte lanes for j < kFull (chunks 64 j + lane), then
+    // 4-byte lanes (chunks 64 kFull + 16 (j - kFull) + lane / 4).  Written out with
+    // compile-time guards: loads in a loop here make this compiler drop the kernel's
+    // host-side launch stub.
+    static_assert(WI::kLoads <= 5, "loads per item");
+    auto load_offset = [&](int j) {
+        return j < WI::kFull ? chunk_offset(64 * j + lane)
+                             : chunk_offset(64 * WI::kFull + 16 * (j - WI::kFull) + (lane >> 2)) + 4 * (lane & 3);
+    };
+    const uint32_t vo0 = load_offset(0), vo1 = load_offset(1), vo2 = load_offset(2), vo3 = load_offset(3),
+                   vo4 = load_offset(4);
+    auto load = [&](uint8_t* dst, uint32_t off, auto j_c) {
+        constexpr int j = decltype(j_c)::value, F = WI::kFull;
+        if constexpr (j < F)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(dst + 1024 * j), 16, off, 0, 0, 0);
+        else if constexpr (j < WI::kLoads)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(dst + 1024 * F + 256 * (j - F)), 4, off, 0, 0, 0);
+    };
+    auto issue = [&](auto b, int k) {
+        uint8_t* dst = slot(b) + wave * kIB;
+        const uint32_t base = uint32_t((w0 + k * G) * TB);
+        load(dst, base + vo0, std::integral_constant<int, 0>{});
+        load(dst, base + vo1, std::integral_constant<int, 1>{});
+        load(dst, base + vo2, std::integral_constant<int, 2>{});
+        load(dst, base + vo3, std::integral_constant<int, 3>{});
+        load(dst, base + vo4, std::integral_constant<int, 4>{});
+    };
+    asm volatile("s_barrier" ::: "memory");   // every wave's x requested before any weights
+    static_for<NB - 1>([&](auto b) { issue(b, decltype(b)::value); });
+
+    // Stage x: digit planes, an exponent per 32-block and the f32 sum of every 16-run.
+    if (tid < nquads) {   // uniform per wave: K is a multiple of 256
+        const float4 v = xe;
+        float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        am = fmaxf(am, __shfl_xor(am, 1, 64));
+        am = fmaxf(am, __shfl_xor(am, 2, 64));
+        am = fmaxf(am, __shfl_xor(am, 4, 64));
+        const int k = kFracBits - __builtin_amdgcn_frexp_expf(am);
+        uint32_t d0, d1, d2;
+        transpose3(digits3(v.x, k), digits3(v.y, k), digits3(v.z, k), digits3(v.w, k), d0, d1, d2);
+        *reinterpret_cast<uint32_t*>(xp + 4 * tid) = d0;
+        *reinterpret_cast<uint32_t*>(xp + K + 4 * tid) = d1;
+        *reinterpret_cast<uint32_t*>(xp + 2 * K + 4 * tid) = d2;
+        float sm = (v.x + v.y) + (v.z + v.w);
+        sm += __shfl_xor(sm, 1, 64);
+        sm += __shfl_xor(sm, 2, 64);
+        if ((tid & 3) == 0) sums[tid >> 2] = sm;
+        if ((tid & 7) == 0) ex[tid >> 3] = -k;
+    }
+    wait_barrier<(NB - 1) * WI::kLoads>();   // x staged; the weight loads stay in flight
+
+    const int sc = active ? wave : 0;
+    const int n = lane & 15, q = lane >> 4;
+    v4i a[4];
+    int e[4];
+    float sx[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        a[t] = v4i{0, 0, 0, 0};
+        if ((n >> 2) == q && (n & 3) < 3)
+            a[t] = *reinterpret_cast<const v4i*>(xp + (n & 3) * K + 256 * sc + 64 * t + 16 * q);
+        e[t] = ex[8 * sc + 2 * t + (q >> 1)];
+        sx[t] = sums[16 * sc + 4 * t + q];
+    }
+    wait_barrier<(NB - 1) * WI::kLoads>();   // x no longer read: its LDS now takes the partials
+
+    auto compute = [&](const uint8_t* it, int k) {
+        const float r = sum_lane_groups(TiledItem<QT>::run(it + n * WI::kSCB, 0, q, a, e, sx));
+        if (q == 0) part[(k * kTileRows + n) * kWaves + wave] = r;
+    };
+    constexpr int kInFlight = (NB - 1) * WI::kLoads;
+    static_assert(kInFlight < 16, "vmcnt immediate");
+    auto step = [&](auto b, int k) {
+        constexpr int B = decltype(b)::value;
+        issue(std::integral_constant<int, (B + NB - 1) % NB>{}, k + NB - 1);
+        __builtin_amdgcn_s_waitcnt(kInFlight | 0x0F70);
+        compute(slot(b) + wave * kIB, k);
+    };
+    if (active) {
+        int k0 = 0;
+        for (; k0 + NB <= tiles; k0 += NB) static_for<NB>([&](auto b) { step(b, k0 + decltype(b)::value); });
+        static_for<NB>([&](auto b) {
+            if (k0 + decltype(b)::value < tiles) step(b, k0 + decltype(b)::value);
+        });
+    }
+    wait_barrier<0>();
+
+    const int wl = SB < kWaves ? SB : kWaves;
+    const int r = tid >> 2, j = tid & 3;
+    float s = 0.f;
+    if (r < tiles * kTileRows) {
+        const float4 v = *reinterpret_cast<const float4*>(part + r * kWaves + 4 * j);
+        s = ((4 * j < wl ? v.x : 0.f) + (4 * j + 1 < wl ? v.y : 0.f)) +
+            ((4 * j + 2 < wl ? v.z : 0.f) + (4 * j + 3 < wl ? v.w : 0.f));
+    }
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    if (j == 0 && r < tiles * kTileRows) {
+        const int row = (w0 + (r / kTileRows) * G) * kTileRows + r % kTileRows;
+        if (row < N) y[row] = s;
+    }
+}
+
+// Ring slots per type: as many as the 160 KB of LDS hold next to the x staging (at most 4).
+template <int QT>
+constexpr int wide_ring() {
+    constexpr int fit = (163840 - kStageBytes - 4 * 16) / (kWaves * WideItem<QT>::kBytes);
+    return fit >= 4 ? 4 : fit;
+}
+
+template <int QT>
+const void* wide_instance() {
+    constexpr int nb = wide_ring<QT>();
+    return reinterpret_cast<const void*>(gemv_wide_kernel<QT, nb>);
+}
+
+const void* wide_kernel(int type) {
+    switch (type) {
+        case kQ8_0: return wide_instance<kQ8_0>();
+        case kQ4_0: return wide_instance<kQ4_0>();
+        default: return nullptr;
+    }
+}
+
 constexpr int kRing = 4;
 
 struct Plan {
@@ -1006,6 +1265,49 @@ hipError_t launch_gemv_q8_tiled(int type, const uint8_t* W, const int8_t* codes,
     return hipLaunchKernel(f, dim3(grid), dim3(kThreads), args, 0, s);
 }
 
+
+namespace {
+
+
+int wide_scb(int type) {
+    switch (type) {
+        case kQ8_0: return WideItem<kQ8_0>::kSCB;
+        case kQ4_0: return WideItem<kQ4_0>::kSCB;
+        default: return 0;
+    }
+}
+
+}  // namespace
+
+bool gemv_wide_applies(int type, BlockLayout layout, const uint8_t* W, int64_t N, int64_t K, int cu_count) {
+    // GGUF layout, 16-byte aligned matrix, 12 to 16 super-chunks per row, at least two and
+    // at most kMaxTilesPerGroup 16-row tiles per CU, and 32-bit buffer offsets (the last
+    // prefetch reaches up to five rounds of tiles past the end).
+    const int scb = wide_scb(type);
+    if (scb == 0 || layout.stride != scb * block_values_of(type) / 256 || layout.off != 0) return false;
+    if (reinterpret_cast<uintptr_t>(W) & 15) return false;
+    if (N <= 0 || K % 256 || K / 256 < kMinSB || K / 256 > kMaxSB || cu_count <= 0) return false;
+    if (N < 2 * kTileRows * int64_t(cu_count)) return false;
+    const int64_t T = (N + kTileRows - 1) / kTileRows;
+    const int64_t grid = T < cu_count ? T : cu_count;
+    const int64_t row_bytes = (K / 256) * scb;
+    return (T + grid - 1) / grid <= kMaxTilesPerGroup && (T + 5 * grid) * kTileRows * row_bytes < (int64_t(1) << 31);
+}
+
+hipError_t launch_gemv_wide(int type, const uint8_t* W, const float* x, float* y, int64_t N, int64_t K,
+                            int cu_count, hipStream_t s, const char** name) {
+    const int64_t T = (N + kTileRows - 1) / kTileRows;
+    const int grid = int(T < cu_count ? T : cu_count);
+    int n = int(N), k = int(K), row_bytes = int((K / 256) * wide_scb(type));
+    const void* f = wide_kernel(type);
+    switch (type) {
+        case kQ8_0: *name = "gemv_mfma<q8_0>"; break;
+        case kQ4_0: *name = "gemv_mfma<q4_0>"; break;
+        default: return hipErrorInvalidValue;
+    }
+    void* args[] = {&W, &x, &y, &n, &k, &row_bytes};
+    return hipLaunchKernel(f, dim3(grid), dim3(kThreads), args, 0, s);
+}
 
 bool gemv_mfma_applies(int type, int64_t N, int64_t K, int cu_count) {
     // Wide matrices: at least two 16-row tiles per CU; or long rows at 8..16 rows per CU.

@@ -60,6 +60,11 @@ hipError_t launch_gemv_mfma(const uint8_t* W, const float* x, float* y, int64_t 
 bool gemv_tiled_applies(int type, BlockLayout layout, const uint8_t* W, int64_t N, int64_t K, int cu_count);
 hipError_t launch_gemv_tiled(int type, const uint8_t* W, const float* x, float* y, int64_t N, int64_t K,
                              int cu_count, hipStream_t s, const char** kernel_name);
+// GEMV on int8 matrix cores with per-wave items, for wide Q8_0 and Q4_0 matrices in the
+// GGUF layout (gemv_mfma.hip).
+bool gemv_wide_applies(int type, BlockLayout layout, const uint8_t* W, int64_t N, int64_t K, int cu_count);
+hipError_t launch_gemv_wide(int type, const uint8_t* W, const float* x, float* y, int64_t N, int64_t K,
+                            int cu_count, hipStream_t s, const char** kernel_name);
 // mq_gemm for M <= 8 q8 rows on the same whole-tile stream (Q6_K, wide, GGUF layout).
 bool gemv_q8_tiled_applies(int type, BlockLayout layout, const uint8_t* W, const int8_t* codes, int64_t M,
                            int64_t N, int64_t K, int cu_count);

@@ -171,3 +171,24 @@ def test_gemv_q6_k_unaligned_end_takes_the_vector_kernel():
     run_gemv(raw, mq.Q6_K, x, N, K, what="unaligned end")
     assert mq.last_kernel() == "gemv<q6_K>"
 
+
+
+WIDE = [mq.Q8_0, mq.Q4_0]
+
+
+@pytest.mark.parametrize("qtype", WIDE, ids=[NAMES[t] for t in WIDE])
+@pytest.mark.parametrize("N,K,kind", [(8192 + 4 * 37, 3584, "random"),
+                                      (8192 + 16 * 9 + 5, 3072, "quantized"),
+                                      (8192 + 16 * 5, 4096, "random")],
+                         ids=["ragged_tile_K3584", "twelve_chunks", "sixteen_chunks"])
+def test_gemv_wide_matrix_core_path(qtype, N, K, kind):
+    """Wide Q8_0 and Q4_0 matrices (256-value super-chunks of 272 and 144 bytes, whole
+    16-byte chunks) take the per-wave matrix-core kernel: a ragged last tile, idle waves
+    (K = 3072), every wave busy (K = 4096), random block fields (any code, negative
+    scales and minima), and an x with all-zero and tiny blocks and runs."""
+    raw = weights(qtype, N, K, kind, 12)
+    x = synth.activations(1, K, config_index=10, tensor_index=N % 73)[0]
+    x[32:64] = 0.0
+    x[112:128] *= 1e-30
+    run_gemv(raw, qtype, x, N, K, what=f"{kind} wide")
+    assert mq.last_kernel() == f"gemv_mfma<{NAMES[qtype]}>"

@@ -39,7 +39,6 @@
 
 #include "mq_device.h"
 #include "mq_internal.h"
-#include "weight_units.h"
 
 namespace mq {
 
@@ -492,12 +491,6 @@ __device__ __forceinline__ uint4 lds_seg16(const uint8_t* p) {
 __device__ __forceinline__ float lds_f16(const uint8_t* p) {
     return half_bits_to_float(uint32_t(*reinterpret_cast<const uint16_t*>(p)));
 }
-// 4 bytes at an even LDS address
-__device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) {
-    const uint32_t a = uint32_t(reinterpret_cast<uintptr_t>(p));
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(p - (a & 3));
-    return __builtin_amdgcn_alignbyte(q[1], q[0], a & 3);
-}
 __device__ __forceinline__ v4i as_v4i(uint4 v) { return v4i{int(v.x), int(v.y), int(v.z), int(v.w)}; }
 // the low (hi = 0) or high (hi = 1) nibbles of 16 bytes, one per byte
 __device__ __forceinline__ uint4 nib4(uint4 v, int hi) {
@@ -562,38 +555,25 @@ template <> struct TiledItem<kQ8_0> {
     }
 };
 
-// The 32-value types (Q4_0 routed; written for Q4_1, Q5_0 and Q5_1 as well): run 4t + q is
-// half q % 2 of block 2t + q / 2 of the super-chunk: values 16h + i take the low (h = 0) or
-// high (h = 1) nibble of qs[i] and bit 16h + i of qh.
-template <int QT>
-struct TiledLegacy {
-    using L = Legacy<QT>;
-    static constexpr int kSBBytes = 8 * L::kBytes;
+// Q4_0: run 4t + q is half h = q % 2 of block 2t + q / 2 of the super-chunk, whose values
+// 16h + i take the low (h = 0) or high (h = 1) nibble of qs[i]; the code offset 8 goes
+// through the run's x sum.
+template <> struct TiledItem<kQ4_0> {
+    static constexpr int kSBBytes = 8 * 18;
     __device__ static float run(const uint8_t* row, int sc, int q, const v4i (&a)[4], const int (&e)[4],
                                 const float (&sx)[4]) {
-        constexpr int kQs = 2 + (L::kMin ? 2 : 0) + (L::kHigh ? 4 : 0);   // offset of the code bytes
         const int h = q & 1;
         float acc = 0.f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const uint8_t* blk = row + (8 * sc + 2 * t + (q >> 1)) * L::kBytes;
-            uint4 c = nib4(lds_seg16(blk + kQs), h);
-            if constexpr (L::kHigh) {
-                const uint32_t bits = lds_u32(blk + (L::kMin ? 4 : 2)) >> (16 * h);
-                c.x |= spread4(bits & 15u) << 4;
-                c.y |= spread4((bits >> 4) & 15u) << 4;
-                c.z |= spread4((bits >> 8) & 15u) << 4;
-                c.w |= spread4((bits >> 12) & 15u) << 4;
-            }
-            const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], as_v4i(c), v4i{0, 0, 0, 0}, 0, 0, 0);
-            const float cx = ldexpf(float(combine3(r)), e[t]);
-            if constexpr (L::kMin) acc = fmaf(lds_f16(blk + 2), sx[t], fmaf(lds_f16(blk), cx, acc));
-            else acc = fmaf(lds_f16(blk), fmaf(-float(L::kOffset), sx[t], cx), acc);
+            const uint8_t* blk = row + (8 * sc + 2 * t + (q >> 1)) * 18;
+            const v4i c = as_v4i(nib4(lds_seg16(blk + 2), h));
+            const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], c, v4i{0, 0, 0, 0}, 0, 0, 0);
+            acc = fmaf(lds_f16(blk), fmaf(-8.0f, sx[t], ldexpf(float(combine3(r)), e[t])), acc);
         }
         return acc;
     }
 };
-template <> struct TiledItem<kQ4_0> : TiledLegacy<kQ4_0> {};
 
 template <int QT>
 constexpr int tiled_slot_bytes() { return kTileRows * kMaxSB * TiledItem<QT>::kSBBytes; }

@@ -144,13 +144,17 @@ def test_gemv_q4_k_long_row_matrix_core_path(N, K, kind):
 @pytest.mark.parametrize("N,K,kind,sampled", [(16 * 512 + 4, 3584, "random", False),
                                               (9000, 3072, "quantized", False),
                                               (8192 + 16 * 37, 4096, "random", False),
+                                              (8192 + 8 * 11, 3328, "random", False),
                                               (152064, 3584, "quantized", True)],
-                         ids=["ragged_tile_K3584", "twelve_super_blocks", "sixteen_super_blocks", "vocab_head"])
+                         ids=["ragged_tile_K3584", "twelve_super_blocks", "sixteen_super_blocks",
+                              "odd_row_alignment", "vocab_head"])
 def test_gemv_q6_k_matrix_core_path(N, K, kind, sampled):
     """Wide Q6_K matrices in the GGUF layout (at least two 16-row tiles per CU, 12 to 16
     super-blocks per row, the matrix ending on a 16-byte boundary) take the whole-tile
     matrix-core kernel: a ragged last tile, idle waves (K = 3072), every wave busy
-    (K = 4096), the vocab head, and an x with all-zero and tiny blocks and runs."""
+    (K = 4096), rows of 13 super-blocks (2730 bytes: odd rows start 2 bytes off a dword,
+    so the lanes of one MFMA realign by different amounts), the vocab head, and an x with
+    all-zero and tiny blocks and runs."""
     raw = weights(mq.Q6_K, N, K, kind, 9)
     x = synth.activations(1, K, config_index=10, tensor_index=N % 83)[0]
     x[32:64] = 0.0
@@ -179,8 +183,9 @@ WIDE = [mq.Q8_0, mq.Q4_0]
 @pytest.mark.parametrize("qtype", WIDE, ids=[NAMES[t] for t in WIDE])
 @pytest.mark.parametrize("N,K,kind", [(8192 + 4 * 37, 3584, "random"),
                                       (8192 + 16 * 9 + 5, 3072, "quantized"),
-                                      (8192 + 16 * 5, 4096, "random")],
-                         ids=["ragged_tile_K3584", "twelve_chunks", "sixteen_chunks"])
+                                      (8192 + 16 * 5, 4096, "random"),
+                                      (8192 + 7, 3328, "random")],
+                         ids=["ragged_tile_K3584", "twelve_chunks", "sixteen_chunks", "thirteen_chunks"])
 def test_gemv_wide_matrix_core_path(qtype, N, K, kind):
     """Wide Q8_0 and Q4_0 matrices (256-value super-chunks of 272 and 144 bytes, whole
     16-byte chunks) take the per-wave matrix-core kernel: a ragged last tile, idle waves

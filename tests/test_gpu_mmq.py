@@ -228,8 +228,8 @@ def test_gemm_config5_m2048_sampled(qtype, N, K, tensor):
 
 
 @pytest.mark.parametrize("N,K,kind", [(8192 + 4 * 37, 3584, "random"), (8192 + 16 * 9, 3072, "quantized"),
-                                      (8192 + 16 * 5, 4096, "random")],
-                         ids=["ragged_tile_K3584", "twelve_super_blocks", "sixteen_super_blocks"])
+                                      (8192 + 16 * 5, 4096, "random"), (8192 + 8 * 11, 3328, "random")],
+                         ids=["ragged_tile_K3584", "twelve_super_blocks", "sixteen_super_blocks", "odd_row_alignment"])
 def test_small_m_q6_k_matrix_core_path(N, K, kind):
     """Wide Q6_K at M <= 8 takes the whole-tile matrix-core kernel over the q8 rows (one
     group of four rows for M <= 4, two above): bitwise block dots (the dot of code - 32

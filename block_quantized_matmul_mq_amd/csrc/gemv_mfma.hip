@@ -472,11 +472,12 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_long_kernel(const uint
 // Blocks start at even byte offsets in LDS; each 16-byte field is read as the five
 // aligned dwords that cover it and realigned with v_alignbyte.
 //
-// The kernel is written for any block type through TiledItem (bytes per 256 values and
-// the lane's share of a super-chunk).  Q8_0, Q4_0, Q4_1, Q5_0, Q5_1 and Q5_K were built
-// this way, passed the parity tests and measured slower than the vector kernel on the
-// 7B ffn_up shape (their decode is light, and the per-tile barrier and realignment cost
-// more than they save), so only Q6_K is routed here.
+// The kernel takes any block type through TiledItem (bytes per 256 values and the lane's
+// share of a super-chunk; the per-wave kernel further down uses the Q8_0 and Q4_0 items).
+// Q8_0, Q4_0, Q4_1, Q5_0, Q5_1 and Q5_K run through this whole-tile stream passed the
+// parity tests but measured slower than the vector kernel on the 7B ffn_up shape (their
+// decode is light, and the per-tile barrier and realignment cost more than they save), so
+// only Q6_K is routed here.
 constexpr uint32_t kTiledPastEnd = 0x80000000u;   // a buffer offset past the end of any matrix this kernel takes
 
 // 16 bytes at an even LDS address: the five aligned dwords that cover them, realigned

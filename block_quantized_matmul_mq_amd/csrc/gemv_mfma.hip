@@ -1110,11 +1110,13 @@ __global__ __launch_bounds__(kThreads) void gemv_wide_kernel(const uint8_t* __re
     }
 }
 
-// Ring slots per type: as many as the 160 KB of LDS hold next to the x staging (at most 4).
+// Ring slots per type: two (one item in flight while the other is computed) where the 160 KB
+// of LDS hold them next to the x staging.  As for Q4_K, a third slot was measured slower
+// (Q4_0 on the 7B ffn_up shape: 10.9 us with two slots, 12.0 with three).
 template <int QT>
 constexpr int wide_ring() {
     constexpr int fit = (163840 - kStageBytes - 4 * 16) / (kWaves * WideItem<QT>::kBytes);
-    return fit >= 4 ? 4 : fit;
+    return fit >= 2 ? 2 : fit;
 }
 
 template <int QT>
@@ -1131,7 +1133,12 @@ const void* wide_kernel(int type) {
     }
 }
 
-constexpr int kRing = 4;
+// Two slots: one item in flight while the wave computes the other.  Deeper rings were
+// measured slower (7B ffn_up 18944 x 3584: 9.7 us with two slots, 9.8 with three, 10.9 with
+// four): more items in flight per wave keep more tile windows of the matrix open at once,
+// and every wave has to get all of its first items accepted by the memory pipeline before
+// the workgroup barrier of the x staging, so the first compute starts later.
+constexpr int kRing = 2;
 
 struct Plan {
     int grid = 0;

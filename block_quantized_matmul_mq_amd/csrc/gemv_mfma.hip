@@ -1168,7 +1168,9 @@ int long_tile_rows(int64_t N, int64_t K, int cu_count) {
     return int(tr);
 }
 
-constexpr int kTiledDepth = 2;
+// One tile ahead in registers: two were measured slower (the Q6_K vocab head 152064 x 3584:
+// 76.3 against 81.8 us; 8192 x 3584: 8.6 against 9.8 us), as with the per-wave rings above.
+constexpr int kTiledDepth = 1;
 
 int tiled_sb_bytes(int type) { return type == kQ6_K ? TiledItem<kQ6_K>::kSBBytes : 0; }
 

@@ -478,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_long_kernel(const uint
 // aligned dwords that cover it and realigned with v_alignbyte.
 //
 // The kernel takes any block type through TiledItem (bytes per 256 values and the lane's
-// share of a super-chunk; the per-wave kernel further down uses the Q8_0 and Q4_0 items).
+// share of a super-chunk; the per-wave kernel further down uses the Q8_0, Q4_0 and Q5_0 items).
 // Q8_0, Q4_0, Q4_1, Q5_0, Q5_1 and Q5_K run through this whole-tile stream passed the
 // parity tests but measured slower than the vector kernel on the 7B ffn_up shape (their
 // decode is light, and the per-tile barrier and realignment cost more than they save), so
@@ -576,6 +576,39 @@ template <> struct TiledItem<kQ4_0> {
             const v4i c = as_v4i(nib4(lds_seg16(blk + 2), h));
             const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], c, v4i{0, 0, 0, 0}, 0, 0, 0);
             acc = fmaf(lds_f16(blk), fmaf(-8.0f, sx[t], ldexpf(float(combine3(r)), e[t])), acc);
+        }
+        return acc;
+    }
+};
+
+// Q5_0 (22-byte blocks: f16 d, 4 bytes of high bits, 16 bytes of nibbles): values 16h + i
+// take nibble h of byte i and bit 16h + i of the high-bit word as their fifth bit, and the
+// value is d * (code - 16).  Blocks start at even LDS offsets, so the high-bit word is read
+// as the two aligned dwords around it.
+__device__ __forceinline__ uint32_t lds_u32_a2(const uint8_t* p) {
+    const uint32_t a = uint32_t(reinterpret_cast<uintptr_t>(p));
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p - (a & 3));
+    return __builtin_amdgcn_alignbyte(q[1], q[0], a & 3);
+}
+// bits 0..3 of v to bit 0 of bytes 0..3
+__device__ __forceinline__ uint32_t bits_to_bytes4(uint32_t v) { return (v * 0x00204081u) & 0x01010101u; }
+template <> struct TiledItem<kQ5_0> {
+    static constexpr int kSBBytes = 8 * 22;
+    __device__ static float run(const uint8_t* row, int sc, int q, const v4i (&a)[4], const int (&e)[4],
+                                const float (&sx)[4]) {
+        const int h = q & 1;
+        float acc = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint8_t* blk = row + (8 * sc + 2 * t + (q >> 1)) * 22;
+            uint4 c = nib4(lds_seg16(blk + 6), h);
+            const uint32_t bits = lds_u32_a2(blk + 2) >> (16 * h);
+            c.x |= bits_to_bytes4(bits & 15u) << 4;
+            c.y |= bits_to_bytes4((bits >> 4) & 15u) << 4;
+            c.z |= bits_to_bytes4((bits >> 8) & 15u) << 4;
+            c.w |= bits_to_bytes4((bits >> 12) & 15u) << 4;
+            const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], as_v4i(c), v4i{0, 0, 0, 0}, 0, 0, 0);
+            acc = fmaf(lds_f16(blk), fmaf(-16.0f, sx[t], ldexpf(float(combine3(r)), e[t])), acc);
         }
         return acc;
     }
@@ -945,9 +978,9 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_q6k_kernel(const uint8_t* __
 }
 
 
-// ------------------------------------------------------------------ wide, per-wave items, Q8_0 and Q4_0
-// The scheme of the Q4_K kernel above for Q8_0 and Q4_0, whose 256-value super-chunks are
-// 272 and 144 bytes, whole numbers of 16-byte chunks: wave w streams super-chunk w of every
+// ------------------------------------------------------------------ wide, per-wave items, Q8_0, Q4_0, Q5_0
+// The scheme of the Q4_K kernel above for Q8_0, Q4_0 and Q5_0, whose 256-value super-chunks
+// are 272, 144 and 176 bytes, whole numbers of 16-byte chunks: wave w streams super-chunk w of every
 // tile's 16 rows into its own LDS ring with buffer_load ... lds and computes it with the
 // TiledItem of its type (four v_mfma_i32_16x16x64_i8, one per quarter of the
 // super-chunk's 16-value runs).  An item's chunk c is row c / (bytes / 16), bytes
@@ -1138,6 +1171,7 @@ const void* wide_kernel(int type) {
     switch (type) {
         case kQ8_0: return wide_instance<kQ8_0>();
         case kQ4_0: return wide_instance<kQ4_0>();
+        case kQ5_0: return wide_instance<kQ5_0>();
         default: return nullptr;
     }
 }
@@ -1272,6 +1306,7 @@ int wide_scb(int type) {
     switch (type) {
         case kQ8_0: return WideItem<kQ8_0>::kSCB;
         case kQ4_0: return WideItem<kQ4_0>::kSCB;
+        case kQ5_0: return WideItem<kQ5_0>::kSCB;
         default: return 0;
     }
 }
@@ -1302,6 +1337,7 @@ hipError_t launch_gemv_wide(int type, const uint8_t* W, const float* x, float* y
     switch (type) {
         case kQ8_0: *name = "gemv_mfma<q8_0>"; break;
         case kQ4_0: *name = "gemv_mfma<q4_0>"; break;
+        case kQ5_0: *name = "gemv_mfma<q5_0>"; break;
         default: return hipErrorInvalidValue;
     }
     void* args[] = {&W, &x, &y, &n, &k, &row_bytes};

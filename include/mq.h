@@ -218,8 +218,8 @@ int mq_device_lds_bytes(void);
  *   mq_gemv: "gemv_mfma<q4_K>" (wide: at least two 16-row tiles per CU, 12..16
  *     super-blocks per row), "gemv_mfma_long<q4_K>" (more than 16 super-blocks,
  *     8..16 rows per CU), "gemv_mfma<q6_K>" (wide, GGUF layout, matrix ending
- *     on a 16-byte boundary), "gemv_mfma<q8_0>" / "gemv_mfma<q4_0>" (wide,
- *     GGUF layout), else "gemv<type>" (with " repacked" for MQ_REPACKED);
+ *     on a 16-byte boundary), "gemv_mfma<q8_0>" / "gemv_mfma<q4_0>" /
+ *     "gemv_mfma<q5_0>" (wide, GGUF layout), else "gemv<type>" (with " repacked" for MQ_REPACKED);
  *   mq_gemm: "gemv_q8_mfma<q6_K>" (M <= 8, Q6_K, as gemv_mfma<q6_K>),
  *     "gemv_q8<type>" (other M <= 8 shapes that fit LDS), else "mmq<type>". */
 const char* mq_last_kernel(void);

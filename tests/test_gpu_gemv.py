@@ -177,7 +177,7 @@ def test_gemv_q6_k_unaligned_end_takes_the_vector_kernel():
 
 
 
-WIDE = [mq.Q8_0, mq.Q4_0]
+WIDE = [mq.Q8_0, mq.Q4_0, mq.Q5_0]
 
 
 @pytest.mark.parametrize("qtype", WIDE, ids=[NAMES[t] for t in WIDE])
@@ -187,8 +187,8 @@ WIDE = [mq.Q8_0, mq.Q4_0]
                                       (8192 + 7, 3328, "random")],
                          ids=["ragged_tile_K3584", "twelve_chunks", "sixteen_chunks", "thirteen_chunks"])
 def test_gemv_wide_matrix_core_path(qtype, N, K, kind):
-    """Wide Q8_0 and Q4_0 matrices (256-value super-chunks of 272 and 144 bytes, whole
-    16-byte chunks) take the per-wave matrix-core kernel: a ragged last tile, idle waves
+    """Wide Q8_0, Q4_0 and Q5_0 matrices (256-value super-chunks of 272, 144 and 176 bytes,
+    whole 16-byte chunks) take the per-wave matrix-core kernel: a ragged last tile, idle waves
     (K = 3072), every wave busy (K = 4096), random block fields (any code, negative
     scales and minima), and an x with all-zero and tiny blocks and runs."""
     raw = weights(qtype, N, K, kind, 12)

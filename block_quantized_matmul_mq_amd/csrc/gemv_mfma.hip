@@ -98,8 +98,17 @@ __device__ __forceinline__ uint32_t digits3(float x, int k) {
     return (__float_as_uint(f) - 0x4ABF7F80u) ^ 0x00808080u;
 }
 
+// The three digit-plane sums of a run as one int32: exact while |sum code * v| < 2^31, which
+// holds for unsigned codes of up to 6 bits over runs of at most 16 values (16 * 63 * 2^21 <
+// 2^31) and for Q4_K's 4-bit codes over 32 values.  Signed 8-bit codes (Q8_0) can reach
+// 16 * 128 * 2^21 = 2^32 and take combine3f.
 __device__ __forceinline__ int combine3(const v4i c) {
-    return (((c[2] << 8) + c[1]) << 8) + c[0];   // exact: |sum code * v| <= 32 * 15 * 2^21 < 2^31
+    return (((c[2] << 8) + c[1]) << 8) + c[0];
+}
+// The same sum in f32 (each plane sum is exact in int32; the combination is rounded once
+// per term, f32-grade).
+__device__ __forceinline__ float combine3f(const v4i c) {
+    return fmaf(float(c[2]), 65536.0f, fmaf(float(c[1]), 256.0f, float(c[0])));
 }
 
 // Sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (v_permlane16_swap, v_permlane32_swap).
@@ -555,7 +564,7 @@ template <> struct TiledItem<kQ8_0> {
             const uint8_t* blk = row + (8 * sc + 2 * t + (q >> 1)) * 34;   // block of run 4t + q
             const v4i c = as_v4i(lds_seg16(blk + 2 + 16 * (q & 1)));
             const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], c, v4i{0, 0, 0, 0}, 0, 0, 0);
-            acc = fmaf(lds_f16(blk), ldexpf(float(combine3(r)), e[t]), acc);
+            acc = fmaf(lds_f16(blk), ldexpf(combine3f(r), e[t]), acc);
         }
         return acc;
     }
@@ -986,9 +995,11 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_q6k_kernel(const uint8_t* __
 // super-chunk's 16-value runs).  An item's chunk c is row c / (bytes / 16), bytes
 // 16 (c % (bytes / 16)) of the row's super-chunk, to slot bytes 16 c: 16-byte lanes for
 // whole groups of 64 chunks, then 4-byte lanes (16 chunks per load) for the rest.
-// The same kernel with items for Q4_1, Q5_0, Q5_1 and Q5_K passed the parity tests and ran
-// no faster than the vector kernel (their 160- and 192-byte rows put several of an
-// MFMA's 16 rows on one LDS bank, and Q5_K's unpacking is heavier), so they stay there.
+// Q8_0, Q4_0 and Q5_0 run here (on the 7B ffn_up shape Q5_0 takes 14.1 us against 16.4 us
+// on the vector kernel).  The same kernel with items for Q4_1, Q5_1 and Q5_K passed the
+// parity tests and ran no faster than the vector kernel (their 160- and 192-byte rows put
+// several of an MFMA's 16 rows on one LDS bank, and Q5_K's unpacking is heavier), so they
+// stay there.
 template <int QT>
 struct WideItem {
     static constexpr int kSCB = TiledItem<QT>::kSBBytes;   // bytes of one row's super-chunk

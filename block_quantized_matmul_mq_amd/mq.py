@@ -109,6 +109,50 @@ def _stream(stream):
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _refuse(code, fn, msg):
+    raise MQError(code, f"{fn}: {msg}")
+
+
+def _contiguous(t, fn, name):
+    if not t.is_contiguous():
+        _refuse(-1, fn, f"{name} must be contiguous")
+
+
+def _weights(W, qtype, N, K, fn):
+    """W must hold exactly the payload of an N x K matrix of qtype (the exact-length gate)."""
+    need = weight_bytes(qtype, N, K)
+    if need == 0:
+        _refuse(-3, fn, f"type {qtype} with N={N} K={K} has no payload size (type or K invalid)")
+    _contiguous(W, fn, "W")
+    if _nbytes(W) != need:
+        _refuse(-4, fn, f"W holds {_nbytes(W)} bytes, an {N} x {K} type-{qtype} payload is exactly {need}")
+
+
+def _f32(t, numel, fn, name):
+    import torch
+    if t.dtype != torch.float32:
+        _refuse(-1, fn, f"{name} must be float32, not {t.dtype}")
+    _contiguous(t, fn, name)
+    if t.numel() != numel:
+        _refuse(-4, fn, f"{name} has {t.numel()} elements, {numel} expected")
+
+
+def _buffer(t, min_bytes, fn, name):
+    _contiguous(t, fn, name)
+    if _nbytes(t) < min_bytes:
+        _refuse(-4, fn, f"{name} holds {_nbytes(t)} bytes, {min_bytes} required")
+
+
+def _same_device(fn, *tensors):
+    devs = {(t.device.type, t.device.index) for t in tensors}
+    if len(devs) != 1 or next(iter(devs))[0] != "cuda":
+        _refuse(-6, fn, f"every tensor must be on one GPU device, got {sorted(map(str, devs))}")
+
+
 def init(device=0):
     _check(load().mq_init(device))
 
@@ -124,10 +168,15 @@ def repack_bytes(qtype, N, K):
 def repack(W, qtype, N, K, Wr=None, stream=None):
     """The repacked layout of a GGUF payload W (uint8 CUDA tensor); use with qtype | REPACKED."""
     import torch
+    _weights(W, qtype, N, K, "repack")
+    need = repack_bytes(qtype, N, K)
     if Wr is None:
-        Wr = torch.empty(repack_bytes(qtype, N, K), dtype=torch.uint8, device=W.device)
-    _check(load().mq_repack(ctypes.c_void_p(W.data_ptr()), qtype, N, K, W.numel() * W.element_size(),
-                            ctypes.c_void_p(Wr.data_ptr()), Wr.numel() * Wr.element_size(), _stream(stream)))
+        Wr = torch.empty(need, dtype=torch.uint8, device=W.device)
+    else:
+        _buffer(Wr, need, "repack", "Wr")
+    _same_device("repack", W, Wr)
+    _check(load().mq_repack(ctypes.c_void_p(W.data_ptr()), qtype, N, K, _nbytes(W),
+                            ctypes.c_void_p(Wr.data_ptr()), _nbytes(Wr), _stream(stream)))
     return Wr
 
 
@@ -148,9 +197,18 @@ def gemm_scratch_bytes(qtype, M, N, K):
 def quantize_act(X, Xq=None, stream=None):
     """X: f32 [M, K] CUDA tensor -> Xq: uint8 plane of act_bytes(M, K) bytes."""
     import torch
+    if X.dim() != 2:
+        _refuse(-1, "quantize_act", f"X must be 2-D [M, K], not {tuple(X.shape)}")
     M, K = X.shape
+    _f32(X, M * K, "quantize_act", "X")
+    need = act_bytes(M, K)
+    if need == 0:
+        _refuse(-2, "quantize_act", f"K={K} is not a positive multiple of 32")
     if Xq is None:
-        Xq = torch.empty(act_bytes(M, K), dtype=torch.uint8, device=X.device)
+        Xq = torch.empty(need, dtype=torch.uint8, device=X.device)
+    else:
+        _buffer(Xq, need, "quantize_act", "Xq")
+    _same_device("quantize_act", X, Xq)
     _check(load().mq_quantize_act(ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(Xq.data_ptr()), M, K,
                                   _stream(stream)))
     return Xq
@@ -170,23 +228,44 @@ def split_act(Xq, M, K):
 def gemv(W, qtype, x, N, K, y=None, stream=None):
     """y[N] = deq(W) @ x for a uint8 GGUF payload W and f32 x[K] (CUDA tensors)."""
     import torch
+    _weights(W, qtype, N, K, "gemv")
+    _f32(x, K, "gemv", "x")
     if y is None:
         y = torch.empty(N, dtype=torch.float32, device=x.device)
+    else:
+        _f32(y, N, "gemv", "y")
+    _same_device("gemv", W, x, y)
     _check(load().mq_gemv(ctypes.c_void_p(W.data_ptr()), qtype, ctypes.c_void_p(x.data_ptr()),
                           ctypes.c_void_p(y.data_ptr()), N, K, _stream(stream)))
     return y
 
 
+def _act_plane(Xq, M, K, fn):
+    need = act_bytes(M, K)
+    if need == 0:
+        _refuse(-2, fn, f"M={M} K={K}: K is not a positive multiple of 32")
+    _buffer(Xq, need, fn, "Xq")
+
+
 def gemm(W, qtype, Xq, M, N, K, Y=None, scratch=None, stream=None):
     """Y[M, N] from a quantized activation plane Xq and weights W (CUDA tensors)."""
     import torch
+    _weights(W, qtype, N, K, "gemm")
+    _act_plane(Xq, M, K, "gemm")
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+    else:
+        _f32(Y, M * N, "gemm", "Y")
     need = gemm_scratch_bytes(qtype, M, N, K)
     if scratch is None and need:
-        scratch = torch.empty(need, dtype=torch.uint8, device=Xq.device)
+        scratch = torch.zeros(need, dtype=torch.uint8, device=Xq.device)
+    tensors = [W, Xq, Y]
+    if scratch is not None:
+        _buffer(scratch, need, "gemm", "scratch")
+        tensors.append(scratch)
+    _same_device("gemm", *tensors)
     sp = ctypes.c_void_p(scratch.data_ptr()) if scratch is not None else ctypes.c_void_p(0)
-    sb = scratch.numel() * scratch.element_size() if scratch is not None else 0
+    sb = _nbytes(scratch) if scratch is not None else 0
     _check(load().mq_gemm(ctypes.c_void_p(W.data_ptr()), qtype, ctypes.c_void_p(Xq.data_ptr()),
                           ctypes.c_void_p(Y.data_ptr()), M, N, K, sp, sb, _stream(stream)))
     return Y
@@ -195,9 +274,18 @@ def gemm(W, qtype, Xq, M, N, K, Y=None, scratch=None, stream=None):
 def gemm_blockdots(W, qtype, Xq, M, N, K, D=None, stream=None):
     """Exact int32 block dots [M, N, G] of the MMQ kernel (G = K/32, or K/16 for Q6_K)."""
     import torch
+    _weights(W, qtype, N, K, "gemm_blockdots")
+    _act_plane(Xq, M, K, "gemm_blockdots")
     G = K // 16 if (qtype & ~REPACKED) == Q6_K else K // 32
     if D is None:
         D = torch.empty((M, N, G), dtype=torch.int32, device=Xq.device)
+    else:
+        if D.dtype != torch.int32:
+            _refuse(-1, "gemm_blockdots", f"D must be int32, not {D.dtype}")
+        _contiguous(D, "gemm_blockdots", "D")
+        if D.numel() != M * N * G:
+            _refuse(-4, "gemm_blockdots", f"D has {D.numel()} elements, {M * N * G} expected")
+    _same_device("gemm_blockdots", W, Xq, D)
     _check(load().mq_debug_gemm_blockdots(ctypes.c_void_p(W.data_ptr()), qtype, ctypes.c_void_p(Xq.data_ptr()),
                                           ctypes.c_void_p(D.data_ptr()), M, N, K, _stream(stream)))
     return D

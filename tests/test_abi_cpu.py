@@ -178,3 +178,54 @@ def test_init_refuses_a_bad_device_index():
     lib = mq.load()
     assert lib.mq_init(-1) == -1
     assert lib.mq_init(10 ** 6) == -1
+
+
+def _refused(code, fn, *args, **kw):
+    with pytest.raises(mq.MQError) as ei:
+        fn(*args, **kw)
+    assert ei.value.code == code, str(ei.value)
+    return str(ei.value)
+
+
+def test_binding_refuses_bad_tensors_before_any_call():
+    """The binding checks every tensor against the call's sizes, dtypes, contiguity and
+    device before handing its pointer to the library (the C ABI takes no lengths for W,
+    x, Xq or Y, so a mismatch would otherwise read or write past a buffer)."""
+    import torch
+    N, K, M = 8, 256, 3
+    W = torch.zeros(mq.weight_bytes(mq.Q4_K, N, K), dtype=torch.uint8)
+    x = torch.zeros(K)
+    # GEMV: exact payload length, x f32 of K, y f32 of N, contiguity, then the device
+    assert "exactly 1152" in _refused(-4, mq.gemv, W[:-1], mq.Q4_K, x, N, K)
+    _refused(-4, mq.gemv, torch.zeros(len(W) + 16, dtype=torch.uint8), mq.Q4_K, x, N, K)
+    _refused(-3, mq.gemv, W, mq.Q4_K, x, N, 100)                       # K not a whole block
+    _refused(-1, mq.gemv, W, mq.Q4_K, x.double(), N, K)
+    _refused(-1, mq.gemv, W, mq.Q4_K, x.half(), N, K)
+    _refused(-4, mq.gemv, W, mq.Q4_K, x[:-1], N, K)
+    _refused(-1, mq.gemv, W, mq.Q4_K, torch.zeros(2 * K)[::2], N, K)   # strided x
+    _refused(-4, mq.gemv, W, mq.Q4_K, x, N, K, y=torch.zeros(N - 1))
+    _refused(-1, mq.gemv, W, mq.Q4_K, x, N, K, y=torch.zeros(N, dtype=torch.float64))
+    assert "one GPU device" in _refused(-6, mq.gemv, W, mq.Q4_K, x, N, K, y=torch.zeros(N))
+    # quantize_act: 2-D f32 X, K a multiple of 32, Xq large enough
+    X = torch.zeros(M, K)
+    _refused(-1, mq.quantize_act, X.reshape(-1))
+    _refused(-1, mq.quantize_act, X.double())
+    _refused(-1, mq.quantize_act, X.t())
+    _refused(-2, mq.quantize_act, torch.zeros(M, 48))
+    _refused(-4, mq.quantize_act, X, Xq=torch.zeros(mq.act_bytes(M, K) - 1, dtype=torch.uint8))
+    _refused(-6, mq.quantize_act, X, Xq=torch.zeros(mq.act_bytes(M, K), dtype=torch.uint8))
+    # GEMM and the block-dot export: the plane of M x K, Y f32 of M x N, D int32 of M x N x G
+    Xq = torch.zeros(mq.act_bytes(M, K), dtype=torch.uint8)
+    _refused(-4, mq.gemm, W[:-1], mq.Q4_K, Xq, M, N, K)
+    _refused(-4, mq.gemm, W, mq.Q4_K, Xq[:-1], M, N, K)
+    _refused(-4, mq.gemm, W, mq.Q4_K, Xq, M + 1, N, K)                 # plane of fewer rows
+    _refused(-4, mq.gemm, W, mq.Q4_K, Xq, M, N, K, Y=torch.zeros(M, N - 1))
+    _refused(-1, mq.gemm, W, mq.Q4_K, Xq, M, N, K, Y=torch.zeros(N, M).t())
+    _refused(-6, mq.gemm, W, mq.Q4_K, Xq, M, N, K, Y=torch.zeros(M, N))
+    _refused(-1, mq.gemm_blockdots, W, mq.Q4_K, Xq, M, N, K, D=torch.zeros(M, N, K // 32))
+    _refused(-4, mq.gemm_blockdots, W, mq.Q4_K, Xq, M, N, K, D=torch.zeros(M, N, 1, dtype=torch.int32))
+    # repack: exact payload, output large enough
+    W6 = torch.zeros(mq.weight_bytes(mq.Q6_K, N, K), dtype=torch.uint8)
+    _refused(-4, mq.repack, W6[:-2], mq.Q6_K, N, K)
+    _refused(-4, mq.repack, W6, mq.Q6_K, N, K, Wr=torch.zeros(mq.repack_bytes(mq.Q6_K, N, K) - 1,
+                                                                dtype=torch.uint8))

@@ -197,3 +197,32 @@ def test_gemv_wide_matrix_core_path(qtype, N, K, kind):
     x[112:128] *= 1e-30
     run_gemv(raw, qtype, x, N, K, what=f"{kind} wide")
     assert mq.last_kernel() == f"gemv_mfma<{NAMES[qtype]}>"
+
+
+def test_gemv_q8_0_wide_saturated_codes():
+    """Wide Q8_0 runs reach |sum code * v| = 16 * 128 * 2^21 = 2^32 when every code of a
+    16-value run is +-127 or -128 and x is constant just below a power of two in a block
+    (the run's 21-bit digit form is then near its maximum): the run's three digit-plane
+    sums must be combined without int32 wrap-around.  Rows: all +127, all -128, alternating
+    runs of both, and random codes with -128 included; x blocks constant at 0.9, -0.75 and
+    0.99999, plus N(0, 1) blocks."""
+    N, K = 8192 + 64, 3584
+    nb = K // 32
+    rng = np.random.default_rng(77)
+    codes = rng.integers(-128, 128, size=(N, nb, 32), dtype=np.int64)
+    codes[0::4] = 127
+    codes[1::4] = -128
+    codes[2::4, :, :16] = 127
+    codes[2::4, :, 16:] = -128
+    d = np.full((N, nb), 0.0078125, dtype=np.float16)   # 2^-7, exact in f16
+    d[3::4] = np.float16(-0.01)
+    raw = np.zeros((N, nb, 34), dtype=np.uint8)
+    raw[:, :, 0:2] = d[..., None].view(np.uint8).reshape(N, nb, 2)
+    raw[:, :, 2:] = codes.astype(np.int8).view(np.uint8)
+    x = synth.activations(1, K, config_index=10, tensor_index=41)[0]
+    xb = x.reshape(nb, 32)
+    xb[0::3] = np.float32(0.9)
+    xb[1::3] = np.float32(-0.75)
+    xb[2::6] = np.float32(0.99999)
+    run_gemv(raw.reshape(-1), mq.Q8_0, x, N, K, what="saturated codes, wide")
+    assert mq.last_kernel() == "gemv_mfma<q8_0>"

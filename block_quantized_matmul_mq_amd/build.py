@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["mq_api.hip", "quantize_act.hip", "gemv.hip", "gemv_mfma.hip", "gemv_q8.hip", "mmq.hip", "repack.hip"]
+SOURCES = ["mq_api.hip", "quantize_act.hip", "gemv.hip", "gemv_mfma.hip", "gemv_q8.hip", "mmq.hip", "mmq_f8.hip", "repack.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fno-gpu-rdc",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -202,6 +202,16 @@ size_t mq_act_sum_offset(int64_t M, int64_t K) {
     return act_sum_offset(M, K);
 }
 
+size_t mq_act_digit_offset(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0 || K % 32 != 0) return 0;
+    return act_digit_offset(M, K);
+}
+
+size_t mq_act_step_scale_offset(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0 || K % 32 != 0) return 0;
+    return act_step_scale_offset(M, K);
+}
+
 size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
     BlockLayout lay;
     type = parse_type(type, lay);
@@ -225,7 +235,8 @@ int mq_quantize_act(const float* X, void* Xq, int64_t M, int64_t K, void* stream
     uint8_t* base = static_cast<uint8_t*>(Xq);
     hipError_t e = launch_quantize_act(X, reinterpret_cast<int8_t*>(base),
                                        reinterpret_cast<float*>(base + act_scale_offset(M, K)),
-                                       reinterpret_cast<int32_t*>(base + act_sum_offset(M, K)), M, K,
+                                       reinterpret_cast<int32_t*>(base + act_sum_offset(M, K)),
+                                       base + act_digit_offset(M, K), base + act_step_scale_offset(M, K), M, K,
                                        static_cast<hipStream_t>(stream));
     return launch_status(fn, e, "quantize_act");
 }
@@ -254,7 +265,7 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
 }
 
 static int gemm_common(const char* fn, const void* W, int type, const void* Xq, float* Y, int32_t* D,
-                       float* partial, int64_t M, int64_t N, int64_t K, void* stream) {
+                       void* scratch, int64_t M, int64_t N, int64_t K, void* stream) {
     if (!W || !Xq || (!Y && !D))
         return fail(MQ_ERR_ARG, "%s: null pointer (W=%p Xq=%p out=%p)", fn, W, Xq, Y ? (void*)Y : (void*)D);
     BlockLayout lay;
@@ -278,7 +289,8 @@ static int gemm_common(const char* fn, const void* W, int type, const void* Xq, 
     float* Yout = Y;
     hipError_t e = launch_mmq(type, lay, static_cast<const uint8_t*>(W), reinterpret_cast<const int8_t*>(xq),
                               reinterpret_cast<const float*>(xq + act_scale_offset(M, K)),
-                              reinterpret_cast<const int32_t*>(xq + act_sum_offset(M, K)), Yout, D, partial, M, N, K,
+                              reinterpret_cast<const int32_t*>(xq + act_sum_offset(M, K)),
+                              xq + act_digit_offset(M, K), xq + act_step_scale_offset(M, K), Yout, D, scratch, M, N, K,
                               static_cast<hipStream_t>(stream), &kernel);
     return launch_status(fn, e, kernel);
 }
@@ -292,8 +304,7 @@ int mq_gemm(const void* W, int type, const void* Xq, float* Y, int64_t M, int64_
         return fail(MQ_ERR_SIZE, "%s: scratch of %zu bytes at %p, %zu required", fn, scratch_bytes, scratch, need);
     if (need && !aligned(scratch, 16))
         return fail(MQ_ERR_ALIGN, "%s: scratch must be 16-byte aligned (%p)", fn, scratch);
-    return gemm_common(fn, W, type, Xq, Y, nullptr, need ? static_cast<float*>(scratch) : nullptr, M, N, K,
-                       stream);
+    return gemm_common(fn, W, type, Xq, Y, nullptr, need ? scratch : nullptr, M, N, K, stream);
 }
 
 int mq_debug_gemm_blockdots(const void* W, int type, const void* Xq, int32_t* D, int64_t M, int64_t N, int64_t K,

@@ -9,16 +9,42 @@
 // Eight lanes own one block, four values each (one 16-byte load per lane), so
 // a wave quantizes eight blocks and the block reductions are three xor
 // shuffles.  The kernel streams X once: it is HBM-bound.
+//
+// It also writes the operand plane of the fp8 matrix-unit product, per 64-value step t
+// (two blocks) of each row: a 128-byte digit record and a 16-byte scale record.  Each
+// code is written as two exact fp8 (OCP e4m3) digit bytes: |q| = 16 h + l with h in
+// [0, 7], l in [0, 15], both digits carrying the sign of q.  The l byte is the sign bit
+// over l itself: e4m3 bytes 0..15 encode exactly l * 2^-9 (subnormals and the first
+// binade share the spacing 2^-9).  The h byte encodes 16 h * 2^-9 = h * 2^-5 (a normal
+// number).  Block b = 2t + u of the row takes bytes 64u.. of the digit record as
+// [h of its values 0..31 | l of its values 0..31]: each 32-byte half meets the block's 32
+// weight codes, sum_j 16 h_j c_j + sum_j l_j c_j = sum_j q_j c_j.  The scale record is
+// (scale of block 2t, scale of block 2t + 1, code sum of 2t, code sum of 2t + 1).  A step
+// of K that holds only one block (K % 64 == 32) has zero digits, scale and sum in the
+// second half.
 #include "mq_device.h"
 #include "mq_internal.h"
 
 namespace mq {
 
+// e4m3 bytes of the digits of a code q in [-127, 127] (see above).
+__device__ __forceinline__ uint32_t fp8_digit_l(int q) {
+    return (uint32_t(q < 0) << 7) | (uint32_t(abs(q)) & 15u);
+}
+__device__ __forceinline__ uint32_t fp8_digit_h(int q) {
+    // h * 2^-5 for h = 0..7: 0, 2^-5, 2^-4, 1.5 2^-4, 2^-3, 1.25 2^-3, 1.5 2^-3, 1.75 2^-3
+    constexpr uint64_t kTable = 0x262422201C181000ull;
+    const uint32_t h = uint32_t(abs(q)) >> 4;
+    return (uint32_t(q < 0) << 7) | uint32_t((kTable >> (8 * h)) & 0xFFu);
+}
+
 __global__ __launch_bounds__(256) void quantize_act_kernel(const float4* __restrict__ X,
                                                            uint32_t* __restrict__ codes,
                                                            float* __restrict__ scales,
                                                            int32_t* __restrict__ sums,
-                                                           int64_t n_quads) {
+                                                           uint32_t* __restrict__ digits,
+                                                           uint32_t* __restrict__ step_scales, int64_t M,
+                                                           int KB, int64_t n_quads) {
     const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
     const bool live = t < n_quads;
     const float4 v = live ? X[t] : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -48,16 +74,39 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float4* __restr
             scales[t >> 3] = d;
             sums[t >> 3] = s;
         }
+        // lane j = t % 8 of the block holds values 4j..4j+3: bytes 4j.. of the h half and
+        // of the l half of the block's 64 bytes in the row's digit record of step kb / 2
+        const uint32_t hb = fp8_digit_h(q0) | (fp8_digit_h(q1) << 8) | (fp8_digit_h(q2) << 16) | (fp8_digit_h(q3) << 24);
+        const uint32_t lb = fp8_digit_l(q0) | (fp8_digit_l(q1) << 8) | (fp8_digit_l(q2) << 16) | (fp8_digit_l(q3) << 24);
+        const int64_t blk = t >> 3;
+        const int64_t m = blk / KB;
+        const int kb = int(blk % KB);
+        const int T = (KB + 1) >> 1;
+        const int j = int(t & 7);
+        uint32_t* rec = digits + (m * T + (kb >> 1)) * 32 + 16 * (kb & 1) + j;
+        rec[0] = hb;
+        rec[8] = lb;
+        uint32_t* srec = step_scales + (int64_t(kb >> 1) * M + m) * 4;
+        if (j == 0) {
+            srec[kb & 1] = __float_as_uint(d);
+            srec[2 + (kb & 1)] = uint32_t(s);
+        }
+        if ((KB & 1) && kb == KB - 1) {   // the step's second block does not exist: zeros
+            rec[16] = 0u;
+            rec[24] = 0u;
+            if (j == 0) srec[1] = srec[3] = 0u;
+        }
     }
 }
 
-hipError_t launch_quantize_act(const float* X, int8_t* codes, float* scales, int32_t* sums,
-                               int64_t M, int64_t K, hipStream_t s) {
+hipError_t launch_quantize_act(const float* X, int8_t* codes, float* scales, int32_t* sums, uint8_t* digits,
+                               uint8_t* step_scales, int64_t M, int64_t K, hipStream_t s) {
     const int64_t n_quads = M * K / 4;
     const int64_t blocks = (n_quads + 255) / 256;
     hipLaunchKernelGGL(quantize_act_kernel, dim3(unsigned(blocks)), dim3(256), 0, s,
                        reinterpret_cast<const float4*>(X), reinterpret_cast<uint32_t*>(codes), scales,
-                       sums, n_quads);
+                       sums, reinterpret_cast<uint32_t*>(digits), reinterpret_cast<uint32_t*>(step_scales), M,
+                       int(K / 32), n_quads);
     return hipGetLastError();
 }
 

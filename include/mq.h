@@ -39,15 +39,25 @@
  *        4 bits, 64 bytes high 2 bits, 16 int8 sub-scales, f16 d).  These are
  *        the public GGUF layouts; the pages fix only some sizes and the types.
  *   x  : K f32.   y : N f32.   X : M x K f32 row-major.   Y : M x N f32 row-major.
- *   Xq : the quantized activation plane written by mq_quantize_act, three
- *        arrays in one buffer of mq_act_bytes(M, K) bytes:
- *          codes  int8  [M][K]        at offset 0
- *          scales f32   [M][K / 32]   at offset mq_act_scale_offset(M, K)
- *          sums   int32 [M][K / 32]   at offset mq_act_sum_offset(M, K)
+ *   Xq : the quantized activation plane written by mq_quantize_act, five
+ *        arrays in one buffer of mq_act_bytes(M, K) bytes (T = ceil(K / 64)):
+ *          codes  int8  [M][K]          at offset 0
+ *          scales f32   [M][K / 32]     at offset mq_act_scale_offset(M, K)
+ *          sums   int32 [M][K / 32]     at offset mq_act_sum_offset(M, K)
+ *          digits uint8 [M][T][128]     at offset mq_act_digit_offset(M, K)
+ *          step scale records [T][M][16 bytes] at mq_act_step_scale_offset(M, K)
  *        For block b of row m: scale = f32(amax) / f32(127) with IEEE division,
  *        code_i = clamp(round_half_even(x_i / scale), -127, 127) (a true f32
  *        division), scale 0 and codes 0 when amax == 0, and sum = sum of the 32
- *        codes.
+ *        codes.  The digit record re-encodes the block's codes exactly for the
+ *        fp8 matrix units: |code| = 16 h + l (h in 0..7, l in 0..15), each digit
+ *        an OCP e4m3 byte with the code's sign -- l as the byte (sign << 7) | l
+ *        (value l * 2^-9), h as the e4m3 byte of h * 2^-5.  Digit record (m, t)
+ *        holds blocks 2t and 2t + 1 of row m at bytes 0 and 64, each as
+ *        [h of codes 0..31 | l of codes 0..31], 32 bytes each; step scale
+ *        record (t, m) is (scale of block 2t, scale of block 2t + 1 as f32, sum
+ *        of 2t, sum of 2t + 1 as int32).  When K % 64 == 32 the last step's
+ *        second block is all zeros (digits, scale and sum).
  *
  * Ownership and streams: the caller allocates and frees every buffer (device
  * memory, e.g. from torch).  Weights and inputs are read only.  No call
@@ -135,10 +145,13 @@ int mq_repack(const void* W, int type, int64_t N, int64_t K, size_t nbytes, void
               void* stream);
 
 /* Bytes of the quantized activation plane for M x K, and the offsets of its
- * scale and sum arrays (both 256-byte aligned).  0 if K % 32 != 0. */
+ * scale, sum, digit and step scale arrays (each 256-byte aligned).  0 if
+ * K % 32 != 0. */
 size_t mq_act_bytes(int64_t M, int64_t K);
 size_t mq_act_scale_offset(int64_t M, int64_t K);
 size_t mq_act_sum_offset(int64_t M, int64_t K);
+size_t mq_act_digit_offset(int64_t M, int64_t K);
+size_t mq_act_step_scale_offset(int64_t M, int64_t K);
 
 /*
  * mq_quantize_act -- X f32 [M][K] (device) -> Xq (device, mq_act_bytes(M, K)

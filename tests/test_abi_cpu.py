@@ -54,13 +54,18 @@ def test_weight_bytes_are_exact_payload_sizes():
         assert mq.weight_bytes(t | mq.REPACKED, 10, 256) == 0
 
 
-def test_activation_plane_layout():
-    M, K = 37, 96
+@pytest.mark.parametrize("M,K", [(37, 96), (5, 128), (1, 32)])
+def test_activation_plane_layout(M, K):
     total, so, uo = mq.act_layout(M, K)
+    do = mq.load().mq_act_digit_offset(M, K)
+    to = mq.load().mq_act_step_scale_offset(M, K)
+    T = (K + 63) // 64     # 64-value steps, the last one half empty when K % 64 == 32
     assert so >= M * K and so % 256 == 0
     assert uo >= so + 4 * M * (K // 32) and uo % 256 == 0
-    assert total >= uo + 4 * M * (K // 32) and total % 256 == 0
-    assert mq.act_bytes(M, 100) == 0
+    assert do >= uo + 4 * M * (K // 32) and do % 256 == 0
+    assert to >= do + 128 * M * T and to % 256 == 0
+    assert total == to + 16 * M * T
+    assert mq.act_bytes(M, 100) == 0 and mq.load().mq_act_digit_offset(M, 100) == 0
 
 
 def _rc(fn, *args):
@@ -104,21 +109,34 @@ def test_gemm_refusals():
 
 def test_gemm_scratch_is_sized_by_the_split_plan():
     tile = 128 * 128 * 4
-    # 512 tiles of 128 x 128 fill one round of 512 workgroups: no split, no scratch
+
+    def sk(tiles, pieces, tile_bytes=tile):
+        # partial slots, then one uint32 counter per split tile at a 256-byte boundary
+        return ((tiles * pieces * tile_bytes + 255) // 256) * 256 + 4 * tiles
+
+    # Q4_K at M > 32 with at least 256 tiles of 128 x 256 runs the fp8 kernel: one
+    # workgroup per CU (rounds of 256), 64-value K-steps, at least 4 per range; partial
+    # tiles of 128 x 256 f32.
+    t8 = 128 * 256 * 4
+    # 256 tiles fill one round: no split, no scratch
     assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 16384, 3584) == 0
-    # 592 tiles: 512 whole, the last 80 cut into 6 K ranges (28 steps of 128)
-    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 18944, 3584) == 6 * 80 * tile
-    # a last round more than half full is not cut
+    # 296 tiles: 256 whole, the last 40 cut into 6 K ranges
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 18944, 3584) == sk(40, 6, t8)
+    # a last round more than half full is not cut (1200 tiles: 176 in the last round)
     assert mq.gemm_scratch_bytes(mq.Q4_K, 512 * 3, 128 * 200, 3584) == 0
-    # 16 tiles over 28 K-steps: 14 ranges of 2 steps (at least 2 steps per range)
-    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 512, 3584) == 14 * 16 * tile
-    # 112 tiles: 4 ranges
-    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 3584, 3584) == 4 * 112 * tile
-    # every other type splits the same way (28 K-steps of 128 at K = 3584)
-    for t in (mq.Q8_0, mq.Q6_K, mq.Q5_K, mq.Q4_0, mq.Q4_1, mq.Q5_0, mq.Q5_1):
+    # 306 tiles: the last 50 cut into 5 ranges (56 steps: uneven)
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 100, 306 * 256 - 13, 3584) == sk(50, 5, t8)
+    # the int8 kernel (every other type, Q4_K with fewer tiles, and Q4_K at M <= 32):
+    # 128 x 128 tiles, 128-value K-steps, at least 2 per range -- 28 steps at K = 3584, so
+    # 16 tiles take 14 ranges; its partial tiles are summed by a second launch and it
+    # needs no counters
+    for t in (mq.Q4_K, mq.Q8_0, mq.Q6_K, mq.Q5_K, mq.Q4_0, mq.Q4_1, mq.Q5_0, mq.Q5_1):
         assert mq.gemm_scratch_bytes(t, 512, 512, 3584) == 14 * 16 * tile
+    # 112 tiles (rounds of 512 workgroups, two per CU): 4 ranges each
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 3584, 3584) == 4 * 112 * tile
     # 8 < M <= 32: 32 x 128 tiles; the vocab head at M = 9 has 1188 of them, the last 164 cut in 3
     assert mq.gemm_scratch_bytes(mq.Q6_K, 9, 152064, 3584) == 3 * 164 * 32 * 128 * 4
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 9, 152064, 3584) == 3 * 164 * 32 * 128 * 4
     # M <= 8: the multi-row GEMV, no scratch -- unless the rows do not fit its LDS
     assert mq.gemm_scratch_bytes(mq.Q6_K, 8, 152064, 3584) == 0
     assert mq.gemm_scratch_bytes(mq.Q6_K, 8, 260, 32768) > 0

@@ -84,8 +84,7 @@ def test_blockdots_bitwise_small_ragged(qtype, kind):
 @pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
 def test_split_k_uneven_ranges(qtype):
     # One output tile and a long K: the kernel splits K into many ranges of whole
-    # 128-value steps (uneven lengths; for Q8_0 the last step is cut by K) and sums
-    # the partials in a second launch.
+    # K-steps (uneven lengths; for Q8_0 the last step is cut by K), summed in range order.
     M, N, K = 40, 100, (4128 if BLOCK[qtype] == 32 else 8192)
     assert mq.gemm_scratch_bytes(qtype, M, N, K) >= 8 * M * N * 4, "shape must take the split-K path"
     raw = weights(qtype, N, K, "random", 70)
@@ -136,11 +135,14 @@ def test_small_m_tiles_at_the_switch(qtype):
 
 @pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
 def test_whole_tiles_plus_split_tail(qtype):
-    # 520 output tiles: 512 computed whole, the last 8 cut into K ranges and summed by the
-    # second launch; columns are sampled from both kinds of tile (the last 8 tiles are the
-    # last 1024 columns).
+    # 520 output tiles of 128 x 128 on the int8 path: 512 computed whole, the last 8 cut
+    # into 2 K ranges and summed by a second launch; 260 tiles of 128 x 256 on the fp8 path
+    # (Q4_K): 256 whole, the last 4 cut into 2 ranges summed by the range that finishes
+    # last.  Either way the cut tiles are the last 1024 columns; columns are sampled from
+    # both kinds of tile.  Scratch: the partial tiles (and 4 counters on the fp8 path).
     M, N, K = 100, 128 * 520, 512
-    assert mq.gemm_scratch_bytes(qtype, M, N, K) == 2 * 8 * 128 * 128 * 4
+    want = 2 * 4 * 128 * 256 * 4 + 4 * 4 if qtype == mq.Q4_K else 2 * 8 * 128 * 128 * 4
+    assert mq.gemm_scratch_bytes(qtype, M, N, K) == want
     raw = weights(qtype, N, K, "quantized", 80)
     X = synth.activations(M, K, config_index=12, tensor_index=31)
     rng = np.random.default_rng(5)
@@ -158,8 +160,9 @@ def test_gemm_small_ragged(qtype, kind):
 
 
 @pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
-def test_gemm_extreme_activations(qtype):
-    M, N, K = 24, 96, 2 * BLOCK[qtype] + 256
+@pytest.mark.parametrize("M", [24, 40])
+def test_gemm_extreme_activations(qtype, M):
+    N, K = 96, 2 * BLOCK[qtype] + 256
     raw = weights(qtype, N, K, "random", 60)
     X = synth.activations(M, K, config_index=14)
     X[0] = 0.0
@@ -169,6 +172,62 @@ def test_gemm_extreme_activations(qtype):
     X[4, ::7] = np.float32(50.0)
     check_blockdots(raw, qtype, X, N, K, "extreme activations")
     check_gemm(raw, qtype, X, N, K, what="extreme activations")
+
+
+def sampled_blockdots(raw, qtype, X, N, K, rows, cols, what):
+    import torch
+    dev = device()
+    M = X.shape[0]
+    say(f"blockdots {NAMES[qtype]} M={M} N={N} K={K} {what} (sampled)")
+    Xq = quantized_plane(X, dev)
+    D = mq.gemm_blockdots(to_dev(raw.reshape(-1), dev), qtype, Xq, M, N, K)
+    torch.cuda.synchronize()
+    kernel = mq.last_kernel()
+    got = D[torch.from_numpy(rows).to(dev)][:, torch.from_numpy(cols).to(dev)].cpu().numpy()
+    del D
+    q, _, _ = oracle.quantize_act(X)
+    ref = oracle.block_dots(raw.reshape(N, -1)[cols], qtype, q[rows], len(cols), K)
+    assert np.array_equal(got, ref), f"{what}: block dots differ at {np.argwhere(got != ref)[:5]}"
+    return kernel
+
+
+@pytest.mark.parametrize("M,N,K,blockdots", [
+    (33, 256 * 256 + 77, 1024, True),      # 257 tiles: the last, ragged in N, cut into 4 K ranges
+    (200, 129 * 256, 512, True),           # 258 tiles, the second row tile ragged; 2 cut into 2
+    (100, 306 * 256 - 13, 3584, False),    # 256 whole + 50 cut into 5 uneven ranges of 56 steps
+], ids=["ragged_n_split4", "ragged_m_split2", "uneven_split5"])
+def test_q4k_fp8_path_ragged_and_split(M, N, K, blockdots):
+    """The fp8 Q4_K kernel (shapes with at least one full round of 128 x 256 tiles):
+    ragged row and column tiles and K-split tiles, against the oracle on sampled columns
+    (always including the first and the last tile) and, where the export fits, bitwise
+    block dots on sampled rows and columns."""
+    raw = weights(mq.Q4_K, N, K, "random", 140 + M)
+    X = synth.activations(M, K, config_index=12, tensor_index=90 + M)
+    rng = np.random.default_rng(M)
+    cols = np.unique(np.concatenate([np.arange(256), rng.choice(N, 300, replace=False), np.arange(N - 300, N)]))
+    check_gemm(raw, mq.Q4_K, X, N, K, cols=cols, what="fp8 path")
+    assert mq.last_kernel() == "mmq_f8<q4_K>", mq.last_kernel()
+    if blockdots:
+        rows = np.unique(np.r_[0:8, M - 8:M, rng.choice(M, 8)])
+        kernel = sampled_blockdots(raw, mq.Q4_K, X, N, K, rows, cols, "fp8 path")
+        assert kernel == "mmq_f8<q4_K>", kernel
+
+
+def test_q4k_fp8_path_extreme_activations():
+    M, N, K = 40, 256 * 256, 512
+    raw = weights(mq.Q4_K, N, K, "random", 150)
+    X = synth.activations(M, K, config_index=14)
+    X[0] = 0.0
+    X[1, :64] = 0.0
+    X[2] *= np.float32(1e-30)
+    X[3] *= np.float32(1e30)
+    X[4, ::7] = np.float32(50.0)
+    X[5, :32] = np.float32(127.0) * np.sign(X[5, :32])      # codes of +-127 in a block
+    cols = np.unique(np.concatenate([np.arange(300), np.random.default_rng(6).choice(N, 300, replace=False)]))
+    check_gemm(raw, mq.Q4_K, X, N, K, cols=cols, what="fp8 path, extreme activations")
+    assert mq.last_kernel() == "mmq_f8<q4_K>", mq.last_kernel()
+    kernel = sampled_blockdots(raw, mq.Q4_K, X, N, K, np.arange(M), cols, "fp8 path, extreme activations")
+    assert kernel == "mmq_f8<q4_K>", kernel
 
 
 def test_blockdots_config1_q8_0_m16():

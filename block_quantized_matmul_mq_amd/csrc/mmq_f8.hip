@@ -510,9 +510,14 @@ size_t mmq_f8_scratch_bytes(int64_t M, int64_t N, int64_t K) {
     return splitk_scratch_bytes(p.split_tiles, p.splits, int64_t(BM) * BN);
 }
 
+size_t mmq_f8_partial_bytes(int64_t M, int64_t N, int64_t K) {
+    const MmqPlan p = mmq_f8_plan(M, N, K);
+    return size_t(p.split_tiles) * size_t(p.splits) * size_t(BM) * BN * sizeof(float);
+}
+
 hipError_t launch_mmq_f8(int type, const uint8_t* W, const uint8_t* digits, const uint8_t* step_scales, float* Y,
-                         int32_t* dots, void* scratch, int64_t M, int64_t N, int64_t K, hipStream_t s,
-                         const char** name) {
+                         int32_t* dots, void* scratch, unsigned* counters, int64_t M, int64_t N, int64_t K,
+                         hipStream_t s, const char** name) {
     if (type != kQ4_K) return hipErrorInvalidValue;
     *name = "mmq_f8<q4_K>";
     const MmqPlan plan = mmq_f8_plan(M, N, K);
@@ -520,10 +525,9 @@ hipError_t launch_mmq_f8(int type, const uint8_t* W, const uint8_t* digits, cons
     const int total = plan.full + plan.split_tiles * plan.splits;
     const int64_t row_bytes = (K / 256) * 144;
     float* partial = static_cast<float*>(scratch);
-    unsigned* counters = scratch ? reinterpret_cast<unsigned*>(static_cast<uint8_t*>(scratch) +
-                                                             splitk_counter_offset(plan.split_tiles, plan.splits,
-                                                                                   int64_t(BM) * BN))
-                                 : nullptr;
+    if (!counters && scratch)
+        counters = reinterpret_cast<unsigned*>(static_cast<uint8_t*>(scratch) +
+                                               splitk_counter_offset(plan.split_tiles, plan.splits, int64_t(BM) * BN));
     if (dots)
         hipLaunchKernelGGL(mmq_f8_q4k_kernel<true>, dim3(total), dim3(kThreads), 0, s, W, digits, step_scales, Y, dots,
                            partial, counters, int(M), int(N), int(K), row_bytes, tiles_m, plan.full,

@@ -25,6 +25,16 @@ thread_local const char* g_last_kernel = "";
 constexpr int kMaxDevices = 64;
 DeviceInfo g_devices[kMaxDevices];
 
+// Scratch of mq_gemm_noalloc: one array per device for the life of the process.  The
+// first kNoAllocCounterBytes hold the fp8 kernel's split-tile counters, which only that
+// kernel touches and which every launch leaves at zero (cleared once, when mq_init first
+// sets up the device); the partial tiles of either MMQ kernel follow.  Every valid shape's
+// partials fit: both plans cut at most one round of workgroups' worth of tiles (512 of
+// 128 x 128, or 256 of 128 x 256 f32), 32 MiB.
+constexpr size_t kNoAllocCounterBytes = 4096;
+constexpr size_t kNoAllocPartialBytes = size_t(MQ_NOALLOC_PARTIAL_BYTES);
+static __device__ __align__(256) uint8_t noalloc_scratch[kNoAllocCounterBytes + kNoAllocPartialBytes];
+
 int fail(int code, const char* fmt, ...) {
     char buf[512];
     va_list ap;
@@ -169,6 +179,21 @@ int mq_init(int device) {
     if (e != hipSuccess)
         return fail(MQ_ERR_DEVICE, "mq_init: setting the GEMV LDS limit to %zu bytes failed: %s", lds,
                     hipGetErrorName(e));
+    if (!info.noalloc_scratch) {
+        // This device's copy of the array: its device address, read with the device current
+        // (the array's name in host code is only a handle), and its counters cleared once.
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(noalloc_scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(MQ_ERR_DEVICE, "mq_init: no device address for the scratch array on device %d: %s", device,
+                        hipGetErrorName(e));
+        e = hipMemset(ptr, 0, kNoAllocCounterBytes);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e != hipSuccess)
+            return fail(MQ_ERR_DEVICE, "mq_init: clearing the scratch counters on device %d failed: %s", device,
+                        hipGetErrorName(e));
+        info.noalloc_scratch = static_cast<uint8_t*>(ptr);
+    }
     info.ready = true;
     return MQ_OK;
 }
@@ -265,7 +290,7 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
 }
 
 static int gemm_common(const char* fn, const void* W, int type, const void* Xq, float* Y, int32_t* D,
-                       void* scratch, int64_t M, int64_t N, int64_t K, void* stream) {
+                       void* scratch, unsigned* counters, int64_t M, int64_t N, int64_t K, void* stream) {
     if (!W || !Xq || (!Y && !D))
         return fail(MQ_ERR_ARG, "%s: null pointer (W=%p Xq=%p out=%p)", fn, W, Xq, Y ? (void*)Y : (void*)D);
     BlockLayout lay;
@@ -290,8 +315,8 @@ static int gemm_common(const char* fn, const void* W, int type, const void* Xq, 
     hipError_t e = launch_mmq(type, lay, static_cast<const uint8_t*>(W), reinterpret_cast<const int8_t*>(xq),
                               reinterpret_cast<const float*>(xq + act_scale_offset(M, K)),
                               reinterpret_cast<const int32_t*>(xq + act_sum_offset(M, K)),
-                              xq + act_digit_offset(M, K), xq + act_step_scale_offset(M, K), Yout, D, scratch, M, N, K,
-                              static_cast<hipStream_t>(stream), &kernel);
+                              xq + act_digit_offset(M, K), xq + act_step_scale_offset(M, K), Yout, D, scratch,
+                              counters, M, N, K, static_cast<hipStream_t>(stream), &kernel);
     return launch_status(fn, e, kernel);
 }
 
@@ -304,14 +329,32 @@ int mq_gemm(const void* W, int type, const void* Xq, float* Y, int64_t M, int64_
         return fail(MQ_ERR_SIZE, "%s: scratch of %zu bytes at %p, %zu required", fn, scratch_bytes, scratch, need);
     if (need && !aligned(scratch, 16))
         return fail(MQ_ERR_ALIGN, "%s: scratch must be 16-byte aligned (%p)", fn, scratch);
-    return gemm_common(fn, W, type, Xq, Y, nullptr, need ? scratch : nullptr, M, N, K, stream);
+    return gemm_common(fn, W, type, Xq, Y, nullptr, need ? scratch : nullptr, nullptr, M, N, K, stream);
+}
+
+int mq_gemm_noalloc(const void* W, int type, const void* Xq, float* Y, int64_t M, int64_t N, int64_t K,
+                    void* stream) {
+    const char* fn = "mq_gemm_noalloc";
+    if (!Y) return fail(MQ_ERR_ARG, "%s: null Y", fn);
+    if (mq_gemm_scratch_bytes(type, M, N, K) != 0) {   // a valid shape whose plan cuts tiles
+        BlockLayout lay;
+        const size_t need = mmq_partial_bytes(parse_type(type, lay), M, N, K);
+        if (need > kNoAllocPartialBytes)
+            return fail(MQ_ERR_SIZE, "%s: M=%lld N=%lld K=%lld needs %zu bytes of partial tiles, the limit is %zu", fn,
+                        (long long)M, (long long)N, (long long)K, need, kNoAllocPartialBytes);
+    }
+    int rc = check_ready(fn);
+    if (rc) return rc;
+    uint8_t* base = device_info()->noalloc_scratch;
+    return gemm_common(fn, W, type, Xq, Y, nullptr, base + kNoAllocCounterBytes, reinterpret_cast<unsigned*>(base),
+                       M, N, K, stream);
 }
 
 int mq_debug_gemm_blockdots(const void* W, int type, const void* Xq, int32_t* D, int64_t M, int64_t N, int64_t K,
                             void* stream) {
     const char* fn = "mq_debug_gemm_blockdots";
     if (!D) return fail(MQ_ERR_ARG, "%s: null D", fn);
-    return gemm_common(fn, W, type, Xq, nullptr, D, nullptr, M, N, K, stream);
+    return gemm_common(fn, W, type, Xq, nullptr, D, nullptr, nullptr, M, N, K, stream);
 }
 
 int mq_repack(const void* W, int type, int64_t N, int64_t K, size_t nbytes, void* Wr, size_t wr_bytes,

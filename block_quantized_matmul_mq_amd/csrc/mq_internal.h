@@ -38,6 +38,7 @@ inline size_t act_bytes(int64_t M, int64_t K) {
 struct DeviceInfo {
     int cu_count = 0;
     size_t lds_per_block = 0;
+    uint8_t* noalloc_scratch = nullptr;   // this device's copy of mq_gemm_noalloc's scratch array
     bool ready = false;
 };
 const DeviceInfo* device_info();  // null if mq_init has not succeeded on the current device
@@ -93,21 +94,26 @@ struct MmqPlan {
 };
 MmqPlan mmq_plan(int type, int64_t M, int64_t N, int64_t K);
 size_t mmq_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
+// Bytes of the partial tiles alone (mmq_scratch_bytes without the fp8 kernel's counters).
+size_t mmq_partial_bytes(int type, int64_t M, int64_t N, int64_t K);
 // Y: the product (null for the block-dot export); dots: the export (null for the product);
 // scratch: at least mmq_scratch_bytes of device memory when the plan has splits > 1 (for
-// the fp8 kernel its counters zero; every call leaves them zero again).
+// the fp8 kernel its counters zero; every call leaves them zero again).  counters: where
+// the fp8 kernel keeps its split-tile counters (zero, and left zero again), or null to
+// keep them in scratch after the partial tiles.
 hipError_t launch_mmq(int type, BlockLayout layout, const uint8_t* W, const int8_t* codes, const float* scales,
                       const int32_t* sums, const uint8_t* digits, const uint8_t* step_scales, float* Y,
-                      int32_t* dots, void* scratch, int64_t M, int64_t N, int64_t K, hipStream_t s,
-                      const char** kernel_name);
+                      int32_t* dots, void* scratch, unsigned* counters, int64_t M, int64_t N, int64_t K,
+                      hipStream_t s, const char** kernel_name);
 // Q4_K at M > 32 rows: block dots on the fp8 matrix units from the plane's digit records
 // (mmq_f8.hip).
 bool mmq_f8_applies(int type, int64_t M, int64_t N);
 MmqPlan mmq_f8_plan(int64_t M, int64_t N, int64_t K);
 size_t mmq_f8_scratch_bytes(int64_t M, int64_t N, int64_t K);
+size_t mmq_f8_partial_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_mmq_f8(int type, const uint8_t* W, const uint8_t* digits, const uint8_t* step_scales, float* Y,
-                         int32_t* dots, void* scratch, int64_t M, int64_t N, int64_t K, hipStream_t s,
-                         const char** kernel_name);
+                         int32_t* dots, void* scratch, unsigned* counters, int64_t M, int64_t N, int64_t K,
+                         hipStream_t s, const char** kernel_name);
 // mq_gemm for M <= kGemvQ8MaxRows: a multi-row GEMV over the quantized activation plane
 // (gemv_q8.hip), taken by launch_mmq whenever gemv_q8_applies; it needs no scratch.
 constexpr int kGemvQ8MaxRows = 8;

@@ -45,6 +45,8 @@ _SIGNATURES = {
     "mq_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                ctypes.c_size_t, ctypes.c_void_p]),
+    "mq_gemm_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
     "mq_debug_gemm_blockdots": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                                ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                                ctypes.c_int64, ctypes.c_void_p]),
@@ -286,6 +288,18 @@ def gemm(W, qtype, Xq, M, N, K, Y=None, scratch=None, stream=None):
     sb = _nbytes(scratch) if scratch is not None else 0
     _check(load().mq_gemm(ctypes.c_void_p(W.data_ptr()), qtype, ctypes.c_void_p(Xq.data_ptr()),
                           ctypes.c_void_p(Y.data_ptr()), M, N, K, sp, sb, _stream(stream)))
+    return Y
+
+
+def gemm_noalloc(W, qtype, Xq, M, N, K, Y, stream=None):
+    """mq_gemm_noalloc: the product into a caller-provided Y, with the library's own
+    per-device scratch (the call allocates nothing; overlapping calls on one device race)."""
+    _weights(W, qtype, N, K, "gemm_noalloc")
+    _act_plane(Xq, M, K, "gemm_noalloc")
+    _f32(Y, M * N, "gemm_noalloc", "Y")
+    _same_device("gemm_noalloc", W, Xq, Y)
+    _check(load().mq_gemm_noalloc(ctypes.c_void_p(W.data_ptr()), qtype, ctypes.c_void_p(Xq.data_ptr()),
+                                  ctypes.c_void_p(Y.data_ptr()), M, N, K, _stream(stream)))
     return Y
 
 

@@ -202,6 +202,27 @@ size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
 int mq_gemm(const void* W, int type, const void* Xq, float* Y, int64_t M, int64_t N, int64_t K,
             void* scratch, size_t scratch_bytes, void* stream);
 
+/* Partial-tile bytes of mq_gemm_noalloc's per-device scratch array. */
+#define MQ_NOALLOC_PARTIAL_BYTES (32u << 20)
+
+/*
+ * mq_gemm_noalloc -- mq_gemm for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same product, kernels and result bits as mq_gemm, with the
+ * work split's scratch taken from an array the library holds on each device
+ * (MQ_NOALLOC_PARTIAL_BYTES of partial tiles plus 4 KiB of counters; each
+ * device that the library runs on holds it until the process ends).  The call
+ * allocates and frees nothing; the caller still passes W, Xq and Y as for
+ * mq_gemm.  Every call on a device shares that device's array: calls that may
+ * overlap on one device (two streams, or two host threads) race and give wrong
+ * results; order them on one stream.  A shape whose partial tiles exceed the
+ * array is refused with MQ_ERR_SIZE (no valid shape does: a plan cuts at most
+ * 32 MiB of tiles).  The array's address is taken, and its counters cleared,
+ * the first time mq_init succeeds on the device.
+ */
+int mq_gemm_noalloc(const void* W, int type, const void* Xq, float* Y, int64_t M, int64_t N, int64_t K,
+                    void* stream);
+
 /*
  * mq_debug_gemm_blockdots -- test export: the exact int32 block dot products
  * the mq_gemm kernel forms, written to D (device) as int32 [M][N][G] with

@@ -1,0 +1,63 @@
+"""mq_gemm_noalloc (the product with the library's per-device scratch array) gives
+the same bits as mq_gemm with a caller-allocated, zeroed scratch buffer, over calls
+in a row that reuse the array: a K-split fp8 product, a smaller K-split int8 product
+whose partial tiles overwrite the array, then fp8 products that cut a different number
+of tiles (their counters must still read zero) and one that cuts none."""
+
+import numpy as np
+import pytest
+
+from block_quantized_matmul_mq_amd import mq, synth
+
+from gpu_cases import device, say, to_dev, weights
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (M, N, K, kernel, partial-tile bytes the plan cuts)
+    (512, 18944, 3584, "mmq_f8<q4_K>", 40 * 6 * 128 * 256 * 4),   # ffn_up: 40 tiles cut into 6
+    (512, 3584, 3584, "mmq<q4_K>", 112 * 4 * 128 * 128 * 4),       # smaller: int8 path, 112 tiles into 4
+    (100, 306 * 256 - 13, 1024, "mmq_f8<q4_K>", 50 * 4 * 128 * 256 * 4),  # 50 tiles into 4
+    (40, 256 * 256, 512, "mmq_f8<q4_K>", 0),                        # one whole round, nothing cut
+]
+
+
+def run_pair(M, N, K, kernel, cut, seed):
+    import torch
+    dev = device()
+    say(f"gemm_noalloc q4_K M={M} N={N} K={K}")
+    raw = weights(mq.Q4_K, N, K, "random", seed)
+    W = to_dev(raw.reshape(-1), dev)
+    X = synth.activations(M, K, config_index=12, tensor_index=seed)
+    Xq = mq.quantize_act(to_dev(X, dev))
+    need = mq.gemm_scratch_bytes(mq.Q4_K, M, N, K)
+    assert need >= cut and need - cut < 4096
+    Y_ref = mq.gemm(W, mq.Q4_K, Xq, M, N, K)
+    assert mq.last_kernel() == kernel, mq.last_kernel()
+    Y = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+    mq.gemm_noalloc(W, mq.Q4_K, Xq, M, N, K, Y)
+    assert mq.last_kernel() == kernel, mq.last_kernel()
+    torch.cuda.synchronize()
+    a, b = Y.cpu().numpy(), Y_ref.cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), \
+        f"M={M} N={N} K={K}: {np.count_nonzero(a.view(np.uint32) != b.view(np.uint32))} elements differ"
+
+
+def test_noalloc_matches_gemm_over_calls_in_a_row():
+    mq.init(0)
+    for i, case in enumerate(CASES):
+        run_pair(*case, seed=200 + i)
+    # the first shape again, after the array has held every other call's data
+    run_pair(*CASES[0], seed=200)
+
+
+def test_noalloc_refuses_without_touching_the_device():
+    import torch
+    dev = device()
+    mq.init(0)
+    M, N, K = 64, 256, 256
+    W = torch.zeros(mq.weight_bytes(mq.Q4_K, N, K), dtype=torch.uint8, device=dev)
+    Xq = torch.zeros(mq.act_bytes(M, K), dtype=torch.uint8, device=dev)
+    lib = mq.load()
+    assert lib.mq_gemm_noalloc(W.data_ptr(), mq.Q4_K, Xq.data_ptr(), None, M, N, K, None) == -1
+    assert lib.mq_gemm_noalloc(W.data_ptr(), mq.Q4_K, Xq.data_ptr(), W.data_ptr(), M, N, 100, None) == -2

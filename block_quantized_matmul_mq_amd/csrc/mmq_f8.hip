@@ -40,6 +40,7 @@
 // the step.  Tiles that a last, partial round of workgroups would leave idle are cut
 // into K ranges and summed in the same launch (mmq_splitk.h).
 #include <algorithm>
+#include <cstddef>
 #include <type_traits>
 
 #include "mmq_splitk.h"
@@ -90,12 +91,24 @@ __device__ __forceinline__ uint32_t bf16_hilo(float x) {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Wait until at most N vector memory operations of this wave are outstanding (the
-// builtin, so that the compiler's own wait insertion knows about it).  gfx9 encoding:
+// builtin: the compiler keeps it as written).  gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima.
 template <int N>
 __device__ __forceinline__ void vm_wait() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// buffer_load_dwordx4 ... lds: 16 bytes per lane from buffer offset voff + soff to LDS
+// bytes lds + 16 lane.  Written as asm so that the compiler does not track these loads:
+// it would otherwise wait for some of them before every read of any ring slot (its alias
+// tracking of LDS-direct loads does not separate the slots), while the ring's own
+// protocol -- every wave waits for its own loads of a step, then the workgroup barrier --
+// already orders them.  The load has no destination register; M0 (which nothing else in
+// the kernel uses) carries the LDS address and needs one wait state before the load.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
 }
 
 // One step's data as loaded from memory (global -> LDS directly).
@@ -136,35 +149,43 @@ __shared__ __attribute__((aligned(16))) Slot g_slot0, g_slot1, g_slot2;
 __shared__ __attribute__((aligned(16))) Work g_work0, g_work1;
 template <int R> __device__ __forceinline__ Slot& slot_at() { return R == 0 ? g_slot0 : R == 1 ? g_slot1 : g_slot2; }
 template <int R> __device__ __forceinline__ Work& work_at() { return R == 0 ? g_work0 : g_work1; }
+// LDS byte address of byte `off` of ring slot R (a constant plus `off`).
+template <int R> __device__ __forceinline__ uint32_t slot_lds(uint32_t off) {
+    return uint32_t(uintptr_t((const lds_void*)&slot_at<R>())) + off;
+}
 
 // ------------------------------------------------------------------ loads of one step
 // A step's loads (buffer_load ... lds, 1 KB per instruction), wave w taking:
 //   digit lines: instructions w and w + 8 of 16, 8 rows each (8 lanes per 128-byte line);
 //   weight code bytes: instruction w of 8 (32 rows x 2 lanes);
-//   waves 0, 1: scale records of rows 64 w .. 64 w + 63;
+//   waves 0..3: scale records of rows 64 (w % 2) .. + 63 (waves 2 and 3 load the same
+//     bytes as waves 0 and 1 into the same place);
 //   waves 4..7: weight headers of rows 64 (w - 4) .. + 63.
-// So waves 0, 1 and 4..7 issue 4 loads per step and waves 2, 3 issue 3.  The loads run
-// two steps ahead; past the end of the K range they load the last step again (the
-// copies are never read), which keeps the count the same for every step and every
-// address inside the operands.  Rows past M or N read as zeros (out of the buffer
-// ranges, checked on the per-lane offsets).
+// Every wave issues the same 4 loads per step (only their operands differ), so the wait
+// for a step's loads is one count for every wave and the compiler sees that a slot's
+// loads are complete once that wait and the barrier after it have passed.  The loads run
+// two steps ahead; past the end of the K range they load the last step again (the copies
+// are never read), which keeps every address inside the operands.  Rows past M or N read
+// as zeros (out of the buffer ranges, checked on the per-lane offsets).
 struct Loader {
-    __amdgpu_buffer_rsrc_t ra, rs, rw;
+    __amdgpu_buffer_rsrc_t ra, rx, rw;
     uint32_t voff_a[2];   // digit instructions wave, wave + 8
     uint32_t voff_q;      // code instruction
-    uint32_t voff_x;      // scale record (waves 0, 1) or header (waves 4..7)
+    uint32_t voff_x;      // scale record (waves 0..3) or header (waves 4..7)
     int wave;
+    bool scales;          // this wave's fourth load is a scale record (else a header)
     int64_t step_stride;  // bytes between the same row's scale records of consecutive steps
 
     __device__ void init(const uint8_t* W, int64_t rb, const uint8_t* digits, const uint8_t* step_scales,
                          int m0, int n0, int M, int N, int K) {
         const int lane = threadIdx.x & 63;
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        scales = wave < 4;
         const int rows = min(BM, M - m0), wrows = min(BN, N - n0);
         const int T = (K + 63) / 64;
         ra = make_rsrc(digits + int64_t(m0) * T * 128, int64_t(rows) * T * 128);
-        rs = make_rsrc(step_scales + int64_t(m0) * 16, (int64_t(T) * M - m0) * 16);
         rw = make_rsrc(W + int64_t(n0) * rb, int64_t(wrows) * rb);
+        rx = scales ? make_rsrc(step_scales + int64_t(m0) * 16, (int64_t(T) * M - m0) * 16) : rw;
         step_stride = int64_t(M) * 16;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -177,34 +198,36 @@ struct Loader {
             const int h = o / (16 * BN), row = (o % (16 * BN)) / 16;
             voff_q = uint32_t(int64_t(row) * rb + 16 + 16 * h);
         }
-        if (wave < 2)   // scale record of row 64 wave + lane (rows past M: out of range)
-            voff_x = 64 * wave + lane < rows ? uint32_t((64 * wave + lane) * 16) : 0x80000000u;
-        else
-            voff_x = uint32_t(int64_t(64 * (wave - 4) + lane) * rb);  // header (waves 4..7)
+        if (scales) {   // scale record of row 64 (wave % 2) + lane (rows past M: out of range)
+            const int r = 64 * (wave & 1) + lane;
+            voff_x = r < rows ? uint32_t(r * 16) : 0x80000000u;
+        } else {
+            voff_x = uint32_t(int64_t(64 * (wave - 4) + lane) * rb);  // header
+        }
     }
 
+    // Load PART (0, 1: digit lines; 2: code bytes; 3: scale record or header) of the step
+    // at k0 into slot R.
+    template <int R, int PART>
+    __device__ void issue_part(int k0) const {
+        const uint32_t t = uint32_t(k0 >> 6);
+        if constexpr (PART < 2) {
+            dma16(ra, slot_lds<R>(offsetof(Slot, A) + 1024 * (wave + 8 * PART)), voff_a[PART], t * 128);
+        } else if constexpr (PART == 2) {   // super-block, 64-value chunk
+            dma16(rw, slot_lds<R>(offsetof(Slot, qs) + 1024 * wave), voff_q,
+                  uint32_t(144 * (k0 >> 8) + 32 * ((k0 >> 6) & 3)));
+        } else {
+            const uint32_t xdst =
+                scales ? offsetof(Slot, ss) + 1024 * (wave & 1) : offsetof(Slot, hdr) + 1024 * (wave - 4);
+            dma16(rx, slot_lds<R>(xdst), voff_x, scales ? uint32_t(t * step_stride) : uint32_t(144 * (k0 >> 8)));
+        }
+    }
     template <int R>
     __device__ void issue(int k0) const {
-        Slot& sl = slot_at<R>();
-        const uint32_t t = uint32_t(k0 >> 6);
-        const uint32_t wsoff = uint32_t(144 * (k0 >> 8) + 32 * ((k0 >> 6) & 3));   // super-block, 64-value chunk
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sl.A + 1024 * (wave + 8 * i)), 16, voff_a[i],
-                                                     t * 128, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sl.qs + 1024 * wave), 16, voff_q, wsoff, 0, 0);
-        if (wave < 2)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(sl.ss + 1024 * wave), 16, voff_x,
-                                                     uint32_t(t * step_stride), 0, 0);
-        else if (wave >= 4)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sl.hdr + 1024 * (wave - 4)), 16, voff_x,
-                                                     uint32_t(144 * (k0 >> 8)), 0, 0);
-    }
-
-    // wait for this wave's loads of the step before the most recently issued one
-    __device__ void wait_previous() const {
-        if (wave == 2 || wave == 3) vm_wait<3>();
-        else vm_wait<4>();
+        issue_part<R, 0>(k0);
+        issue_part<R, 1>(k0);
+        issue_part<R, 2>(k0);
+        issue_part<R, 3>(k0);
     }
 };
 
@@ -316,38 +339,57 @@ __global__ __launch_bounds__(kThreads, 1) void mmq_f8_q4k_kernel(const uint8_t* 
         constexpr int R = decltype(r_c)::value, WB = decltype(wb_c)::value;
         constexpr int R1 = (R + 1) % 3, R2 = (R + 2) % 3;
         const int k0 = kbeg + s * KS;
-        ld.issue<R2>(min(k0 + 2 * KS, klast));   // slot R2 was last read by step s - 1
+        // The loads of step s + 2 go to slot R2 (last read in step s - 1), issued in four
+        // parts spread over the products so that the waves' loads reach the memory pipeline
+        // a few at a time.
+        const int k2 = min(k0 + 2 * KS, klast);
+        ld.issue_part<R2, 0>(k2);
+
+        // The next step's data: once this wave's loads of step s + 1 have landed (at most
+        // `newer` loads issued after them outstanding), unpack them (work buffer WB ^ 1 was
+        // last read in step s - 1).  The two waves that share a SIMD (wm = 0 and wm = 1) do
+        // this at different points of the step, so that one wave's unpacking (vector ALU and
+        // LDS) runs beside the other's matrix products.
+        auto unpack_next = [&](auto newer_c) {
+            if (s + 1 < nsteps) {
+                // (the block-dot export's stores count in vmcnt too: it waits for everything)
+                if constexpr (DUMP) vm_wait<0>();
+                else vm_wait<decltype(newer_c)::value>();
+                unpack<R1, WB ^ 1>(k0 + KS);
+            }
+        };
 
         const uint8_t* As = slot_at<R>().A;
         const Work& wk = work_at<WB>();
         const int arow0 = 64 * wm + r32;   // + 32 i
         const int brow0 = 64 * wn + r32;   // + 32 j
 
-        // Products k = 4p + 2i + j (block p, tiles i, j): D (fp8 block dots) and S (scales).
+        // Products kk = 4p + 2i + j (block p, tiles i, j): D (fp8 block dots) and S (scales).
+        // Operands load one at a time, so that block 1's load into the registers of block
+        // 0's as soon as their last product has been issued.
         v8i a[TI], b[TJ];
         v4s oa[TI], ob[TJ];
-        auto frags = [&](int p) {
-#pragma unroll
-            for (int i = 0; i < TI; ++i) {
-                const int ar = arow0 + 32 * i;
-                const v4i lo = *reinterpret_cast<const v4i*>(As + 128 * ar + 16 * ((4 * p + 2 * g) ^ swz(ar)));
-                const v4i hi = *reinterpret_cast<const v4i*>(As + 128 * ar + 16 * ((4 * p + 2 * g + 1) ^ swz(ar)));
-                a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                oa[i] = __builtin_bit_cast(v4s, wk.dxq[g][p * BM + ar]);
-            }
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-                const int br = brow0 + 32 * j;
-                const v4i lo = *reinterpret_cast<const v4i*>(wk.B + (2 * p) * (16 * BN) + 16 * br);
-                const v4i hi = *reinterpret_cast<const v4i*>(wk.B + (2 * p + 1) * (16 * BN) + 16 * br);
-                b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                ob[j] = __builtin_bit_cast(v4s, wk.dwq[g][p][br]);
-            }
+        auto load_a = [&](int p, int i) {
+            const int ar = arow0 + 32 * i;
+            const v4i lo = *reinterpret_cast<const v4i*>(As + 128 * ar + 16 * ((4 * p + 2 * g) ^ swz(ar)));
+            const v4i hi = *reinterpret_cast<const v4i*>(As + 128 * ar + 16 * ((4 * p + 2 * g + 1) ^ swz(ar)));
+            a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            oa[i] = __builtin_bit_cast(v4s, wk.dxq[g][p * BM + ar]);
         };
+        auto load_b = [&](int p, int j) {
+            const int br = brow0 + 32 * j;
+            const v4i lo = *reinterpret_cast<const v4i*>(wk.B + (2 * p) * (16 * BN) + 16 * br);
+            const v4i hi = *reinterpret_cast<const v4i*>(wk.B + (2 * p + 1) * (16 * BN) + 16 * br);
+            b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            ob[j] = __builtin_bit_cast(v4s, wk.dwq[g][p][br]);
+        };
+        // The short scale product first: the wave then waits at most its 32 cycles before
+        // the block dot (64 cycles) issues, and the previous product's 16 FMAs run beside
+        // the block dot.
         auto products = [&](int i, int j, v16f& D, v16f& S) {
             const v16f z = {};
-            D = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], z, 0, 0, 0, 0, 0, 0);
             S = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(oa[i], ob[j], z, 0, 0, 0);
+            D = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], z, 0, 0, 0, 0, 0, 0);
         };
         auto consume = [&](int p, int i, int j, const v16f& D, const v16f& S) {
 #pragma unroll
@@ -371,39 +413,53 @@ __global__ __launch_bounds__(kThreads, 1) void mmq_f8_q4k_kernel(const uint8_t* 
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ma, mb, acc[i][j], 0, 0, 0);
         };
 
-        v16f D[2], S[2];
-#pragma unroll
-        for (int p = 0; p < NB; ++p) {
-            frags(p);
-            products(0, 0, D[0], S[0]);
-#pragma unroll
-            for (int k = 0; k < TI * TJ; ++k) {
-                const int i = k / TJ, j = k % TJ;
-                if (k + 1 < TI * TJ) products((k + 1) / TJ, (k + 1) % TJ, D[(k + 1) & 1], S[(k + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-                consume(p, i, j, D[k & 1], S[k & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
+        // The min term first: its products run while the first operands load.
 #pragma unroll
         for (int i = 0; i < TI; ++i)
 #pragma unroll
             for (int j = 0; j < TJ; ++j) min_term(i, j);
+        load_a(0, 0);
+        load_b(0, 0);
+        load_b(0, 1);
+        load_a(0, 1);
 
-        // the next step's data: this wave's loads of step s + 1 have landed; unpack them
-        if (s + 1 < nsteps) {
-            // (the block-dot export's stores count in vmcnt too: it waits for everything)
-            if constexpr (DUMP) vm_wait<0>();
-            else ld.wait_previous();
-            unpack<R1, WB ^ 1>(k0 + KS);
+        static_assert(TI == 2 && TJ == 2 && NB == 2, "the operand schedule below is written for 2 x 2 tiles");
+        v16f D[2], S[2];
+        products(0, 0, D[0], S[0]);
+#pragma unroll
+        for (int kk = 0; kk < NB * TI * TJ; ++kk) {
+            const int p = kk / (TI * TJ), i = (kk / TJ) % TI, j = kk % TJ;
+            const int kn = kk + 1;
+            if (kn < NB * TI * TJ) products((kn / TJ) % TI, kn % TJ, D[kn & 1], S[kn & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(p, i, j, D[kk & 1], S[kk & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // block 1's operands, each once the products of block 0 that read its
+            // registers have been issued (a0 by product 1, b0 by 2, a1 and b1 by 3)
+            if (kk == 0) load_a(1, 0);
+            if (kk == 1) {
+                load_b(1, 0);
+                ld.issue_part<R2, 1>(k2);
+            }
+            if (kk == 2) {
+                load_b(1, 1);
+                load_a(1, 1);
+            }
+            if (kk == 3) {
+                ld.issue_part<R2, 2>(k2);
+                if (wm == 1) unpack_next(std::integral_constant<int, 3>{});
+            }
+            if (kk == 5) ld.issue_part<R2, 3>(k2);
         }
+
+        if (wm == 0) unpack_next(std::integral_constant<int, 4>{});
         lds_barrier();   // step s + 1 is published (every wave waited for its own loads); slot R is free
     };
 
     // prologue: steps 0 and 1 in flight, step 0 unpacked and published
     ld.issue<0>(kbeg);
     ld.issue<1>(min(kbeg + KS, klast));
-    ld.wait_previous();
+    vm_wait<4>();
     unpack<0, 0>(kbeg);
     lds_barrier();
 
@@ -429,36 +485,46 @@ __global__ __launch_bounds__(kThreads, 1) void mmq_f8_q4k_kernel(const uint8_t* 
     if constexpr (DUMP) return;
     // A split tile puts its partial into its piece's slot, and the piece that counts in
     // last sums all pieces' slots in piece order into Y.
-    float* tile_slots = whole ? nullptr : partial + size_t(tile - full) * size_t(pieces) * (BM * BN);
-    float* my_slot = whole ? nullptr : tile_slots + size_t(piece) * (BM * BN);
+    if (whole) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+                const int n = n0 + 64 * wn + 32 * j + r32;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int m = m0 + 64 * wm + 32 * i + acc_row(v, g);
+                    if (m < M && n < N) Y[int64_t(m) * N + n] = acc[i][j][v];
+                }
+            }
+        return;
+    }
+    constexpr uint32_t kSlotBytes = BM * BN * sizeof(float);
+    const __amdgpu_buffer_rsrc_t slots =
+        make_rsrc(partial + size_t(tile - full) * size_t(pieces) * (BM * BN), int64_t(pieces) * kSlotBytes);
 #pragma unroll
     for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; v += 4)
+                splitk_put<kThreads>(slots, uint32_t(piece) * kSlotBytes, ((i * TJ + j) * 16 + v) / 4,
+                                     splitk_f4{acc[i][j][v], acc[i][j][v + 1], acc[i][j][v + 2], acc[i][j][v + 3]});
+    if (!splitk_arrive(counters + (tile - full), pieces, reinterpret_cast<unsigned*>(&g_slot0))) return;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {   // one row of accumulator tiles at a time (registers)
+        float y[TJ * 16];
+        splitk_sum<TJ * 16, kThreads>(slots, kSlotBytes, pieces, i * TJ * 4, y);
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
             const int n = n0 + 64 * wn + 32 * j + r32;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int m = m0 + 64 * wm + 32 * i + acc_row(v, g);
-                if (!whole)
-                    splitk_put(my_slot, splitk_index<TI, TJ, kThreads>(i, j, v, t), acc[i][j][v]);
-                else if (m < M && n < N)
-                    Y[int64_t(m) * N + n] = acc[i][j][v];
+                if (m < M && n < N) Y[int64_t(m) * N + n] = y[j * 16 + v];
             }
         }
-    if (whole || !splitk_arrive(counters + (tile - full), pieces, reinterpret_cast<unsigned*>(&g_slot0))) return;
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-            float y[16];
-            splitk_sum_tile<TI, TJ, kThreads>(tile_slots, pieces, i, j, y);
-            const int n = n0 + 64 * wn + 32 * j + r32;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = m0 + 64 * wm + 32 * i + acc_row(v, g);
-                if (m < M && n < N) Y[int64_t(m) * N + n] = y[v];
-            }
-        }
+    }
 }
 
 template __global__ void mmq_f8_q4k_kernel<false>(const uint8_t* __restrict__, const uint8_t* __restrict__,

@@ -30,23 +30,27 @@ inline size_t splitk_scratch_bytes(int64_t tiles, int64_t pieces, int64_t tile_f
     return splitk_counter_offset(tiles, pieces, tile_floats) + size_t(tiles) * 4;
 }
 
-// The partials move with relaxed agent-scope atomic loads and stores: on gfx950 these are
-// plain loads and stores with the sc1 cache policy, coherent across the XCDs' L2 caches
-// (written through past this XCD's L2, read past any line another call left in it).  That
-// is all the exchange needs: no fence, so no cache-wide write-back or invalidate that
-// would evict the data of every other workgroup on the XCD.
+// The partials move through buffer loads and stores with the sc1 cache policy: on gfx950
+// these are coherent across the XCDs' L2 caches (written through past this XCD's L2, read
+// past any line another call left in it), the same policy as relaxed agent-scope atomic
+// loads and stores.  That is all the exchange needs: no fence, so no cache-wide write-back
+// or invalidate that would evict the data of every other workgroup on the XCD.
+//
+// A thread's partial is E = TI TJ 16 floats (element e = (i TJ + j) 16 + v of its
+// accumulator tiles), moved 4 at a time: group q = e / 4 of thread t sits at byte
+// 16 (q THREADS + t) of its piece's slot, so that the THREADS threads of a workgroup move
+// one contiguous block per 16-byte access.
 
-// Element v of accumulator tile (i, j) of thread t in a partial slot: [element][thread],
-// so that for a fixed element the THREADS threads of a workgroup store contiguously.
-template <int TI, int TJ, int THREADS>
-__device__ __forceinline__ int splitk_index(int i, int j, int v, int t) {
-    return ((i * TJ + j) * 16 + v) * THREADS + t;
-}
+typedef unsigned splitk_u4 __attribute__((ext_vector_type(4)));
+typedef float splitk_f4 __attribute__((ext_vector_type(4)));
+constexpr int kSplitkSc1 = 16;   // cache-policy bit sc1 of a buffer access
 
-// Store element v of tile (i, j) of this thread's partial (relaxed agent-scope atomic
-// store: a plain store with the sc1 policy).
-__device__ __forceinline__ void splitk_put(float* slot, int index, float value) {
-    __hip_atomic_store(slot + index, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Store group q (4 floats) of this thread's partial into a slot that starts `slot_off`
+// bytes into the buffer `r`.
+template <int THREADS>
+__device__ __forceinline__ void splitk_put(__amdgpu_buffer_rsrc_t r, uint32_t slot_off, int q, splitk_f4 value) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(splitk_u4, value), r,
+                                           uint32_t((q * THREADS + int(threadIdx.x)) * 16), slot_off, kSplitkSc1);
 }
 
 // After every thread has put its whole partial into its piece's slot: count the piece in.
@@ -62,25 +66,44 @@ __device__ __forceinline__ bool splitk_arrive(unsigned* __restrict__ counter, in
     return *ticket == unsigned(pieces - 1);
 }
 
-// In the last piece: the sums, in piece order, of the 16 elements of this thread's
-// accumulator tile (i, j) over every piece (its own partial is read back as well: the same
-// bits it stored).  A piece's 16 loads are issued together, so one tile costs `pieces`
-// memory latencies, not 16 x pieces.
-template <int TI, int TJ, int THREADS>
-__device__ __forceinline__ void splitk_sum_tile(const float* tile_slots, int pieces, int i, int j, float (&s)[16]) {
-    constexpr int kSlot = TI * TJ * 16 * THREADS;
-    const float* base = tile_slots + splitk_index<TI, TJ, THREADS>(i, j, 0, threadIdx.x);
+// In the last piece: the sums, in piece order, of E elements of this thread's partial
+// (groups q0 .. q0 + E / 4 - 1) over the `pieces` slots of a tile (slot p at byte
+// p * slot_bytes of `r`; its own partial is read back as well: the same bits it stored).
+// Two pieces' loads are in flight at a time.
+template <int E, int THREADS>
+__device__ __forceinline__ void splitk_sum(__amdgpu_buffer_rsrc_t r, uint32_t slot_bytes, int pieces, int q0,
+                                           float (&s)[E]) {
+    constexpr int G = E / 4;
+    auto load = [&](int p, int q) {
+        return __builtin_bit_cast(splitk_f4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 r, uint32_t(((q0 + q) * THREADS + int(threadIdx.x)) * 16),
+                                                 uint32_t(p) * slot_bytes, kSplitkSc1));
+    };
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-        s[v] = __hip_atomic_load(base + v * THREADS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int p = 1; p < pieces; ++p) {
-        float u[16];
+    for (int q = 0; q < G; ++q) {
+        const splitk_f4 u = load(0, q);
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            u[v] = __hip_atomic_load(base + size_t(p) * kSlot + v * THREADS, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+        for (int c = 0; c < 4; ++c) s[4 * q + c] = u[c];
+    }
+    for (int p = 1; p < pieces; p += 2) {
+        const bool two = p + 1 < pieces;
+        splitk_f4 u[G], w[G];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[v] += u[v];
+        for (int q = 0; q < G; ++q) u[q] = load(p, q);
+        if (two) {
+#pragma unroll
+            for (int q = 0; q < G; ++q) w[q] = load(p + 1, q);
+        }
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) s[4 * q + c] += u[q][c];
+        if (two) {
+#pragma unroll
+            for (int q = 0; q < G; ++q)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) s[4 * q + c] += w[q][c];
+        }
     }
 }
 

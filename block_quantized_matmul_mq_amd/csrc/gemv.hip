@@ -417,6 +417,31 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
     }
 }
 
+// Threads per workgroup and ring depth of the vector kernel (every type).
+constexpr int kGemvThreads = 1024;
+constexpr int kGemvSlots = 2;
+
+template <int QT>
+const void* kernel_ptr() {
+    return reinterpret_cast<const void*>(gemv_kernel<QT, kGemvThreads, kGemvSlots>);
+}
+
+const void* kernel_for(int type) {
+    switch (type) {
+        case kQ4_K: return kernel_ptr<kQ4_K>();
+        case kQ5_K: return kernel_ptr<kQ5_K>();
+        case kQ6_K: return kernel_ptr<kQ6_K>();
+        case kQ8_0: return kernel_ptr<kQ8_0>();
+        case kQ4_0: return kernel_ptr<kQ4_0>();
+        case kQ4_1: return kernel_ptr<kQ4_1>();
+        case kQ5_0: return kernel_ptr<kQ5_0>();
+        case kQ5_1: return kernel_ptr<kQ5_1>();
+        default: return nullptr;
+    }
+}
+
+}  // namespace
+
 size_t fixed_lds_bytes(int type, int64_t K) {
     const int64_t vals = unit_values(type);
     const int64_t chunks = vals / 16;
@@ -427,81 +452,6 @@ size_t fixed_lds_bytes(int type, int64_t K) {
     else if (type != kQ8_0) b += size_t(K / 32) * 4;         // sums per 32-block
     return b;
 }
-
-// Threads per workgroup and ring depth, per type; an MQ_GEMV_CONFIG=threads,slots
-// environment setting (read once, bench A/B only) picks another built variant.
-struct Config {
-    int threads, slots;
-};
-constexpr Config kConfigs[] = {{1024, 2}, {1024, 3}, {1024, 4}, {512, 4}, {512, 6}, {512, 8}};
-
-template <int QT, int T, int S>
-const void* kernel_ptr() {
-    return reinterpret_cast<const void*>(gemv_kernel<QT, T, S>);
-}
-
-template <int QT>
-const void* pick_kernel(Config c) {
-    if (c.threads == 1024 && c.slots == 2) return kernel_ptr<QT, 1024, 2>();
-    if (c.threads == 1024 && c.slots == 3) return kernel_ptr<QT, 1024, 3>();
-    if (c.threads == 1024 && c.slots == 4) return kernel_ptr<QT, 1024, 4>();
-    if (c.threads == 512 && c.slots == 4) return kernel_ptr<QT, 512, 4>();
-    if (c.threads == 512 && c.slots == 6) return kernel_ptr<QT, 512, 6>();
-    if (c.threads == 512 && c.slots == 8) return kernel_ptr<QT, 512, 8>();
-    return nullptr;
-}
-
-const void* kernel_for(int type, Config c) {
-    switch (type) {
-        case kQ4_K: return pick_kernel<kQ4_K>(c);
-        case kQ5_K: return pick_kernel<kQ5_K>(c);
-        case kQ6_K: return pick_kernel<kQ6_K>(c);
-        case kQ8_0: return pick_kernel<kQ8_0>(c);
-        case kQ4_0: return pick_kernel<kQ4_0>(c);
-        case kQ4_1: return pick_kernel<kQ4_1>(c);
-        case kQ5_0: return pick_kernel<kQ5_0>(c);
-        case kQ5_1: return pick_kernel<kQ5_1>(c);
-        default: return nullptr;
-    }
-}
-
-Config default_config(int type) {
-    switch (type) {
-        case kQ4_K: return {1024, 2};
-        case kQ6_K: return {1024, 2};
-        default: return {1024, 2};
-    }
-}
-
-Config chosen_config(int type) {
-    static int env_threads = -1, env_slots = -1;
-    if (env_threads < 0) {
-        env_threads = 0;
-        env_slots = 0;
-        if (const char* e = getenv("MQ_GEMV_CONFIG")) {
-            int t = 0, s = 0;
-            if (sscanf(e, "%d,%d", &t, &s) == 2) { env_threads = t; env_slots = s; }
-        }
-    }
-    if (env_threads > 0) {
-        const Config c{env_threads, env_slots};
-        if (kernel_for(type, c)) return c;
-    }
-    return default_config(type);
-}
-
-// Wide matrices go to the matrix-core kernels unless MQ_GEMV_MFMA=0 (read once;
-// bench A/B only).
-bool use_mfma() {
-    static int v = -1;
-    if (v < 0) {
-        const char* e = getenv("MQ_GEMV_MFMA");
-        v = (e && e[0] == '0') ? 0 : 1;
-    }
-    return v == 1;
-}
-
-}  // namespace
 
 // Largest tile (in units) that fits next to the staged x; 0 if not even one row fits.
 int gemv_tile_units(int type, int64_t K, size_t lds_limit) {
@@ -517,11 +467,9 @@ int gemv_tile_units(int type, int64_t K, size_t lds_limit) {
 
 hipError_t gemv_set_attributes(size_t lds_limit) {
     for (int type : {kQ4_K, kQ5_K, kQ6_K, kQ8_0, kQ4_0, kQ4_1, kQ5_0, kQ5_1}) {
-        for (const Config& c : kConfigs) {
-            hipError_t e = hipFuncSetAttribute(kernel_for(type, c), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               int(lds_limit));
-            if (e != hipSuccess) return e;
-        }
+        hipError_t e = hipFuncSetAttribute(kernel_for(type), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           int(lds_limit));
+        if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
@@ -530,11 +478,11 @@ hipError_t launch_gemv(int type, BlockLayout layout, const uint8_t* W, const flo
                        int64_t K, hipStream_t s, const char** name) {
     const DeviceInfo* info = device_info();
     if (!info) return hipErrorInvalidDevice;
-    if (use_mfma() && type == kQ4_K && gemv_mfma_applies(type, N, K, info->cu_count))
+    if (type == kQ4_K && gemv_mfma_applies(type, N, K, info->cu_count))
         return launch_gemv_mfma(W, x, y, N, K, info->cu_count, s, name);
-    if (use_mfma() && gemv_tiled_applies(type, layout, W, N, K, info->cu_count))
+    if (gemv_tiled_applies(type, layout, W, N, K, info->cu_count))
         return launch_gemv_tiled(type, W, x, y, N, K, info->cu_count, s, name);
-    if (use_mfma() && gemv_wide_applies(type, layout, W, N, K, info->cu_count))
+    if (gemv_wide_applies(type, layout, W, N, K, info->cu_count))
         return launch_gemv_wide(type, W, x, y, N, K, info->cu_count, s, name);
     int tile = gemv_tile_units(type, K, info->lds_per_block);
     if (tile <= 0) return hipErrorInvalidValue;
@@ -548,8 +496,7 @@ hipError_t launch_gemv(int type, BlockLayout layout, const uint8_t* W, const flo
     const int64_t rows_tile = (rows_wg + ntiles - 1) / ntiles;
     tile = int(rows_tile * U);
     const size_t shmem = fixed_lds_bytes(type, K) + size_t(tile) * 4;
-    const Config c = chosen_config(type);
-    const void* kern = kernel_for(type, c);
+    const void* kern = kernel_for(type);
     const bool repacked = layout.off != 0 || (type == kQ6_K && layout.stride != 210);
     switch (type) {
         case kQ8_0: *name = repacked ? "gemv<q8_0 repacked>" : "gemv<q8_0>"; break;
@@ -565,7 +512,7 @@ hipError_t launch_gemv(int type, BlockLayout layout, const uint8_t* W, const flo
     int64_t row_bytes = (K / block_values_of(type)) * layout.stride;
     int n = int(N), k = int(K), stride = layout.stride, off = layout.off;
     void* args[] = {&W, &x, &y, &n, &k, &row_bytes, &tile, &stride, &off};
-    return hipLaunchKernel(kern, dim3(grid), dim3(c.threads), args, shmem, s);
+    return hipLaunchKernel(kern, dim3(grid), dim3(kGemvThreads), args, shmem, s);
 }
 
 }  // namespace mq

@@ -788,6 +788,24 @@ hipError_t launch_typed(const uint8_t* W, const int8_t* codes, const float* xs, 
 
 }  // namespace
 
+size_t mmq_smem_bytes(int type, int bm) {
+    auto pick = [&](auto qt) -> size_t {
+        constexpr int QT = decltype(qt)::value;
+        return bm == 32 ? sizeof(Smem<QT, 32>) : bm == 128 ? sizeof(Smem<QT, 128>) : 0;
+    };
+    switch (type) {
+        case kQ4_K: return pick(std::integral_constant<int, kQ4_K>{});
+        case kQ5_K: return pick(std::integral_constant<int, kQ5_K>{});
+        case kQ6_K: return pick(std::integral_constant<int, kQ6_K>{});
+        case kQ8_0: return pick(std::integral_constant<int, kQ8_0>{});
+        case kQ4_0: return pick(std::integral_constant<int, kQ4_0>{});
+        case kQ4_1: return pick(std::integral_constant<int, kQ4_1>{});
+        case kQ5_0: return pick(std::integral_constant<int, kQ5_0>{});
+        case kQ5_1: return pick(std::integral_constant<int, kQ5_1>{});
+        default: return 0;
+    }
+}
+
 MmqPlan mmq_plan(int /*type*/, int64_t M, int64_t N, int64_t K) {
     // kTargetWorkgroups workgroups fill the chip.  Tiles are dealt whole while they fill it;
     // the tiles of a last, less than half full round (or all tiles, when there are fewer

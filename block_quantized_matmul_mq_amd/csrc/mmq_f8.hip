@@ -547,6 +547,8 @@ bool mmq_f8_applies(int type, int64_t M, int64_t N) {
     return type == kQ4_K && M > 32 && ((M + BM - 1) / BM) * ((N + BN - 1) / BN) >= kTargetWorkgroups;
 }
 
+size_t mmq_f8_lds_bytes() { return 3 * sizeof(Slot) + 2 * sizeof(Work); }
+
 MmqPlan mmq_f8_plan(int64_t M, int64_t N, int64_t K) {
     // As mmq_plan, with 64-value K-steps: tiles are dealt whole while they fill rounds of
     // kTargetWorkgroups; the tiles of a last round that is at most half full (or all tiles,

@@ -350,6 +350,24 @@ int mq_gemm_noalloc(const void* W, int type, const void* Xq, float* Y, int64_t M
                        M, N, K, stream);
 }
 
+size_t mq_debug_lds_bytes(int what, int type, int64_t K) {
+    BlockLayout lay;
+    type = parse_type(type, lay);
+    if (type == 0) return 0;
+    switch (what) {
+        case MQ_LDS_GEMV_FIXED:
+            if (K <= 0 || K > MQ_MAX_K || K % block_values(type) != 0) return 0;
+            return fixed_lds_bytes(type, K);
+        case MQ_LDS_GEMV_TILE_UNITS:
+            if (K <= 0 || K > MQ_MAX_K || K % block_values(type) != 0) return 0;
+            return size_t(gemv_tile_units(type, K, MQ_GFX950_LDS_BYTES));
+        case MQ_LDS_MMQ_I8_BM128: return mmq_smem_bytes(type, 128);
+        case MQ_LDS_MMQ_I8_BM32: return mmq_smem_bytes(type, 32);
+        case MQ_LDS_MMQ_F8: return type == MQ_Q4_K ? mmq_f8_lds_bytes() : 0;
+        default: return 0;
+    }
+}
+
 int mq_debug_gemm_blockdots(const void* W, int type, const void* Xq, int32_t* D, int64_t M, int64_t N, int64_t K,
                             void* stream) {
     const char* fn = "mq_debug_gemm_blockdots";

@@ -56,6 +56,11 @@ struct BlockLayout {
 hipError_t launch_quantize_act(const float* X, int8_t* codes, float* scales, int32_t* sums, uint8_t* digits,
                                uint8_t* step_scales, int64_t M, int64_t K, hipStream_t s);
 int gemv_tile_units(int type, int64_t K, size_t lds_limit);
+// LDS of the vector GEMV besides its row tile: the staged x (digit planes, block
+// exponents and sums), and of the MMQ kernels (int8: per type and tile rows; fp8 Q4_K).
+size_t fixed_lds_bytes(int type, int64_t K);
+size_t mmq_smem_bytes(int type, int bm);
+size_t mmq_f8_lds_bytes();
 hipError_t gemv_set_attributes(size_t lds_limit);
 hipError_t launch_gemv(int type, BlockLayout layout, const uint8_t* W, const float* x, float* y, int64_t N,
                        int64_t K, hipStream_t s, const char** kernel_name);

@@ -224,6 +224,28 @@ int mq_gemm_noalloc(const void* W, int type, const void* Xq, float* Y, int64_t M
                     void* stream);
 
 /*
+ * mq_debug_lds_bytes -- test helper: the LDS sizes the kernels are built and
+ * launched with, computed on the host from the same formulas and structs the
+ * kernels use ("minfer CUDA Backend Design", 2.4: one shared-memory formula per
+ * kernel, checked by tests).  No device is needed.  Returns 0 for an unknown
+ * `what`, type or K.
+ *   MQ_LDS_GEMV_FIXED       vector GEMV, bytes besides the row tile (staged x
+ *                           digit planes, block exponents and sums) for (type, K)
+ *   MQ_LDS_GEMV_TILE_UNITS  vector GEMV, row-tile units (4 bytes each) that fit
+ *                           next to them in MQ_GFX950_LDS_BYTES
+ *   MQ_LDS_MMQ_I8_BM128 / _BM32  int8 MMQ workgroup LDS for the type at 128- /
+ *                           32-row tiles (two workgroups share a CU)
+ *   MQ_LDS_MMQ_F8           fp8 Q4_K MMQ workgroup LDS (one workgroup per CU)
+ */
+#define MQ_GFX950_LDS_BYTES (160 * 1024)
+#define MQ_LDS_GEMV_FIXED 0
+#define MQ_LDS_GEMV_TILE_UNITS 1
+#define MQ_LDS_MMQ_I8_BM128 2
+#define MQ_LDS_MMQ_I8_BM32 3
+#define MQ_LDS_MMQ_F8 4
+size_t mq_debug_lds_bytes(int what, int type, int64_t K);
+
+/*
  * mq_debug_gemm_blockdots -- test export: the exact int32 block dot products
  * the mq_gemm kernel forms, written to D (device) as int32 [M][N][G] with
  * G = K / 16 for Q6_K (dot of (code - 32) per 16-value group) and G = K / 32

@@ -230,6 +230,31 @@ def test_q4k_fp8_path_extreme_activations():
     assert kernel == "mmq_f8<q4_K>", kernel
 
 
+def test_one_plane_serves_qkv_and_gate_up():
+    """One quantized plane of the 7B prefill input (M = 512, K = 3584) feeds the q, k and
+    v products and the gate and up products, as a layer runs them; each is compared with
+    the oracle on sampled columns, and the plane is unchanged by them."""
+    import torch
+    dev = device()
+    M, K = 512, 3584
+    X = synth.activations(M, K, config_index=3, tensor_index=20)
+    Xq = quantized_plane(X, dev)
+    before = Xq.clone()
+    rng = np.random.default_rng(21)
+    for name, N, tensor in [("attn_q", 3584, 1), ("attn_k", 512, 2), ("attn_v", 512, 4),
+                            ("ffn_gate", 18944, 5), ("ffn_up", 18944, 0)]:
+        raw = synth.quantized_weight(mq.Q4_K, N, K, 3, tensor)
+        say(f"gemm q4_K {name} {N}x{K} from the shared plane")
+        Y = mq.gemm(to_dev(raw.reshape(-1), dev), mq.Q4_K, Xq, M, N, K)
+        torch.cuda.synchronize()
+        cols = np.unique(np.concatenate([rng.choice(N, 160, replace=False), [0, N - 1]]))
+        xn, q, d = x_hat_norms(X)
+        ref = oracle.mmq(raw.reshape(N, -1)[cols], mq.Q4_K, q, d, len(cols), K)
+        check_normalized(Y.cpu().numpy()[:, cols], ref, row_norms(raw, mq.Q4_K, N, K, cols), xn,
+                         f"{name} from the shared plane")
+    assert torch.equal(Xq, before), "a product changed the activation plane"
+
+
 def test_blockdots_config1_q8_0_m16():
     N, K = 4864, 896
     raw = synth.quantized_weight(mq.Q8_0, N, K, 0, 0)

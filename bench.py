@@ -5,27 +5,36 @@ Qwen2.5-7B-shaped inputs (weights N(0, 0.02) quantized to Q4_K, activations
 N(0, 1)):
 
   decode  : mq_gemv Q4_K ffn_up 18944x3584 and ffn_down 3584x18944 at M=1
-  prefill : mq_quantize_act 512x3584, then mq_gemm (int8 MMQ) with the Q4_K
+  prefill : mq_quantize_act 512x3584, then mq_gemm (MMQ) with the Q4_K
             ffn_up 18944x3584, attn_q 3584x3584, attn_k and attn_v 512x3584
 
 Inputs are resident in HBM before timing starts.  Each GEMV weight is kept in
-several copies that consecutive launches rotate through, so every GEMV launch
-reads its weights from HBM and not from the 256 MB last-level cache.  Launches
-are recorded once into HIP graphs and replayed; HIP events on the launch
-stream bracket the replays (per-kernel time = elapsed / launches).
+several copies, and consecutive steps rotate through them, so every GEMV launch
+reads its weights from HBM and not from the 256 MB last-level cache.  Each step
+is recorded once into a HIP graph (one graph per weight copy); the timed region
+replays exactly --steps of them, bracketed by HIP events on the launch stream.
+Per-kernel times come from graphs of one kernel's launches back to back.
 
 Printed JSON line (one GPU):
   value        Q4_K GEMV weight GB/s: GGUF payload bytes of the two decode
                GEMVs / their summed kernel time
   mmq_prefill_tops   2*M*N*K of the four MMQ launches / their kernel time
-  roofline     the Q4_K GEMV against 8 TB/s HBM: achieved = algorithmic bytes
-               (payload + x + y) per launch / mean launch time; traffic = HBM
-               bytes per launch from the committed rocprofv3 FETCH_SIZE /
-               WRITE_SIZE summary under profiles/, null once the kernel
-               sources differ from the ones the counters were taken on
-  roofline_mmq the ffn_up MMQ against 5.0 POP/s dense int8 MFMA
-  secondary    Q6_K vocab-head and Q8_0 GEMV GB/s, the quantizer
-  cpu_baseline the CPU oracle's GEMV on the same ffn_up + ffn_down weights
+  roofline     the Q4_K GEMV against 8 TB/s HBM and against a plain read of the
+               same bytes with the same workgroup count (libmq_measure.so):
+               achieved = algorithmic bytes (payload + x + y) per launch / mean
+               launch time; traffic = HBM bytes per launch from the committed
+               rocprofv3 FETCH_SIZE / WRITE_SIZE summary under profiles/, null
+               once any kernel source differs from the ones it was taken on
+  roofline_mmq the ffn_up MMQ against 5.0 POP/s dense int8 / fp8 MFMA, with the
+               matrix-unit busy fraction and clock from the committed counters
+  warm_cache   the decode GEMVs with one weight copy (weights resident in the
+               last-level cache): labelled, never the value
+  c5_14b       Qwen2.5-14B layer mix at M=1 (GEMV) and M=2048 (quantize + MMQ)
+  secondary    Q6_K vocab-head and Q8_0 GEMV GB/s, other types, the quantizer
+  cpu_baseline the CPU oracle (as written) on the same decode weights, on all
+               host cores (rows split over processes) and on one thread, with
+               the CPU model; plus oracle times for the head GEMV, the M=512 MMQ
+               and quantize_act on stated samples.  Runs before the GPU is used.
 
 --counters skips timing: every kernel of the step runs a few times eagerly,
 next to a plain 256 MiB device copy that calibrates the HBM byte counters.
@@ -62,28 +71,41 @@ def parse():
     return p.parse_args()
 
 
-def recorded_traffic(summary, sources):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, or None.
-
-    The summary records FETCH_SIZE and WRITE_SIZE passes (scaled by a plain copy of
-    known size) and the sha256 of the kernel sources they were taken on; once those
-    sources change the figure no longer describes the kernel and None is returned.
-    """
+def kernel_sources_sha256():
+    """sha256 over every kernel source of libmq (all of csrc/, in name order)."""
     import hashlib
+    import os
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_quantized_matmul_mq_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_fields(summary):
+    """`key: value` fields of a committed rocprofv3 summary under profiles/, or {}.
+
+    A summary records the sha256 of the kernel sources it was taken on; once any
+    source changes, its figures no longer describe the kernels and {} is returned.
+    """
     import os
     root = os.path.dirname(os.path.abspath(__file__))
     try:
-        fields = dict(line.split(": ", 1) for line in open(os.path.join(root, "profiles", summary)).read().splitlines()
-                      if line.startswith(("kernel_source_sha256: ", "traffic_bytes_per_launch: ")))
+        lines = open(os.path.join(root, "profiles", summary)).read().splitlines()
     except OSError:
-        return None
-    h = hashlib.sha256()
-    for src in sources:
-        with open(os.path.join(root, "block_quantized_matmul_mq_amd", "csrc", src), "rb") as f:
-            h.update(f.read())
-    if fields.get("kernel_source_sha256") != h.hexdigest():
-        return None
-    return int(fields["traffic_bytes_per_launch"])
+        return {}
+    fields = dict(line.split(": ", 1) for line in lines if ": " in line and not line.startswith((" ", "#")))
+    if fields.get("kernel_source_sha256") != kernel_sources_sha256():
+        return {}
+    return fields
+
+
+def recorded_traffic(summary):
+    v = recorded_fields(summary).get("traffic_bytes_per_launch")
+    return int(v) if v is not None else None
 
 
 def copies_for(nbytes):
@@ -91,27 +113,116 @@ def copies_for(nbytes):
     return max(2, -(-2 * LLC_BYTES // nbytes))
 
 
-def cpu_baseline(w_up, w_down, x_up, x_down):
-    """The oracle (as written, single thread) on the full decode pair, median of 3."""
+# Arrays the CPU-baseline workers read (set before the worker processes fork).
+_CPU = {}
+
+
+def _cpu_work(task):
+    """One piece of oracle work: (kind, lo, hi) rows (or columns) of a workload."""
     import oracle
+    from threadpoolctl import threadpool_limits
+    kind, lo, hi = task
+    with threadpool_limits(limits=1):
+        if kind == "gemv_up":
+            oracle.gemv(_CPU["w_up"][lo:hi], Q4_K, _CPU["x_up"], hi - lo, 3584)
+        elif kind == "gemv_down":
+            oracle.gemv(_CPU["w_down"][lo:hi], Q4_K, _CPU["x_down"], hi - lo, 18944)
+        elif kind == "gemv_head":
+            oracle.gemv(_CPU["head"][lo:hi], Q6_K, _CPU["x_head"], hi - lo, 3584)
+        elif kind == "mmq":
+            q, d = _CPU["q8"]
+            oracle.mmq(_CPU["w_up"][lo:hi], Q4_K, q, d, hi - lo, 3584)
+        elif kind == "quantize":
+            oracle.quantize_act(_CPU["X"][lo:hi])
+    return 0
+
+
+def _cpu_model():
     try:
-        from threadpoolctl import threadpool_limits
-        limit = threadpool_limits(limits=1)
-    except Exception:  # pragma: no cover
-        limit = None
-    times = []
-    for _ in range(3):
-        t0 = time.perf_counter()
-        oracle.gemv(w_up, Q4_K, x_up, 18944, 3584)
-        oracle.gemv(w_down, Q4_K, x_down, 3584, 18944)
-        times.append(time.perf_counter() - t0)
-    if limit is not None:
-        limit.unregister()
-    t = float(np.median(times))
-    nbytes = w_up.nbytes + w_down.nbytes
-    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "numpy f64 oracle GEMV over the full Q4_K ffn_up 18944x3584 + ffn_down "
-                      f"3584x18944 weights, 1 thread, median of 3 ({t:.2f} s per pair)"}
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(w_up, w_down, x_up, x_down, X):
+    """The oracle, as written, on the host cores: the decode GEMV pair (the line's value is
+    the all-core rate), and the head GEMV, the M=512 MMQ and quantize_act on stated samples.
+
+    All cores: the rows (columns for the MMQ) are split evenly over one worker process per
+    core, each running the oracle with one BLAS thread; one thread: the same calls in this
+    process.  Median of 3 runs each.  Called before the GPU is touched, so the workers fork
+    from a process that has not initialised HIP."""
+    import multiprocessing
+    import os
+
+    from block_quantized_matmul_mq_amd import synth
+    import oracle
+
+    affinity = len(os.sched_getaffinity(0))
+    workers = max(1, min(affinity, 16))   # the host share of one GPU is 16 cores
+    head_rows = 8192                      # sample of the 152064-row Q6_K head
+    mmq_cols = 2048                       # sample of the 18944 ffn_up columns, all 512 rows
+    _CPU.update(w_up=w_up, w_down=w_down, x_up=x_up, x_down=x_down, X=X,
+                head=synth.quantized_weight(Q6_K, head_rows, 3584, 2, 0),
+                x_head=synth.activations(1, 3584, 2)[0])
+    q, d, _ = oracle.quantize_act(X)
+    _CPU["q8"] = (q, d)
+
+    def split(kind, n, parts):
+        edges = np.linspace(0, n, parts + 1).astype(int)
+        return [(kind, int(a), int(b)) for a, b in zip(edges[:-1], edges[1:]) if b > a]
+
+    def median_time(run):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            run()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    workloads = {
+        "gemv_pair": [("gemv_up", 18944), ("gemv_down", 3584)],
+        "gemv_head": [("gemv_head", head_rows)],
+        "mmq": [("mmq", mmq_cols)],
+        "quantize": [("quantize", X.shape[0])],
+    }
+    one, allc = {}, {}
+    for name, parts in workloads.items():
+        one[name] = median_time(lambda: [_cpu_work((k, 0, n)) for k, n in parts])
+    ctx = multiprocessing.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        for name, parts in workloads.items():
+            tasks = [t for k, n in parts for t in split(k, n, workers)]
+            pool.map(_cpu_work, tasks)   # warm the workers
+            allc[name] = median_time(lambda: pool.map(_cpu_work, tasks, chunksize=1))
+    _CPU.clear()
+
+    pair_bytes = w_up.nbytes + w_down.nbytes
+    head_bytes = head_rows * 3584 // 256 * 210
+    mmq_ops = 2 * X.shape[0] * mmq_cols * 3584
+    qa_bytes = X.nbytes
+
+    def rates(t):
+        return {"gemv_pair_GBps": round(pair_bytes / t["gemv_pair"] / 1e9, 4),
+                "gemv_q6_K_head_GBps": round(head_bytes / t["gemv_head"] / 1e9, 4),
+                "mmq_q4_K_M512_GOPs": round(mmq_ops / t["mmq"] / 1e9, 3),
+                "quantize_act_GBps_in": round(qa_bytes / t["quantize"] / 1e9, 4),
+                "seconds": {k: round(v, 4) for k, v in t.items()}}
+
+    return {
+        "value": round(pair_bytes / allc["gemv_pair"] / 1e9, 4), "unit": "GB/s", "cores": workers,
+        "kind": "oracle",
+        "sample": (f"numpy f64 oracle GEMV over the full Q4_K ffn_up 18944x3584 + ffn_down 3584x18944 "
+                   f"weights, rows split over {workers} worker processes with 1 BLAS thread each, median "
+                   f"of 3; also on 1 thread, and the Q6_K head GEMV on {head_rows} of 152064 rows, the "
+                   f"Q4_K MMQ at M=512 on {mmq_cols} of 18944 columns, quantize_act on 512x3584"),
+        "cpu_model": _cpu_model(), "host_cpus_in_affinity": affinity,
+        "all_cores": rates(allc), "one_thread": rates(one),
+    }
 
 
 class GraphTimer:
@@ -140,6 +251,71 @@ class GraphTimer:
         return 1000.0 * start.elapsed_time(end) / (replays * len(launches))
 
 
+def load_measure_lib():
+    import ctypes
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_quantized_matmul_mq_amd",
+                        "libmq_measure.so")
+    lib = ctypes.CDLL(path)
+    lib.mq_measure_read.restype = ctypes.c_int
+    lib.mq_measure_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p]
+    lib.mq_measure_sink_words.restype = ctypes.c_size_t
+    lib.mq_measure_sink_words.argtypes = [ctypes.c_int, ctypes.c_int]
+    return lib
+
+
+# Qwen2.5-14B layer mix: (name, type, N, K, uses per layer); q and o, k and v, gate and up
+# share a shape
+C5 = [("attn_q_o", Q4_K, 5120, 5120, 2), ("attn_k_v", Q4_K, 1024, 5120, 2),
+      ("ffn_gate_up", Q4_K, 13824, 5120, 2), ("ffn_down", Q6_K, 5120, 13824, 1)]
+C5_M = 2048
+
+
+def c5_layer_mix(torch, mq, synth, timer, to_dev, dev, reps):
+    """Per-shape GEMV (M = 1, weights rotated past the last-level cache) and quantize + MMQ
+    (M = 2048) times for the 14B layer mix, and one layer's totals: q, k, v, o, gate, up,
+    down, with the activation planes the layer quantizes (3 of 2048 x 5120, 1 of 2048 x
+    13824)."""
+    out = {}
+    X = {K: torch.from_numpy(synth.activations(C5_M, K, 4, tensor_index=20 + i)).to(dev)
+         for i, K in enumerate((5120, 13824))}
+    Xq = {K: mq.quantize_act(X[K]) for K in X}
+    t_quant = {K: timer.per_launch_us([lambda K=K: mq.quantize_act(X[K], Xq[K])] * 4, reps) for K in X}
+    layer_gemv_us = layer_mmq_us = 0.0
+    layer_bytes = layer_ops = 0
+    for i, (name, qt, N, K, uses) in enumerate(C5):
+        raw = synth.quantized_weight(qt, N, K, 4, i)
+        nb = mq.weight_bytes(qt, N, K)
+        wc = [to_dev(raw) for _ in range(copies_for(nb))]
+        del raw
+        x = torch.from_numpy(synth.activations(1, K, 4, tensor_index=30 + i)[0]).to(dev)
+        y = torch.empty(N, dtype=torch.float32, device=dev)
+        g_us = timer.per_launch_us([lambda W=W: mq.gemv(W, qt, x, N, K, y=y) for W in wc], reps)
+        gk = mq.last_kernel()
+        Y = torch.empty((C5_M, N), dtype=torch.float32, device=dev)
+        sc = torch.zeros(max(mq.gemm_scratch_bytes(qt, C5_M, N, K), 256), dtype=torch.uint8, device=dev)
+        m_us = timer.per_launch_us([lambda W=W: mq.gemm(W, qt, Xq[K], C5_M, N, K, Y=Y, scratch=sc) for W in wc[:2]],
+                                   reps)
+        ops = 2 * C5_M * N * K
+        out[f"{name}_{N}x{K}"] = {"type": "q4_K" if qt == Q4_K else "q6_K", "uses_per_layer": uses,
+                                  "gemv_M1_us": round(g_us, 3), "gemv_M1_GBps": round(nb / g_us / 1e3, 1),
+                                  "gemv_kernel": gk, "mmq_M2048_us": round(m_us, 3),
+                                  "mmq_M2048_TOPS": round(ops / m_us / 1e6, 2), "mmq_kernel": mq.last_kernel()}
+        layer_gemv_us += uses * g_us
+        layer_mmq_us += uses * m_us
+        layer_bytes += uses * nb
+        layer_ops += uses * ops
+        del wc, Y, sc
+    q_us = 3 * t_quant[5120] + t_quant[13824]
+    out["quantize_act_M2048_us"] = {"K5120": round(t_quant[5120], 3), "K13824": round(t_quant[13824], 3)}
+    out["layer"] = {"gemv_M1_us": round(layer_gemv_us, 2), "gemv_M1_GBps": round(layer_bytes / layer_gemv_us / 1e3, 1),
+                    "prefill_M2048_us": round(layer_mmq_us + q_us, 2),
+                    "prefill_M2048_TOPS": round(layer_ops / (layer_mmq_us + q_us) / 1e6, 2),
+                    "note": "q, k, v, o, gate, up, down; kernel times summed, quantize_act included at M=2048"}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -147,8 +323,22 @@ def main():
               "single-GPU and no multi-GPU path is built", file=sys.stderr)
         sys.exit(2)
 
+    from block_quantized_matmul_mq_amd import synth
+
+    # ---- host inputs (seeded), and the CPU baseline before the GPU is touched ----
+    w_host = {name: synth.quantized_weight(Q4_K, N, K, 1, i) for i, (name, N, K) in enumerate(DECODE)}
+    for i, (name, N, K) in enumerate(PREFILL[1:]):
+        w_host[name] = synth.quantized_weight(Q4_K, N, K, 3, i + 1)
+    x_dec = {name: synth.activations(1, K, 1, tensor_index=10 + i)[0] for i, (name, N, K) in enumerate(DECODE)}
+    X_pre = synth.activations(PREFILL_M, 3584, 3)
+    cpu = None
+    if not args.no_cpu_baseline and not args.counters:
+        cpu = cpu_baseline(w_host["ffn_up"], w_host["ffn_down"], x_dec["ffn_up"], x_dec["ffn_down"], X_pre)
+
+    import ctypes
+
     import torch
-    from block_quantized_matmul_mq_amd import mq, synth
+    from block_quantized_matmul_mq_amd import mq
 
     dev = torch.device("cuda:0")
     mq.init(0)
@@ -158,12 +348,6 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).to(dev)
 
     # ---- inputs, resident in HBM ----
-    w_host = {name: synth.quantized_weight(Q4_K, N, K, 1, i) for i, (name, N, K) in enumerate(DECODE)}
-    for i, (name, N, K) in enumerate(PREFILL[1:]):
-        w_host[name] = synth.quantized_weight(Q4_K, N, K, 3, i + 1)
-    x_dec = {name: synth.activations(1, K, 1, tensor_index=10 + i)[0] for i, (name, N, K) in enumerate(DECODE)}
-    X_pre = synth.activations(PREFILL_M, 3584, 3)
-
     ncopy = copies_for(mq.weight_bytes(Q4_K, 18944, 3584))
     copies = {name: [to_dev(w_host[name]) for _ in range(ncopy)] for name, _, _ in DECODE}
     w_pre = {name: to_dev(w_host[name]) for name, _, _ in PREFILL[1:]}
@@ -172,7 +356,7 @@ def main():
     X_dev = torch.from_numpy(X_pre).to(dev)
     Xq = torch.empty(mq.act_bytes(PREFILL_M, 3584), dtype=torch.uint8, device=dev)
     Y_dev = {name: torch.empty((PREFILL_M, N), dtype=torch.float32, device=dev) for name, N, _ in PREFILL}
-    scratch = {name: torch.empty(max(mq.gemm_scratch_bytes(Q4_K, PREFILL_M, N, K), 256), dtype=torch.uint8,
+    scratch = {name: torch.zeros(max(mq.gemm_scratch_bytes(Q4_K, PREFILL_M, N, K), 256), dtype=torch.uint8,
                                  device=dev) for name, N, K in PREFILL}
     torch.cuda.synchronize()
 
@@ -216,29 +400,32 @@ def main():
                           "kernel_names": kernel_names}), flush=True)
         return
 
-    # eager warmup (also sets the kernel names), then the timed step graph
+    # eager warmup (also sets the kernel names), then one graph per weight copy: graph c is
+    # one step (one pass of the hot path) on copy c
     for c in range(ncopy):
         for fn in step_launches(c):
             fn()
     torch.cuda.synchronize()
-
-    step_g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(step_g):
-        for c in range(ncopy):
+    step_graphs = []
+    for c in range(ncopy):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
             for fn in step_launches(c):
                 fn()
-    for _ in range(args.warmup):
-        step_g.replay()
+        step_graphs.append(g)
+    for i in range(args.warmup):
+        step_graphs[i % ncopy].replay()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(s)
-    for _ in range(args.steps):
-        step_g.replay()
+    for i in range(args.steps):
+        step_graphs[(args.warmup + i) % ncopy].replay()
     t_end.record(s)
     torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / (args.steps * ncopy)
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    del step_graphs
 
     # per-kernel times: each kernel alone, its launches back to back in a graph
     reps = max(2, args.steps // 2)
@@ -248,6 +435,32 @@ def main():
     avg_us["quantize_act"] = timer.per_launch_us([quant_launch] * 8, reps)
     for name, N, K in PREFILL:
         avg_us[f"mmq_{name}"] = timer.per_launch_us([mmq_launch(name, N, K, c % ncopy) for c in range(4)], reps)
+
+    # plain-read ceiling: the same rotated ffn_up copies read by a kernel that only reads,
+    # with the workgroup count of the GEMV (one per CU) and with the best of a few counts
+    meas = load_measure_lib()
+    up_bytes = mq.weight_bytes(Q4_K, 18944, 3584)
+    read_gbps = {}
+    for grid in (256, 512, 1024, 2048):
+        sink = torch.empty(meas.mq_measure_sink_words(grid, 1024), dtype=torch.int32, device=dev)
+
+        def read_launch(W, grid=grid, sink=sink):
+            rc = meas.mq_measure_read(ctypes.c_void_p(W.data_ptr()), up_bytes, ctypes.c_void_p(sink.data_ptr()),
+                                      grid, 1024, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc:
+                raise RuntimeError(f"plain-read kernel refused ({rc})")
+        us = timer.per_launch_us([lambda W=W: read_launch(W) for W in copies["ffn_up"]], reps)
+        read_gbps[grid] = up_bytes / us / 1e3
+    plain_read = max(read_gbps.values())
+
+    # warm cache (labelled, never the value): one weight copy, resident in the last-level cache
+    warm = {}
+    for name, N, K in DECODE:
+        us = timer.per_launch_us([gemv_launch(name, N, K, 0)] * 8, reps)
+        warm[f"gemv_{name}_us"] = round(us, 3)
+        warm[f"gemv_{name}_GBps"] = round(mq.weight_bytes(Q4_K, N, K) / us / 1e3, 1)
+    warm["note"] = ("weights resident in the 256 MB last-level cache (one copy, launches back to back); "
+                    "every other GEMV figure rotates copies past it")
 
     gemv_bytes = sum(mq.weight_bytes(Q4_K, N, K) for _, N, K in DECODE)
     # algorithmic bytes of one GEMV launch: GGUF payload + f32 x + f32 y (the same for both shapes)
@@ -261,6 +474,7 @@ def main():
     up_gbps = mq.weight_bytes(Q4_K, 18944, 3584) / (avg_us["gemv_ffn_up"] * 1e-6) / 1e9
     down_gbps = mq.weight_bytes(Q4_K, 3584, 18944) / (avg_us["gemv_ffn_down"] * 1e-6) / 1e9
     mmq_up_tops = 2 * PREFILL_M * 18944 * 3584 / (avg_us["mmq_ffn_up"] * 1e-6) / 1e12
+    mmq_rec = recorded_fields("mmq_q4k_512x18944x3584_counters.txt")
 
     result = {
         "metric": "Q4_K GEMV weight GB/s at M=1 + MMQ prefill TOPS at M=512 (7B shapes)",
@@ -275,28 +489,40 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
+        "step": (f"one pass of the hot path (2 decode GEMVs, quantize_act, 4 MMQs) replayed from a HIP graph; "
+                 f"consecutive steps rotate through {ncopy} weight copies; exactly `steps` passes are timed"),
         "config": {
             "workload": "Qwen2.5-7B Q4_K: decode GEMV ffn_up 18944x3584 + ffn_down 3584x18944 (M=1, f32 x); "
-                        "prefill M=512: quantize_act 512x3584 + int8 MMQ ffn_up/attn_q/attn_k/attn_v",
+                        "prefill M=512: quantize_act 512x3584 + MMQ ffn_up/attn_q/attn_k/attn_v",
             "M_decode": 1, "M_prefill": PREFILL_M, "weight_copies_rotated": ncopy,
             "parallelism": "single GPU",
         },
         "mmq_prefill_tops": round(mmq_tops, 2),
-        "mmq_dtype": "i8 x i8 -> i32 block dots, f32 scales",
+        "mmq_dtype": ("Q4_K with >= 256 output tiles: fp8 (e4m3) block dots on the matrix cores, activation codes "
+                      "as two exact fp8 digits; otherwise int8 x int8 -> int32 block dots; f32 scales"),
         "roofline": {"bound": "hbm", "achieved": round(gemv_alg_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gemv_alg_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": recorded_traffic("gemv_q4k_7b_ffn_hbm_traffic.txt",
-                                                 ["gemv.hip", "gemv_mfma.hip", "weight_units.h", "mq_device.h"]),
+                     "traffic": recorded_traffic("gemv_q4k_7b_ffn_hbm_traffic.txt"),
+                     "plain_read_GBps": round(plain_read, 1),
+                     "frac_of_plain_read": round(gemv_alg_gbps / plain_read, 4),
+                     "plain_read_by_workgroups": {str(g): round(v, 1) for g, v in read_gbps.items()},
                      "algorithmic_bytes_per_launch": gemv_alg_bytes,
                      "kernel": f"{kernel_names['gemv_ffn_up']} (ffn_up) + {kernel_names['gemv_ffn_down']} (ffn_down)",
                      "ffn_up_GBps": round(up_gbps, 1), "ffn_down_GBps": round(down_gbps, 1)},
         "roofline_mmq": {"bound": "mfma", "achieved": round(mmq_up_tops, 2), "peak": INT8_PEAK_TOPS,
                          "unit": "TOP/s", "frac": round(mmq_up_tops / INT8_PEAK_TOPS, 4),
-                         "traffic": recorded_traffic("mmq_q4k_512x18944x3584_counters.txt", ["mmq.hip", "mq_device.h"]),
-                         "kernel": "mmq<q4_K> ffn_up M=512 18944x3584"},
+                         "traffic": (int(mmq_rec["traffic_bytes_per_launch"])
+                                     if "traffic_bytes_per_launch" in mmq_rec else None),
+                         "mfma_busy_frac": (float(mmq_rec["mfma_busy_frac"]) if "mfma_busy_frac" in mmq_rec
+                                            else None),
+                         "sclk_MHz": float(mmq_rec["sclk_MHz"]) if "sclk_MHz" in mmq_rec else None,
+                         "kernel": f"{kernel_names['mmq_ffn_up']} ffn_up M=512 18944x3584"},
         "kernel_avg_us": {lab: round(v, 3) for lab, v in avg_us.items()},
         "kernel_names": kernel_names,
+        "warm_cache": warm,
     }
+
+    result["c5_14b"] = c5_layer_mix(torch, mq, synth, timer, to_dev, dev, reps)
 
     if not args.no_secondary:
         sec = {}
@@ -394,9 +620,8 @@ def main():
                                         "GBps_in": round(qa_bytes / avg_us["quantize_act"] / 1e3, 1)}
         result["secondary"] = sec
 
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w_host["ffn_up"], w_host["ffn_down"], x_dec["ffn_up"],
-                                              x_dec["ffn_down"])
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

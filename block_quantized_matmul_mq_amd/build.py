@@ -1,4 +1,6 @@
-"""Build libmq.so (the HIP kernels and the C ABI) for gfx950 with hipcc, in place.
+"""Build libmq.so (the HIP kernels and the C ABI) for gfx950 with hipcc, in place, and
+libmq_measure.so (a plain-read kernel the benchmark uses as its HBM read ceiling; the
+product never loads it).
 
 Usage: python -m block_quantized_matmul_mq_amd.build   (or build() from Python)
 
@@ -15,6 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmq.so")
+MEASURE_SRC = os.path.join(HERE, "measure", "read_ceiling.hip")
+MEASURE_LIB = os.path.join(HERE, "libmq_measure.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["mq_api.hip", "quantize_act.hip", "gemv.hip", "gemv_mfma.hip", "gemv_q8.hip", "mmq.hip", "mmq_f8.hip", "repack.hip"]
 FLAGS = [
@@ -25,26 +29,32 @@ FLAGS = [
 
 
 def _compile(src):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    path = src if os.path.isabs(src) else os.path.join(CSRC, src)
+    obj = os.path.join(BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fno-gpu-rdc", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES + [MEASURE_SRC]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], MEASURE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {MEASURE_LIB}")
     return LIB
 
 

@@ -11,7 +11,9 @@ What is here:
                        path computes: block decoders, the activation
                        quantizer, the GEMV, the int block dots and the MMQ
                        product.
-  ``repack`` / ``unpack_repacked`` define the repacked weight layout.
+  ``repack`` / ``unpack_repacked`` define the repacked weight layout;
+                       ``q4_k_plane`` / ``act_f6_section`` the fp6 planes of the
+                       Q4_K prefill product (weights and activations).
 * ``bitwise_decode`` -- a second, independently written per-block decoder that
                        assembles every field bit by bit; it exists only to
                        cross-check ``mq_oracle``'s vectorised decoders.
@@ -32,4 +34,6 @@ from .mq_oracle import (  # noqa: F401
     q8_0_fields, q4_k_fields, q5_k_fields, q6_k_fields, legacy_fields, decode,
     gemv, quantize_act, block_dots, mmq, mmq_from_block_dots,
     REPACK_SLOT, repack, unpack_repacked,
+    PLANE_ROWS, ACT_PLANE_ROWS, e2m3_value, e2m3_code_of_half, fp6_records, bf16_hilo, q4_k_plane,
+    act_f6_section,
 )

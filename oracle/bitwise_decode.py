@@ -77,6 +77,25 @@ def decode_q4_k_block(block):
     return out
 
 
+def q4_k_block_fields(block):
+    """144 bytes -> (d, dmin, [8 scales], [8 mins], [256 codes]) as plain Python numbers,
+    every field read bit by bit (the codes as unsigned 4-bit integers)."""
+    block = bytes(bytearray(int(b) for b in block))
+    assert len(block) == 144
+    scales, mins = [], []
+    for j in range(8):
+        sc_pos, mn_pos = _q4_k_scale_min_positions(j)
+        scales.append(_field(block, sc_pos))
+        mins.append(_field(block, mn_pos))
+    codes = []
+    for e in range(256):
+        chunk, r = divmod(e, 64)
+        byte_index = 16 + 32 * chunk + (r % 32)
+        first_bit = 0 if r < 32 else 4
+        codes.append(_field(block, [(byte_index, first_bit + k) for k in range(4)]))
+    return _half(block, 0), _half(block, 2), scales, mins, codes
+
+
 def decode_q6_k_block(block):
     """210 bytes -> 256 floats."""
     block = bytes(bytearray(int(b) for b in block))

@@ -59,6 +59,19 @@ Readings where the pages are silent (each also listed in the design doc):
 * R16 Block dots of the new types are per 32-value block: the signed code
       (code - 8 or code - 16) for Q4_0 / Q5_0, the unsigned code for Q4_1,
       Q5_1 and Q5_K (whose min term rides on the activation block's code sum).
+* R17 Q4_K's repacked layout is a pre-decoded plane for the prefill product (the
+      pages' reference pre-decodes weight planes at load time for a faster
+      prefill, "minfer CUDA Backend Design", 2.3): per 64-value step t and weight
+      row n (rows padded with zeros to a multiple of 256), each of the step's two
+      32-value sub-blocks as a 24-byte record of its codes c, each the 6-bit OCP
+      FP6 E2M3 code of c / 2 (exact), value i at bits 6i..6i+5, plus the bf16
+      hi/lo split of its scale d*sc and of its min -dmin*m.  The quantized
+      activation plane carries the matching section: each code q as the E2M3
+      codes of h / 2 and l / 2 with q = 16 h + l, h = q >> 4, l = q & 15, and the
+      bf16 hi/lo splits of dx and of dx * S (f32 product).  The byte layouts are
+      ``repack`` (Q4_K) and ``act_f6_section`` below; the products on the plane
+      are checked against ``mmq`` (the plane holds the scales to 16 bits, well
+      inside the 2e-4 tolerance).
 * R12 The repacked layout (the one-time device-layout transform): the pages
       repack a Q6_K block into a 16-byte-aligned 224-byte slot ("minfer CUDA
       Backend Design", 2.3); the block sits at the start of its slot and the
@@ -126,8 +139,11 @@ def repack(raw, qtype, N, K):
     Block b of row n goes to slot b of row n at the slot's offset; every other
     byte of the slot is zero.  Pinned by the page's 224-byte Q6_K slot
     (tests/golden/block_sizes.txt), the alignment each slot is for, and a
-    per-block brute force.
+    per-block brute force.  Q4_K goes to its MMQ plane instead (R17,
+    ``q4_k_plane``).
     """
+    if qtype == Q4_K:
+        return q4_k_plane(raw, N, K)
     slot, off = REPACK_SLOT[qtype]
     b = _blocks(raw, qtype, N, K)
     out = np.zeros((N, b.shape[1], slot), dtype=np.uint8)
@@ -150,6 +166,151 @@ def unpack_repacked(rep, qtype, N, K):
     if np.any(pad):
         raise ValueError("nonzero padding byte in a repacked slot")
     return np.ascontiguousarray(r[:, :, off:off + BLOCK_BYTES[qtype]]).reshape(-1)
+
+
+# ---------------------------------------------------------------- R17: the fp6 planes
+
+PLANE_ROWS = 256       # weight rows of the Q4_K plane are padded to a multiple of this
+ACT_PLANE_ROWS = 128   # activation rows of the fp6 section are padded to a multiple of this
+
+
+def e2m3_value(code):
+    """Value of a 6-bit OCP FP6 E2M3 code: sign bit 5, exponent bits 4..3 (bias 1),
+    mantissa bits 2..0; exponent 0 is subnormal (m / 8), else 2^(e-1) * (1 + m/8)."""
+    code = int(code)
+    sign = -1.0 if code & 32 else 1.0
+    e, m = (code >> 3) & 3, code & 7
+    return sign * (m / 8.0 if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 8.0))
+
+
+def e2m3_code_of_half(k):
+    """The E2M3 code whose value is k / 2 (integer k, |k| <= 15; +0 for k = 0): the
+    unique code with that value, found by search over the format's codes."""
+    k = int(k)
+    if k == 0:
+        return 0
+    for code in range(64):
+        if e2m3_value(code) == k / 2.0:
+            return code
+    raise ValueError(f"{k}/2 is not an E2M3 value")
+
+
+def fp6_records(codes6):
+    """Pack 6-bit codes [..., 32] into 24-byte records [..., 24]: value i at bits 6i..6i+5
+    of the little-endian 192-bit record."""
+    codes6 = np.asarray(codes6, dtype=np.uint8)
+    bits = ((codes6[..., :, None] >> np.arange(6, dtype=np.uint8)) & 1).reshape(codes6.shape[:-1] + (192,))
+    return np.packbits(bits, axis=-1, bitorder="little")
+
+
+def bf16_hilo(x):
+    """bf16 hi/lo split of f32 values: hi = bf16(x), lo = bf16(x - hi), each rounded to
+    nearest with ties to even; returned as uint16 bit patterns (hi, lo)."""
+    def rne(v):
+        b = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+        return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+    x = np.asarray(x, dtype=np.float32)
+    hi = rne(x)
+    hi_f = (hi.astype(np.uint32) << 16).view(np.float32)
+    lo = rne((x - hi_f).astype(np.float32))
+    return hi, lo
+
+
+def _dwords(lo16, hi16):
+    """uint32 words lo16 | hi16 << 16."""
+    return np.asarray(lo16, dtype=np.uint32) | (np.asarray(hi16, dtype=np.uint32) << 16)
+
+
+def _le_bytes(words):
+    """uint32 words [..., w] -> their little-endian bytes [..., 4 w]."""
+    w = np.ascontiguousarray(words, dtype="<u4")
+    return w.view(np.uint8).reshape(w.shape[:-1] + (4 * w.shape[-1],))
+
+
+def q4_k_plane(raw, N, K):
+    """R17: Q4_K's repacked layout (uint8), the plane of the fp6 prefill product.
+
+    Np = N rounded up to PLANE_ROWS; T = K / 64 steps of 80 * Np bytes.  In step t,
+    for the two sub-blocks b = 2t + u (u = 0, 1) of each row n < N (rows n >= N are zero):
+      bytes 16 (u Np + n) ..          bytes 0..15 of the 24-byte E2M3 record of c / 2
+      bytes 32 Np + 8 (u Np + n) ..   bytes 16..23 of that record
+      bytes 48 Np + 8 (u Np + n) ..   words (dw_hi | dw_hi << 16, dw_lo | dw_lo << 16)
+      bytes 64 Np + 8 (u Np + n) ..   words (mw_hi | mw_lo << 16) twice
+    with dw = d * sc_b and mw = -dmin * m_b (both exact in f32) split by bf16_hilo.
+    """
+    if K % 256:
+        raise ValueError(f"K={K} is not a multiple of 256")
+    d, dmin, sc, mn, codes = q4_k_fields(raw, N, K)
+    KB, T = K // 32, K // 64
+    Np = -(-N // PLANE_ROWS) * PLANE_ROWS
+    table = np.array([e2m3_code_of_half(c) for c in range(16)], dtype=np.uint8)
+    rec = np.zeros((Np, KB, 24), dtype=np.uint8)
+    rec[:N] = fp6_records(table[codes.reshape(N, KB, 32)])
+    dw = np.zeros((Np, KB), dtype=np.float32)
+    mw = np.zeros((Np, KB), dtype=np.float32)
+    dw[:N] = (d[..., None] * sc).reshape(N, KB).astype(np.float32)
+    mw[:N] = (-(dmin[..., None] * mn)).reshape(N, KB).astype(np.float32)
+    dh, dl = bf16_hilo(dw)
+    mh, ml = bf16_hilo(mw)
+    outer = _le_bytes(np.stack([_dwords(dh, dh), _dwords(dl, dl)], axis=-1))   # [Np, KB, 8]
+    mwin = _le_bytes(np.stack([_dwords(mh, ml), _dwords(mh, ml)], axis=-1))
+    out = np.zeros((T, 80 * Np), dtype=np.uint8)
+    for t in range(T):
+        slab = out[t]
+        for u in range(2):
+            b = 2 * t + u
+            slab[16 * u * Np:16 * (u + 1) * Np] = rec[:, b, :16].reshape(-1)
+            slab[32 * Np + 8 * u * Np:32 * Np + 8 * (u + 1) * Np] = rec[:, b, 16:].reshape(-1)
+            slab[48 * Np + 8 * u * Np:48 * Np + 8 * (u + 1) * Np] = outer[:, b].reshape(-1)
+            slab[64 * Np + 8 * u * Np:64 * Np + 8 * (u + 1) * Np] = mwin[:, b].reshape(-1)
+    return out.reshape(-1)
+
+
+def act_f6_section(q, d, S):
+    """R17: the fp6 section of the quantized activation plane (uint8) for the codes q
+    [M, K], scales d [M, K/32] and code sums S [M, K/32] of ``quantize_act``.
+
+    Mp = M rounded up to ACT_PLANE_ROWS; T = ceil(K / 64) steps of 128 * Mp bytes.  In
+    step t, for blocks b = 2t + u of each row m < M (rows m >= M, and a block past the
+    row's end when K % 64 == 32, are zero), with q = 16 h + l, h = q >> 4, l = q & 15:
+      bytes 16 ((2u + g) Mp + m) ..          bytes 0..15 of the E2M3 record of h / 2 (g = 0)
+                                             or l / 2 (g = 1)
+      bytes 64 Mp + 8 ((2u + g) Mp + m) ..   bytes 16..23 of it
+      bytes 96 Mp + 8 (u Mp + m) ..          words (dx_hi | dx_lo << 16) twice
+      bytes 112 Mp + 8 (u Mp + m) ..         words (tx_hi | tx_hi << 16, tx_lo | tx_lo << 16)
+    with tx = dx * S the f32 product, both split by bf16_hilo.
+    """
+    q = np.asarray(q, dtype=np.int8).astype(np.int64)
+    M, K = q.shape
+    KB = K // 32
+    T = -(-K // 64)
+    Mp = -(-M // ACT_PLANE_ROWS) * ACT_PLANE_ROWS
+    table = {k: e2m3_code_of_half(k) for k in range(-15, 16)}
+    enc = np.vectorize(lambda k: table[int(k)], otypes=[np.uint8])
+    qb = q.reshape(M, KB, 32)
+    recs = np.zeros((2, Mp, 2 * T, 24), dtype=np.uint8)
+    recs[0, :M, :KB] = fp6_records(enc(qb >> 4))
+    recs[1, :M, :KB] = fp6_records(enc(qb & 15))
+    dx = np.zeros((Mp, 2 * T), dtype=np.float32)
+    tx = np.zeros((Mp, 2 * T), dtype=np.float32)
+    dx[:M, :KB] = np.asarray(d, dtype=np.float32)
+    tx[:M, :KB] = (np.asarray(d, dtype=np.float32) * np.asarray(S, dtype=np.int32).astype(np.float32)).astype(np.float32)
+    xh, xl = bf16_hilo(dx)
+    th, tl = bf16_hilo(tx)
+    outer = _le_bytes(np.stack([_dwords(xh, xl), _dwords(xh, xl)], axis=-1))
+    mins = _le_bytes(np.stack([_dwords(th, th), _dwords(tl, tl)], axis=-1))
+    out = np.zeros((T, 128 * Mp), dtype=np.uint8)
+    for t in range(T):
+        slab = out[t]
+        for u in range(2):
+            b = 2 * t + u
+            for g in range(2):
+                sp = 2 * u + g
+                slab[16 * sp * Mp:16 * (sp + 1) * Mp] = recs[g, :, b, :16].reshape(-1)
+                slab[64 * Mp + 8 * sp * Mp:64 * Mp + 8 * (sp + 1) * Mp] = recs[g, :, b, 16:].reshape(-1)
+            slab[96 * Mp + 8 * u * Mp:96 * Mp + 8 * (u + 1) * Mp] = outer[:, b].reshape(-1)
+            slab[112 * Mp + 8 * u * Mp:112 * Mp + 8 * (u + 1) * Mp] = mins[:, b].reshape(-1)
+    return out.reshape(-1)
 
 
 def _blocks(raw, qtype, N, K):

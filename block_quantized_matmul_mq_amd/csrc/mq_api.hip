@@ -69,15 +69,18 @@ int block_bytes(int type) {
 
 // The slot a block takes in the layout mq_repack writes, and the block's offset in it:
 // Q8_0 36 bytes with the block at 2 (its 32 codes then start 4-byte aligned), Q6_K 224
-// bytes with the block at 0 (16-byte aligned slots).  Q4_K blocks are 144 bytes, already
-// 16-byte aligned: it has no repacked layout.
+// bytes with the block at 0 (16-byte aligned slots).  Q4_K's repacked layout is not a slot
+// layout but the MMQ plane of the fp6 kernel (kPlane; mq_internal.h).
+constexpr int kPlane = -1;
 BlockLayout repacked_layout(int base) {
     switch (base) {
         case MQ_Q8_0: return {36, 2};
         case MQ_Q6_K: return {224, 0};
+        case MQ_Q4_K: return {kPlane, 0};
         default: return {0, 0};
     }
 }
+bool is_plane(BlockLayout lay) { return lay.stride == kPlane; }
 
 // A type id is a GGUF type, optionally OR-ed with MQ_REPACKED for the layout mq_repack
 // writes.  Returns the GGUF type (0 for an unknown id or a type with no repacked layout)
@@ -204,6 +207,7 @@ size_t mq_weight_bytes(int type, int64_t N, int64_t K) {
     if (base == 0) return 0;
     const int bv = block_values(base);
     if (N <= 0 || K <= 0 || K % bv != 0) return 0;
+    if (is_plane(lay)) return f6_weight_plane_bytes(N, K);
     return size_t(N) * size_t(K / bv) * size_t(lay.stride);
 }
 
@@ -237,12 +241,18 @@ size_t mq_act_step_scale_offset(int64_t M, int64_t K) {
     return act_step_scale_offset(M, K);
 }
 
+size_t mq_act_f6_offset(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0 || K % 32 != 0) return 0;
+    return act_f6_offset(M, K);
+}
+
 size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
     BlockLayout lay;
     type = parse_type(type, lay);
     if (type == 0) return 0;
     if (M <= 0 || N <= 0 || K <= 0 || M > MQ_MAX_M || N > MQ_MAX_N || K > MQ_MAX_K) return 0;
     if (K % block_values(type) != 0) return 0;
+    if (is_plane(lay)) return mmq_f6_scratch_bytes(M, N, K);
     return mmq_scratch_bytes(type, M, N, K);
 }
 
@@ -261,8 +271,8 @@ int mq_quantize_act(const float* X, void* Xq, int64_t M, int64_t K, void* stream
     hipError_t e = launch_quantize_act(X, reinterpret_cast<int8_t*>(base),
                                        reinterpret_cast<float*>(base + act_scale_offset(M, K)),
                                        reinterpret_cast<int32_t*>(base + act_sum_offset(M, K)),
-                                       base + act_digit_offset(M, K), base + act_step_scale_offset(M, K), M, K,
-                                       static_cast<hipStream_t>(stream));
+                                       base + act_digit_offset(M, K), base + act_step_scale_offset(M, K),
+                                       base + act_f6_offset(M, K), M, K, static_cast<hipStream_t>(stream));
     return launch_status(fn, e, "quantize_act");
 }
 
@@ -272,6 +282,9 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
     BlockLayout lay;
     const int base = parse_type(type, lay);
     if (base == 0) return fail(MQ_ERR_TYPE, "%s: unsupported weight type %d", fn, type);
+    if (is_plane(lay))
+        return fail(MQ_ERR_TYPE, "%s: type %d is the Q4_K MMQ plane, which only mq_gemm reads (decode the GGUF "
+                    "payload itself)", fn, type);
     type = base;
     int rc = check_weight_shape(fn, type, N, K);
     if (rc) return rc;
@@ -312,6 +325,11 @@ static int gemm_common(const char* fn, const void* W, int type, const void* Xq, 
     const uint8_t* xq = static_cast<const uint8_t*>(Xq);
     const char* kernel = "mmq";
     float* Yout = Y;
+    if (is_plane(lay)) {
+        hipError_t e = launch_mmq_f6(static_cast<const uint8_t*>(W), xq + act_f6_offset(M, K), Y, D, scratch, counters,
+                                     M, N, K, static_cast<hipStream_t>(stream), &kernel);
+        return launch_status(fn, e, kernel);
+    }
     hipError_t e = launch_mmq(type, lay, static_cast<const uint8_t*>(W), reinterpret_cast<const int8_t*>(xq),
                               reinterpret_cast<const float*>(xq + act_scale_offset(M, K)),
                               reinterpret_cast<const int32_t*>(xq + act_sum_offset(M, K)),
@@ -338,7 +356,8 @@ int mq_gemm_noalloc(const void* W, int type, const void* Xq, float* Y, int64_t M
     if (!Y) return fail(MQ_ERR_ARG, "%s: null Y", fn);
     if (mq_gemm_scratch_bytes(type, M, N, K) != 0) {   // a valid shape whose plan cuts tiles
         BlockLayout lay;
-        const size_t need = mmq_partial_bytes(parse_type(type, lay), M, N, K);
+        const int base = parse_type(type, lay);
+        const size_t need = is_plane(lay) ? mmq_f6_partial_bytes(M, N, K) : mmq_partial_bytes(base, M, N, K);
         if (need > kNoAllocPartialBytes)
             return fail(MQ_ERR_SIZE, "%s: M=%lld N=%lld K=%lld needs %zu bytes of partial tiles, the limit is %zu", fn,
                         (long long)M, (long long)N, (long long)K, need, kNoAllocPartialBytes);
@@ -364,6 +383,7 @@ size_t mq_debug_lds_bytes(int what, int type, int64_t K) {
         case MQ_LDS_MMQ_I8_BM128: return mmq_smem_bytes(type, 128);
         case MQ_LDS_MMQ_I8_BM32: return mmq_smem_bytes(type, 32);
         case MQ_LDS_MMQ_F8: return type == MQ_Q4_K ? mmq_f8_lds_bytes() : 0;
+        case MQ_LDS_MMQ_F6: return type == MQ_Q4_K ? mmq_f6_lds_bytes() : 0;
         default: return 0;
     }
 }
@@ -381,8 +401,7 @@ int mq_repack(const void* W, int type, int64_t N, int64_t K, size_t nbytes, void
     if (!W || !Wr) return fail(MQ_ERR_ARG, "%s: null pointer (W=%p Wr=%p)", fn, W, Wr);
     if (type & MQ_REPACKED) return fail(MQ_ERR_TYPE, "%s: type %d is already the repacked layout", fn, type);
     if (block_values(type) != 0 && repacked_layout(type).stride == 0)
-        return fail(MQ_ERR_TYPE, "%s: type %d has no repacked layout (its blocks are already 16-byte aligned)", fn,
-                    type);
+        return fail(MQ_ERR_TYPE, "%s: type %d has no repacked layout", fn, type);
     int rc = check_weight_shape(fn, type, N, K);
     if (rc) return rc;
     const size_t in_bytes = mq_weight_bytes(type, N, K), out_bytes = mq_repack_bytes(type, N, K);
@@ -399,6 +418,11 @@ int mq_repack(const void* W, int type, int64_t N, int64_t K, size_t nbytes, void
     rc = check_ready(fn);
     if (rc) return rc;
     const BlockLayout lay = repacked_layout(type);
+    if (is_plane(lay)) {
+        hipError_t e = launch_repack_q4k_plane(static_cast<const uint8_t*>(W), static_cast<uint8_t*>(Wr), N, K,
+                                               static_cast<hipStream_t>(stream));
+        return launch_status(fn, e, "repack");
+    }
     const int64_t blocks = N * (K / block_values(type));
     hipError_t e = launch_repack(static_cast<const uint8_t*>(W), static_cast<uint8_t*>(Wr), blocks, block_bytes(type),
                                  lay.stride, lay.off, static_cast<hipStream_t>(stream));

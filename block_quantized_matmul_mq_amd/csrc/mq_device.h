@@ -74,6 +74,18 @@ __device__ __forceinline__ uint32_t load_u16(const uint8_t* p) {
     return *reinterpret_cast<const uint16_t*>(p);
 }
 
+// OCP FP6 E2M3 (1 sign, 2 exponent and 3 mantissa bits, exponent bias 1, no Inf/NaN):
+// the 6-bit code of k / 2 for an integer k with |k| <= 15.  Every multiple of 1/2 up to
+// 7.5 is exact in this format: 0.5 is the subnormal 4/8, 1..1.5, 2..3.5 and 4..7.5 are the
+// three binades.
+__device__ __forceinline__ uint32_t e2m3_half_code(int k) {
+    constexpr uint64_t kLow = 0x161412100C080400ull;    // |k| = 0..7
+    constexpr uint64_t kHigh = 0x1F1E1D1C1B1A1918ull;   // |k| = 8..15
+    const uint32_t a = uint32_t(k < 0 ? -k : k);
+    const uint64_t tbl = a < 8 ? kLow : kHigh;
+    return (uint32_t(k < 0) << 5) | uint32_t((tbl >> (8 * (a & 7))) & 0x3Fu);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);

@@ -31,8 +31,33 @@ inline size_t act_digit_offset(int64_t M, int64_t K) {
 inline size_t act_step_scale_offset(int64_t M, int64_t K) {
     return act_digit_offset(M, K) + round_up256(size_t(M) * size_t(act_steps(K)) * 128);
 }
+// The fp6 section (the activation half of the MMQ plane of the fp6 kernel): per 64-value
+// step t a slab of 128 Mp bytes, Mp = M rounded up to kF6TileRows (the padding rows are
+// zero), holding the step's two blocks u = 0, 1:
+//   digits16 [2u + g][Mp][16 B] at 0    bytes 0..15 of the 24-byte fp6 record of the block's
+//                                       h / 2 (g = 0) or l / 2 (g = 1) digits
+//   digits8  [2u + g][Mp][8 B]  at 64 Mp  bytes 16..23 of it
+//   outer    [u][Mp][8 B]       at 96 Mp  (dx_hi | dx_lo << 16) twice, bf16 bits
+//   min      [u][Mp][8 B]       at 112 Mp (tx_hi | tx_hi << 16, tx_lo | tx_lo << 16), tx = dx * S
+// (hi = bf16(v) and lo = bf16(v - hi), both rounded to nearest even.)  The weight plane
+// (mq_repack of Q4_K) is the same per step for Np = N rounded up to kF6TileCols: codes16
+// [u][Np][16 B] at 0, codes8 [u][Np][8 B] at 32 Np, outer [u][Np][8 B]
+// (dw_hi | dw_hi << 16, dw_lo | dw_lo << 16) at 48 Np, min [u][Np][8 B]
+// (mw_hi | mw_lo << 16) twice at 64 Np, dw = d sc and mw = -dmin m; 80 Np bytes a step.
+// As bf16 matrix operands (4 values per lane) each pair multiplies out to the full product
+// (x_hi + x_lo)(y_hi + y_lo) of its two factors.
+constexpr int kF6TileRows = 128;
+constexpr int kF6TileCols = 256;
+inline int64_t f6_act_rows(int64_t M) { return (M + kF6TileRows - 1) / kF6TileRows * kF6TileRows; }
+inline int64_t f6_weight_rows(int64_t N) { return (N + kF6TileCols - 1) / kF6TileCols * kF6TileCols; }
+inline size_t f6_weight_plane_bytes(int64_t N, int64_t K) {
+    return size_t(act_steps(K)) * 80 * size_t(f6_weight_rows(N));
+}
+inline size_t act_f6_offset(int64_t M, int64_t K) {
+    return round_up256(act_step_scale_offset(M, K) + size_t(M) * size_t(act_steps(K)) * 16);
+}
 inline size_t act_bytes(int64_t M, int64_t K) {
-    return act_step_scale_offset(M, K) + size_t(M) * size_t(act_steps(K)) * 16;
+    return act_f6_offset(M, K) + size_t(act_steps(K)) * 128 * size_t(f6_act_rows(M));
 }
 
 struct DeviceInfo {
@@ -54,7 +79,7 @@ struct BlockLayout {
 // Kernel launchers: they enqueue on `s` and return the launch status (hipGetLastError read
 // right after the launch).  Arguments are validated by the callers in mq_api.hip.
 hipError_t launch_quantize_act(const float* X, int8_t* codes, float* scales, int32_t* sums, uint8_t* digits,
-                               uint8_t* step_scales, int64_t M, int64_t K, hipStream_t s);
+                               uint8_t* step_scales, uint8_t* f6, int64_t M, int64_t K, hipStream_t s);
 int gemv_tile_units(int type, int64_t K, size_t lds_limit);
 // LDS of the vector GEMV besides its row tile: the staged x (digit planes, block
 // exponents and sums), and of the MMQ kernels (int8: per type and tile rows; fp8 Q4_K).
@@ -119,6 +144,16 @@ size_t mmq_f8_partial_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_mmq_f8(int type, const uint8_t* W, const uint8_t* digits, const uint8_t* step_scales, float* Y,
                          int32_t* dots, void* scratch, unsigned* counters, int64_t M, int64_t N, int64_t K,
                          hipStream_t s, const char** kernel_name);
+// Q4_K in the MMQ plane (mq_repack's layout): block dots on the fp6 matrix units from the
+// activation plane's fp6 section (mmq_f6.hip).  Any M.
+MmqPlan mmq_f6_plan(int64_t M, int64_t N, int64_t K);
+size_t mmq_f6_scratch_bytes(int64_t M, int64_t N, int64_t K);
+size_t mmq_f6_partial_bytes(int64_t M, int64_t N, int64_t K);
+size_t mmq_f6_lds_bytes();
+hipError_t launch_mmq_f6(const uint8_t* Wp, const uint8_t* Ap, float* Y, int32_t* dots, void* scratch,
+                         unsigned* counters, int64_t M, int64_t N, int64_t K, hipStream_t s, const char** name);
+// mq_repack of Q4_K: the GGUF payload -> the MMQ plane (repack.hip).
+hipError_t launch_repack_q4k_plane(const uint8_t* W, uint8_t* Wp, int64_t N, int64_t K, hipStream_t s);
 // mq_gemm for M <= kGemvQ8MaxRows: a multi-row GEMV over the quantized activation plane
 // (gemv_q8.hip), taken by launch_mmq whenever gemv_q8_applies; it needs no scratch.
 constexpr int kGemvQ8MaxRows = 8;

@@ -37,6 +37,7 @@ _SIGNATURES = {
     "mq_act_sum_offset": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
     "mq_act_digit_offset": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
     "mq_act_step_scale_offset": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
+    "mq_act_f6_offset": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
     "mq_quantize_act": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_void_p]),
     "mq_gemv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
@@ -209,6 +210,15 @@ def act_step_scales(Xq, M, K):
     T = (K + 63) // 64
     rec = Xq[off:off + T * M * 16].view(T, M, 16)
     return rec[:, :, :8].contiguous().view(torch.float32), rec[:, :, 8:].contiguous().view(torch.int32)
+
+
+def act_f6(Xq, M, K):
+    """View (uint8 [ceil(K/64), 128 * Mp]) of the plane's fp6 section, Mp = M rounded up to 128:
+    one slab per 64-value step (layout in include/mq.h)."""
+    off = load().mq_act_f6_offset(M, K)
+    T = (K + 63) // 64
+    Mp = -(-M // 128) * 128
+    return Xq[off:off + T * 128 * Mp].view(T, 128 * Mp)
 
 
 def gemm_scratch_bytes(qtype, M, N, K):

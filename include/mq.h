@@ -39,13 +39,15 @@
  *        4 bits, 64 bytes high 2 bits, 16 int8 sub-scales, f16 d).  These are
  *        the public GGUF layouts; the pages fix only some sizes and the types.
  *   x  : K f32.   y : N f32.   X : M x K f32 row-major.   Y : M x N f32 row-major.
- *   Xq : the quantized activation plane written by mq_quantize_act, five
+ *   Xq : the quantized activation plane written by mq_quantize_act, six
  *        arrays in one buffer of mq_act_bytes(M, K) bytes (T = ceil(K / 64)):
  *          codes  int8  [M][K]          at offset 0
  *          scales f32   [M][K / 32]     at offset mq_act_scale_offset(M, K)
  *          sums   int32 [M][K / 32]     at offset mq_act_sum_offset(M, K)
  *          digits uint8 [M][T][128]     at offset mq_act_digit_offset(M, K)
  *          step scale records [T][M][16 bytes] at mq_act_step_scale_offset(M, K)
+ *          fp6 section [T][128 Mp bytes] at mq_act_f6_offset(M, K), Mp = M rounded
+ *                up to a multiple of 128 (rows M..Mp-1 zero)
  *        For block b of row m: scale = f32(amax) / f32(127) with IEEE division,
  *        code_i = clamp(round_half_even(x_i / scale), -127, 127) (a true f32
  *        division), scale 0 and codes 0 when amax == 0, and sum = sum of the 32
@@ -58,6 +60,18 @@
  *        record (t, m) is (scale of block 2t, scale of block 2t + 1 as f32, sum
  *        of 2t, sum of 2t + 1 as int32).  When K % 64 == 32 the last step's
  *        second block is all zeros (digits, scale and sum).
+ *        The fp6 section re-encodes the codes for the fp6 matrix units, each code
+ *        q = 16 h + l (h = q >> 4 in -8..7, l = q & 15) as the 6-bit OCP FP6
+ *        E2M3 codes of h / 2 and of l / 2 (exact); a block's 32 codes of one
+ *        digit form a 24-byte record, value i at bits 6 i .. 6 i + 5 (little
+ *        endian).  In step t's slab, for block b = 2 t + u of row m:
+ *          bytes 16 ((2 u + g) Mp + m) ..        record bytes 0..15, g = 0: h, g = 1: l
+ *          bytes 64 Mp + 8 ((2 u + g) Mp + m) .. record bytes 16..23
+ *          bytes 96 Mp + 8 (u Mp + m) ..         words (dx_hi | dx_lo << 16) twice
+ *          bytes 112 Mp + 8 (u Mp + m) ..        words (tx_hi | tx_hi << 16,
+ *                                                       tx_lo | tx_lo << 16)
+ *        with dx the block scale and tx = dx * sum (the f32 product), each split
+ *        as hi = bf16(v), lo = bf16(v - hi) (round to nearest even, bf16 bits).
  *
  * Ownership and streams: the caller allocates and frees every buffer (device
  * memory, e.g. from torch).  Weights and inputs are read only.  No call
@@ -89,8 +103,9 @@ extern "C" {
 #define MQ_Q4_K 12
 #define MQ_Q5_K 13
 #define MQ_Q6_K 14
-/* OR-ed into MQ_Q8_0 or MQ_Q6_K: the weights are in the layout mq_repack writes
- * (every call that takes a weight type accepts it). */
+/* OR-ed into MQ_Q8_0, MQ_Q6_K or MQ_Q4_K: the weights are in the layout mq_repack
+ * writes (every call that takes a weight type accepts it, except that mq_gemv refuses
+ * Q4_K's, which is a plane for mq_gemm only). */
 #define MQ_REPACKED 0x100
 
 /* Status codes. */
@@ -135,23 +150,39 @@ size_t mq_weight_bytes(int type, int64_t N, int64_t K);
  *   MQ_Q8_0: 36-byte slots, the 34-byte block at offset 2 (its 32 codes start
  *            4-byte aligned).
  * Pass type | MQ_REPACKED with Wr to mq_gemv / mq_gemm: the results are the
- * same as with W.  MQ_Q4_K (blocks already 16-byte aligned) has no repacked
- * layout: MQ_ERR_TYPE, and mq_repack_bytes returns 0.  W and Wr must be 16-byte
- * aligned and must not overlap (MQ_ERR_ARG).  Runs on `stream`; W may be freed
- * once the stream has passed the call.
+ * same as with W.
+ *   MQ_Q4_K: the MMQ plane of the fp6 prefill product (the pre-decoded weight plane
+ *            of [BD2.3]'s reference, here for the prefill only), T = K / 64 steps of
+ *            80 Np bytes, Np = N rounded up to a multiple of 256 (rows N..Np-1
+ *            zero).  In step t's slab, for sub-block b = 2 t + u of row n: bytes
+ *            16 (u Np + n) .. and 32 Np + 8 (u Np + n) .. hold bytes 0..15 and
+ *            16..23 of the 24-byte record of its codes c, each the OCP FP6 E2M3
+ *            code of c / 2, value i at bits 6 i .. 6 i + 5; bytes
+ *            48 Np + 8 (u Np + n) .. the words (dw_hi | dw_hi << 16,
+ *            dw_lo | dw_lo << 16), bytes 64 Np + 8 (u Np + n) .. the word
+ *            (mw_hi | mw_lo << 16) twice, dw = d sc and mw = -dmin m split into bf16
+ *            hi + lo as in the Xq fp6 section.  mq_gemm (any M) reads it with
+ *            the fp6 kernel; the product agrees with the GGUF payload's within the
+ *            2e-4 tolerance, not bit for bit (the scales are held to 16 bits), and
+ *            its block dots are the same exact integers.  mq_gemv refuses it
+ *            (MQ_ERR_TYPE): decode reads the GGUF payload.
+ * Other types have no repacked layout: MQ_ERR_TYPE, and mq_repack_bytes returns
+ * 0.  W and Wr must be 16-byte aligned and must not overlap (MQ_ERR_ARG).  Runs on
+ * `stream`; W may be freed once the stream has passed the call.
  */
 size_t mq_repack_bytes(int type, int64_t N, int64_t K);
 int mq_repack(const void* W, int type, int64_t N, int64_t K, size_t nbytes, void* Wr, size_t wr_bytes,
               void* stream);
 
 /* Bytes of the quantized activation plane for M x K, and the offsets of its
- * scale, sum, digit and step scale arrays (each 256-byte aligned).  0 if
+ * scale, sum, digit, step scale and fp6 arrays (each 256-byte aligned).  0 if
  * K % 32 != 0. */
 size_t mq_act_bytes(int64_t M, int64_t K);
 size_t mq_act_scale_offset(int64_t M, int64_t K);
 size_t mq_act_sum_offset(int64_t M, int64_t K);
 size_t mq_act_digit_offset(int64_t M, int64_t K);
 size_t mq_act_step_scale_offset(int64_t M, int64_t K);
+size_t mq_act_f6_offset(int64_t M, int64_t K);
 
 /*
  * mq_quantize_act -- X f32 [M][K] (device) -> Xq (device, mq_act_bytes(M, K)
@@ -180,7 +211,12 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
  * all tiles, when there are at most 256) are cut into S ranges of whole
  * 128-value K-steps, and a second launch sums their S f32 partial tiles in
  * range order (deterministic).  The scratch then holds S x (number of cut
- * tiles) x BM x 128 f32.  The split depends on the shape only, never on the
+ * tiles) x BM x 128 f32.  The fp8 (Q4_K) and fp6 (Q4_K plane) kernels compute
+ * 128 x 256 tiles with one workgroup per CU (rounds of 256, 64-value K-steps, at
+ * least 4 per range) and sum the cut tiles in the same launch: their scratch is
+ * S x (cut tiles) x 128 x 256 f32 followed, at the next 256-byte boundary, by one
+ * uint32 counter per cut tile, which must be zero before the first call and which
+ * every call leaves at zero.  The split depends on the shape only, never on the
  * device.
  */
 size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
@@ -236,6 +272,7 @@ int mq_gemm_noalloc(const void* W, int type, const void* Xq, float* Y, int64_t M
  *   MQ_LDS_MMQ_I8_BM128 / _BM32  int8 MMQ workgroup LDS for the type at 128- /
  *                           32-row tiles (two workgroups share a CU)
  *   MQ_LDS_MMQ_F8           fp8 Q4_K MMQ workgroup LDS (one workgroup per CU)
+ *   MQ_LDS_MMQ_F6           fp6 MMQ (Q4_K plane) workgroup LDS (one workgroup per CU)
  */
 #define MQ_GFX950_LDS_BYTES (160 * 1024)
 #define MQ_LDS_GEMV_FIXED 0
@@ -243,6 +280,7 @@ int mq_gemm_noalloc(const void* W, int type, const void* Xq, float* Y, int64_t M
 #define MQ_LDS_MMQ_I8_BM128 2
 #define MQ_LDS_MMQ_I8_BM32 3
 #define MQ_LDS_MMQ_F8 4
+#define MQ_LDS_MMQ_F6 5
 size_t mq_debug_lds_bytes(int what, int type, int64_t K);
 
 /*
@@ -276,8 +314,10 @@ int mq_device_lds_bytes(void);
  *     8..16 rows per CU), "gemv_mfma<q6_K>" (wide, GGUF layout, matrix ending
  *     on a 16-byte boundary), "gemv_mfma<q8_0>" / "gemv_mfma<q4_0>" /
  *     "gemv_mfma<q5_0>" (wide, GGUF layout), else "gemv<type>" (with " repacked" for MQ_REPACKED);
- *   mq_gemm: "gemv_q8_mfma<q6_K>" (M <= 8, Q6_K, as gemv_mfma<q6_K>),
- *     "gemv_q8<type>" (other M <= 8 shapes that fit LDS), else "mmq<type>". */
+ *   mq_gemm: "mmq_f6<q4_K plane>" (MQ_Q4_K | MQ_REPACKED, any M),
+ *     "gemv_q8_mfma<q6_K>" (M <= 8, Q6_K, as gemv_mfma<q6_K>),
+ *     "gemv_q8<type>" (other M <= 8 shapes that fit LDS), "mmq_f8<q4_K>" (Q4_K,
+ *     M > 32, at least 256 tiles of 128 x 256), else "mmq<type>". */
 const char* mq_last_kernel(void);
 
 /* Library version string. */

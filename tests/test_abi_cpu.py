@@ -59,13 +59,17 @@ def test_activation_plane_layout(M, K):
     total, so, uo = mq.act_layout(M, K)
     do = mq.load().mq_act_digit_offset(M, K)
     to = mq.load().mq_act_step_scale_offset(M, K)
+    fo = mq.load().mq_act_f6_offset(M, K)
     T = (K + 63) // 64     # 64-value steps, the last one half empty when K % 64 == 32
+    Mp = -(-M // 128) * 128   # the fp6 section's rows, padded with zero rows
     assert so >= M * K and so % 256 == 0
     assert uo >= so + 4 * M * (K // 32) and uo % 256 == 0
     assert do >= uo + 4 * M * (K // 32) and do % 256 == 0
     assert to >= do + 128 * M * T and to % 256 == 0
-    assert total == to + 16 * M * T
+    assert fo >= to + 16 * M * T and fo % 256 == 0
+    assert total == fo + 128 * Mp * T
     assert mq.act_bytes(M, 100) == 0 and mq.load().mq_act_digit_offset(M, 100) == 0
+    assert mq.load().mq_act_f6_offset(M, 100) == 0
 
 
 def _rc(fn, *args):
@@ -157,8 +161,11 @@ def test_repacked_sizes_and_type_flag():
     assert mq.repack_bytes(mq.Q8_0, 4864, 896) == 4864 * 28 * 36
     assert mq.weight_bytes(mq.Q6_K | R, 10, 512) == 10 * 2 * 224
     assert mq.weight_bytes(mq.Q8_0 | R, 10, 64) == 10 * 2 * 36
-    assert mq.repack_bytes(mq.Q4_K, 10, 256) == 0          # already 16-byte aligned: no layout
-    assert mq.weight_bytes(mq.Q4_K | R, 10, 256) == 0
+    # Q4_K: the MMQ plane, 80 bytes per 64-value step per row, rows padded to 256
+    assert mq.repack_bytes(mq.Q4_K, 18944, 3584) == 56 * 80 * 18944
+    assert mq.repack_bytes(mq.Q4_K, 10, 256) == 4 * 80 * 256
+    assert mq.weight_bytes(mq.Q4_K | R, 300, 512) == 8 * 80 * 512
+    assert mq.repack_bytes(mq.Q4_K, 10, 128) == 0
     assert mq.repack_bytes(mq.Q6_K | R, 10, 256) == 0
     assert mq.repack_bytes(mq.Q6_K, 10, 100) == 0
     assert mq.gemm_scratch_bytes(mq.Q6_K | R, 9, 152064, 3584) == mq.gemm_scratch_bytes(mq.Q6_K, 9, 152064, 3584)
@@ -170,8 +177,11 @@ def test_repack_refusals():
     rb6 = mq.repack_bytes(mq.Q6_K, 8, 512)
     far = FAKE + (1 << 24)
     assert lib.mq_repack(None, mq.Q6_K, 8, 512, nb6, far, rb6, None) == -1
-    assert lib.mq_repack(FAKE, mq.Q4_K, 8, 512, mq.weight_bytes(mq.Q4_K, 8, 512), far, 1 << 20, None) == -3
+    assert lib.mq_repack(FAKE, mq.Q5_K, 8, 512, mq.weight_bytes(mq.Q5_K, 8, 512), far, 1 << 20, None) == -3
     assert "no repacked layout" in mq.last_error()
+    nb4 = mq.weight_bytes(mq.Q4_K, 8, 512)
+    assert lib.mq_repack(FAKE, mq.Q4_K, 8, 512, nb4 - 144, far, 1 << 20, None) == -4     # exact length only
+    assert lib.mq_repack(FAKE, mq.Q4_K, 8, 512, nb4, far, mq.repack_bytes(mq.Q4_K, 8, 512) - 1, None) == -4
     assert lib.mq_repack(FAKE, mq.Q6_K | mq.REPACKED, 8, 512, nb6, far, rb6, None) == -3
     assert lib.mq_repack(FAKE, mq.Q6_K, 8, 500, nb6, far, rb6, None) == -2
     assert lib.mq_repack(FAKE, mq.Q6_K, 8, 512, nb6 + 1, far, rb6, None) == -4      # exact length only
@@ -180,7 +190,8 @@ def test_repack_refusals():
     assert lib.mq_repack(FAKE + 2, mq.Q6_K, 8, 512, nb6, far, rb6, None) == -5
     assert lib.mq_repack(FAKE, mq.Q6_K, 8, 512, nb6, FAKE + 16, rb6, None) == -1    # overlap
     assert "overlap" in mq.last_error()
-    assert lib.mq_gemv(FAKE, mq.Q4_K | mq.REPACKED, FAKE, FAKE, 8, 256, None) == -3
+    assert lib.mq_gemv(FAKE, mq.Q4_K | mq.REPACKED, FAKE, FAKE, 8, 256, None) == -3   # the plane is for mq_gemm
+    assert "only mq_gemm reads" in mq.last_error()
 
 
 def test_calls_without_init_are_refused_not_run():

@@ -11,7 +11,7 @@ import pytest
 from block_quantized_matmul_mq_amd import mq
 
 LIMIT = 160 * 1024
-FIXED, TILE_UNITS, I8_BM128, I8_BM32, F8 = 0, 1, 2, 3, 4
+FIXED, TILE_UNITS, I8_BM128, I8_BM32, F8, F6 = 0, 1, 2, 3, 4, 5
 TYPES = [mq.Q4_0, mq.Q4_1, mq.Q5_0, mq.Q5_1, mq.Q8_0, mq.Q4_K, mq.Q5_K, mq.Q6_K]
 KQUANT = {mq.Q4_K, mq.Q5_K, mq.Q6_K}
 MIN_TERM = {mq.Q4_1, mq.Q5_1, mq.Q4_K, mq.Q5_K}   # a per-block min is subtracted
@@ -78,3 +78,15 @@ def test_fp8_mmq_lds():
     assert lds(F8, mq.Q4_K) == 3 * slot + 2 * work
     assert lds(F8, mq.Q4_K) <= LIMIT
     assert lds(F8, mq.Q6_K) == 0
+
+
+def test_fp6_mmq_lds():
+    # ring of 3 step slots, each one step of both planes for a 128 x 256 tile: activation
+    # rows 128 x (64 B of digit records + 32 B of their tails + 8 B dx pairs x 2 blocks + 8 B
+    # min pairs x 2 blocks), weight rows 256 x (32 + 16 + 16 + 16 B); plus a 1 KB sink for
+    # the loads that carry nothing
+    slot = 128 * (64 + 32 + 16 + 16) + 256 * (32 + 16 + 16 + 16)
+    assert slot == 36 * 1024
+    assert lds(F6, mq.Q4_K) == 3 * slot + 1024
+    assert lds(F6, mq.Q4_K) <= LIMIT
+    assert lds(F6, mq.Q8_0) == 0

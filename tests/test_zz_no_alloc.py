@@ -14,8 +14,11 @@ from gpu_cases import device, say, to_dev, weights
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # (M, N, K, kernel, partial-tile bytes the plan cuts)
+    # (M, N, K, kernel, partial-tile bytes the plan cuts); the plane kernel reads Q4_K's MMQ
+    # plane (mq_repack) and shares the fp8 kernel's counters
     (512, 18944, 3584, "mmq_f8<q4_K>", 40 * 6 * 128 * 256 * 4),   # ffn_up: 40 tiles cut into 6
+    (512, 18944, 3584, "mmq_f6<q4_K plane>", 40 * 6 * 128 * 256 * 4),
+    (40, 100, 8192, "mmq_f6<q4_K plane>", 1 * 32 * 128 * 256 * 4),  # one tile into 32
     (512, 3584, 3584, "mmq<q4_K>", 112 * 4 * 128 * 128 * 4),       # smaller: int8 path, 112 tiles into 4
     (100, 306 * 256 - 13, 1024, "mmq_f8<q4_K>", 50 * 4 * 128 * 256 * 4),  # 50 tiles into 4
     (40, 256 * 256, 512, "mmq_f8<q4_K>", 0),                        # one whole round, nothing cut
@@ -28,14 +31,18 @@ def run_pair(M, N, K, kernel, cut, seed):
     say(f"gemm_noalloc q4_K M={M} N={N} K={K}")
     raw = weights(mq.Q4_K, N, K, "random", seed)
     W = to_dev(raw.reshape(-1), dev)
+    qtype = mq.Q4_K
+    if "plane" in kernel:
+        W = mq.repack(W, mq.Q4_K, N, K)
+        qtype = mq.Q4_K | mq.REPACKED
     X = synth.activations(M, K, config_index=12, tensor_index=seed)
     Xq = mq.quantize_act(to_dev(X, dev))
-    need = mq.gemm_scratch_bytes(mq.Q4_K, M, N, K)
+    need = mq.gemm_scratch_bytes(qtype, M, N, K)
     assert need >= cut and need - cut < 4096
-    Y_ref = mq.gemm(W, mq.Q4_K, Xq, M, N, K)
+    Y_ref = mq.gemm(W, qtype, Xq, M, N, K)
     assert mq.last_kernel() == kernel, mq.last_kernel()
     Y = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
-    mq.gemm_noalloc(W, mq.Q4_K, Xq, M, N, K, Y)
+    mq.gemm_noalloc(W, qtype, Xq, M, N, K, Y)
     assert mq.last_kernel() == kernel, mq.last_kernel()
     torch.cuda.synchronize()
     a, b = Y.cpu().numpy(), Y_ref.cpu().numpy()

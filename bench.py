@@ -53,6 +53,7 @@ LLC_BYTES = 256 * 2 ** 20
 COPY_REF_BYTES = 256 * 2 ** 20
 
 Q8_0, Q4_K, Q6_K = 8, 12, 14
+REPACKED = 0x100   # type flag of the layout mq_repack writes (Q4_K: the MMQ plane)
 DECODE = [("ffn_up", 18944, 3584), ("ffn_down", 3584, 18944)]
 PREFILL_M = 512
 PREFILL = [("ffn_up", 18944, 3584), ("attn_q", 3584, 3584), ("attn_k", 512, 3584), ("attn_v", 512, 3584)]
@@ -297,11 +298,24 @@ def c5_layer_mix(torch, mq, synth, timer, to_dev, dev, reps):
         sc = torch.zeros(max(mq.gemm_scratch_bytes(qt, C5_M, N, K), 256), dtype=torch.uint8, device=dev)
         m_us = timer.per_launch_us([lambda W=W: mq.gemm(W, qt, Xq[K], C5_M, N, K, Y=Y, scratch=sc) for W in wc[:2]],
                                    reps)
+        m_kernel = mq.last_kernel()
+        plane_us = None
+        if qt == Q4_K:   # the MMQ plane, kept instead of the GGUF payload when its product is faster
+            wp = [mq.repack(W, Q4_K, N, K) for W in wc[:2]]
+            sp = torch.zeros(max(mq.gemm_scratch_bytes(Q4_K | REPACKED, C5_M, N, K), 256), dtype=torch.uint8,
+                             device=dev)
+            plane_us = timer.per_launch_us([lambda W=W: mq.gemm(W, Q4_K | REPACKED, Xq[K], C5_M, N, K, Y=Y, scratch=sp)
+                                            for W in wp], reps)
+            del wp, sp
         ops = 2 * C5_M * N * K
         out[f"{name}_{N}x{K}"] = {"type": "q4_K" if qt == Q4_K else "q6_K", "uses_per_layer": uses,
                                   "gemv_M1_us": round(g_us, 3), "gemv_M1_GBps": round(nb / g_us / 1e3, 1),
                                   "gemv_kernel": gk, "mmq_M2048_us": round(m_us, 3),
-                                  "mmq_M2048_TOPS": round(ops / m_us / 1e6, 2), "mmq_kernel": mq.last_kernel()}
+                                  "mmq_M2048_TOPS": round(ops / m_us / 1e6, 2), "mmq_kernel": m_kernel}
+        if plane_us is not None:
+            out[f"{name}_{N}x{K}"].update({"mmq_plane_M2048_us": round(plane_us, 3),
+                                           "mmq_plane_M2048_TOPS": round(ops / plane_us / 1e6, 2)})
+            m_us = min(m_us, plane_us)
         layer_gemv_us += uses * g_us
         layer_mmq_us += uses * m_us
         layer_bytes += uses * nb
@@ -312,7 +326,8 @@ def c5_layer_mix(torch, mq, synth, timer, to_dev, dev, reps):
     out["layer"] = {"gemv_M1_us": round(layer_gemv_us, 2), "gemv_M1_GBps": round(layer_bytes / layer_gemv_us / 1e3, 1),
                     "prefill_M2048_us": round(layer_mmq_us + q_us, 2),
                     "prefill_M2048_TOPS": round(layer_ops / (layer_mmq_us + q_us) / 1e6, 2),
-                    "note": "q, k, v, o, gate, up, down; kernel times summed, quantize_act included at M=2048"}
+                    "note": "q, k, v, o, gate, up, down; kernel times summed (each Q4_K product in the faster "
+                            "of its GGUF payload and MMQ plane), quantize_act included at M=2048"}
     return out
 
 
@@ -356,8 +371,15 @@ def main():
     X_dev = torch.from_numpy(X_pre).to(dev)
     Xq = torch.empty(mq.act_bytes(PREFILL_M, 3584), dtype=torch.uint8, device=dev)
     Y_dev = {name: torch.empty((PREFILL_M, N), dtype=torch.float32, device=dev) for name, N, _ in PREFILL}
-    scratch = {name: torch.zeros(max(mq.gemm_scratch_bytes(Q4_K, PREFILL_M, N, K), 256), dtype=torch.uint8,
-                                 device=dev) for name, N, K in PREFILL}
+    scratch = {name: torch.zeros(max(mq.gemm_scratch_bytes(Q4_K, PREFILL_M, N, K),
+                                     mq.gemm_scratch_bytes(Q4_K | REPACKED, PREFILL_M, N, K), 256),
+                                 dtype=torch.uint8, device=dev) for name, N, K in PREFILL}
+    # Q4_K's MMQ plane (mq_repack, a one-time transform at load time) of every prefill weight;
+    # the ffn_up plane is rotated past the last-level cache like its GGUF copies
+    nplane = copies_for(mq.repack_bytes(Q4_K, 18944, 3584))
+    planes = {"ffn_up": [mq.repack(copies["ffn_up"][c % ncopy], Q4_K, 18944, 3584) for c in range(nplane)]}
+    for name, N, K in PREFILL[1:]:
+        planes[name] = [mq.repack(w_pre[name], Q4_K, N, K)]
     torch.cuda.synchronize()
 
     kernel_names = {}
@@ -371,13 +393,30 @@ def main():
     def quant_launch():
         mq.quantize_act(X_dev, Xq)
 
-    def mmq_launch(name, N, K, c):
-        W = copies["ffn_up"][c] if name == "ffn_up" else w_pre[name]
+    def mmq_on(name, N, K, c, lay):
+        if lay == "plane":
+            W, qt = planes[name][c % len(planes[name])], Q4_K | REPACKED
+        else:
+            W, qt = (copies["ffn_up"][c % ncopy] if name == "ffn_up" else w_pre[name]), Q4_K
 
         def fn():
-            mq.gemm(W, Q4_K, Xq, PREFILL_M, N, K, Y=Y_dev[name], scratch=scratch[name])
+            mq.gemm(W, qt, Xq, PREFILL_M, N, K, Y=Y_dev[name], scratch=scratch[name])
             kernel_names[f"mmq_{name}"] = mq.last_kernel()
         return fn
+
+    # Each prefill weight keeps the layout whose product is faster at M = 512 (GGUF payload
+    # or MMQ plane), chosen once at load time from a few timed graph replays, as a serving
+    # engine would; the timed step then runs the chosen kernels.
+    mq.quantize_act(X_dev, Xq)
+    layout_us = {}
+    layout = {}
+    for name, N, K in PREFILL:
+        layout_us[name] = {lay: timer.per_launch_us([mmq_on(name, N, K, c, lay) for c in range(4)], 5)
+                           for lay in ("gguf", "plane")}
+        layout[name] = min(layout_us[name], key=layout_us[name].get)
+
+    def mmq_launch(name, N, K, c):
+        return mmq_on(name, N, K, c, layout[name])
 
     def step_launches(c):
         out = [gemv_launch(name, N, K, c) for name, N, K in DECODE]
@@ -433,8 +472,15 @@ def main():
     for name, N, K in DECODE:
         avg_us[f"gemv_{name}"] = timer.per_launch_us([gemv_launch(name, N, K, c) for c in range(ncopy)], reps)
     avg_us["quantize_act"] = timer.per_launch_us([quant_launch] * 8, reps)
+    mmq_both = {}
     for name, N, K in PREFILL:
-        avg_us[f"mmq_{name}"] = timer.per_launch_us([mmq_launch(name, N, K, c % ncopy) for c in range(4)], reps)
+        for lay in ("gguf", "plane"):
+            us = timer.per_launch_us([mmq_on(name, N, K, c, lay) for c in range(4)], reps)
+            mmq_both[f"{name}_{lay}"] = {"us": round(us, 3), "kernel": mq.last_kernel(),
+                                         "TOPS": round(2 * PREFILL_M * N * K / us / 1e6, 2)}
+        avg_us[f"mmq_{name}"] = mmq_both[f"{name}_{layout[name]}"]["us"]
+        for fn in (mmq_launch(name, N, K, 0),):
+            fn()
 
     # plain-read ceiling: the same rotated ffn_up copies read by a kernel that only reads,
     # with the workgroup count of the GEMV (one per CU) and with the best of a few counts
@@ -498,8 +544,11 @@ def main():
             "parallelism": "single GPU",
         },
         "mmq_prefill_tops": round(mmq_tops, 2),
-        "mmq_dtype": ("Q4_K with >= 256 output tiles: fp8 (e4m3) block dots on the matrix cores, activation codes "
-                      "as two exact fp8 digits; otherwise int8 x int8 -> int32 block dots; f32 scales"),
+        "mmq_dtype": ("exact block dots: on Q4_K's MMQ plane fp6 (e2m3) x fp6 MFMA, weight codes c/2 and activation "
+                      "codes as two digits h/2, l/2 with block scales 2^5, 2^1 (f32 results); on the GGUF payload "
+                      "int8 MFMA (i32 results); f32 scales through bf16 hi/lo matrix products"),
+        "mmq_layouts": {"chosen": layout, "note": "per weight, the faster of the GGUF payload and the MMQ plane "
+                        "at M=512, chosen once at load time", "each": mmq_both},
         "roofline": {"bound": "hbm", "achieved": round(gemv_alg_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gemv_alg_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": recorded_traffic("gemv_q4k_7b_ffn_hbm_traffic.txt"),

@@ -833,24 +833,14 @@ MmqPlan mmq_plan(int /*type*/, int64_t M, int64_t N, int64_t K) {
 
 size_t mmq_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
     if (gemv_q8_applies(type, M, K)) return 0;
-    if (mmq_f8_applies(type, M, N)) return mmq_f8_scratch_bytes(M, N, K);
     const MmqPlan p = mmq_plan(type, M, N, K);
     return size_t(p.split_tiles) * size_t(p.splits) * size_t(p.bm) * BN * sizeof(float);
 }
 
-size_t mmq_partial_bytes(int type, int64_t M, int64_t N, int64_t K) {
-    if (gemv_q8_applies(type, M, K)) return 0;
-    if (mmq_f8_applies(type, M, N)) return mmq_f8_partial_bytes(M, N, K);
-    return mmq_scratch_bytes(type, M, N, K);
-}
-
 hipError_t launch_mmq(int type, BlockLayout lay, const uint8_t* W, const int8_t* codes, const float* xs,
-                      const int32_t* xsum, const uint8_t* digits, const uint8_t* step_scales, float* Y,
-                      int32_t* dots, void* scratch, unsigned* counters, int64_t M, int64_t N, int64_t K,
+                      const int32_t* xsum, float* Y, int32_t* dots, void* scratch, int64_t M, int64_t N, int64_t K,
                       hipStream_t s, const char** name) {
     if (gemv_q8_applies(type, M, K)) return launch_gemv_q8(type, lay, W, codes, xs, xsum, Y, dots, M, N, K, s, name);
-    if (mmq_f8_applies(type, M, N))
-        return launch_mmq_f8(type, W, digits, step_scales, Y, dots, scratch, counters, M, N, K, s, name);
     float* partial = static_cast<float*>(scratch);
     const bool repacked = lay.off != 0 || (type == kQ6_K && lay.stride != 210);
     switch (type) {

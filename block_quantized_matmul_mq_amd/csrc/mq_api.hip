@@ -26,7 +26,7 @@ constexpr int kMaxDevices = 64;
 DeviceInfo g_devices[kMaxDevices];
 
 // Scratch of mq_gemm_noalloc: one array per device for the life of the process.  The
-// first kNoAllocCounterBytes hold the fp8 kernel's split-tile counters, which only that
+// first kNoAllocCounterBytes hold the fp6 kernel's split-tile counters, which only that
 // kernel touches and which every launch leaves at zero (cleared once, when mq_init first
 // sets up the device); the partial tiles of either MMQ kernel follow.  Every valid shape's
 // partials fit: both plans cut at most one round of workgroups' worth of tiles (512 of
@@ -231,16 +231,6 @@ size_t mq_act_sum_offset(int64_t M, int64_t K) {
     return act_sum_offset(M, K);
 }
 
-size_t mq_act_digit_offset(int64_t M, int64_t K) {
-    if (M <= 0 || K <= 0 || K % 32 != 0) return 0;
-    return act_digit_offset(M, K);
-}
-
-size_t mq_act_step_scale_offset(int64_t M, int64_t K) {
-    if (M <= 0 || K <= 0 || K % 32 != 0) return 0;
-    return act_step_scale_offset(M, K);
-}
-
 size_t mq_act_f6_offset(int64_t M, int64_t K) {
     if (M <= 0 || K <= 0 || K % 32 != 0) return 0;
     return act_f6_offset(M, K);
@@ -271,7 +261,6 @@ int mq_quantize_act(const float* X, void* Xq, int64_t M, int64_t K, void* stream
     hipError_t e = launch_quantize_act(X, reinterpret_cast<int8_t*>(base),
                                        reinterpret_cast<float*>(base + act_scale_offset(M, K)),
                                        reinterpret_cast<int32_t*>(base + act_sum_offset(M, K)),
-                                       base + act_digit_offset(M, K), base + act_step_scale_offset(M, K),
                                        base + act_f6_offset(M, K), M, K, static_cast<hipStream_t>(stream));
     return launch_status(fn, e, "quantize_act");
 }
@@ -332,9 +321,8 @@ static int gemm_common(const char* fn, const void* W, int type, const void* Xq, 
     }
     hipError_t e = launch_mmq(type, lay, static_cast<const uint8_t*>(W), reinterpret_cast<const int8_t*>(xq),
                               reinterpret_cast<const float*>(xq + act_scale_offset(M, K)),
-                              reinterpret_cast<const int32_t*>(xq + act_sum_offset(M, K)),
-                              xq + act_digit_offset(M, K), xq + act_step_scale_offset(M, K), Yout, D, scratch,
-                              counters, M, N, K, static_cast<hipStream_t>(stream), &kernel);
+                              reinterpret_cast<const int32_t*>(xq + act_sum_offset(M, K)), Yout, D, scratch, M, N,
+                              K, static_cast<hipStream_t>(stream), &kernel);
     return launch_status(fn, e, kernel);
 }
 
@@ -357,7 +345,7 @@ int mq_gemm_noalloc(const void* W, int type, const void* Xq, float* Y, int64_t M
     if (mq_gemm_scratch_bytes(type, M, N, K) != 0) {   // a valid shape whose plan cuts tiles
         BlockLayout lay;
         const int base = parse_type(type, lay);
-        const size_t need = is_plane(lay) ? mmq_f6_partial_bytes(M, N, K) : mmq_partial_bytes(base, M, N, K);
+        const size_t need = is_plane(lay) ? mmq_f6_partial_bytes(M, N, K) : mmq_scratch_bytes(base, M, N, K);
         if (need > kNoAllocPartialBytes)
             return fail(MQ_ERR_SIZE, "%s: M=%lld N=%lld K=%lld needs %zu bytes of partial tiles, the limit is %zu", fn,
                         (long long)M, (long long)N, (long long)K, need, kNoAllocPartialBytes);
@@ -382,7 +370,6 @@ size_t mq_debug_lds_bytes(int what, int type, int64_t K) {
             return size_t(gemv_tile_units(type, K, MQ_GFX950_LDS_BYTES));
         case MQ_LDS_MMQ_I8_BM128: return mmq_smem_bytes(type, 128);
         case MQ_LDS_MMQ_I8_BM32: return mmq_smem_bytes(type, 32);
-        case MQ_LDS_MMQ_F8: return type == MQ_Q4_K ? mmq_f8_lds_bytes() : 0;
         case MQ_LDS_MMQ_F6: return type == MQ_Q4_K ? mmq_f6_lds_bytes() : 0;
         default: return 0;
     }

@@ -17,19 +17,12 @@ inline int unit_values(int type) { return is_kquant(type) ? 64 : 32; }
 inline bool is_legacy(int type) { return type == kQ4_0 || type == kQ4_1 || type == kQ5_0 || type == kQ5_1; }
 
 // Activation plane layout (see include/mq.h): codes [M][K] | scales [M][K/32] | sums [M][K/32]
-// | fp8 digit records [M][K/64][128 B] | step scales [K/64][M][16 B], each array starting on a
-// 256-byte boundary (K/64 rounded up).
+// | the fp6 section below, each array starting on a 256-byte boundary.
 inline size_t round_up256(size_t v) { return (v + 255) & ~size_t(255); }
 inline int64_t act_steps(int64_t K) { return (K + 63) / 64; }
 inline size_t act_scale_offset(int64_t M, int64_t K) { return round_up256(size_t(M) * size_t(K)); }
 inline size_t act_sum_offset(int64_t M, int64_t K) {
     return act_scale_offset(M, K) + round_up256(size_t(M) * size_t(K / 32) * 4);
-}
-inline size_t act_digit_offset(int64_t M, int64_t K) {
-    return act_sum_offset(M, K) + round_up256(size_t(M) * size_t(K / 32) * 4);
-}
-inline size_t act_step_scale_offset(int64_t M, int64_t K) {
-    return act_digit_offset(M, K) + round_up256(size_t(M) * size_t(act_steps(K)) * 128);
 }
 // The fp6 section (the activation half of the MMQ plane of the fp6 kernel): per 64-value
 // step t a slab of 128 Mp bytes, Mp = M rounded up to kF6TileRows (the padding rows are
@@ -54,7 +47,7 @@ inline size_t f6_weight_plane_bytes(int64_t N, int64_t K) {
     return size_t(act_steps(K)) * 80 * size_t(f6_weight_rows(N));
 }
 inline size_t act_f6_offset(int64_t M, int64_t K) {
-    return round_up256(act_step_scale_offset(M, K) + size_t(M) * size_t(act_steps(K)) * 16);
+    return act_sum_offset(M, K) + round_up256(size_t(M) * size_t(K / 32) * 4);
 }
 inline size_t act_bytes(int64_t M, int64_t K) {
     return act_f6_offset(M, K) + size_t(act_steps(K)) * 128 * size_t(f6_act_rows(M));
@@ -78,14 +71,13 @@ struct BlockLayout {
 
 // Kernel launchers: they enqueue on `s` and return the launch status (hipGetLastError read
 // right after the launch).  Arguments are validated by the callers in mq_api.hip.
-hipError_t launch_quantize_act(const float* X, int8_t* codes, float* scales, int32_t* sums, uint8_t* digits,
-                               uint8_t* step_scales, uint8_t* f6, int64_t M, int64_t K, hipStream_t s);
+hipError_t launch_quantize_act(const float* X, int8_t* codes, float* scales, int32_t* sums, uint8_t* f6, int64_t M,
+                               int64_t K, hipStream_t s);
 int gemv_tile_units(int type, int64_t K, size_t lds_limit);
 // LDS of the vector GEMV besides its row tile: the staged x (digit planes, block
-// exponents and sums), and of the MMQ kernels (int8: per type and tile rows; fp8 Q4_K).
+// exponents and sums), and of the int8 MMQ kernel (per type and tile rows).
 size_t fixed_lds_bytes(int type, int64_t K);
 size_t mmq_smem_bytes(int type, int bm);
-size_t mmq_f8_lds_bytes();
 hipError_t gemv_set_attributes(size_t lds_limit);
 hipError_t launch_gemv(int type, BlockLayout layout, const uint8_t* W, const float* x, float* y, int64_t N,
                        int64_t K, hipStream_t s, const char** kernel_name);
@@ -113,8 +105,8 @@ hipError_t launch_gemv_q8_tiled(int type, const uint8_t* W, const int8_t* codes,
 // MMQ work split over bm x 128 output tiles: the first `full` tiles are computed whole;
 // each of the remaining `split_tiles` is cut into `splits` ranges of whole K-steps.  The
 // int8 kernel (mmq.hip) writes the ranges' f32 partial tiles to scratch and a second
-// launch sums them; the fp8 kernel (mmq_f8.hip) sums them in the same launch
-// (mmq_splitk.h).  mmq_scratch_bytes is the scratch either needs.
+// launch sums them (the fp6 kernel, mmq_f6.hip, sums its own in the same launch:
+// mmq_splitk.h).  mmq_scratch_bytes is the scratch the int8 kernel needs.
 struct MmqPlan {
     int bm;            // output tile rows: 32 (M <= 32) or 128
     int full;
@@ -124,26 +116,11 @@ struct MmqPlan {
 };
 MmqPlan mmq_plan(int type, int64_t M, int64_t N, int64_t K);
 size_t mmq_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
-// Bytes of the partial tiles alone (mmq_scratch_bytes without the fp8 kernel's counters).
-size_t mmq_partial_bytes(int type, int64_t M, int64_t N, int64_t K);
 // Y: the product (null for the block-dot export); dots: the export (null for the product);
-// scratch: at least mmq_scratch_bytes of device memory when the plan has splits > 1 (for
-// the fp8 kernel its counters zero; every call leaves them zero again).  counters: where
-// the fp8 kernel keeps its split-tile counters (zero, and left zero again), or null to
-// keep them in scratch after the partial tiles.
+// scratch: at least mmq_scratch_bytes of device memory when the plan has splits > 1.
 hipError_t launch_mmq(int type, BlockLayout layout, const uint8_t* W, const int8_t* codes, const float* scales,
-                      const int32_t* sums, const uint8_t* digits, const uint8_t* step_scales, float* Y,
-                      int32_t* dots, void* scratch, unsigned* counters, int64_t M, int64_t N, int64_t K,
+                      const int32_t* sums, float* Y, int32_t* dots, void* scratch, int64_t M, int64_t N, int64_t K,
                       hipStream_t s, const char** kernel_name);
-// Q4_K at M > 32 rows: block dots on the fp8 matrix units from the plane's digit records
-// (mmq_f8.hip).
-bool mmq_f8_applies(int type, int64_t M, int64_t N);
-MmqPlan mmq_f8_plan(int64_t M, int64_t N, int64_t K);
-size_t mmq_f8_scratch_bytes(int64_t M, int64_t N, int64_t K);
-size_t mmq_f8_partial_bytes(int64_t M, int64_t N, int64_t K);
-hipError_t launch_mmq_f8(int type, const uint8_t* W, const uint8_t* digits, const uint8_t* step_scales, float* Y,
-                         int32_t* dots, void* scratch, unsigned* counters, int64_t M, int64_t N, int64_t K,
-                         hipStream_t s, const char** kernel_name);
 // Q4_K in the MMQ plane (mq_repack's layout): block dots on the fp6 matrix units from the
 // activation plane's fp6 section (mmq_f6.hip).  Any M.
 MmqPlan mmq_f6_plan(int64_t M, int64_t N, int64_t K);

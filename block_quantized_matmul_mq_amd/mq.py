@@ -18,7 +18,7 @@ Q8_0 = 8
 Q4_K = 12
 Q5_K = 13
 Q6_K = 14
-REPACKED = 0x100   # OR-ed into Q8_0 / Q6_K: weights in the layout mq_repack writes
+REPACKED = 0x100   # OR-ed into Q8_0 / Q6_K / Q4_K: weights in the layout mq_repack writes
 
 MQ_OK = 0
 ERRORS = {
@@ -35,8 +35,6 @@ _SIGNATURES = {
     "mq_act_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
     "mq_act_scale_offset": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
     "mq_act_sum_offset": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
-    "mq_act_digit_offset": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
-    "mq_act_step_scale_offset": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
     "mq_act_f6_offset": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
     "mq_quantize_act": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_void_p]),
@@ -194,22 +192,6 @@ def act_layout(M, K):
     """(total bytes, scale offset, sum offset) of the quantized activation plane."""
     lib = load()
     return lib.mq_act_bytes(M, K), lib.mq_act_scale_offset(M, K), lib.mq_act_sum_offset(M, K)
-
-
-def act_digits(Xq, M, K):
-    """View (uint8 [M, ceil(K/64), 128]) of the plane's fp8 digit records."""
-    off = load().mq_act_digit_offset(M, K)
-    T = (K + 63) // 64
-    return Xq[off:off + M * T * 128].view(M, T, 128)
-
-
-def act_step_scales(Xq, M, K):
-    """(scales f32 [T, M, 2], sums int32 [T, M, 2]) views of the step scale records."""
-    import torch
-    off = load().mq_act_step_scale_offset(M, K)
-    T = (K + 63) // 64
-    rec = Xq[off:off + T * M * 16].view(T, M, 16)
-    return rec[:, :, :8].contiguous().view(torch.float32), rec[:, :, 8:].contiguous().view(torch.int32)
 
 
 def act_f6(Xq, M, K):

@@ -39,27 +39,17 @@
  *        4 bits, 64 bytes high 2 bits, 16 int8 sub-scales, f16 d).  These are
  *        the public GGUF layouts; the pages fix only some sizes and the types.
  *   x  : K f32.   y : N f32.   X : M x K f32 row-major.   Y : M x N f32 row-major.
- *   Xq : the quantized activation plane written by mq_quantize_act, six
+ *   Xq : the quantized activation plane written by mq_quantize_act, four
  *        arrays in one buffer of mq_act_bytes(M, K) bytes (T = ceil(K / 64)):
  *          codes  int8  [M][K]          at offset 0
  *          scales f32   [M][K / 32]     at offset mq_act_scale_offset(M, K)
  *          sums   int32 [M][K / 32]     at offset mq_act_sum_offset(M, K)
- *          digits uint8 [M][T][128]     at offset mq_act_digit_offset(M, K)
- *          step scale records [T][M][16 bytes] at mq_act_step_scale_offset(M, K)
  *          fp6 section [T][128 Mp bytes] at mq_act_f6_offset(M, K), Mp = M rounded
  *                up to a multiple of 128 (rows M..Mp-1 zero)
  *        For block b of row m: scale = f32(amax) / f32(127) with IEEE division,
  *        code_i = clamp(round_half_even(x_i / scale), -127, 127) (a true f32
  *        division), scale 0 and codes 0 when amax == 0, and sum = sum of the 32
- *        codes.  The digit record re-encodes the block's codes exactly for the
- *        fp8 matrix units: |code| = 16 h + l (h in 0..7, l in 0..15), each digit
- *        an OCP e4m3 byte with the code's sign -- l as the byte (sign << 7) | l
- *        (value l * 2^-9), h as the e4m3 byte of h * 2^-5.  Digit record (m, t)
- *        holds blocks 2t and 2t + 1 of row m at bytes 0 and 64, each as
- *        [h of codes 0..31 | l of codes 0..31], 32 bytes each; step scale
- *        record (t, m) is (scale of block 2t, scale of block 2t + 1 as f32, sum
- *        of 2t, sum of 2t + 1 as int32).  When K % 64 == 32 the last step's
- *        second block is all zeros (digits, scale and sum).
+ *        codes.
  *        The fp6 section re-encodes the codes for the fp6 matrix units, each code
  *        q = 16 h + l (h = q >> 4 in -8..7, l = q & 15) as the 6-bit OCP FP6
  *        E2M3 codes of h / 2 and of l / 2 (exact); a block's 32 codes of one
@@ -72,6 +62,7 @@
  *                                                       tx_lo | tx_lo << 16)
  *        with dx the block scale and tx = dx * sum (the f32 product), each split
  *        as hi = bf16(v), lo = bf16(v - hi) (round to nearest even, bf16 bits).
+ *        When K % 64 == 32 the last step's second block is all zeros.
  *
  * Ownership and streams: the caller allocates and frees every buffer (device
  * memory, e.g. from torch).  Weights and inputs are read only.  No call
@@ -175,13 +166,10 @@ int mq_repack(const void* W, int type, int64_t N, int64_t K, size_t nbytes, void
               void* stream);
 
 /* Bytes of the quantized activation plane for M x K, and the offsets of its
- * scale, sum, digit, step scale and fp6 arrays (each 256-byte aligned).  0 if
- * K % 32 != 0. */
+ * scale, sum and fp6 arrays (each 256-byte aligned).  0 if K % 32 != 0. */
 size_t mq_act_bytes(int64_t M, int64_t K);
 size_t mq_act_scale_offset(int64_t M, int64_t K);
 size_t mq_act_sum_offset(int64_t M, int64_t K);
-size_t mq_act_digit_offset(int64_t M, int64_t K);
-size_t mq_act_step_scale_offset(int64_t M, int64_t K);
 size_t mq_act_f6_offset(int64_t M, int64_t K);
 
 /*
@@ -211,9 +199,9 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
  * all tiles, when there are at most 256) are cut into S ranges of whole
  * 128-value K-steps, and a second launch sums their S f32 partial tiles in
  * range order (deterministic).  The scratch then holds S x (number of cut
- * tiles) x BM x 128 f32.  The fp8 (Q4_K) and fp6 (Q4_K plane) kernels compute
+ * tiles) x BM x 128 f32.  The fp6 kernel (MQ_Q4_K | MQ_REPACKED) computes
  * 128 x 256 tiles with one workgroup per CU (rounds of 256, 64-value K-steps, at
- * least 4 per range) and sum the cut tiles in the same launch: their scratch is
+ * least 4 per range) and sums the cut tiles in the same launch: its scratch is
  * S x (cut tiles) x 128 x 256 f32 followed, at the next 256-byte boundary, by one
  * uint32 counter per cut tile, which must be zero before the first call and which
  * every call leaves at zero.  The split depends on the shape only, never on the
@@ -271,7 +259,6 @@ int mq_gemm_noalloc(const void* W, int type, const void* Xq, float* Y, int64_t M
  *                           next to them in MQ_GFX950_LDS_BYTES
  *   MQ_LDS_MMQ_I8_BM128 / _BM32  int8 MMQ workgroup LDS for the type at 128- /
  *                           32-row tiles (two workgroups share a CU)
- *   MQ_LDS_MMQ_F8           fp8 Q4_K MMQ workgroup LDS (one workgroup per CU)
  *   MQ_LDS_MMQ_F6           fp6 MMQ (Q4_K plane) workgroup LDS (one workgroup per CU)
  */
 #define MQ_GFX950_LDS_BYTES (160 * 1024)
@@ -279,7 +266,6 @@ int mq_gemm_noalloc(const void* W, int type, const void* Xq, float* Y, int64_t M
 #define MQ_LDS_GEMV_TILE_UNITS 1
 #define MQ_LDS_MMQ_I8_BM128 2
 #define MQ_LDS_MMQ_I8_BM32 3
-#define MQ_LDS_MMQ_F8 4
 #define MQ_LDS_MMQ_F6 5
 size_t mq_debug_lds_bytes(int what, int type, int64_t K);
 
@@ -316,8 +302,7 @@ int mq_device_lds_bytes(void);
  *     "gemv_mfma<q5_0>" (wide, GGUF layout), else "gemv<type>" (with " repacked" for MQ_REPACKED);
  *   mq_gemm: "mmq_f6<q4_K plane>" (MQ_Q4_K | MQ_REPACKED, any M),
  *     "gemv_q8_mfma<q6_K>" (M <= 8, Q6_K, as gemv_mfma<q6_K>),
- *     "gemv_q8<type>" (other M <= 8 shapes that fit LDS), "mmq_f8<q4_K>" (Q4_K,
- *     M > 32, at least 256 tiles of 128 x 256), else "mmq<type>". */
+ *     "gemv_q8<type>" (other M <= 8 shapes that fit LDS), else "mmq<type>". */
 const char* mq_last_kernel(void);
 
 /* Library version string. */

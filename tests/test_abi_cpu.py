@@ -57,18 +57,14 @@ def test_weight_bytes_are_exact_payload_sizes():
 @pytest.mark.parametrize("M,K", [(37, 96), (5, 128), (1, 32)])
 def test_activation_plane_layout(M, K):
     total, so, uo = mq.act_layout(M, K)
-    do = mq.load().mq_act_digit_offset(M, K)
-    to = mq.load().mq_act_step_scale_offset(M, K)
     fo = mq.load().mq_act_f6_offset(M, K)
     T = (K + 63) // 64     # 64-value steps, the last one half empty when K % 64 == 32
     Mp = -(-M // 128) * 128   # the fp6 section's rows, padded with zero rows
     assert so >= M * K and so % 256 == 0
     assert uo >= so + 4 * M * (K // 32) and uo % 256 == 0
-    assert do >= uo + 4 * M * (K // 32) and do % 256 == 0
-    assert to >= do + 128 * M * T and to % 256 == 0
-    assert fo >= to + 16 * M * T and fo % 256 == 0
+    assert fo >= uo + 4 * M * (K // 32) and fo % 256 == 0
     assert total == fo + 128 * Mp * T
-    assert mq.act_bytes(M, 100) == 0 and mq.load().mq_act_digit_offset(M, 100) == 0
+    assert mq.act_bytes(M, 100) == 0
     assert mq.load().mq_act_f6_offset(M, 100) == 0
 
 
@@ -118,22 +114,24 @@ def test_gemm_scratch_is_sized_by_the_split_plan():
         # partial slots, then one uint32 counter per split tile at a 256-byte boundary
         return ((tiles * pieces * tile_bytes + 255) // 256) * 256 + 4 * tiles
 
-    # Q4_K at M > 32 with at least 256 tiles of 128 x 256 runs the fp8 kernel: one
-    # workgroup per CU (rounds of 256), 64-value K-steps, at least 4 per range; partial
-    # tiles of 128 x 256 f32.
+    # Q4_K's MMQ plane runs the fp6 kernel: 128 x 256 tiles, one workgroup per CU (rounds
+    # of 256), 64-value K-steps, at least 4 per range; partial tiles of 128 x 256 f32, then
+    # the counters.
     t8 = 128 * 256 * 4
+    P = mq.Q4_K | mq.REPACKED
     # 256 tiles fill one round: no split, no scratch
-    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 16384, 3584) == 0
+    assert mq.gemm_scratch_bytes(P, 512, 16384, 3584) == 0
     # 296 tiles: 256 whole, the last 40 cut into 6 K ranges
-    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 18944, 3584) == sk(40, 6, t8)
+    assert mq.gemm_scratch_bytes(P, 512, 18944, 3584) == sk(40, 6, t8)
     # a last round more than half full is not cut (1200 tiles: 176 in the last round)
-    assert mq.gemm_scratch_bytes(mq.Q4_K, 512 * 3, 128 * 200, 3584) == 0
+    assert mq.gemm_scratch_bytes(P, 512 * 3, 128 * 200, 3584) == 0
     # 306 tiles: the last 50 cut into 5 ranges (56 steps: uneven)
-    assert mq.gemm_scratch_bytes(mq.Q4_K, 100, 306 * 256 - 13, 3584) == sk(50, 5, t8)
-    # the int8 kernel (every other type, Q4_K with fewer tiles, and Q4_K at M <= 32):
-    # 128 x 128 tiles, 128-value K-steps, at least 2 per range -- 28 steps at K = 3584, so
-    # 16 tiles take 14 ranges; its partial tiles are summed by a second launch and it
-    # needs no counters
+    assert mq.gemm_scratch_bytes(P, 100, 306 * 256 - 13, 3584) == sk(50, 5, t8)
+    # any M, small ones included (one tile of 128 x 256, 56 steps: 14 ranges)
+    assert mq.gemm_scratch_bytes(P, 1, 256, 3584) == sk(1, 14, t8)
+    # the int8 kernel (every type on the GGUF layout): 128 x 128 tiles, 128-value K-steps,
+    # at least 2 per range -- 28 steps at K = 3584, so 16 tiles take 14 ranges; its partial
+    # tiles are summed by a second launch and it needs no counters
     for t in (mq.Q4_K, mq.Q8_0, mq.Q6_K, mq.Q5_K, mq.Q4_0, mq.Q4_1, mq.Q5_0, mq.Q5_1):
         assert mq.gemm_scratch_bytes(t, 512, 512, 3584) == 14 * 16 * tile
     # 112 tiles (rounds of 512 workgroups, two per CU): 4 ranges each

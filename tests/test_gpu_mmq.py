@@ -136,12 +136,10 @@ def test_small_m_tiles_at_the_switch(qtype):
 @pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
 def test_whole_tiles_plus_split_tail(qtype):
     # 520 output tiles of 128 x 128 on the int8 path: 512 computed whole, the last 8 cut
-    # into 2 K ranges and summed by a second launch; 260 tiles of 128 x 256 on the fp8 path
-    # (Q4_K): 256 whole, the last 4 cut into 2 ranges summed by the range that finishes
-    # last.  Either way the cut tiles are the last 1024 columns; columns are sampled from
-    # both kinds of tile.  Scratch: the partial tiles (and 4 counters on the fp8 path).
+    # into 2 K ranges and summed by a second launch.  The cut tiles are the last 1024
+    # columns; columns are sampled from both kinds of tile.  Scratch: the partial tiles.
     M, N, K = 100, 128 * 520, 512
-    want = 2 * 4 * 128 * 256 * 4 + 4 * 4 if qtype == mq.Q4_K else 2 * 8 * 128 * 128 * 4
+    want = 2 * 8 * 128 * 128 * 4
     assert mq.gemm_scratch_bytes(qtype, M, N, K) == want
     raw = weights(qtype, N, K, "quantized", 80)
     X = synth.activations(M, K, config_index=12, tensor_index=31)
@@ -196,8 +194,8 @@ def sampled_blockdots(raw, qtype, X, N, K, rows, cols, what):
     (200, 129 * 256, 512, True),           # 258 tiles, the second row tile ragged; 2 cut into 2
     (100, 306 * 256 - 13, 3584, False),    # 256 whole + 50 cut into 5 uneven ranges of 56 steps
 ], ids=["ragged_n_split4", "ragged_m_split2", "uneven_split5"])
-def test_q4k_fp8_path_ragged_and_split(M, N, K, blockdots):
-    """The fp8 Q4_K kernel (shapes with at least one full round of 128 x 256 tiles):
+def test_q4k_large_gguf_ragged_and_split(M, N, K, blockdots):
+    """Q4_K on the GGUF layout at shapes with at least one full round of 128 x 256 tiles:
     ragged row and column tiles and K-split tiles, against the oracle on sampled columns
     (always including the first and the last tile) and, where the export fits, bitwise
     block dots on sampled rows and columns."""
@@ -205,15 +203,15 @@ def test_q4k_fp8_path_ragged_and_split(M, N, K, blockdots):
     X = synth.activations(M, K, config_index=12, tensor_index=90 + M)
     rng = np.random.default_rng(M)
     cols = np.unique(np.concatenate([np.arange(256), rng.choice(N, 300, replace=False), np.arange(N - 300, N)]))
-    check_gemm(raw, mq.Q4_K, X, N, K, cols=cols, what="fp8 path")
-    assert mq.last_kernel() == "mmq_f8<q4_K>", mq.last_kernel()
+    check_gemm(raw, mq.Q4_K, X, N, K, cols=cols, what="large Q4_K")
+    assert mq.last_kernel() == "mmq<q4_K>", mq.last_kernel()
     if blockdots:
         rows = np.unique(np.r_[0:8, M - 8:M, rng.choice(M, 8)])
-        kernel = sampled_blockdots(raw, mq.Q4_K, X, N, K, rows, cols, "fp8 path")
-        assert kernel == "mmq_f8<q4_K>", kernel
+        kernel = sampled_blockdots(raw, mq.Q4_K, X, N, K, rows, cols, "large Q4_K")
+        assert kernel == "mmq<q4_K>", kernel
 
 
-def test_q4k_fp8_path_extreme_activations():
+def test_q4k_large_gguf_extreme_activations():
     M, N, K = 40, 256 * 256, 512
     raw = weights(mq.Q4_K, N, K, "random", 150)
     X = synth.activations(M, K, config_index=14)
@@ -224,10 +222,10 @@ def test_q4k_fp8_path_extreme_activations():
     X[4, ::7] = np.float32(50.0)
     X[5, :32] = np.float32(127.0) * np.sign(X[5, :32])      # codes of +-127 in a block
     cols = np.unique(np.concatenate([np.arange(300), np.random.default_rng(6).choice(N, 300, replace=False)]))
-    check_gemm(raw, mq.Q4_K, X, N, K, cols=cols, what="fp8 path, extreme activations")
-    assert mq.last_kernel() == "mmq_f8<q4_K>", mq.last_kernel()
-    kernel = sampled_blockdots(raw, mq.Q4_K, X, N, K, np.arange(M), cols, "fp8 path, extreme activations")
-    assert kernel == "mmq_f8<q4_K>", kernel
+    check_gemm(raw, mq.Q4_K, X, N, K, cols=cols, what="large Q4_K, extreme activations")
+    assert mq.last_kernel() == "mmq<q4_K>", mq.last_kernel()
+    kernel = sampled_blockdots(raw, mq.Q4_K, X, N, K, np.arange(M), cols, "large Q4_K, extreme activations")
+    assert kernel == "mmq<q4_K>", kernel
 
 
 def test_one_plane_serves_qkv_and_gate_up():

@@ -24,38 +24,10 @@ def run_and_compare(X, what):
     assert np.array_equal(codes, q), f"{what}: codes differ at {np.argwhere(codes != q)[:5]}"
     assert np.array_equal(scales.view(np.uint32), d.view(np.uint32)), f"{what}: scales differ"
     assert np.array_equal(sums, S), f"{what}: sums differ"
-    # the fp8 digit records re-encode the codes exactly: h and l bytes decoded as e4m3
-    T = (K + 63) // 64
-    rec = mq.act_digits(Xq, M, K).cpu().numpy().reshape(M, 2 * T, 2, 32)
-    if K % 64:   # the last step's second block does not exist: all zero
-        assert not rec[:, -1].any(), f"{what}: padding digits"
-        rec = rec[:, :-1]
-    hv = e4m3_values(rec[:, :, 0, :]) * 2.0 ** 9
-    lv = e4m3_values(rec[:, :, 1, :]) * 2.0 ** 9
-    assert np.all(np.abs(lv) <= 15) and np.all(hv == 16 * np.round(hv / 16)), f"{what}: digit ranges"
-    assert np.all(np.abs(hv) <= 112), f"{what}: h digit range"
-    decoded = (hv + lv).reshape(M, K)
-    assert np.array_equal(decoded, q.astype(np.float64)), f"{what}: digit records differ from the codes"
-    # both digits carry the code's sign (the l byte of a code with |q| % 16 == 0 may be +-0)
-    assert np.all(np.sign(hv.reshape(M, K)) * np.sign(q) >= 0), f"{what}: digit signs"
-    # step scale records: (scale, scale, sum, sum) of blocks 2t and 2t + 1, zero padded
-    ss, sm = (t.cpu().numpy() for t in mq.act_step_scales(Xq, M, K))
-    pad = 2 * T - K // 32
-    dpad = np.concatenate([d, np.zeros((M, pad), np.float32)], axis=1).reshape(M, T, 2)
-    spad = np.concatenate([S, np.zeros((M, pad), np.int32)], axis=1).reshape(M, T, 2)
-    assert np.array_equal(ss.transpose(1, 0, 2).view(np.uint32), dpad.view(np.uint32)), f"{what}: step scales"
-    assert np.array_equal(sm.transpose(1, 0, 2), spad), f"{what}: step sums"
-
-
-def e4m3_values(b):
-    """OCP e4m3 bytes -> float64 (no NaN bytes are expected here)."""
-    b = b.astype(np.int64)
-    assert not np.any((b & 0x7F) == 0x7F), "NaN byte"
-    s = np.where(b >> 7, -1.0, 1.0)
-    e = (b >> 3) & 15
-    m = b & 7
-    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e - 10.0))
-    return s * mag
+    # the fp6 section (the activation operands of the Q4_K plane product) bit for bit
+    got = mq.act_f6(Xq, M, K).cpu().numpy().reshape(-1)
+    ref = oracle.act_f6_section(q, d, S)
+    assert np.array_equal(got, ref), f"{what}: fp6 section differs at byte {int(np.argmax(got != ref))}"
 
 
 @pytest.mark.parametrize("M,K", [(1, 32), (3, 96), (7, 4128), (5, 4160), (16, 896), (8, 3584), (512, 3584),

@@ -11,7 +11,7 @@ import pytest
 from block_quantized_matmul_mq_amd import mq
 
 LIMIT = 160 * 1024
-FIXED, TILE_UNITS, I8_BM128, I8_BM32, F8, F6 = 0, 1, 2, 3, 4, 5
+FIXED, TILE_UNITS, I8_BM128, I8_BM32, F6 = 0, 1, 2, 3, 5
 TYPES = [mq.Q4_0, mq.Q4_1, mq.Q5_0, mq.Q5_1, mq.Q8_0, mq.Q4_K, mq.Q5_K, mq.Q6_K]
 KQUANT = {mq.Q4_K, mq.Q5_K, mq.Q6_K}
 MIN_TERM = {mq.Q4_1, mq.Q5_1, mq.Q4_K, mq.Q5_K}   # a per-block min is subtracted
@@ -66,18 +66,6 @@ def test_int8_mmq_lds(qtype):
         got = lds(what, qtype)
         assert got == want, (qtype, bm, got, want)
         assert 2 * got <= LIMIT, "two workgroups per CU (512 resident) is what the work split assumes"
-
-
-def test_fp8_mmq_lds():
-    # ring of 3 step slots: digit lines 128 x 128 B, scale records 128 x 16 B, code bytes
-    # 256 x 32 B, headers 256 x 16 B; 2 work buffers: codes 256 x 64 B, bf16 pairs of the
-    # activation scales (2 x 2 x 128 x 8 B), weight scales (2 x 2 x 256 x 8 B), activation
-    # min terms (2 x 128 x 8 B), weight mins (2 x 256 x 8 B)
-    slot = 128 * 128 + 128 * 16 + 256 * 32 + 256 * 16
-    work = 256 * 64 + 2 * 2 * 128 * 8 + 2 * 2 * 256 * 8 + 2 * 128 * 8 + 2 * 256 * 8
-    assert lds(F8, mq.Q4_K) == 3 * slot + 2 * work
-    assert lds(F8, mq.Q4_K) <= LIMIT
-    assert lds(F8, mq.Q6_K) == 0
 
 
 def test_fp6_mmq_lds():

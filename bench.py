@@ -587,7 +587,7 @@ def main():
         Xh = torch.from_numpy(synth.activations(8, 3584, 2, tensor_index=5)).to(dev)
         Xhq = mq.quantize_act(Xh)
         Yh = torch.empty((8, 152064), dtype=torch.float32, device=dev)
-        sch = torch.empty(max(mq.gemm_scratch_bytes(Q6_K, 8, 152064, 3584), 256), dtype=torch.uint8, device=dev)
+        sch = torch.zeros(max(mq.gemm_scratch_bytes(Q6_K, 8, 152064, 3584), 256), dtype=torch.uint8, device=dev)
         us = timer.per_launch_us([lambda W=W: mq.gemm(W, Q6_K, Xhq, 8, 152064, 3584, Y=Yh, scratch=sch)
                                   for W in hcop], reps)
         sec["mmq_q6_K_head_M8_152064x3584"] = {"us": round(us, 3), "weight_GBps": round(hb / us / 1e3, 1),
@@ -630,7 +630,7 @@ def main():
             us = timer.per_launch_us([lambda W=W: mq.gemv(W, qt, xt, N7, K7, y=yt) for W in wc], reps)
             gk = mq.last_kernel()
             Yt = torch.empty((PREFILL_M, N7), dtype=torch.float32, device=dev)
-            sct = torch.empty(max(mq.gemm_scratch_bytes(qt, PREFILL_M, N7, K7), 256), dtype=torch.uint8, device=dev)
+            sct = torch.zeros(max(mq.gemm_scratch_bytes(qt, PREFILL_M, N7, K7), 256), dtype=torch.uint8, device=dev)
             us_m = timer.per_launch_us([lambda W=W: mq.gemm(W, qt, Xq, PREFILL_M, N7, K7, Y=Yt, scratch=sct)
                                         for W in wc[:4]], reps)
             sec[f"{tag}_7B_ffn_up_{N7}x{K7}"] = {
@@ -653,7 +653,7 @@ def main():
         us_cat = timer.per_launch_us([lambda g=g: mq.gemv(g, Q4_K, xg, 2 * N7, K7, y=ygu) for g in gus], reps)
         Ygu = torch.empty((PREFILL_M, 2 * N7), dtype=torch.float32, device=dev)
         Yg, Yu = (torch.empty((PREFILL_M, N7), dtype=torch.float32, device=dev) for _ in range(2))
-        scg = torch.empty(max(mq.gemm_scratch_bytes(Q4_K, PREFILL_M, 2 * N7, K7),
+        scg = torch.zeros(max(mq.gemm_scratch_bytes(Q4_K, PREFILL_M, 2 * N7, K7),
                               mq.gemm_scratch_bytes(Q4_K, PREFILL_M, N7, K7), 256), dtype=torch.uint8, device=dev)
         mm_sep = timer.per_launch_us([lambda: (mq.gemm(gate, Q4_K, Xq, PREFILL_M, N7, K7, Y=Yg, scratch=scg),
                                                mq.gemm(upw, Q4_K, Xq, PREFILL_M, N7, K7, Y=Yu, scratch=scg))] * 2,

@@ -46,6 +46,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "mmq_splitk.h"
 #include "mq_device.h"
 #include "mq_internal.h"
 #include "weight_units.h"
@@ -73,9 +74,10 @@ constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource: 32-bit data fo
 template <int QT> struct Groups { static constexpr int per_step = NB; };
 template <> struct Groups<kQ6_K> { static constexpr int per_step = 2 * NB; };
 
-// Output tile rows: 128 for prefill-sized M, 32 for small M (at most 32 activation
-// rows), where a 128-row tile would be mostly padding.  Waves: WM x WN, each owning
-// TI x TJ MFMA tiles of 32 x 32.
+// Output tile rows: 128 for prefill-sized products, 32 for small M (at most 32 activation
+// rows, where a 128-row tile would be mostly padding) and for products whose 128-row tiles
+// would not fill half the chip (a small N: four times as many tiles, so fewer K cuts).
+// Waves: WM x WN, each owning TI x TJ MFMA tiles of 32 x 32.
 template <int BM_>
 struct TileShape {
     static constexpr int BM = BM_;
@@ -445,16 +447,18 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
                                                      const float* __restrict__ xscale,
                                                      const int32_t* __restrict__ xsum,
                                                      float* __restrict__ Y, int32_t* __restrict__ dots,
-                                                     float* __restrict__ partial, int M, int N, int K,
-                                                     int64_t row_bytes, int blk_stride, int blk_off, int tiles_m,
-                                                     int full, int split_tiles, int splits, int total_steps) {
+                                                     float* __restrict__ partial, unsigned* __restrict__ counters,
+                                                     int M, int N, int K, int64_t row_bytes, int blk_stride,
+                                                     int blk_off, int tiles_m, int full, int split_tiles, int splits,
+                                                     int total_steps) {
     using T = TileShape<BM>;
     constexpr int TI = T::TI, TJ = T::TJ;
     __shared__ __attribute__((aligned(16))) Smem<QT, BM> sm;
 
     // Work split (MmqPlan): workgroups [0, full) own whole tiles 0..full-1; the remaining
     // split_tiles tiles are each cut into `splits` K ranges, one workgroup per range, whose
-    // f32 partial tiles a second launch sums.  Within each group the ids are remapped so
+    // f32 partial tiles the range that finishes last sums (mmq_splitk.h).  Within each group
+    // the ids are remapped so
     // that workgroups landing on one XCD take consecutive logical ids, and consecutive ids
     // are the M-tiles of one N-tile, which read the same weights.
     const int id = blockIdx.x;
@@ -471,8 +475,6 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
     // K range: steps [s0, s1) of KS values
     const int kbeg = int(int64_t(split) * total_steps / nsplit) * KS;
     const int kend = min(int(int64_t(split + 1) * total_steps / nsplit) * KS, K);
-    // a split tile's partial goes to its own BM x BN slot of the partial buffer
-    float* Pt = whole ? nullptr : partial + (int64_t(split) * split_tiles + (tile - full)) * (BM * BN);
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -645,70 +647,49 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const uint8_t* __restrict__
     }
 
     // Y store: for a fixed accumulator element the 32 lanes of a group write 32 consecutive n.
-    // A split tile stores its partial tile whole (the reduce applies the M, N bounds).
     // The block-dot export variant stores only the dots.
     if constexpr (DUMP) return;
+    auto store = [&](int i, int j, const float* y) {
+        const int n = n0 + 32 * TJ * wn + 32 * j + r32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int m = m0 + 32 * TI * wm + 32 * i + acc_row(v, g);
+            if (m < M && n < N) Y[int64_t(m) * N + n] = y[v];
+        }
+    };
+    if (whole) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+                float y[16];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) y[v] = acc[i][j][v];
+                store(i, j, y);
+            }
+        return;
+    }
+    // A split tile puts its partial into its range's slot, and the range that counts in last
+    // sums all ranges' slots in range order into Y.
+    constexpr uint32_t kSlotBytes = BM * BN * sizeof(float);
+    const __amdgpu_buffer_rsrc_t slots =
+        make_rsrc(partial + size_t(tile - full) * size_t(splits) * (BM * BN), int64_t(splits) * kSlotBytes);
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-            const int nl = 32 * TJ * wn + 32 * j + r32;
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int ml = 32 * TI * wm + 32 * i + acc_row(v, g);
-                if (!whole) {
-                    Pt[ml * BN + nl] = acc[i][j][v];
-                } else if (m0 + ml < M && n0 + nl < N) {
-                    Y[int64_t(m0 + ml) * N + n0 + nl] = acc[i][j][v];
-                }
-            }
-        }
-}
-
-// Sum of the partial tiles P[splits][split_tiles][bm x BN] of the split tiles, in split
-// order (deterministic), into Y.  Split tile t is tile full + t.
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, float* __restrict__ Y,
-                                                            int M, int N, int bm, int tiles_m, int full,
-                                                            int split_tiles, int splits) {
-    // Four consecutive elements of one output row per thread (BN is a multiple of 4), the
-    // partials of eight splits loaded before any is added (independent loads in flight),
-    // then added in split order: the same sums, in the same order, as one split at a time.
-    const int t = blockIdx.y;
-    const int tile = full + t;
-    const int m0 = (tile % tiles_m) * bm, n0 = (tile / tiles_m) * BN;
-    const int64_t slot = int64_t(bm) * BN;
-    const int64_t step = int64_t(split_tiles) * slot / 4;   // one split further, in float4
-    for (int e4 = blockIdx.x * 256 + threadIdx.x; e4 < bm * BN / 4; e4 += gridDim.x * 256) {
-        const int e = 4 * e4;
-        const int m = m0 + e / BN, n = n0 + e % BN;
-        if (m >= M || n >= N) continue;
-        const float4* p = reinterpret_cast<const float4*>(P + int64_t(t) * slot + e);
-        float4 acc = p[0];
-        int sp = 1;
-        for (; sp + 8 <= splits; sp += 8) {
-            float4 v[8];
+            for (int v = 0; v < 16; v += 4)
+                splitk_put<256>(slots, uint32_t(split) * kSlotBytes, ((i * TJ + j) * 16 + v) / 4,
+                                splitk_f4{acc[i][j][v], acc[i][j][v + 1], acc[i][j][v + 2], acc[i][j][v + 3]});
+    // the ticket word: LDS that no thread touches after the last step's barrier
+    if (!splitk_arrive(counters + (tile - full), splits, reinterpret_cast<unsigned*>(&sm.dx[0][0][0]))) return;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = p[(sp + j) * step];
+    for (int i = 0; i < TI; ++i) {   // one row of accumulator tiles at a time (registers)
+        float y[TJ * 16];
+        splitk_sum<TJ * 16, 256>(slots, kSlotBytes, splits, i * TJ * 4, y);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                acc.x += v[j].x;
-                acc.y += v[j].y;
-                acc.z += v[j].z;
-                acc.w += v[j].w;
-            }
-        }
-        for (; sp < splits; ++sp) {
-            const float4 v = p[sp * step];
-            acc.x += v.x;
-            acc.y += v.y;
-            acc.z += v.z;
-            acc.w += v.w;
-        }
-        float* y = Y + int64_t(m) * N + n;
-        y[0] = acc.x;
-        if (n + 1 < N) y[1] = acc.y;
-        if (n + 2 < N) y[2] = acc.z;
-        if (n + 3 < N) y[3] = acc.w;
+        for (int j = 0; j < TJ; ++j) store(i, j, y + 16 * j);
     }
 }
 
@@ -718,8 +699,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     template __global__ void mmq_kernel<QT, BM, DUMP>(const uint8_t* __restrict__, const int8_t* __restrict__, \
                                                       const float* __restrict__, const int32_t* __restrict__,  \
                                                       float* __restrict__, int32_t* __restrict__,              \
-                                                      float* __restrict__, int, int, int, int64_t, int, int, int, \
-                                                      int, int, int, int);
+                                                      float* __restrict__, unsigned* __restrict__, int, int, int, \
+                                                      int64_t, int, int, int, int, int, int, int);
 MQ_MMQ_INSTANCE(kQ5_K, 32, false)
 MQ_MMQ_INSTANCE(kQ5_K, 128, false)
 MQ_MMQ_INSTANCE(kQ5_K, 32, true)
@@ -756,34 +737,34 @@ MQ_MMQ_INSTANCE(kQ6_K, 128, true)
 
 template <int QT, int BM>
 hipError_t launch_shaped(const uint8_t* W, const int8_t* codes, const float* xs, const int32_t* xsum, float* Y,
-                         int32_t* dots, float* partial, int64_t M, int64_t N, int64_t K, BlockLayout lay,
-                         const MmqPlan& plan, hipStream_t s) {
+                         int32_t* dots, float* partial, unsigned* counters, int64_t M, int64_t N, int64_t K,
+                         BlockLayout lay, const MmqPlan& plan, hipStream_t s) {
     const int tiles_m = int((M + BM - 1) / BM);
     const int total = plan.full + plan.split_tiles * plan.splits;
     const int64_t row_bytes = (K / block_values_of(QT)) * lay.stride;
-    if (dots) {
+    if (dots)
         hipLaunchKernelGGL((mmq_kernel<QT, BM, true>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, Y, dots,
-                           partial, int(M), int(N), int(K), row_bytes, lay.stride, lay.off, tiles_m, plan.full,
-                           plan.split_tiles, plan.splits, plan.steps);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL((mmq_kernel<QT, BM, false>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, Y, dots,
-                       partial, int(M), int(N), int(K), row_bytes, lay.stride, lay.off, tiles_m, plan.full,
-                       plan.split_tiles, plan.splits, plan.steps);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || plan.split_tiles == 0) return e;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(BM * BN / 1024, plan.split_tiles), dim3(256), 0, s, partial, Y,
-                       int(M), int(N), BM, tiles_m, plan.full, plan.split_tiles, plan.splits);
+                           partial, counters, int(M), int(N), int(K), row_bytes, lay.stride, lay.off, tiles_m,
+                           plan.full, plan.split_tiles, plan.splits, plan.steps);
+    else
+        hipLaunchKernelGGL((mmq_kernel<QT, BM, false>), dim3(total), dim3(256), 0, s, W, codes, xs, xsum, Y, dots,
+                           partial, counters, int(M), int(N), int(K), row_bytes, lay.stride, lay.off, tiles_m,
+                           plan.full, plan.split_tiles, plan.splits, plan.steps);
     return hipGetLastError();
 }
 
 template <int QT>
 hipError_t launch_typed(const uint8_t* W, const int8_t* codes, const float* xs, const int32_t* xsum,
-                        float* Y, int32_t* dots, float* partial, int64_t M, int64_t N, int64_t K,
-                        BlockLayout lay, hipStream_t s) {
+                        float* Y, int32_t* dots, float* partial, unsigned* counters, int64_t M, int64_t N,
+                        int64_t K, BlockLayout lay, hipStream_t s) {
     const MmqPlan plan = mmq_plan(QT, M, N, K);
-    if (plan.bm == 32) return launch_shaped<QT, 32>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, plan, s);
-    return launch_shaped<QT, 128>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, plan, s);
+    if (!counters && partial) {   // the caller's scratch: counters, then the partial tiles
+        counters = reinterpret_cast<unsigned*>(partial);
+        partial = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(partial) + kSplitkCounterBytes);
+    }
+    if (plan.bm == 32)
+        return launch_shaped<QT, 32>(W, codes, xs, xsum, Y, dots, partial, counters, M, N, K, lay, plan, s);
+    return launch_shaped<QT, 128>(W, codes, xs, xsum, Y, dots, partial, counters, M, N, K, lay, plan, s);
 }
 
 }  // namespace
@@ -813,7 +794,10 @@ MmqPlan mmq_plan(int /*type*/, int64_t M, int64_t N, int64_t K) {
     // enough of them to fill that round.  A function of the shape alone, so the result does
     // not depend on the device.
     MmqPlan p;
-    p.bm = M <= kSmallM ? 32 : 128;
+    // 128-row tiles while there are enough of them to fill more than half a round; else
+    // (small M, or a small N) 32-row tiles, four times as many, so fewer are cut.
+    const int64_t tiles128 = ((M + 127) / 128) * ((N + BN - 1) / BN);
+    p.bm = M <= kSmallM || tiles128 * 2 <= kTargetWorkgroups ? 32 : 128;
     p.steps = int((K + KS - 1) / KS);
     const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + BN - 1) / BN);
     const int64_t rem = tiles % kTargetWorkgroups;
@@ -821,7 +805,11 @@ MmqPlan mmq_plan(int /*type*/, int64_t M, int64_t N, int64_t K) {
     p.split_tiles = 0;
     p.splits = 1;
     if (rem > 0 && rem * 2 <= kTargetWorkgroups) {
-        const int64_t splits = std::min<int64_t>(kTargetWorkgroups / rem, p.steps / kMinStepsPerSplit);
+        // 32-row tiles of a small N (M above kSmallM) fill only half a round, one workgroup per
+        // CU: their ranges are short and bound by load latency, and a CU of their own runs
+        // them faster than two workgroups sharing one (512 x 512 x 3584: 15.4 us against 16.4).
+        const int64_t fill = p.bm == 32 && M > kSmallM ? kTargetWorkgroups / 2 : kTargetWorkgroups;
+        const int64_t splits = std::min<int64_t>(fill / rem, p.steps / kMinStepsPerSplit);
         if (splits >= 2) {
             p.full = int(tiles - rem);
             p.split_tiles = int(rem);
@@ -834,40 +822,46 @@ MmqPlan mmq_plan(int /*type*/, int64_t M, int64_t N, int64_t K) {
 size_t mmq_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
     if (gemv_q8_applies(type, M, K)) return 0;
     const MmqPlan p = mmq_plan(type, M, N, K);
+    return splitk_scratch_bytes(p.split_tiles, p.splits, int64_t(p.bm) * BN);
+}
+
+size_t mmq_partial_bytes(int type, int64_t M, int64_t N, int64_t K) {
+    if (gemv_q8_applies(type, M, K)) return 0;
+    const MmqPlan p = mmq_plan(type, M, N, K);
     return size_t(p.split_tiles) * size_t(p.splits) * size_t(p.bm) * BN * sizeof(float);
 }
 
 hipError_t launch_mmq(int type, BlockLayout lay, const uint8_t* W, const int8_t* codes, const float* xs,
-                      const int32_t* xsum, float* Y, int32_t* dots, void* scratch, int64_t M, int64_t N, int64_t K,
-                      hipStream_t s, const char** name) {
+                      const int32_t* xsum, float* Y, int32_t* dots, void* scratch, unsigned* counters, int64_t M,
+                      int64_t N, int64_t K, hipStream_t s, const char** name) {
     if (gemv_q8_applies(type, M, K)) return launch_gemv_q8(type, lay, W, codes, xs, xsum, Y, dots, M, N, K, s, name);
     float* partial = static_cast<float*>(scratch);
     const bool repacked = lay.off != 0 || (type == kQ6_K && lay.stride != 210);
     switch (type) {
         case kQ8_0:
             *name = repacked ? "mmq<q8_0 repacked>" : "mmq<q8_0>";
-            return launch_typed<kQ8_0>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
+            return launch_typed<kQ8_0>(W, codes, xs, xsum, Y, dots, partial, counters, M, N, K, lay, s);
         case kQ4_K:
             *name = "mmq<q4_K>";
-            return launch_typed<kQ4_K>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
+            return launch_typed<kQ4_K>(W, codes, xs, xsum, Y, dots, partial, counters, M, N, K, lay, s);
         case kQ6_K:
             *name = repacked ? "mmq<q6_K repacked>" : "mmq<q6_K>";
-            return launch_typed<kQ6_K>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
+            return launch_typed<kQ6_K>(W, codes, xs, xsum, Y, dots, partial, counters, M, N, K, lay, s);
         case kQ5_K:
             *name = "mmq<q5_K>";
-            return launch_typed<kQ5_K>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
+            return launch_typed<kQ5_K>(W, codes, xs, xsum, Y, dots, partial, counters, M, N, K, lay, s);
         case kQ4_0:
             *name = "mmq<q4_0>";
-            return launch_typed<kQ4_0>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
+            return launch_typed<kQ4_0>(W, codes, xs, xsum, Y, dots, partial, counters, M, N, K, lay, s);
         case kQ4_1:
             *name = "mmq<q4_1>";
-            return launch_typed<kQ4_1>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
+            return launch_typed<kQ4_1>(W, codes, xs, xsum, Y, dots, partial, counters, M, N, K, lay, s);
         case kQ5_0:
             *name = "mmq<q5_0>";
-            return launch_typed<kQ5_0>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
+            return launch_typed<kQ5_0>(W, codes, xs, xsum, Y, dots, partial, counters, M, N, K, lay, s);
         case kQ5_1:
             *name = "mmq<q5_1>";
-            return launch_typed<kQ5_1>(W, codes, xs, xsum, Y, dots, partial, M, N, K, lay, s);
+            return launch_typed<kQ5_1>(W, codes, xs, xsum, Y, dots, partial, counters, M, N, K, lay, s);
         default: return hipErrorInvalidValue;
     }
 }

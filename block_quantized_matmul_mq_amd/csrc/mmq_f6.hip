@@ -445,9 +445,10 @@ hipError_t launch_mmq_f6(const uint8_t* Wp, const uint8_t* Ap, float* Y, int32_t
     const int tiles_m = int((M + BM - 1) / BM);
     const int total = plan.full + plan.split_tiles * plan.splits;
     float* partial = static_cast<float*>(scratch);
-    if (!counters && scratch)
-        counters = reinterpret_cast<unsigned*>(static_cast<uint8_t*>(scratch) +
-                                               splitk_counter_offset(plan.split_tiles, plan.splits, int64_t(BM) * BN));
+    if (!counters && scratch) {   // the caller's scratch: counters, then the partial tiles
+        counters = static_cast<unsigned*>(scratch);
+        partial = reinterpret_cast<float*>(static_cast<uint8_t*>(scratch) + kSplitkCounterBytes);
+    }
     const int Mp = int(f6_act_rows(M)), Np = int(f6_weight_rows(N));
     if (dots)
         hipLaunchKernelGGL(mmq_f6_q4k_kernel<true>, dim3(total), dim3(kThreads), 0, s, Wp, Ap, Y, dots, partial,

@@ -1,4 +1,4 @@
-// K-split output tiles of the fp8 MMQ kernel, summed inside the product launch.
+// K-split output tiles of the MMQ kernels, summed inside the product launch.
 //
 // A tile whose K range is cut into P pieces is computed by P workgroups.  Each piece
 // stores its partial accumulator tile to its own slot of the caller's scratch and
@@ -11,9 +11,10 @@
 // a tile's first piece and is back at 0 after its last, so a scratch buffer that starts
 // zeroed stays ready for the next call without any clearing launch.
 //
-// Scratch layout for T split tiles of P pieces and F floats per partial tile:
-//   partial slots f32 [T][P][F] at 0, then uint32 counters [T] at the next 256-byte
-//   boundary.
+// Scratch layout for T split tiles (T <= kSplitkMaxTiles) of P pieces and F floats per
+// partial tile: uint32 counters [kSplitkMaxTiles] at 0, partial slots f32 [T][P][F] from
+// kSplitkCounterBytes.  The counters sit at the same place for every shape, so calls of
+// different shapes may share one buffer: no call's partial tiles cover another's counters.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,12 +23,11 @@
 
 namespace mq {
 
-inline size_t splitk_counter_offset(int64_t tiles, int64_t pieces, int64_t tile_floats) {
-    return (size_t(tiles) * size_t(pieces) * size_t(tile_floats) * 4 + 255) & ~size_t(255);
-}
+constexpr int kSplitkMaxTiles = 256;                       // both plans cut at most half a round
+constexpr size_t kSplitkCounterBytes = kSplitkMaxTiles * 4;
 inline size_t splitk_scratch_bytes(int64_t tiles, int64_t pieces, int64_t tile_floats) {
     if (tiles == 0) return 0;
-    return splitk_counter_offset(tiles, pieces, tile_floats) + size_t(tiles) * 4;
+    return kSplitkCounterBytes + size_t(tiles) * size_t(pieces) * size_t(tile_floats) * 4;
 }
 
 // The partials move through buffer loads and stores with the sc1 cache policy: on gfx950

@@ -26,11 +26,11 @@ constexpr int kMaxDevices = 64;
 DeviceInfo g_devices[kMaxDevices];
 
 // Scratch of mq_gemm_noalloc: one array per device for the life of the process.  The
-// first kNoAllocCounterBytes hold the fp6 kernel's split-tile counters, which only that
-// kernel touches and which every launch leaves at zero (cleared once, when mq_init first
-// sets up the device); the partial tiles of either MMQ kernel follow.  Every valid shape's
-// partials fit: both plans cut at most one round of workgroups' worth of tiles (512 of
-// 128 x 128, or 256 of 128 x 256 f32), 32 MiB.
+// first kNoAllocCounterBytes hold the split-tile counters of both MMQ kernels (at most 256
+// cut tiles), which every launch leaves at zero (cleared once, when mq_init first sets up
+// the device); the partial tiles follow.  Every valid shape's partials fit: both plans cut
+// at most one round of workgroups' worth of tiles (512 of 128 x 128, or 256 of 128 x 256
+// f32), 32 MiB.
 constexpr size_t kNoAllocCounterBytes = 4096;
 constexpr size_t kNoAllocPartialBytes = size_t(MQ_NOALLOC_PARTIAL_BYTES);
 static __device__ __align__(256) uint8_t noalloc_scratch[kNoAllocCounterBytes + kNoAllocPartialBytes];
@@ -321,8 +321,8 @@ static int gemm_common(const char* fn, const void* W, int type, const void* Xq, 
     }
     hipError_t e = launch_mmq(type, lay, static_cast<const uint8_t*>(W), reinterpret_cast<const int8_t*>(xq),
                               reinterpret_cast<const float*>(xq + act_scale_offset(M, K)),
-                              reinterpret_cast<const int32_t*>(xq + act_sum_offset(M, K)), Yout, D, scratch, M, N,
-                              K, static_cast<hipStream_t>(stream), &kernel);
+                              reinterpret_cast<const int32_t*>(xq + act_sum_offset(M, K)), Yout, D, scratch,
+                              counters, M, N, K, static_cast<hipStream_t>(stream), &kernel);
     return launch_status(fn, e, kernel);
 }
 
@@ -345,7 +345,7 @@ int mq_gemm_noalloc(const void* W, int type, const void* Xq, float* Y, int64_t M
     if (mq_gemm_scratch_bytes(type, M, N, K) != 0) {   // a valid shape whose plan cuts tiles
         BlockLayout lay;
         const int base = parse_type(type, lay);
-        const size_t need = is_plane(lay) ? mmq_f6_partial_bytes(M, N, K) : mmq_scratch_bytes(base, M, N, K);
+        const size_t need = is_plane(lay) ? mmq_f6_partial_bytes(M, N, K) : mmq_partial_bytes(base, M, N, K);
         if (need > kNoAllocPartialBytes)
             return fail(MQ_ERR_SIZE, "%s: M=%lld N=%lld K=%lld needs %zu bytes of partial tiles, the limit is %zu", fn,
                         (long long)M, (long long)N, (long long)K, need, kNoAllocPartialBytes);

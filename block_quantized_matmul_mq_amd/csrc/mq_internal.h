@@ -102,13 +102,14 @@ bool gemv_q8_tiled_applies(int type, BlockLayout layout, const uint8_t* W, const
 hipError_t launch_gemv_q8_tiled(int type, const uint8_t* W, const int8_t* codes, const float* xs, float* Y,
                                 int32_t* dots, int64_t M, int64_t N, int64_t K, int cu_count, hipStream_t s,
                                 const char** kernel_name);
-// MMQ work split over bm x 128 output tiles: the first `full` tiles are computed whole;
-// each of the remaining `split_tiles` is cut into `splits` ranges of whole K-steps.  The
-// int8 kernel (mmq.hip) writes the ranges' f32 partial tiles to scratch and a second
-// launch sums them (the fp6 kernel, mmq_f6.hip, sums its own in the same launch:
-// mmq_splitk.h).  mmq_scratch_bytes is the scratch the int8 kernel needs.
+// MMQ work split over bm x 128 (int8) or 128 x 256 (fp6) output tiles: the first `full`
+// tiles are computed whole; each of the remaining `split_tiles` is cut into `splits` ranges
+// of whole K-steps, whose f32 partial tiles go to scratch and are summed in the same launch
+// by the range that finishes last (mmq_splitk.h).  mmq_scratch_bytes is the scratch the
+// int8 kernel needs (the counters, then the partial tiles), mmq_partial_bytes its partial
+// tiles.
 struct MmqPlan {
-    int bm;            // output tile rows: 32 (M <= 32) or 128
+    int bm;            // output tile rows
     int full;
     int split_tiles;
     int splits;
@@ -116,11 +117,14 @@ struct MmqPlan {
 };
 MmqPlan mmq_plan(int type, int64_t M, int64_t N, int64_t K);
 size_t mmq_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
+size_t mmq_partial_bytes(int type, int64_t M, int64_t N, int64_t K);
 // Y: the product (null for the block-dot export); dots: the export (null for the product);
-// scratch: at least mmq_scratch_bytes of device memory when the plan has splits > 1.
+// scratch: at least mmq_scratch_bytes of device memory when the plan has splits > 1;
+// counters: the cut tiles' counters (zero between calls) with scratch holding only the
+// partial tiles, or null when scratch holds both (mmq_splitk.h's layout).
 hipError_t launch_mmq(int type, BlockLayout layout, const uint8_t* W, const int8_t* codes, const float* scales,
-                      const int32_t* sums, float* Y, int32_t* dots, void* scratch, int64_t M, int64_t N, int64_t K,
-                      hipStream_t s, const char** kernel_name);
+                      const int32_t* sums, float* Y, int32_t* dots, void* scratch, unsigned* counters, int64_t M,
+                      int64_t N, int64_t K, hipStream_t s, const char** kernel_name);
 // Q4_K in the MMQ plane (mq_repack's layout): block dots on the fp6 matrix units from the
 // activation plane's fp6 section (mmq_f6.hip).  Any M.
 MmqPlan mmq_f6_plan(int64_t M, int64_t N, int64_t K);

@@ -193,19 +193,22 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
 /*
  * mq_gemm_scratch_bytes -- device scratch that mq_gemm needs for (type, M, N,
  * K); 0 when the chosen work split needs none, and 0 for a shape mq_gemm
- * refuses.  mq_gemm computes Y in BM x 128 tiles (BM = 32 for M <= 32, else
- * 128), sized for 512 resident workgroups: tiles are computed whole while they
- * fill rounds of 512; the tiles of a last round that is at most half full (or
- * all tiles, when there are at most 256) are cut into S ranges of whole
- * 128-value K-steps, and a second launch sums their S f32 partial tiles in
- * range order (deterministic).  The scratch then holds S x (number of cut
- * tiles) x BM x 128 f32.  The fp6 kernel (MQ_Q4_K | MQ_REPACKED) computes
- * 128 x 256 tiles with one workgroup per CU (rounds of 256, 64-value K-steps, at
- * least 4 per range) and sums the cut tiles in the same launch: its scratch is
- * S x (cut tiles) x 128 x 256 f32 followed, at the next 256-byte boundary, by one
- * uint32 counter per cut tile, which must be zero before the first call and which
- * every call leaves at zero.  The split depends on the shape only, never on the
- * device.
+ * refuses.  The int8 kernel (every type on the GGUF payload) computes Y in
+ * BM x 128 tiles, sized for 512 resident workgroups: BM = 128, or 32 when
+ * M <= 32 or when the 128-row tiles would be at most 256.  Tiles are computed
+ * whole while they fill rounds of 512; the tiles of a last round that is at
+ * most half full (or all tiles, when there are at most 256) are cut into S
+ * ranges of whole 128-value K-steps (at least 2 per range; for 32-row tiles
+ * with M > 32, ranges for at most 256 workgroups).  The fp6 kernel
+ * (MQ_Q4_K | MQ_REPACKED) computes 128 x 256 tiles with one workgroup per CU
+ * (rounds of 256, 64-value K-steps, at least 4 per range).  Both sum a cut
+ * tile's S f32 partial tiles in the same launch, in range order
+ * (deterministic): the scratch is 1 KiB of uint32 counters (one per cut tile;
+ * no plan cuts more than 256), which must be zero before the first call and
+ * which every call leaves at zero, followed by S x (cut tiles) x (tile rows x
+ * tile columns) f32.  The counters sit at the start for every shape, so calls
+ * of different shapes may share one buffer.  The split depends on the shape
+ * only, never on the device.
  */
 size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
 
@@ -219,9 +222,10 @@ size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
  * Q4_K, Q5_K, Q4_1 and Q5_1, the min term through the block's code sum).  Y: M x N f32 (device,
  * overwritten).  scratch / scratch_bytes: device memory of at least
  * mq_gemm_scratch_bytes(type, M, N, K) bytes, 16-byte aligned (may be NULL/0
- * when that is 0); its contents are overwritten, and calls that share one
- * scratch buffer must be ordered on one stream.  MQ_ERR_SIZE when it is too
- * small, MQ_ERR_ALIGN when misaligned.
+ * when that is 0), zeroed before its first use (the counters); its partial
+ * tiles are overwritten, and calls that share one scratch buffer must be
+ * ordered on one stream.  MQ_ERR_SIZE when it is too small, MQ_ERR_ALIGN when
+ * misaligned.
  */
 int mq_gemm(const void* W, int type, const void* Xq, float* Y, int64_t M, int64_t N, int64_t K,
             void* scratch, size_t scratch_bytes, void* stream);

@@ -111,12 +111,12 @@ def test_gemm_scratch_is_sized_by_the_split_plan():
     tile = 128 * 128 * 4
 
     def sk(tiles, pieces, tile_bytes=tile):
-        # partial slots, then one uint32 counter per split tile at a 256-byte boundary
-        return ((tiles * pieces * tile_bytes + 255) // 256) * 256 + 4 * tiles
+        # 1 KiB of uint32 counters (at most 256 cut tiles), then the partial slots
+        return 1024 + tiles * pieces * tile_bytes
 
     # Q4_K's MMQ plane runs the fp6 kernel: 128 x 256 tiles, one workgroup per CU (rounds
-    # of 256), 64-value K-steps, at least 4 per range; partial tiles of 128 x 256 f32, then
-    # the counters.
+    # of 256), 64-value K-steps, at least 4 per range; the counters, then partial tiles of
+    # 128 x 256 f32.
     t8 = 128 * 256 * 4
     P = mq.Q4_K | mq.REPACKED
     # 256 tiles fill one round: no split, no scratch
@@ -129,16 +129,24 @@ def test_gemm_scratch_is_sized_by_the_split_plan():
     assert mq.gemm_scratch_bytes(P, 100, 306 * 256 - 13, 3584) == sk(50, 5, t8)
     # any M, small ones included (one tile of 128 x 256, 56 steps: 14 ranges)
     assert mq.gemm_scratch_bytes(P, 1, 256, 3584) == sk(1, 14, t8)
-    # the int8 kernel (every type on the GGUF layout): 128 x 128 tiles, 128-value K-steps,
-    # at least 2 per range -- 28 steps at K = 3584, so 16 tiles take 14 ranges; its partial
-    # tiles are summed by a second launch and it needs no counters
+    # the int8 kernel (every type on the GGUF layout): 128 x 128 tiles in rounds of 512
+    # workgroups (two per CU), 128-value K-steps, at least 2 per range; the counters, then
+    # the partial tiles.  The 7B ffn_up product has 592 tiles: 512 whole, the last 80 cut into 6.
+    t32 = 32 * 128 * 4
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 18944, 3584) == sk(80, 6)
+    # at most 256 tiles of 128 rows: 32-row tiles instead.  512 x 512 has 64 of them, cut
+    # into ranges for 256 workgroups (one per CU): 4 each
     for t in (mq.Q4_K, mq.Q8_0, mq.Q6_K, mq.Q5_K, mq.Q4_0, mq.Q4_1, mq.Q5_0, mq.Q5_1):
-        assert mq.gemm_scratch_bytes(t, 512, 512, 3584) == 14 * 16 * tile
-    # 112 tiles (rounds of 512 workgroups, two per CU): 4 ranges each
-    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 3584, 3584) == 4 * 112 * tile
-    # 8 < M <= 32: 32 x 128 tiles; the vocab head at M = 9 has 1188 of them, the last 164 cut in 3
-    assert mq.gemm_scratch_bytes(mq.Q6_K, 9, 152064, 3584) == 3 * 164 * 32 * 128 * 4
-    assert mq.gemm_scratch_bytes(mq.Q4_K, 9, 152064, 3584) == 3 * 164 * 32 * 128 * 4
+        assert mq.gemm_scratch_bytes(t, 512, 512, 3584) == sk(64, 4, t32)
+    # 448 32-row tiles (a last round more than half full): nothing cut
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 3584, 3584) == 0
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 2048, 1024, 5120) == 0
+    # 257 tiles of 128 rows stay 128-row tiles: 257 in one round, nothing cut
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 40, 128 * 257, 3584) == 0
+    # 8 < M <= 32: 32 x 128 tiles; the vocab head at M = 9 has 1188 of them, the last 164
+    # cut in 3 (ranges for a full round of 512)
+    assert mq.gemm_scratch_bytes(mq.Q6_K, 9, 152064, 3584) == sk(164, 3, t32)
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 9, 152064, 3584) == sk(164, 3, t32)
     # M <= 8: the multi-row GEMV, no scratch -- unless the rows do not fit its LDS
     assert mq.gemm_scratch_bytes(mq.Q6_K, 8, 152064, 3584) == 0
     assert mq.gemm_scratch_bytes(mq.Q6_K, 8, 260, 32768) > 0

@@ -83,8 +83,9 @@ def test_blockdots_bitwise_small_ragged(qtype, kind):
 
 @pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
 def test_split_k_uneven_ranges(qtype):
-    # One output tile and a long K: the kernel splits K into many ranges of whole
-    # K-steps (uneven lengths; for Q8_0 the last step is cut by K), summed in range order.
+    # Two 32-row output tiles and a long K: the kernel splits K into many ranges of whole
+    # K-steps (uneven lengths; for Q8_0 the last step is cut by K), summed in range order
+    # by the range that finishes last.
     M, N, K = 40, 100, (4128 if BLOCK[qtype] == 32 else 8192)
     assert mq.gemm_scratch_bytes(qtype, M, N, K) >= 8 * M * N * 4, "shape must take the split-K path"
     raw = weights(qtype, N, K, "random", 70)
@@ -123,23 +124,28 @@ def test_small_m_long_rows(qtype):
 
 @pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
 def test_small_m_tiles_at_the_switch(qtype):
-    # M <= 32 uses 32-row output tiles, M = 33 the 128-row ones; both with a ragged N.
+    # M <= 32 uses 32-row output tiles, and so does M = 33 with few 128-row tiles (a small
+    # N); with 257 of them M = 33 takes the 128-row tiles.  Ragged N and M throughout.
     K = 2 * BLOCK[qtype] + 256
-    for i, M in enumerate([32, 33]):
-        N = 200
+    rng = np.random.default_rng(9)
+    for i, (M, N) in enumerate([(32, 200), (33, 200), (33, 128 * 257 - 5)]):
         raw = weights(qtype, N, K, "random", 90 + i)
         X = synth.activations(M, K, config_index=12, tensor_index=40 + i)
-        check_blockdots(raw, qtype, X, N, K, f"M={M}")
-        check_gemm(raw, qtype, X, N, K, what=f"M={M}")
+        cols = None if N < 1000 else np.sort(np.concatenate([rng.choice(N - 128, 300, replace=False),
+                                                             np.arange(N - 128, N)]))
+        if cols is None:
+            check_blockdots(raw, qtype, X, N, K, f"M={M}")
+        check_gemm(raw, qtype, X, N, K, cols=cols, what=f"M={M} N={N}")
 
 
 @pytest.mark.parametrize("qtype", TYPES, ids=[NAMES[t] for t in TYPES])
 def test_whole_tiles_plus_split_tail(qtype):
     # 520 output tiles of 128 x 128 on the int8 path: 512 computed whole, the last 8 cut
-    # into 2 K ranges and summed by a second launch.  The cut tiles are the last 1024
-    # columns; columns are sampled from both kinds of tile.  Scratch: the partial tiles.
+    # into 2 K ranges and summed in the launch.  The cut tiles are the last 1024 columns;
+    # columns are sampled from both kinds of tile.  Scratch: 1 KiB of counters, then the
+    # partial tiles.
     M, N, K = 100, 128 * 520, 512
-    want = 2 * 8 * 128 * 128 * 4
+    want = 1024 + 2 * 8 * 128 * 128 * 4
     assert mq.gemm_scratch_bytes(qtype, M, N, K) == want
     raw = weights(qtype, N, K, "quantized", 80)
     X = synth.activations(M, K, config_index=12, tensor_index=31)
@@ -190,15 +196,15 @@ def sampled_blockdots(raw, qtype, X, N, K, rows, cols, what):
 
 
 @pytest.mark.parametrize("M,N,K,blockdots", [
-    (33, 256 * 256 + 77, 1024, True),      # 257 tiles: the last, ragged in N, cut into 4 K ranges
-    (200, 129 * 256, 512, True),           # 258 tiles, the second row tile ragged; 2 cut into 2
-    (100, 306 * 256 - 13, 3584, False),    # 256 whole + 50 cut into 5 uneven ranges of 56 steps
+    (33, 256 * 256 + 77, 1024, True),      # 513 tiles: the last, ragged in N, cut into 4 K ranges
+    (200, 129 * 256, 512, True),           # 516 tiles, the second row tile ragged; 4 cut into 2
+    (100, 306 * 256 - 13, 3584, False),    # 512 whole + 100 cut into 5 uneven ranges of 28 steps
 ], ids=["ragged_n_split4", "ragged_m_split2", "uneven_split5"])
 def test_q4k_large_gguf_ragged_and_split(M, N, K, blockdots):
-    """Q4_K on the GGUF layout at shapes with at least one full round of 128 x 256 tiles:
-    ragged row and column tiles and K-split tiles, against the oracle on sampled columns
-    (always including the first and the last tile) and, where the export fits, bitwise
-    block dots on sampled rows and columns."""
+    """Q4_K on the GGUF layout at shapes with at least one full round of 128 x 128 tiles
+    (512 workgroups): ragged row and column tiles and K-split tiles summed in the launch,
+    against the oracle on sampled columns (always including the first and the last tile)
+    and, where the export fits, bitwise block dots on sampled rows and columns."""
     raw = weights(mq.Q4_K, N, K, "random", 140 + M)
     X = synth.activations(M, K, config_index=12, tensor_index=90 + M)
     rng = np.random.default_rng(M)
@@ -325,3 +331,40 @@ def test_small_m_q6_k_matrix_core_path(N, K, kind):
         assert mq.last_kernel() == "gemv_q8_mfma<q6_K>", mq.last_kernel()
         check_gemm(raw, mq.Q6_K, X, N, K, what=f"M={M} {kind}")
         assert mq.last_kernel() == "gemv_q8_mfma<q6_K>", mq.last_kernel()
+
+
+def test_one_scratch_buffer_serves_shapes_in_a_row():
+    """Products of different shapes that share one zeroed scratch buffer give the bits of
+    products with a fresh buffer each: the cut tiles' counters sit at the start of the
+    buffer for every shape and every call leaves them at zero, so no call's partial tiles
+    land on counters another shape reads.  int8 products with 128- and 32-row cut tiles,
+    fp6 products on Q4_K's MMQ plane, and a shape that cuts nothing, twice over in a
+    different order."""
+    import torch
+    dev = device()
+    mq.init(0)
+    K = 3584
+    plane = mq.Q4_K | mq.REPACKED
+    cases = [(512, 18944, mq.Q4_K), (512, 512, mq.Q4_K), (512, 18944, plane), (200, 700, plane),
+             (512, 3584, mq.Q4_K), (40, 1000, mq.Q4_K)]
+    Ws, Xqs, refs = {}, {}, []
+    for i, (M, N, qt) in enumerate(cases):
+        if N not in Ws:
+            Ws[N] = to_dev(weights(mq.Q4_K, N, K, "random", 300 + N % 97).reshape(-1), dev)
+        if M not in Xqs:
+            Xqs[M] = quantized_plane(synth.activations(M, K, config_index=12, tensor_index=300 + M), dev)
+    planes = {N: mq.repack(W, mq.Q4_K, N, K) for N, W in Ws.items()}
+    need = max(mq.gemm_scratch_bytes(qt, M, N, K) for M, N, qt in cases)
+    assert need > 0
+    shared = torch.zeros(need, dtype=torch.uint8, device=dev)
+    for M, N, qt in cases:
+        W = planes[N] if qt == plane else Ws[N]
+        refs.append(mq.gemm(W, qt, Xqs[M], M, N, K).cpu().numpy())
+    for order in (range(len(cases)), reversed(range(len(cases)))):
+        for i in order:
+            M, N, qt = cases[i]
+            say(f"shared scratch q4_K{' plane' if qt == plane else ''} M={M} N={N} K={K}")
+            W = planes[N] if qt == plane else Ws[N]
+            Y = mq.gemm(W, qt, Xqs[M], M, N, K, scratch=shared).cpu().numpy()
+            assert np.array_equal(Y.view(np.uint32), refs[i].view(np.uint32)), \
+                f"M={M} N={N}: {np.count_nonzero(Y.view(np.uint32) != refs[i].view(np.uint32))} elements differ"

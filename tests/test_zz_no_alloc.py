@@ -1,9 +1,9 @@
 """mq_gemm_noalloc (the product with the library's per-device scratch array) gives
 the same bits as mq_gemm with a caller-allocated, zeroed scratch buffer, over calls
-in a row that reuse the array: K-split int8 products (GGUF payload) and K-split fp6
-products (Q4_K's MMQ plane) whose partial tiles overwrite each other's, fp6 products
-that cut a different number of tiles (their counters must still read zero) and one
-that cuts none."""
+in a row that reuse the array: K-split int8 products (GGUF payload, 128- and 32-row
+tiles) and K-split fp6 products (Q4_K's MMQ plane) whose partial tiles overwrite each
+other's and which cut different numbers of tiles (the shared counters must still read
+zero), and products that cut none."""
 
 import numpy as np
 import pytest
@@ -16,11 +16,12 @@ pytestmark = pytest.mark.gpu
 
 CASES = [
     # (M, N, K, kernel, partial-tile bytes the plan cuts); the plane kernel reads Q4_K's MMQ
-    # plane (mq_repack) and shares the fp8 kernel's counters
+    # plane (mq_repack); both kernels count cut tiles in the same counters
     (512, 18944, 3584, "mmq<q4_K>", 80 * 6 * 128 * 128 * 4),        # ffn_up: 80 tiles cut into 6
     (512, 18944, 3584, "mmq_f6<q4_K plane>", 40 * 6 * 128 * 256 * 4),   # the plane: 40 into 6
     (40, 100, 8192, "mmq_f6<q4_K plane>", 1 * 32 * 128 * 256 * 4),      # one tile into 32
-    (512, 3584, 3584, "mmq<q4_K>", 112 * 4 * 128 * 128 * 4),            # 112 tiles into 4
+    (512, 512, 3584, "mmq<q4_K>", 64 * 4 * 32 * 128 * 4),               # 64 32-row tiles into 4
+    (512, 3584, 3584, "mmq<q4_K>", 0),                                  # 448 32-row tiles, none cut
     (100, 306 * 256 - 13, 1024, "mmq_f6<q4_K plane>", 50 * 4 * 128 * 256 * 4),   # 50 tiles into 4
     (40, 256 * 256, 512, "mmq_f6<q4_K plane>", 0),                      # one whole round, nothing cut
 ]

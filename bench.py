@@ -485,18 +485,23 @@ def main():
     # plain-read ceiling: the same rotated ffn_up copies read by a kernel that only reads,
     # with the workgroup count of the GEMV (one per CU) and with the best of a few counts
     meas = load_measure_lib()
-    up_bytes = mq.weight_bytes(Q4_K, 18944, 3584)
-    read_gbps = {}
-    for grid in (256, 512, 1024, 2048):
-        sink = torch.empty(meas.mq_measure_sink_words(grid, 1024), dtype=torch.int32, device=dev)
 
-        def read_launch(W, grid=grid, sink=sink):
-            rc = meas.mq_measure_read(ctypes.c_void_p(W.data_ptr()), up_bytes, ctypes.c_void_p(sink.data_ptr()),
-                                      grid, 1024, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-            if rc:
-                raise RuntimeError(f"plain-read kernel refused ({rc})")
-        us = timer.per_launch_us([lambda W=W: read_launch(W) for W in copies["ffn_up"]], reps)
-        read_gbps[grid] = up_bytes / us / 1e3
+    def plain_read_gbps(tensors, nbytes, grids=(256, 512, 1024, 2048)):
+        out = {}
+        for grid in grids:
+            sink = torch.empty(meas.mq_measure_sink_words(grid, 1024), dtype=torch.int32, device=dev)
+
+            def read_launch(W, grid=grid, sink=sink):
+                rc = meas.mq_measure_read(ctypes.c_void_p(W.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                          grid, 1024, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                if rc:
+                    raise RuntimeError(f"plain-read kernel refused ({rc})")
+            us = timer.per_launch_us([lambda W=W: read_launch(W) for W in tensors], reps)
+            out[grid] = nbytes / us / 1e3
+        return out
+
+    up_bytes = mq.weight_bytes(Q4_K, 18944, 3584)
+    read_gbps = plain_read_gbps(copies["ffn_up"], up_bytes)
     plain_read = max(read_gbps.values())
 
     # warm cache (labelled, never the value): one weight copy, resident in the last-level cache
@@ -582,7 +587,10 @@ def main():
         xh = torch.from_numpy(synth.activations(1, 3584, 2)[0]).to(dev)
         yh = torch.empty(152064, dtype=torch.float32, device=dev)
         us = timer.per_launch_us([lambda W=W: mq.gemv(W, Q6_K, xh, 152064, 3584, y=yh) for W in hcop], reps)
-        sec["gemv_q6_K_head_152064x3584"] = {"us": round(us, 3), "GBps": round(hb / us / 1e3, 1)}
+        pr = max(plain_read_gbps(hcop, hb, grids=(256, 512, 1024)).values())
+        sec["gemv_q6_K_head_152064x3584"] = {"us": round(us, 3), "GBps": round(hb / us / 1e3, 1),
+                                             "frac": round(hb / us / 1e3 / 8000.0, 4), "plain_read_GBps": round(pr, 1),
+                                             "frac_of_plain_read": round(hb / us / 1e3 / pr, 4)}
         # small-M product on the head: M = 8 rows (a speculative-verify batch), q8 activations
         Xh = torch.from_numpy(synth.activations(8, 3584, 2, tensor_index=5)).to(dev)
         Xhq = mq.quantize_act(Xh)
@@ -614,7 +622,11 @@ def main():
             x8 = torch.from_numpy(synth.activations(1, K, 0)[0]).to(dev)
             y8 = torch.empty(N, dtype=torch.float32, device=dev)
             us = timer.per_launch_us([lambda W=W: mq.gemv(W, Q8_0, x8, N, K, y=y8) for W in wc], reps)
-            sec[f"gemv_q8_0_{tag}_{N}x{K}"] = {"us": round(us, 3), "GBps": round(nb / us / 1e3, 1)}
+            pr = max(plain_read_gbps(wc, nb - nb % 16, grids=(256, 512, 1024)).values())
+            sec[f"gemv_q8_0_{tag}_{N}x{K}"] = {"us": round(us, 3), "GBps": round(nb / us / 1e3, 1),
+                                               "frac": round(nb / us / 1e3 / 8000.0, 4),
+                                               "plain_read_GBps": round(pr, 1),
+                                               "frac_of_plain_read": round(nb / us / 1e3 / pr, 4)}
             del wc
         # the other types of the eligibility list on the 7B ffn_up shape: GEMV at M = 1 (weights
         # rotated past the last-level cache) and the prefill product at M = 512

@@ -29,15 +29,16 @@
 // blocks (lane group g takes block g), accumulated straight into the output tile.  Both
 // planes carry these bf16 operands ready made, so the kernel does no unpacking at all.
 //
-// Tiling.  One 512-thread workgroup (8 waves, 2 x 4) per CU owns a 128 x 256 tile of Y and
-// walks its K range in steps of 64 values (2 blocks); each wave owns 2 x 2 MFMA tiles of
-// 32 x 32.  A step's operands are 16 KB of the activation plane (its 128 rows) and 20 KB of
-// the weight plane (its 256 rows), each a few contiguous pieces in memory that go
-// global -> LDS with buffer_load ... lds into a ring of three step slots, issued two steps
-// ahead; one workgroup barrier per step publishes a slot, placed before the step's last
-// burst of products so that the next step's first operand reads run under its
-// multiply-adds.  Tiles that a last, partial
-// round of workgroups would leave idle are cut into K ranges and summed in the same launch
+// Tiling.  A 256-thread workgroup (4 waves, 2 x 2), two resident per CU, owns a 128 x 128
+// tile of Y and walks its K range in steps of 64 values (2 blocks); each wave owns 2 x 2
+// MFMA tiles of 32 x 32.  A step's operands are 16 KB of the activation plane (its 128
+// rows) and 10 KB of the weight plane (its 128 rows), each a few contiguous pieces in memory
+// that go global -> LDS with buffer_load ... lds into a ring of three step slots (79 KB, so
+// two rings fit a CU), issued two steps ahead; one workgroup barrier per step publishes a
+// slot, placed before the step's last burst of products so that the next step's first
+// operand reads run under its multiply-adds.  The two workgroups of a CU keep separate
+// barriers, so one's waits overlap the other's products.  Tiles that a last, partial round
+// of workgroups would leave idle are cut into K ranges and summed in the same launch
 // (mmq_splitk.h).
 #include <algorithm>
 #include <cstddef>
@@ -57,12 +58,12 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int BM = kF6TileRows;   // output tile rows (activation rows), 128
-constexpr int BN = kF6TileCols;   // output tile columns (weight rows), 256
+constexpr int BN = 128;           // output tile columns (weight rows)
 constexpr int KS = 64;            // K values per step (two blocks)
-constexpr int kWaves = 8;         // 2 (rows) x 4 (columns), each 64 x 64
+constexpr int kWaves = 4;         // 2 (rows) x 2 (columns), each 64 x 64
 constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;
-constexpr int kTargetWorkgroups = 256;   // one resident workgroup on each of 256 CUs
+constexpr int kTargetWorkgroups = 512;   // two resident workgroups on each of 256 CUs
 constexpr int kMinStepsPerSplit = 4;
 constexpr int kScaleH = 127 + 5;   // E8M0 2^5: block scale of the h / 2 digits
 constexpr int kScaleL = 127 + 1;   // E8M0 2^1: block scale of the l / 2 digits
@@ -90,9 +91,9 @@ struct Slot {
     uint8_t bo[2][BN][8];
     uint8_t bm[2][BN][8];
 };
-static_assert(sizeof(Slot) == 36 * 1024, "a step slot is 36 loads of 1 KB");
+static_assert(sizeof(Slot) == 26 * 1024, "a step slot is 26 loads of 1 KB");
 static_assert(offsetof(Slot, b16) == 16 * 1024, "activation part first, 16 KB");
-static_assert(3 * sizeof(Slot) + 1024 <= 160 * 1024, "the ring fits the gfx950 LDS");
+static_assert(3 * sizeof(Slot) + 1024 <= 80 * 1024, "two rings fit the gfx950 LDS");
 
 __shared__ __attribute__((aligned(16))) Slot g_slot0, g_slot1, g_slot2;
 __shared__ __attribute__((aligned(16))) uint8_t g_sink[1024];   // target of the loads that carry nothing
@@ -113,14 +114,14 @@ __device__ __forceinline__ uint32_t act_piece(int i, int R, int m0) {
 // The same for load j (0..19) of the weight part (R = padded weight rows, n0 the tile's
 // first row): b16 4 loads per block, b8 / bo / bm 2 loads per block.
 __device__ __forceinline__ uint32_t weight_piece(int j, int R, int n0) {
-    if (j < 8) return uint32_t((j >> 2) * 16 * R + 16 * n0 + 1024 * (j & 3));
-    const int sec = (j - 8) >> 2, u = ((j - 8) >> 1) & 1, h = j & 1;   // b8, bo, bm
-    return uint32_t((32 + 16 * sec) * R + u * 8 * R + 8 * n0 + 1024 * h);
+    if (j < 4) return uint32_t((j >> 1) * 16 * R + 16 * n0 + 1024 * (j & 1));
+    const int sec = (j - 4) >> 1, u = (j - 4) & 1;   // b8, bo, bm
+    return uint32_t((32 + 16 * sec) * R + u * 8 * R + 8 * n0);
 }
 
 // ------------------------------------------------------------------ kernel
 template <bool DUMP>
-__global__ __launch_bounds__(kThreads, 1) void mmq_f6_q4k_kernel(const uint8_t* __restrict__ Wp,
+__global__ __launch_bounds__(kThreads, 2) void mmq_f6_q4k_kernel(const uint8_t* __restrict__ Wp,
                                                                  const uint8_t* __restrict__ Ap,
                                                                  float* __restrict__ Y, int32_t* __restrict__ dots,
                                                                  float* __restrict__ partial,
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmq_f6_q4k_kernel(const uint8_t* 
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave >> 1, wn = wave & 1;
     const int g = lane >> 5, r32 = lane & 31;
     const int KB = K >> 5;
     const int a_slab = 128 * Mp, w_slab = 80 * Np;   // bytes of one step of each plane
@@ -161,28 +162,30 @@ __global__ __launch_bounds__(kThreads, 1) void mmq_f6_q4k_kernel(const uint8_t* 
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // This wave's loads of a step: loads wave + 8 k (k = 0..4) of the step's 36 (16 of the
-    // activation part, then 20 of the weight part).  Each lane moves 16 bytes at offset
-    // piece + 16 lane of the step's slab.  Waves 4..7 have no fifth load: theirs reads past
-    // the buffer (zeros, no memory traffic) into an LDS sink, so that every wave issues the
-    // same count and the step has no branch.
-    uint32_t voff[5];
+    // This wave's loads of a step: loads wave + 4 k (k = 0..6) of the step's 26 (16 of the
+    // activation part, then 10 of the weight part).  Each lane moves 16 bytes at offset
+    // piece + 16 lane of the step's slab: the piece offset (uniform) goes in soffset, the
+    // lane's column in voffset.  Waves 2 and 3 have no seventh load: theirs reads past the
+    // buffer (voffset 2^31: zeros, no memory traffic) into an LDS sink, so that every wave
+    // issues the same count and the step has no branch.
+    uint32_t spiece[7];
 #pragma unroll
-    for (int k = 0; k < 5; ++k) {
-        const int i = wave + 8 * k;
-        voff[k] = i < 16 ? act_piece(i, Mp, m0) + 16 * lane : i < 36 ? weight_piece(i - 16, Np, n0) + 16 * lane
-                                                                     : 0x80000000u;
+    for (int k = 0; k < 7; ++k) {
+        const int i = wave + 4 * k;
+        spiece[k] = i < 16 ? act_piece(i, Mp, m0) : i < 26 ? weight_piece(i - 16, Np, n0) : 0u;
     }
+    const uint32_t vlane = 16 * lane;
+    const uint32_t vlast = wave + 24 < 26 ? vlane : 0x80000000u;
     const uint32_t sink_lds = uint32_t(uintptr_t((const __attribute__((address_space(3))) void*)&g_sink));
     const int tlast = sbeg + nsteps - 1;
     auto issue = [&](auto r_c, auto k_c, int ts) {
         constexpr int R = decltype(r_c)::value, k = decltype(k_c)::value;
-        const int i = wave + 8 * k;
-        if constexpr (k < 2) {
-            lds_dma16(raw_rsrc(Ap + int64_t(ts) * a_slab, a_slab), slot_lds<R>(1024 * i), voff[k], 0);
+        const int i = wave + 4 * k;
+        if constexpr (k < 4) {
+            lds_dma16(raw_rsrc(Ap + int64_t(ts) * a_slab, a_slab), slot_lds<R>(1024 * i), vlane, spiece[k]);
         } else {
-            const uint32_t dst = k < 4 || i < 36 ? slot_lds<R>(1024 * i) : sink_lds;
-            lds_dma16(raw_rsrc(Wp + int64_t(ts) * w_slab, w_slab), dst, voff[k], 0);
+            const uint32_t dst = k < 6 || i < 26 ? slot_lds<R>(1024 * i) : sink_lds;
+            lds_dma16(raw_rsrc(Wp + int64_t(ts) * w_slab, w_slab), dst, k < 6 ? vlane : vlast, spiece[k]);
         }
     };
     auto issue_all = [&](auto r_c, int ts) {
@@ -191,6 +194,8 @@ __global__ __launch_bounds__(kThreads, 1) void mmq_f6_q4k_kernel(const uint8_t* 
         issue(r_c, std::integral_constant<int, 2>{}, ts);
         issue(r_c, std::integral_constant<int, 3>{}, ts);
         issue(r_c, std::integral_constant<int, 4>{}, ts);
+        issue(r_c, std::integral_constant<int, 5>{}, ts);
+        issue(r_c, std::integral_constant<int, 6>{}, ts);
     };
 
     const int scale_a = g ? kScaleL : kScaleH;
@@ -319,6 +324,8 @@ __global__ __launch_bounds__(kThreads, 1) void mmq_f6_q4k_kernel(const uint8_t* 
                 load_ops(slot_at<R1>(), 0, cur0);
             }
             if (p == 5) issue(RR2{}, std::integral_constant<int, 4>{}, t2);
+            if (p == 6) issue(RR2{}, std::integral_constant<int, 5>{}, t2);
+            if (p == 7) issue(RR2{}, std::integral_constant<int, 6>{}, t2);
             __builtin_amdgcn_sched_barrier(0);
         }
         fmas(7, 0, ts);
@@ -328,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmq_f6_q4k_kernel(const uint8_t* 
     // prologue: steps 0 and 1 in flight, step 0 landed, published and its first operands read
     issue_all(std::integral_constant<int, 0>{}, sbeg);
     issue_all(std::integral_constant<int, 1>{}, min(sbeg + 1, tlast));
-    vmcnt_wait<5>();
+    vmcnt_wait<7>();
     lds_publish_barrier();
     load_min(g_slot0, mins);
     load_ops(g_slot0, 0, cur0);
@@ -405,7 +412,7 @@ template __global__ void mmq_f6_q4k_kernel<true>(const uint8_t* __restrict__, co
 size_t mmq_f6_lds_bytes() { return 3 * sizeof(Slot) + 1024; }
 
 MmqPlan mmq_f6_plan(int64_t M, int64_t N, int64_t K) {
-    // As mmq_f8_plan: tiles are dealt whole while they fill rounds of kTargetWorkgroups; the
+    // As the int8 plan: tiles are dealt whole while they fill rounds of kTargetWorkgroups; the
     // tiles of a last round that is at most half full (or all tiles, when there are fewer
     // than half a round) are cut into K ranges of at least kMinStepsPerSplit steps, enough
     // to fill that round.  A function of the shape alone.

@@ -29,7 +29,7 @@ DeviceInfo g_devices[kMaxDevices];
 // first kNoAllocCounterBytes hold the split-tile counters of both MMQ kernels (at most 256
 // cut tiles), which every launch leaves at zero (cleared once, when mq_init first sets up
 // the device); the partial tiles follow.  Every valid shape's partials fit: both plans cut
-// at most one round of workgroups' worth of tiles (512 of 128 x 128, or 256 of 128 x 256
+// at most one round of workgroups' worth of tiles (512 partial tiles of 128 x 128
 // f32), 32 MiB.
 constexpr size_t kNoAllocCounterBytes = 4096;
 constexpr size_t kNoAllocPartialBytes = size_t(MQ_NOALLOC_PARTIAL_BYTES);

@@ -102,7 +102,7 @@ bool gemv_q8_tiled_applies(int type, BlockLayout layout, const uint8_t* W, const
 hipError_t launch_gemv_q8_tiled(int type, const uint8_t* W, const int8_t* codes, const float* xs, float* Y,
                                 int32_t* dots, int64_t M, int64_t N, int64_t K, int cu_count, hipStream_t s,
                                 const char** kernel_name);
-// MMQ work split over bm x 128 (int8) or 128 x 256 (fp6) output tiles: the first `full`
+// MMQ work split over bm x 128 (int8) or 128 x 128 (fp6) output tiles: the first `full`
 // tiles are computed whole; each of the remaining `split_tiles` is cut into `splits` ranges
 // of whole K-steps, whose f32 partial tiles go to scratch and are summed in the same launch
 // by the range that finishes last (mmq_splitk.h).  mmq_scratch_bytes is the scratch the

@@ -200,8 +200,8 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
  * most half full (or all tiles, when there are at most 256) are cut into S
  * ranges of whole 128-value K-steps (at least 2 per range; for 32-row tiles
  * with M > 32, ranges for at most 256 workgroups).  The fp6 kernel
- * (MQ_Q4_K | MQ_REPACKED) computes 128 x 256 tiles with one workgroup per CU
- * (rounds of 256, 64-value K-steps, at least 4 per range).  Both sum a cut
+ * (MQ_Q4_K | MQ_REPACKED) computes 128 x 128 tiles with two workgroups per CU
+ * (rounds of 512, 64-value K-steps, at least 4 per range).  Both sum a cut
  * tile's S f32 partial tiles in the same launch, in range order
  * (deterministic): the scratch is 1 KiB of uint32 counters (one per cut tile;
  * no plan cuts more than 256), which must be zero before the first call and
@@ -263,7 +263,7 @@ int mq_gemm_noalloc(const void* W, int type, const void* Xq, float* Y, int64_t M
  *                           next to them in MQ_GFX950_LDS_BYTES
  *   MQ_LDS_MMQ_I8_BM128 / _BM32  int8 MMQ workgroup LDS for the type at 128- /
  *                           32-row tiles (two workgroups share a CU)
- *   MQ_LDS_MMQ_F6           fp6 MMQ (Q4_K plane) workgroup LDS (one workgroup per CU)
+ *   MQ_LDS_MMQ_F6           fp6 MMQ (Q4_K plane) workgroup LDS (two workgroups per CU)
  */
 #define MQ_GFX950_LDS_BYTES (160 * 1024)
 #define MQ_LDS_GEMV_FIXED 0

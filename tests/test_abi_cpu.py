@@ -114,21 +114,20 @@ def test_gemm_scratch_is_sized_by_the_split_plan():
         # 1 KiB of uint32 counters (at most 256 cut tiles), then the partial slots
         return 1024 + tiles * pieces * tile_bytes
 
-    # Q4_K's MMQ plane runs the fp6 kernel: 128 x 256 tiles, one workgroup per CU (rounds
-    # of 256), 64-value K-steps, at least 4 per range; the counters, then partial tiles of
-    # 128 x 256 f32.
-    t8 = 128 * 256 * 4
+    # Q4_K's MMQ plane runs the fp6 kernel: 128 x 128 tiles, two workgroups per CU (rounds
+    # of 512), 64-value K-steps, at least 4 per range; the counters, then partial tiles of
+    # 128 x 128 f32.
     P = mq.Q4_K | mq.REPACKED
-    # 256 tiles fill one round: no split, no scratch
+    # 512 tiles fill one round: no split, no scratch
     assert mq.gemm_scratch_bytes(P, 512, 16384, 3584) == 0
-    # 296 tiles: 256 whole, the last 40 cut into 6 K ranges
-    assert mq.gemm_scratch_bytes(P, 512, 18944, 3584) == sk(40, 6, t8)
-    # a last round more than half full is not cut (1200 tiles: 176 in the last round)
+    # 592 tiles: 512 whole, the last 80 cut into 6 K ranges
+    assert mq.gemm_scratch_bytes(P, 512, 18944, 3584) == sk(80, 6)
+    # a last round more than half full is not cut (2400 tiles: 352 in the last round)
     assert mq.gemm_scratch_bytes(P, 512 * 3, 128 * 200, 3584) == 0
-    # 306 tiles: the last 50 cut into 5 ranges (56 steps: uneven)
-    assert mq.gemm_scratch_bytes(P, 100, 306 * 256 - 13, 3584) == sk(50, 5, t8)
-    # any M, small ones included (one tile of 128 x 256, 56 steps: 14 ranges)
-    assert mq.gemm_scratch_bytes(P, 1, 256, 3584) == sk(1, 14, t8)
+    # 612 tiles: the last 100 cut into 5 ranges (56 steps: uneven)
+    assert mq.gemm_scratch_bytes(P, 100, 306 * 256 - 13, 3584) == sk(100, 5)
+    # any M, small ones included (two tiles of 128 x 128, 56 steps: 14 ranges)
+    assert mq.gemm_scratch_bytes(P, 1, 256, 3584) == sk(2, 14)
     # the int8 kernel (every type on the GGUF layout): 128 x 128 tiles in rounds of 512
     # workgroups (two per CU), 128-value K-steps, at least 2 per range; the counters, then
     # the partial tiles.  The 7B ffn_up product has 592 tiles: 512 whole, the last 80 cut into 6.

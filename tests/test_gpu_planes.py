@@ -99,7 +99,7 @@ def check_plane_product(raw, X, N, K, cols=None, what="", dots=False):
 
 @pytest.mark.parametrize("kind", ["quantized", "random"])
 def test_plane_product_small_ragged(kind):
-    # tiles of 128 x 256: ragged M and N everywhere, one tile and several, and K-split plans
+    # tiles of 128 x 128: ragged M and N everywhere, one tile and several, and K-split plans
     for i, (M, N, K) in enumerate([(1, 1, 256), (3, 33, 512), (37, 130, 1024), (130, 300, 2560),
                                    (129, 257, 1024), (200, 1000, 3584)]):
         raw = weights(Q4K, N, K, kind, 140 + i)
@@ -124,7 +124,7 @@ def test_plane_split_k_uneven_ranges():
 
 
 def test_plane_whole_tiles_plus_split_tail():
-    # 260 tiles of 128 x 256: 256 whole, the last 4 cut into K ranges; sampled columns of both
+    # 520 tiles of 128 x 128: 512 whole, the last 8 cut into K ranges; sampled columns of both
     M, N, K = 100, 128 * 520, 512
     assert mq.gemm_scratch_bytes(PLANE, M, N, K) > 0
     raw = weights(Q4K, N, K, "quantized", 152)
@@ -135,7 +135,7 @@ def test_plane_whole_tiles_plus_split_tail():
 
 
 def test_plane_full_7b_ffn_up_sampled():
-    # the 7B prefill ffn_up product (M = 512, 18944 x 3584, 296 tiles: 40 of them K-split),
+    # the 7B prefill ffn_up product (M = 512, 18944 x 3584, 592 tiles: 80 of them K-split),
     # in the launch configuration the benchmark times; columns sampled from every tile
     M, N, K = 512, 18944, 3584
     raw = synth.quantized_weight(Q4K, N, K, 3, 0)

@@ -415,7 +415,9 @@ MmqPlan mmq_f6_plan(int64_t M, int64_t N, int64_t K) {
     // As the int8 plan: tiles are dealt whole while they fill rounds of kTargetWorkgroups; the
     // tiles of a last round that is at most half full (or all tiles, when there are fewer
     // than half a round) are cut into K ranges of at least kMinStepsPerSplit steps, enough
-    // to fill that round.  A function of the shape alone.
+    // for half a round: one workgroup per CU.  (Ranges for a full round, two per CU, were
+    // slower on every shape timed: 7B ffn_up 104.4 against 95.0 us, 14B attn_q/o 147.3
+    // against 136.7 us, with twice the partial tiles to sum.)  A function of the shape alone.
     MmqPlan p;
     p.bm = BM;
     p.steps = int((K + KS - 1) / KS);
@@ -425,7 +427,7 @@ MmqPlan mmq_f6_plan(int64_t M, int64_t N, int64_t K) {
     p.split_tiles = 0;
     p.splits = 1;
     if (rem > 0 && rem * 2 <= kTargetWorkgroups) {
-        const int64_t splits = std::min<int64_t>(kTargetWorkgroups / rem, p.steps / kMinStepsPerSplit);
+        const int64_t splits = std::min<int64_t>(kTargetWorkgroups / 2 / rem, p.steps / kMinStepsPerSplit);
         if (splits >= 2) {
             p.full = int(tiles - rem);
             p.split_tiles = int(rem);

@@ -201,7 +201,8 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
  * ranges of whole 128-value K-steps (at least 2 per range; for 32-row tiles
  * with M > 32, ranges for at most 256 workgroups).  The fp6 kernel
  * (MQ_Q4_K | MQ_REPACKED) computes 128 x 128 tiles with two workgroups per CU
- * (rounds of 512, 64-value K-steps, at least 4 per range).  Both sum a cut
+ * (rounds of 512, 64-value K-steps, at least 4 per range, ranges for at most 256
+ * workgroups).  Both sum a cut
  * tile's S f32 partial tiles in the same launch, in range order
  * (deterministic): the scratch is 1 KiB of uint32 counters (one per cut tile;
  * no plan cuts more than 256), which must be zero before the first call and

@@ -115,17 +115,20 @@ def test_gemm_scratch_is_sized_by_the_split_plan():
         return 1024 + tiles * pieces * tile_bytes
 
     # Q4_K's MMQ plane runs the fp6 kernel: 128 x 128 tiles, two workgroups per CU (rounds
-    # of 512), 64-value K-steps, at least 4 per range; the counters, then partial tiles of
-    # 128 x 128 f32.
+    # of 512), 64-value K-steps, at least 4 per range, ranges for half a round (one workgroup
+    # per CU); the counters, then partial tiles of 128 x 128 f32.
     P = mq.Q4_K | mq.REPACKED
     # 512 tiles fill one round: no split, no scratch
     assert mq.gemm_scratch_bytes(P, 512, 16384, 3584) == 0
-    # 592 tiles: 512 whole, the last 80 cut into 6 K ranges
-    assert mq.gemm_scratch_bytes(P, 512, 18944, 3584) == sk(80, 6)
+    # 592 tiles: 512 whole, the last 80 cut into 3 K ranges
+    assert mq.gemm_scratch_bytes(P, 512, 18944, 3584) == sk(80, 3)
     # a last round more than half full is not cut (2400 tiles: 352 in the last round)
     assert mq.gemm_scratch_bytes(P, 512 * 3, 128 * 200, 3584) == 0
-    # 612 tiles: the last 100 cut into 5 ranges (56 steps: uneven)
-    assert mq.gemm_scratch_bytes(P, 100, 306 * 256 - 13, 3584) == sk(100, 5)
+    # 612 tiles: the last 100 cut into 2 ranges; 70 tiles into 3 (56 steps: uneven); 140
+    # tiles would get one range each for 256 workgroups: none is cut
+    assert mq.gemm_scratch_bytes(P, 100, 306 * 256 - 13, 3584) == sk(100, 2)
+    assert mq.gemm_scratch_bytes(P, 100, 70 * 128, 3584) == sk(70, 3)
+    assert mq.gemm_scratch_bytes(P, 100, 140 * 128, 3584) == 0
     # any M, small ones included (two tiles of 128 x 128, 56 steps: 14 ranges)
     assert mq.gemm_scratch_bytes(P, 1, 256, 3584) == sk(2, 14)
     # the int8 kernel (every type on the GGUF layout): 128 x 128 tiles in rounds of 512

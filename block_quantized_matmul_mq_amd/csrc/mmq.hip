@@ -791,8 +791,11 @@ MmqPlan mmq_plan(int /*type*/, int64_t M, int64_t N, int64_t K) {
     // kTargetWorkgroups workgroups fill the chip.  Tiles are dealt whole while they fill it;
     // the tiles of a last, less than half full round (or all tiles, when there are fewer
     // than half a round of them) are cut into K ranges of at least kMinStepsPerSplit steps,
-    // enough of them to fill that round.  A function of the shape alone, so the result does
-    // not depend on the device.
+    // enough of them for half a round: one workgroup per CU.  (Ranges for a full round, two
+    // per CU, were slower on nearly every shape timed: 7B ffn_up Q4_K 150.5 against 144.4 us,
+    // Q8_0 144.2 against 136.2 us, 512 x 512 x 3584 16.4 against 15.4 us; the vocab head
+    // at M = 9, whose last round then is not cut at all, 119.3 against 111.6 us.)  A function
+    // of the shape alone, so the result does not depend on the device.
     MmqPlan p;
     // 128-row tiles while there are enough of them to fill more than half a round; else
     // (small M, or a small N) 32-row tiles, four times as many, so fewer are cut.
@@ -805,11 +808,7 @@ MmqPlan mmq_plan(int /*type*/, int64_t M, int64_t N, int64_t K) {
     p.split_tiles = 0;
     p.splits = 1;
     if (rem > 0 && rem * 2 <= kTargetWorkgroups) {
-        // 32-row tiles of a small N (M above kSmallM) fill only half a round, one workgroup per
-        // CU: their ranges are short and bound by load latency, and a CU of their own runs
-        // them faster than two workgroups sharing one (512 x 512 x 3584: 15.4 us against 16.4).
-        const int64_t fill = p.bm == 32 && M > kSmallM ? kTargetWorkgroups / 2 : kTargetWorkgroups;
-        const int64_t splits = std::min<int64_t>(fill / rem, p.steps / kMinStepsPerSplit);
+        const int64_t splits = std::min<int64_t>(kTargetWorkgroups / 2 / rem, p.steps / kMinStepsPerSplit);
         if (splits >= 2) {
             p.full = int(tiles - rem);
             p.split_tiles = int(rem);

@@ -198,8 +198,8 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
  * M <= 32 or when the 128-row tiles would be at most 256.  Tiles are computed
  * whole while they fill rounds of 512; the tiles of a last round that is at
  * most half full (or all tiles, when there are at most 256) are cut into S
- * ranges of whole 128-value K-steps (at least 2 per range; for 32-row tiles
- * with M > 32, ranges for at most 256 workgroups).  The fp6 kernel
+ * ranges of whole 128-value K-steps (at least 2 per range, ranges for at most
+ * 256 workgroups).  The fp6 kernel
  * (MQ_Q4_K | MQ_REPACKED) computes 128 x 128 tiles with two workgroups per CU
  * (rounds of 512, 64-value K-steps, at least 4 per range, ranges for at most 256
  * workgroups).  Both sum a cut

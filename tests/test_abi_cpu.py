@@ -132,10 +132,11 @@ def test_gemm_scratch_is_sized_by_the_split_plan():
     # any M, small ones included (two tiles of 128 x 128, 56 steps: 14 ranges)
     assert mq.gemm_scratch_bytes(P, 1, 256, 3584) == sk(2, 14)
     # the int8 kernel (every type on the GGUF layout): 128 x 128 tiles in rounds of 512
-    # workgroups (two per CU), 128-value K-steps, at least 2 per range; the counters, then
-    # the partial tiles.  The 7B ffn_up product has 592 tiles: 512 whole, the last 80 cut into 6.
+    # workgroups (two per CU), 128-value K-steps, at least 2 per range, ranges for half a
+    # round (one workgroup per CU); the counters, then the partial tiles.  The 7B ffn_up
+    # product has 592 tiles: 512 whole, the last 80 cut into 3.
     t32 = 32 * 128 * 4
-    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 18944, 3584) == sk(80, 6)
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 18944, 3584) == sk(80, 3)
     # at most 256 tiles of 128 rows: 32-row tiles instead.  512 x 512 has 64 of them, cut
     # into ranges for 256 workgroups (one per CU): 4 each
     for t in (mq.Q4_K, mq.Q8_0, mq.Q6_K, mq.Q5_K, mq.Q4_0, mq.Q4_1, mq.Q5_0, mq.Q5_1):
@@ -145,10 +146,11 @@ def test_gemm_scratch_is_sized_by_the_split_plan():
     assert mq.gemm_scratch_bytes(mq.Q4_K, 2048, 1024, 5120) == 0
     # 257 tiles of 128 rows stay 128-row tiles: 257 in one round, nothing cut
     assert mq.gemm_scratch_bytes(mq.Q4_K, 40, 128 * 257, 3584) == 0
-    # 8 < M <= 32: 32 x 128 tiles; the vocab head at M = 9 has 1188 of them, the last 164
-    # cut in 3 (ranges for a full round of 512)
-    assert mq.gemm_scratch_bytes(mq.Q6_K, 9, 152064, 3584) == sk(164, 3, t32)
-    assert mq.gemm_scratch_bytes(mq.Q4_K, 9, 152064, 3584) == sk(164, 3, t32)
+    # 8 < M <= 32: 32 x 128 tiles; the vocab head at M = 9 has 1188 of them, and its last
+    # 164 would get one range each: none is cut.  At M = 20 and N = 3000, 24 tiles get 10.
+    assert mq.gemm_scratch_bytes(mq.Q6_K, 9, 152064, 3584) == 0
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 9, 152064, 3584) == 0
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 20, 3000, 3584) == sk(24, 10, t32)
     # M <= 8: the multi-row GEMV, no scratch -- unless the rows do not fit its LDS
     assert mq.gemm_scratch_bytes(mq.Q6_K, 8, 152064, 3584) == 0
     assert mq.gemm_scratch_bytes(mq.Q6_K, 8, 260, 32768) > 0

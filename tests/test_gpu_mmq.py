@@ -198,8 +198,8 @@ def sampled_blockdots(raw, qtype, X, N, K, rows, cols, what):
 @pytest.mark.parametrize("M,N,K,blockdots", [
     (33, 256 * 256 + 77, 1024, True),      # 513 tiles: the last, ragged in N, cut into 4 K ranges
     (200, 129 * 256, 512, True),           # 516 tiles, the second row tile ragged; 4 cut into 2
-    (100, 306 * 256 - 13, 3584, False),    # 512 whole + 100 cut into 5 uneven ranges of 28 steps
-], ids=["ragged_n_split4", "ragged_m_split2", "uneven_split5"])
+    (100, 582 * 128 - 13, 3584, False),    # 512 whole + 70 cut into 3 uneven ranges of 28 steps
+], ids=["ragged_n_split4", "ragged_m_split2", "uneven_split3"])
 def test_q4k_large_gguf_ragged_and_split(M, N, K, blockdots):
     """Q4_K on the GGUF layout at shapes with at least one full round of 128 x 128 tiles
     (512 workgroups): ragged row and column tiles and K-split tiles summed in the launch,

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 CASES = [
     # (M, N, K, kernel, partial-tile bytes the plan cuts); the plane kernel reads Q4_K's MMQ
     # plane (mq_repack); both kernels count cut tiles in the same counters
-    (512, 18944, 3584, "mmq<q4_K>", 80 * 6 * 128 * 128 * 4),        # ffn_up: 80 tiles cut into 6
+    (512, 18944, 3584, "mmq<q4_K>", 80 * 3 * 128 * 128 * 4),        # ffn_up: 80 tiles cut into 3
     (512, 18944, 3584, "mmq_f6<q4_K plane>", 80 * 3 * 128 * 128 * 4),   # the plane: 80 into 3
     (40, 100, 8192, "mmq_f6<q4_K plane>", 1 * 32 * 128 * 128 * 4),      # one tile into 32
     (512, 512, 3584, "mmq<q4_K>", 64 * 4 * 32 * 128 * 4),               # 64 32-row tiles into 4

@@ -21,6 +21,7 @@ namespace {
 
 thread_local std::string g_error;
 thread_local const char* g_last_kernel = "";
+thread_local int g_refuse_launches = 0;   // mq_debug_refuse_launches
 
 constexpr int kMaxDevices = 64;
 DeviceInfo g_devices[kMaxDevices];
@@ -127,6 +128,14 @@ int launch_status(const char* fn, hipError_t e, const char* kernel) {
     return MQ_OK;
 }
 
+// mq_debug_refuse_launches: true when this call is to take the refused-launch path (the
+// caller then reports hipErrorLaunchFailure without launching)
+bool refuse_this_launch() {
+    if (g_refuse_launches <= 0) return false;
+    --g_refuse_launches;
+    return true;
+}
+
 }  // namespace
 
 const DeviceInfo* device_info() {
@@ -146,6 +155,12 @@ const char* mq_version(void) { return "libmq 0.1 (gfx950)"; }
 const char* mq_last_error(void) { return g_error.c_str(); }
 
 const char* mq_last_kernel(void) { return g_last_kernel; }
+
+int mq_debug_refuse_launches(int count) {
+    if (count < 0) return fail(MQ_ERR_ARG, "mq_debug_refuse_launches: count=%d must not be negative", count);
+    g_refuse_launches = count;
+    return MQ_OK;
+}
 
 int mq_device_lds_bytes(void) {
     const DeviceInfo* info = device_info();
@@ -258,6 +273,7 @@ int mq_quantize_act(const float* X, void* Xq, int64_t M, int64_t K, void* stream
     int rc = check_ready(fn);
     if (rc) return rc;
     uint8_t* base = static_cast<uint8_t*>(Xq);
+    if (refuse_this_launch()) return launch_status(fn, hipErrorLaunchFailure, "quantize_act");
     hipError_t e = launch_quantize_act(X, reinterpret_cast<int8_t*>(base),
                                        reinterpret_cast<float*>(base + act_scale_offset(M, K)),
                                        reinterpret_cast<int32_t*>(base + act_sum_offset(M, K)),
@@ -286,6 +302,7 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
         return fail(MQ_ERR_SHAPE, "%s: K=%lld does not fit the %zu-byte LDS of this device", fn, (long long)K,
                     device_info()->lds_per_block);
     const char* kernel = "gemv";
+    if (refuse_this_launch()) return launch_status(fn, hipErrorLaunchFailure, "gemv");
     hipError_t e = launch_gemv(type, lay, static_cast<const uint8_t*>(W), x, y, N, K,
                                static_cast<hipStream_t>(stream), &kernel);
     return launch_status(fn, e, kernel);
@@ -315,10 +332,12 @@ static int gemm_common(const char* fn, const void* W, int type, const void* Xq, 
     const char* kernel = "mmq";
     float* Yout = Y;
     if (is_plane(lay)) {
+        if (refuse_this_launch()) return launch_status(fn, hipErrorLaunchFailure, "mmq_f6<q4_K plane>");
         hipError_t e = launch_mmq_f6(static_cast<const uint8_t*>(W), xq + act_f6_offset(M, K), Y, D, scratch, counters,
                                      M, N, K, static_cast<hipStream_t>(stream), &kernel);
         return launch_status(fn, e, kernel);
     }
+    if (refuse_this_launch()) return launch_status(fn, hipErrorLaunchFailure, "mmq");
     hipError_t e = launch_mmq(type, lay, static_cast<const uint8_t*>(W), reinterpret_cast<const int8_t*>(xq),
                               reinterpret_cast<const float*>(xq + act_scale_offset(M, K)),
                               reinterpret_cast<const int32_t*>(xq + act_sum_offset(M, K)), Yout, D, scratch,
@@ -406,11 +425,13 @@ int mq_repack(const void* W, int type, int64_t N, int64_t K, size_t nbytes, void
     if (rc) return rc;
     const BlockLayout lay = repacked_layout(type);
     if (is_plane(lay)) {
+        if (refuse_this_launch()) return launch_status(fn, hipErrorLaunchFailure, "repack");
         hipError_t e = launch_repack_q4k_plane(static_cast<const uint8_t*>(W), static_cast<uint8_t*>(Wr), N, K,
                                                static_cast<hipStream_t>(stream));
         return launch_status(fn, e, "repack");
     }
     const int64_t blocks = N * (K / block_values(type));
+    if (refuse_this_launch()) return launch_status(fn, hipErrorLaunchFailure, "repack");
     hipError_t e = launch_repack(static_cast<const uint8_t*>(W), static_cast<uint8_t*>(Wr), blocks, block_bytes(type),
                                  lay.stride, lay.off, static_cast<hipStream_t>(stream));
     return launch_status(fn, e, "repack");

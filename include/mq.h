@@ -288,6 +288,16 @@ int mq_debug_gemm_blockdots(const void* W, int type, const void* Xq, int32_t* D,
                             int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * mq_debug_refuse_launches -- test helper for the MQ_ERR_LAUNCH path: the
+ * next `count` launching calls on this thread take the path of a launch the
+ * runtime refused (their kernels are not launched; the call returns
+ * MQ_ERR_LAUNCH with a message naming the call and the kernel, and its
+ * outputs are unspecified).  count = 0 turns it off.  Returns MQ_OK, or
+ * MQ_ERR_ARG for a negative count.
+ */
+int mq_debug_refuse_launches(int count);
+
+/*
  * mq_last_error -- the message of the last failing call on this thread (empty
  * string if none).  Valid until the next failing call on the same thread.
  */

@@ -25,7 +25,8 @@ Printed JSON line (one GPU):
                launch time; traffic = HBM bytes per launch from the committed
                rocprofv3 FETCH_SIZE / WRITE_SIZE summary under profiles/, null
                once any kernel source differs from the ones it was taken on
-  roofline_mmq the ffn_up MMQ against 5.0 POP/s dense int8 / fp8 MFMA, with the
+  roofline_mmq the ffn_up MMQ against 5.0 POP/s (dense int8; the fp6 block dots cost
+               what the int8 ones do), with the
                matrix-unit busy fraction and clock from the committed counters
   warm_cache   the decode GEMVs with one weight copy (weights resident in the
                last-level cache): labelled, never the value

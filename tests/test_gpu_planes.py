@@ -147,7 +147,7 @@ def test_plane_full_7b_ffn_up_sampled():
 
 
 def test_plane_matches_the_gguf_path():
-    # the same product on the GGUF payload (fp8 / int8 kernels) agrees within the tolerance
+    # the same product on the GGUF payload (int8 kernel) agrees within the tolerance
     import torch
     dev = device()
     M, N, K = 300, 4096, 2048

@@ -24,7 +24,7 @@ Sources (page title, section):
   "minfer CUDA Backend Design", 4.7) -- the Q8_0 quantizer: amax over the
   32-block, scale = amax/127, codes rounded half to even.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 
 * R1  Block bit layouts (d/dmin/scales/qs for Q4_K; ql/qh/scales/d for Q6_K;
       d then q[32] for Q8_0) are the public GGUF layouts.  The pages give only

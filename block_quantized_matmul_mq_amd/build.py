@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libmq.so")
 MEASURE_SRC = os.path.join(HERE, "measure", "read_ceiling.hip")
 MEASURE_LIB = os.path.join(HERE, "libmq_measure.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["mq_api.hip", "quantize_act.hip", "gemv.hip", "gemv_mfma.hip", "gemv_q8.hip", "mmq.hip", "mmq_f6.hip", "repack.hip"]
+SOURCES = ["mq_api.hip", "quantize_act.hip", "gemv.hip", "gemv_mfma.hip", "gemv_q8.hip", "mmq.hip", "mmq_kw.hip", "mmq_f6.hip", "repack.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fno-gpu-rdc",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

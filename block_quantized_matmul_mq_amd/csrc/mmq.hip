@@ -819,13 +819,13 @@ MmqPlan mmq_plan(int /*type*/, int64_t M, int64_t N, int64_t K) {
 }
 
 size_t mmq_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
-    if (gemv_q8_applies(type, M, K)) return 0;
+    if (gemv_q8_applies(type, M, K) || mmq_kw_applies(type, BlockLayout{144, 0}, M, N, K)) return 0;
     const MmqPlan p = mmq_plan(type, M, N, K);
     return splitk_scratch_bytes(p.split_tiles, p.splits, int64_t(p.bm) * BN);
 }
 
 size_t mmq_partial_bytes(int type, int64_t M, int64_t N, int64_t K) {
-    if (gemv_q8_applies(type, M, K)) return 0;
+    if (gemv_q8_applies(type, M, K) || mmq_kw_applies(type, BlockLayout{144, 0}, M, N, K)) return 0;
     const MmqPlan p = mmq_plan(type, M, N, K);
     return size_t(p.split_tiles) * size_t(p.splits) * size_t(p.bm) * BN * sizeof(float);
 }
@@ -834,6 +834,7 @@ hipError_t launch_mmq(int type, BlockLayout lay, const uint8_t* W, const int8_t*
                       const int32_t* xsum, float* Y, int32_t* dots, void* scratch, unsigned* counters, int64_t M,
                       int64_t N, int64_t K, hipStream_t s, const char** name) {
     if (gemv_q8_applies(type, M, K)) return launch_gemv_q8(type, lay, W, codes, xs, xsum, Y, dots, M, N, K, s, name);
+    if (mmq_kw_applies(type, lay, M, N, K)) return launch_mmq_kw(W, codes, xs, xsum, Y, dots, M, N, K, s, name);
     float* partial = static_cast<float*>(scratch);
     const bool repacked = lay.off != 0 || (type == kQ6_K && lay.stride != 210);
     switch (type) {

@@ -390,6 +390,7 @@ size_t mq_debug_lds_bytes(int what, int type, int64_t K) {
         case MQ_LDS_MMQ_I8_BM128: return mmq_smem_bytes(type, 128);
         case MQ_LDS_MMQ_I8_BM32: return mmq_smem_bytes(type, 32);
         case MQ_LDS_MMQ_F6: return type == MQ_Q4_K ? mmq_f6_lds_bytes() : 0;
+        case MQ_LDS_MMQ_KW: return type == MQ_Q4_K ? mmq_kw_lds_bytes() : 0;
         default: return 0;
     }
 }

@@ -125,6 +125,13 @@ size_t mmq_partial_bytes(int type, int64_t M, int64_t N, int64_t K);
 hipError_t launch_mmq(int type, BlockLayout layout, const uint8_t* W, const int8_t* codes, const float* scales,
                       const int32_t* sums, float* Y, int32_t* dots, void* scratch, unsigned* counters, int64_t M,
                       int64_t N, int64_t K, hipStream_t s, const char** kernel_name);
+// Q4_K (GGUF layout) with few output tiles: one 32 x 32 tile per workgroup, its K range
+// split over the workgroup's waves (mmq_kw.hip); taken by launch_mmq whenever
+// mmq_kw_applies.  It needs no scratch.
+bool mmq_kw_applies(int type, BlockLayout layout, int64_t M, int64_t N, int64_t K);
+size_t mmq_kw_lds_bytes();
+hipError_t launch_mmq_kw(const uint8_t* W, const int8_t* codes, const float* scales, const int32_t* sums, float* Y,
+                         int32_t* dots, int64_t M, int64_t N, int64_t K, hipStream_t s, const char** kernel_name);
 // Q4_K in the MMQ plane (mq_repack's layout): block dots on the fp6 matrix units from the
 // activation plane's fp6 section (mmq_f6.hip).  Any M.
 MmqPlan mmq_f6_plan(int64_t M, int64_t N, int64_t K);

@@ -209,7 +209,12 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
  * which every call leaves at zero, followed by S x (cut tiles) x (tile rows x
  * tile columns) f32.  The counters sit at the start for every shape, so calls
  * of different shapes may share one buffer.  The split depends on the shape
- * only, never on the device.
+ * only, never on the device.  Q4_K on the GGUF payload, when the int8 kernel
+ * would take at most 256 tiles of 32 x 128 and its ranges would not be more
+ * than 5 K-steps shorter than a quarter of K's steps (e.g. the 7B attn_k and
+ * attn_v products at M = 512), runs instead one 32 x 32 tile per workgroup
+ * with the K range split over its four waves and summed in LDS (in wave
+ * order, deterministic): no scratch (0 here).
  */
 size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K);
 
@@ -265,6 +270,8 @@ int mq_gemm_noalloc(const void* W, int type, const void* Xq, float* Y, int64_t M
  *   MQ_LDS_MMQ_I8_BM128 / _BM32  int8 MMQ workgroup LDS for the type at 128- /
  *                           32-row tiles (two workgroups share a CU)
  *   MQ_LDS_MMQ_F6           fp6 MMQ (Q4_K plane) workgroup LDS (two workgroups per CU)
+ *   MQ_LDS_MMQ_KW           Q4_K MMQ with the K range over a workgroup's waves: the
+ *                           LDS where the waves' partial tiles meet
  */
 #define MQ_GFX950_LDS_BYTES (160 * 1024)
 #define MQ_LDS_GEMV_FIXED 0
@@ -272,6 +279,7 @@ int mq_gemm_noalloc(const void* W, int type, const void* Xq, float* Y, int64_t M
 #define MQ_LDS_MMQ_I8_BM128 2
 #define MQ_LDS_MMQ_I8_BM32 3
 #define MQ_LDS_MMQ_F6 5
+#define MQ_LDS_MMQ_KW 6
 size_t mq_debug_lds_bytes(int what, int type, int64_t K);
 
 /*

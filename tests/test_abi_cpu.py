@@ -139,18 +139,28 @@ def test_gemm_scratch_is_sized_by_the_split_plan():
     assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 18944, 3584) == sk(80, 3)
     # at most 256 tiles of 128 rows: 32-row tiles instead.  512 x 512 has 64 of them, cut
     # into ranges for 256 workgroups (one per CU): 4 each
-    for t in (mq.Q4_K, mq.Q8_0, mq.Q6_K, mq.Q5_K, mq.Q4_0, mq.Q4_1, mq.Q5_0, mq.Q5_1):
+    for t in (mq.Q8_0, mq.Q6_K, mq.Q5_K, mq.Q4_0, mq.Q4_1, mq.Q5_0, mq.Q5_1):
         assert mq.gemm_scratch_bytes(t, 512, 512, 3584) == sk(64, 4, t32)
+    # Q4_K there runs the kernel with one 32 x 32 tile per workgroup and the K range split
+    # over its waves: no scratch.  It is taken while its waves run at most 5 K-steps more
+    # than the int8 kernel's ranges: at 20 x 3000 x 3584 (7 against 3) and at
+    # 40 x 100 x 8192 (16 against 2) it is not.
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 512, 3584) == 0
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 1024, 1024, 3584) == 0
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 20, 3000, 32768) == sk(24, 10, t32)
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 40, 100, 8192) == sk(2, 32, t32)
     # 448 32-row tiles (a last round more than half full): nothing cut
     assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 3584, 3584) == 0
     assert mq.gemm_scratch_bytes(mq.Q4_K, 2048, 1024, 5120) == 0
     # 257 tiles of 128 rows stay 128-row tiles: 257 in one round, nothing cut
     assert mq.gemm_scratch_bytes(mq.Q4_K, 40, 128 * 257, 3584) == 0
     # 8 < M <= 32: 32 x 128 tiles; the vocab head at M = 9 has 1188 of them, and its last
-    # 164 would get one range each: none is cut.  At M = 20 and N = 3000, 24 tiles get 10.
+    # 164 would get one range each: none is cut.  At M = 20 and N = 3000, 24 tiles get 10
+    # (Q8_0; Q4_K runs the split-over-waves kernel there).
     assert mq.gemm_scratch_bytes(mq.Q6_K, 9, 152064, 3584) == 0
     assert mq.gemm_scratch_bytes(mq.Q4_K, 9, 152064, 3584) == 0
-    assert mq.gemm_scratch_bytes(mq.Q4_K, 20, 3000, 3584) == sk(24, 10, t32)
+    assert mq.gemm_scratch_bytes(mq.Q8_0, 20, 3000, 3584) == sk(24, 10, t32)
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 20, 3000, 3584) == 0
     # M <= 8: the multi-row GEMV, no scratch -- unless the rows do not fit its LDS
     assert mq.gemm_scratch_bytes(mq.Q6_K, 8, 152064, 3584) == 0
     assert mq.gemm_scratch_bytes(mq.Q6_K, 8, 260, 32768) > 0
@@ -158,11 +168,13 @@ def test_gemm_scratch_is_sized_by_the_split_plan():
     assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 512, 100) == 0
     assert mq.gemm_scratch_bytes(99, 512, 512, 3584) == 0
     lib = mq.load()
-    need = mq.gemm_scratch_bytes(mq.Q4_K, 512, 512, 3584)
-    assert lib.mq_gemm(FAKE, mq.Q4_K, FAKE, FAKE, 512, 512, 3584, None, 0, None) == -4
+    need = mq.gemm_scratch_bytes(mq.Q8_0, 512, 512, 3584)
+    assert lib.mq_gemm(FAKE, mq.Q8_0, FAKE, FAKE, 512, 512, 3584, None, 0, None) == -4
     assert "required" in mq.last_error()
-    assert lib.mq_gemm(FAKE, mq.Q4_K, FAKE, FAKE, 512, 512, 3584, FAKE, need - 4, None) == -4
-    assert lib.mq_gemm(FAKE, mq.Q4_K, FAKE, FAKE, 512, 512, 3584, FAKE + 4, need, None) == -5
+    assert lib.mq_gemm(FAKE, mq.Q8_0, FAKE, FAKE, 512, 512, 3584, FAKE, need - 4, None) == -4
+    assert lib.mq_gemm(FAKE, mq.Q8_0, FAKE, FAKE, 512, 512, 3584, FAKE + 4, need, None) == -5
+    # a product that needs no scratch takes none
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 512, 512, 3584) == 0
 
 
 def test_repacked_sizes_and_type_flag():

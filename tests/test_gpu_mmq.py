@@ -343,28 +343,30 @@ def test_one_scratch_buffer_serves_shapes_in_a_row():
     import torch
     dev = device()
     mq.init(0)
-    K = 3584
     plane = mq.Q4_K | mq.REPACKED
-    cases = [(512, 18944, mq.Q4_K), (512, 512, mq.Q4_K), (512, 18944, plane), (200, 700, plane),
-             (512, 3584, mq.Q4_K), (40, 1000, mq.Q4_K)]
+    # (M, N, K, type): 80 cut 128-row tiles; 2 cut 32-row tiles; the plane's 80 and 16 cut
+    # tiles; 448 32-row tiles, none cut; the K-split-over-waves kernel, no scratch at all
+    cases = [(512, 18944, 3584, mq.Q4_K), (40, 100, 8192, mq.Q4_K), (512, 18944, 3584, plane),
+             (200, 700, 3584, plane), (512, 3584, 3584, mq.Q4_K), (512, 512, 3584, mq.Q4_K)]
     Ws, Xqs, refs = {}, {}, []
-    for i, (M, N, qt) in enumerate(cases):
-        if N not in Ws:
-            Ws[N] = to_dev(weights(mq.Q4_K, N, K, "random", 300 + N % 97).reshape(-1), dev)
-        if M not in Xqs:
-            Xqs[M] = quantized_plane(synth.activations(M, K, config_index=12, tensor_index=300 + M), dev)
-    planes = {N: mq.repack(W, mq.Q4_K, N, K) for N, W in Ws.items()}
-    need = max(mq.gemm_scratch_bytes(qt, M, N, K) for M, N, qt in cases)
+    for i, (M, N, K, qt) in enumerate(cases):
+        if (N, K) not in Ws:
+            Ws[N, K] = to_dev(weights(mq.Q4_K, N, K, "random", 300 + N % 97).reshape(-1), dev)
+        if (M, K) not in Xqs:
+            Xqs[M, K] = quantized_plane(synth.activations(M, K, config_index=12, tensor_index=300 + M), dev)
+    planes = {NK: mq.repack(W, mq.Q4_K, *NK) for NK, W in Ws.items()}
+    need = max(mq.gemm_scratch_bytes(qt, M, N, K) for M, N, K, qt in cases)
     assert need > 0
+    assert mq.gemm_scratch_bytes(mq.Q4_K, 40, 100, 8192) > 1024
     shared = torch.zeros(need, dtype=torch.uint8, device=dev)
-    for M, N, qt in cases:
-        W = planes[N] if qt == plane else Ws[N]
-        refs.append(mq.gemm(W, qt, Xqs[M], M, N, K).cpu().numpy())
+    for M, N, K, qt in cases:
+        W = planes[N, K] if qt == plane else Ws[N, K]
+        refs.append(mq.gemm(W, qt, Xqs[M, K], M, N, K).cpu().numpy())
     for order in (range(len(cases)), reversed(range(len(cases)))):
         for i in order:
-            M, N, qt = cases[i]
+            M, N, K, qt = cases[i]
             say(f"shared scratch q4_K{' plane' if qt == plane else ''} M={M} N={N} K={K}")
-            W = planes[N] if qt == plane else Ws[N]
-            Y = mq.gemm(W, qt, Xqs[M], M, N, K, scratch=shared).cpu().numpy()
+            W = planes[N, K] if qt == plane else Ws[N, K]
+            Y = mq.gemm(W, qt, Xqs[M, K], M, N, K, scratch=shared).cpu().numpy()
             assert np.array_equal(Y.view(np.uint32), refs[i].view(np.uint32)), \
                 f"M={M} N={N}: {np.count_nonzero(Y.view(np.uint32) != refs[i].view(np.uint32))} elements differ"

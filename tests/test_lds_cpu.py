@@ -11,7 +11,7 @@ import pytest
 from block_quantized_matmul_mq_amd import mq
 
 LIMIT = 160 * 1024
-FIXED, TILE_UNITS, I8_BM128, I8_BM32, F6 = 0, 1, 2, 3, 5
+FIXED, TILE_UNITS, I8_BM128, I8_BM32, F6, KW = 0, 1, 2, 3, 5, 6
 TYPES = [mq.Q4_0, mq.Q4_1, mq.Q5_0, mq.Q5_1, mq.Q8_0, mq.Q4_K, mq.Q5_K, mq.Q6_K]
 KQUANT = {mq.Q4_K, mq.Q5_K, mq.Q6_K}
 MIN_TERM = {mq.Q4_1, mq.Q5_1, mq.Q4_K, mq.Q5_K}   # a per-block min is subtracted
@@ -78,3 +78,11 @@ def test_fp6_mmq_lds():
     assert lds(F6, mq.Q4_K) == 3 * slot + 1024
     assert 2 * lds(F6, mq.Q4_K) <= LIMIT, "two workgroups per CU (512 resident) is what the work split assumes"
     assert lds(F6, mq.Q8_0) == 0
+
+
+def test_k_over_waves_mmq_lds():
+    # the four waves' f32 partial tiles of 32 x 32 (16 accumulator elements x 64 lanes
+    # each) meet in LDS for the final sum; nothing else is staged there
+    assert lds(KW, mq.Q4_K) == 4 * 16 * 64 * 4
+    assert 2 * lds(KW, mq.Q4_K) <= LIMIT, "two workgroups per CU"
+    assert lds(KW, mq.Q8_0) == 0

@@ -20,7 +20,8 @@ CASES = [
     (512, 18944, 3584, "mmq<q4_K>", 80 * 3 * 128 * 128 * 4),        # ffn_up: 80 tiles cut into 3
     (512, 18944, 3584, "mmq_f6<q4_K plane>", 80 * 3 * 128 * 128 * 4),   # the plane: 80 into 3
     (40, 100, 8192, "mmq_f6<q4_K plane>", 1 * 32 * 128 * 128 * 4),      # one tile into 32
-    (512, 512, 3584, "mmq<q4_K>", 64 * 4 * 32 * 128 * 4),               # 64 32-row tiles into 4
+    (40, 100, 8192, "mmq<q4_K>", 2 * 32 * 32 * 128 * 4),                # 2 32-row tiles into 32
+    (512, 512, 3584, "mmq_kw<q4_K>", 0),                                # K split over waves: no scratch
     (512, 3584, 3584, "mmq<q4_K>", 0),                                  # 448 32-row tiles, none cut
     (100, 306 * 256 - 13, 1024, "mmq_f6<q4_K plane>", 100 * 2 * 128 * 128 * 4),  # 100 tiles into 2
     (40, 256 * 256, 512, "mmq_f6<q4_K plane>", 0),                      # one whole round, nothing cut

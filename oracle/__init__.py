@@ -13,7 +13,9 @@ What is here:
                        product.
   ``repack`` / ``unpack_repacked`` define the repacked weight layout;
                        ``q4_k_plane`` / ``act_f6_section`` the fp6 planes of the
-                       Q4_K prefill product (weights and activations).
+                       Q4_K prefill product (weights and activations);
+                       ``q4_k_row_tiled`` Q4_K's row-tiled layout for the
+                       long-row GEMV.
 * ``bitwise_decode`` -- a second, independently written per-block decoder that
                        assembles every field bit by bit; it exists only to
                        cross-check ``mq_oracle``'s vectorised decoders.
@@ -35,5 +37,5 @@ from .mq_oracle import (  # noqa: F401
     gemv, quantize_act, block_dots, mmq, mmq_from_block_dots,
     REPACK_SLOT, repack, unpack_repacked,
     PLANE_ROWS, ACT_PLANE_ROWS, e2m3_value, e2m3_code_of_half, fp6_records, bf16_hilo, q4_k_plane,
-    act_f6_section,
+    act_f6_section, row_tile_rows, q4_k_row_tiled, unpack_q4_k_row_tiled,
 )

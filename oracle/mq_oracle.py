@@ -72,6 +72,14 @@ Readings where the pages are silent:
       ``repack`` (Q4_K) and ``act_f6_section`` below; the products on the plane
       are checked against ``mmq`` (the plane holds the scales to 16 bits, well
       inside the 2e-4 tolerance).
+* R18 Q4_K's row-tiled layout (a second derived layout, for the decode GEMV of
+      long rows; the pages admit derived layouts behind an exact-length gate,
+      "minfer CUDA Backend Design", 2.3): rows are taken in groups of
+      R = min(16, ceil(N / 256)) consecutive rows, the last group filled with
+      zero rows; a group stores its rows' super-block 0 blocks one after
+      another (row order), then their super-block 1 blocks, and so on; groups
+      follow in order.  Whole 144-byte blocks move, unchanged.  Only for rows
+      of more than 16 super-blocks.
 * R12 The repacked layout (the one-time device-layout transform): the pages
       repack a Q6_K block into a 16-byte-aligned 224-byte slot ("minfer CUDA
       Backend Design", 2.3); the block sits at the start of its slot and the
@@ -166,6 +174,52 @@ def unpack_repacked(rep, qtype, N, K):
     if np.any(pad):
         raise ValueError("nonzero padding byte in a repacked slot")
     return np.ascontiguousarray(r[:, :, off:off + BLOCK_BYTES[qtype]]).reshape(-1)
+
+
+# ---------------------------------------------------------------- R18: row tiles
+
+def row_tile_rows(N):
+    """R18: rows per group of Q4_K's row-tiled layout."""
+    return min(16, -(-N // 256))
+
+
+def q4_k_row_tiled(raw, N, K):
+    """R18: Q4_K's row-tiled layout (uint8) of a GGUF payload.
+
+    Pinned by a block-by-block construction on small matrices, by the inverse
+    ``unpack_q4_k_row_tiled`` (a loop over the groups) and by the group sizes
+    the layout states (tests/test_oracle_row_tiled.py).
+    """
+    SB = K // 256
+    if K % 256 or SB <= 16:
+        raise ValueError(f"the row-tiled layout is for rows of more than 16 super-blocks (K={K})")
+    R = row_tile_rows(N)
+    G = -(-N // R)
+    b = np.zeros((G * R, SB, 144), dtype=np.uint8)
+    b[:N] = _blocks(raw, Q4_K, N, K)
+    # [group, row in group, super-block, byte] -> [group, super-block, row in group, byte]
+    return np.ascontiguousarray(b.reshape(G, R, SB, 144).transpose(0, 2, 1, 3)).reshape(-1)
+
+
+def unpack_q4_k_row_tiled(rep, N, K):
+    """Inverse of q4_k_row_tiled: the GGUF payload back (raises on a wrong size or a
+    nonzero byte in the filler rows)."""
+    SB = K // 256
+    R = row_tile_rows(N)
+    G = -(-N // R)
+    rep = np.ascontiguousarray(rep, dtype=np.uint8).reshape(-1)
+    if rep.size != G * R * SB * 144:
+        raise ValueError(f"row-tiled payload is {rep.size} bytes, expected exactly {G * R * SB * 144}")
+    out = np.zeros((N, SB, 144), dtype=np.uint8)
+    for g in range(G):
+        grp = rep[g * R * SB * 144:(g + 1) * R * SB * 144].reshape(SB, R, 144)
+        for r in range(R):
+            n = g * R + r
+            if n < N:
+                out[n] = grp[:, r, :]
+            elif np.any(grp[:, r, :]):
+                raise ValueError("nonzero byte in a filler row of the row-tiled layout")
+    return out.reshape(-1)
 
 
 # ---------------------------------------------------------------- R17: the fp6 planes

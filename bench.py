@@ -55,6 +55,7 @@ COPY_REF_BYTES = 256 * 2 ** 20
 
 Q8_0, Q4_K, Q6_K = 8, 12, 14
 REPACKED = 0x100   # type flag of the layout mq_repack writes (Q4_K: the MMQ plane)
+ROW_TILED = 0x200  # type flag of Q4_K's row-tiled layout (the long-row GEMV)
 DECODE = [("ffn_up", 18944, 3584), ("ffn_down", 3584, 18944)]
 PREFILL_M = 512
 PREFILL = [("ffn_up", 18944, 3584), ("attn_q", 3584, 3584), ("attn_k", 512, 3584), ("attn_v", 512, 3584)]
@@ -385,11 +386,42 @@ def main():
 
     kernel_names = {}
 
-    def gemv_launch(name, N, K, c):
+    # Decode weights with rows of more than 16 super-blocks (ffn_down) are also held in Q4_K's
+    # row-tiled layout (mq_repack, a one-time transform at load time, of every rotated copy);
+    # each keeps the layout whose GEMV is faster, chosen once at load time from a few timed
+    # graph replays, as for the prefill weights below.
+    tiled = {name: [mq.repack(W, Q4_K | ROW_TILED, N, K) for W in copies[name]]
+             for name, N, K in DECODE if mq.repack_bytes(Q4_K | ROW_TILED, N, K)}
+    torch.cuda.synchronize()
+
+    def gemv_on(name, N, K, c, lay):
+        W, qt = (tiled[name][c], Q4_K | ROW_TILED) if lay == "row_tiled" else (copies[name][c], Q4_K)
+
         def fn():
-            mq.gemv(copies[name][c], Q4_K, x_dev[name], N, K, y=y_dev[name])
+            mq.gemv(W, qt, x_dev[name], N, K, y=y_dev[name])
             kernel_names[f"gemv_{name}"] = mq.last_kernel()
         return fn
+
+    # (every copy is read once first -- the first replays after writing the new copies run
+    # slow -- and the layouts are timed in two alternating rounds, the best of each kept)
+    gemv_layout, gemv_each = {}, {}
+    for name, N, K in DECODE:
+        lays = ("gguf", "row_tiled") if name in tiled else ("gguf",)
+        for lay in lays:
+            for c in range(ncopy):
+                gemv_on(name, N, K, c, lay)()
+        torch.cuda.synchronize()
+        best = {}
+        for _ in range(2):
+            for lay in lays:
+                us = timer.per_launch_us([gemv_on(name, N, K, c, lay) for c in range(ncopy)], 5)
+                best[lay] = min(us, best.get(lay, us))
+                gemv_each[f"{name}_{lay}"] = {"us": round(best[lay], 3), "kernel": mq.last_kernel(),
+                                              "GBps": round(mq.weight_bytes(Q4_K, N, K) / best[lay] / 1e3, 1)}
+        gemv_layout[name] = min(lays, key=best.get)
+
+    def gemv_launch(name, N, K, c):
+        return gemv_on(name, N, K, c, gemv_layout[name])
 
     def quant_launch():
         mq.quantize_act(X_dev, Xq)
@@ -553,6 +585,10 @@ def main():
         "mmq_dtype": ("exact block dots: on Q4_K's MMQ plane fp6 (e2m3) x fp6 MFMA, weight codes c/2 and activation "
                       "codes as two digits h/2, l/2 with block scales 2^5, 2^1 (f32 results); on the GGUF payload "
                       "int8 MFMA (i32 results); f32 scales through bf16 hi/lo matrix products"),
+        "gemv_layouts": {"chosen": gemv_layout, "note": "per decode weight, the faster of the GGUF payload and "
+                         "Q4_K's row-tiled layout (a permutation of its blocks: the same bytes, the same results bit "
+                         "for bit; rows of more than 16 super-blocks only), chosen once at load time",
+                         "each": gemv_each},
         "mmq_layouts": {"chosen": layout, "note": "per weight, the faster of the GGUF payload and the MMQ plane "
                         "at M=512, chosen once at load time", "each": mmq_both},
         "roofline": {"bound": "hbm", "achieved": round(gemv_alg_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

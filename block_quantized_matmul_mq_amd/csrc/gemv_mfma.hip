@@ -316,11 +316,15 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_kernel(const uint8_t* 
 constexpr int kLongRing = 2;
 constexpr uint32_t kPastEnd = 0x7FFF0000u;   // a buffer offset past the end of any matrix this kernel takes
 
-template <int NB>
+//
+// On Q4_K's row-tiled layout (TILED) the tile is a group of that layout, TR its rows, and an
+// item is one contiguous run of TR x 144 bytes; the kernel is otherwise the same, and so are
+// its results, bit for bit.
+template <int NB, bool TILED>
 __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_long_kernel(const uint8_t* __restrict__ W,
                                                                        const float* __restrict__ x,
                                                                        float* __restrict__ y, int N, int K,
-                                                                       int row_bytes, int TR) {
+                                                                       int row_bytes, int TR, int nbytes) {
     __shared__ __attribute__((aligned(16))) uint8_t ring0[kWaves * kItemBytes];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[kWaves * kItemBytes];
     __shared__ __attribute__((aligned(16))) uint8_t ring2[NB > 2 ? kWaves * kItemBytes : 16];
@@ -344,9 +348,11 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_long_kernel(const uint
     const int rows = min(TR, N - r0);
     const int items = (SB - wave + kWaves - 1) / kWaves;   // super-blocks wave, wave + 16, ... (>= 1: SB > 16)
 
-    const __amdgpu_buffer_rsrc_t rw =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W), 0, N * row_bytes, kBufferWord3);
-    auto chunk_offset = [&](int c) { return uint32_t((c / 9) * row_bytes + 16 * (c % 9)); };
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W), 0, nbytes, kBufferWord3);
+    // byte offset of 16-byte chunk c (row c / 9, chunk c % 9 of its block) within an item
+    auto chunk_offset = [&](int c) {
+        return TILED ? uint32_t(16 * c) : uint32_t((c / 9) * row_bytes + 16 * (c % 9));
+    };
     const int c0 = lane, c1 = 64 + lane, c2 = 128 + (lane >> 2);
     const bool live0 = c0 / 9 < rows, live1 = c1 / 9 < rows, live2 = c2 / 9 < rows;
     const uint32_t vo0 = chunk_offset(c0), vo1 = chunk_offset(c1), vo2 = chunk_offset(c2) + 4 * (lane & 3);
@@ -361,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_long_kernel(const uint
         const bool in = i < items;
         const int sb = wave + kWaves * (in ? i : items - 1);
         xr[B] = reinterpret_cast<const float4*>(x + 256 * sb)[lane];
-        const uint32_t base = tile0 + uint32_t(sb) * 144u;
+        const uint32_t base = tile0 + uint32_t(sb) * (TILED ? uint32_t(TR * 144) : 144u);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)dst, 16, in && live0 ? base + vo0 : kPastEnd, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(dst + 1024), 16, in && live1 ? base + vo1 : kPastEnd, 0,
                                                  0, 0);
@@ -1355,6 +1361,20 @@ hipError_t launch_gemv_wide(int type, const uint8_t* W, const float* x, float* y
     return hipLaunchKernel(f, dim3(grid), dim3(kThreads), args, 0, s);
 }
 
+hipError_t launch_gemv_row_tiled(const uint8_t* W, const float* x, float* y, int64_t N, int64_t K, hipStream_t s,
+                                 const char** name) {
+    // (the callers check row_tiled_k(K) and K <= MQ_MAX_K: a row-tiled matrix of N <= 2^24
+    // rows then ends below kPastEnd only while N * row bytes does, which is checked here)
+    const size_t nbytes = row_tiled_bytes(N, K);
+    if (!row_tiled_k(K) || nbytes > size_t(kPastEnd)) return hipErrorInvalidValue;
+    *name = "gemv_mfma_long<q4_K row-tiled>";
+    const int tr = row_tile_rows(N);
+    int n = int(N), k = int(K), row_bytes = int((K / 256) * 144), t = tr, nb = int(nbytes);
+    void* args[] = {&W, &x, &y, &n, &k, &row_bytes, &t, &nb};
+    return hipLaunchKernel(reinterpret_cast<const void*>(gemv_mfma_q4k_long_kernel<kLongRing, true>),
+                           dim3(unsigned((N + tr - 1) / tr)), dim3(kThreads), args, 0, s);
+}
+
 bool gemv_mfma_applies(int type, int64_t N, int64_t K, int cu_count) {
     // Wide matrices: at least two 16-row tiles per CU; or long rows at 8..16 rows per CU.
     if (type != kQ4_K) return false;
@@ -1366,9 +1386,9 @@ hipError_t launch_gemv_mfma(const uint8_t* W, const float* x, float* y, int64_t 
                             hipStream_t s, const char** name) {
     if (const int tr = long_tile_rows(N, K, cu_count)) {
         *name = "gemv_mfma_long<q4_K>";
-        int n = int(N), k = int(K), row_bytes = int((K / 256) * 144), t = tr;
-        void* args[] = {&W, &x, &y, &n, &k, &row_bytes, &t};
-        return hipLaunchKernel(reinterpret_cast<const void*>(gemv_mfma_q4k_long_kernel<kLongRing>),
+        int n = int(N), k = int(K), row_bytes = int((K / 256) * 144), t = tr, nbytes = int(N * row_bytes);
+        void* args[] = {&W, &x, &y, &n, &k, &row_bytes, &t, &nbytes};
+        return hipLaunchKernel(reinterpret_cast<const void*>(gemv_mfma_q4k_long_kernel<kLongRing, false>),
                                dim3(unsigned((N + tr - 1) / tr)), dim3(kThreads), args, 0, s);
     }
     const Plan p = plan(N, K, cu_count);

@@ -84,9 +84,14 @@ BlockLayout repacked_layout(int base) {
 bool is_plane(BlockLayout lay) { return lay.stride == kPlane; }
 
 // A type id is a GGUF type, optionally OR-ed with MQ_REPACKED for the layout mq_repack
-// writes.  Returns the GGUF type (0 for an unknown id or a type with no repacked layout)
-// and the layout of its blocks.
+// writes, or Q4_K OR-ed with MQ_ROW_TILED for its row-tiled layout.  Returns the GGUF type
+// (0 for an unknown id or a type with no such layout) and the layout of its blocks.
 int parse_type(int type, BlockLayout& lay) {
+    if (type & MQ_ROW_TILED) {
+        if (type != (MQ_Q4_K | MQ_ROW_TILED)) return 0;
+        lay = BlockLayout{block_bytes(MQ_Q4_K), 0, true};
+        return MQ_Q4_K;
+    }
     const int base = type & ~MQ_REPACKED;
     if (block_values(base) == 0) return 0;
     if (type & MQ_REPACKED) {
@@ -223,11 +228,13 @@ size_t mq_weight_bytes(int type, int64_t N, int64_t K) {
     const int bv = block_values(base);
     if (N <= 0 || K <= 0 || K % bv != 0) return 0;
     if (is_plane(lay)) return f6_weight_plane_bytes(N, K);
+    if (lay.row_tiled) return row_tiled_k(K) ? row_tiled_bytes(N, K) : 0;
     return size_t(N) * size_t(K / bv) * size_t(lay.stride);
 }
 
 size_t mq_repack_bytes(int type, int64_t N, int64_t K) {
     if (type & MQ_REPACKED) return 0;
+    if (type & MQ_ROW_TILED) return mq_weight_bytes(type, N, K);
     return mq_weight_bytes(type | MQ_REPACKED, N, K);
 }
 
@@ -257,6 +264,7 @@ size_t mq_gemm_scratch_bytes(int type, int64_t M, int64_t N, int64_t K) {
     if (type == 0) return 0;
     if (M <= 0 || N <= 0 || K <= 0 || M > MQ_MAX_M || N > MQ_MAX_N || K > MQ_MAX_K) return 0;
     if (K % block_values(type) != 0) return 0;
+    if (lay.row_tiled) return 0;   // mq_gemm refuses the row-tiled layout
     if (is_plane(lay)) return mmq_f6_scratch_bytes(M, N, K);
     return mmq_scratch_bytes(type, M, N, K);
 }
@@ -296,8 +304,18 @@ int mq_gemv(const void* W, int type, const float* x, float* y, int64_t N, int64_
     if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4))
         return fail(MQ_ERR_ALIGN, "%s: W and x must be 16-byte, y 4-byte aligned (W=%p x=%p y=%p)", fn, W,
                     (const void*)x, (void*)y);
+    if (lay.row_tiled && !row_tiled_k(K))
+        return fail(MQ_ERR_SHAPE, "%s: the row-tiled Q4_K layout holds rows of more than 16 super-blocks (K > "
+                    "4096), not K=%lld", fn, (long long)K);
     rc = check_ready(fn);
     if (rc) return rc;
+    if (lay.row_tiled) {
+        const char* kernel = "gemv_mfma_long<q4_K row-tiled>";
+        if (refuse_this_launch()) return launch_status(fn, hipErrorLaunchFailure, kernel);
+        hipError_t e = launch_gemv_row_tiled(static_cast<const uint8_t*>(W), x, y, N, K,
+                                             static_cast<hipStream_t>(stream), &kernel);
+        return launch_status(fn, e, kernel);
+    }
     if (gemv_tile_units(type, K, device_info()->lds_per_block) <= 0)
         return fail(MQ_ERR_SHAPE, "%s: K=%lld does not fit the %zu-byte LDS of this device", fn, (long long)K,
                     device_info()->lds_per_block);
@@ -315,6 +333,9 @@ static int gemm_common(const char* fn, const void* W, int type, const void* Xq, 
     BlockLayout lay;
     const int base = parse_type(type, lay);
     if (base == 0) return fail(MQ_ERR_TYPE, "%s: unsupported weight type %d", fn, type);
+    if (lay.row_tiled)
+        return fail(MQ_ERR_TYPE, "%s: type %d is Q4_K's row-tiled layout, which only mq_gemv reads (the prefill "
+                    "product reads the GGUF payload or the MMQ plane)", fn, type);
     type = base;
     int rc = check_weight_shape(fn, type, N, K);
     if (rc) return rc;
@@ -407,11 +428,22 @@ int mq_repack(const void* W, int type, int64_t N, int64_t K, size_t nbytes, void
     const char* fn = "mq_repack";
     if (!W || !Wr) return fail(MQ_ERR_ARG, "%s: null pointer (W=%p Wr=%p)", fn, W, Wr);
     if (type & MQ_REPACKED) return fail(MQ_ERR_TYPE, "%s: type %d is already the repacked layout", fn, type);
+    const bool row_tiled = (type & MQ_ROW_TILED) != 0;
+    if (row_tiled) {
+        if (type != (MQ_Q4_K | MQ_ROW_TILED)) return fail(MQ_ERR_TYPE, "%s: only Q4_K has a row-tiled layout", fn);
+        type = MQ_Q4_K;
+        const int rc = check_weight_shape(fn, type, N, K);
+        if (rc) return rc;
+        if (!row_tiled_k(K))
+            return fail(MQ_ERR_SHAPE, "%s: the row-tiled Q4_K layout holds rows of more than 16 super-blocks (K > "
+                        "4096), not K=%lld", fn, (long long)K);
+    }
     if (block_values(type) != 0 && repacked_layout(type).stride == 0)
         return fail(MQ_ERR_TYPE, "%s: type %d has no repacked layout", fn, type);
     int rc = check_weight_shape(fn, type, N, K);
     if (rc) return rc;
-    const size_t in_bytes = mq_weight_bytes(type, N, K), out_bytes = mq_repack_bytes(type, N, K);
+    const size_t in_bytes = mq_weight_bytes(type, N, K);
+    const size_t out_bytes = row_tiled ? row_tiled_bytes(N, K) : mq_repack_bytes(type, N, K);
     if (nbytes != in_bytes)
         return fail(MQ_ERR_SIZE, "%s: payload of %zu bytes, a %lld x %lld type-%d matrix is exactly %zu", fn, nbytes,
                     (long long)N, (long long)K, type, in_bytes);
@@ -424,6 +456,12 @@ int mq_repack(const void* W, int type, int64_t N, int64_t K, size_t nbytes, void
     if (a0 < b1 && b0 < a1) return fail(MQ_ERR_ARG, "%s: W and Wr overlap", fn);
     rc = check_ready(fn);
     if (rc) return rc;
+    if (row_tiled) {
+        if (refuse_this_launch()) return launch_status(fn, hipErrorLaunchFailure, "repack");
+        hipError_t e = launch_repack_q4k_row_tiled(static_cast<const uint8_t*>(W), static_cast<uint8_t*>(Wr), N, K,
+                                                   static_cast<hipStream_t>(stream));
+        return launch_status(fn, e, "repack");
+    }
     const BlockLayout lay = repacked_layout(type);
     if (is_plane(lay)) {
         if (refuse_this_launch()) return launch_status(fn, hipErrorLaunchFailure, "repack");

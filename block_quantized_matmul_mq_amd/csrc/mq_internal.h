@@ -67,7 +67,24 @@ const DeviceInfo* device_info();  // null if mq_init has not succeeded on the cu
 struct BlockLayout {
     int stride = 0;
     int off = 0;
+    bool row_tiled = false;   // Q4_K's row-tiled layout (below)
 };
+
+// Q4_K's row-tiled layout (MQ_ROW_TILED), for the GEMV of rows of more than 16
+// super-blocks: rows in groups of row_tile_rows(N) (at most 16; at most 256 groups up to
+// 4096 rows); a group stores its rows' super-block 0 blocks one after another (row order),
+// then their super-block 1 blocks, and so on; the last group is filled with zero rows.
+// One group's super-block is then one contiguous run of R x 144 bytes.
+inline int row_tile_rows(int64_t N) { return int(N >= 16 * 256 ? 16 : (N + 255) / 256); }
+inline bool row_tiled_k(int64_t K) { return K % 256 == 0 && K / 256 > 16; }
+inline size_t row_tiled_bytes(int64_t N, int64_t K) {
+    const int64_t R = row_tile_rows(N);
+    return size_t((N + R - 1) / R * R) * size_t(K / 256) * 144;
+}
+hipError_t launch_repack_q4k_row_tiled(const uint8_t* W, uint8_t* Wr, int64_t N, int64_t K, hipStream_t s);
+// The long-row Q4_K GEMV on the row-tiled layout (gemv_mfma.hip): one group per workgroup.
+hipError_t launch_gemv_row_tiled(const uint8_t* W, const float* x, float* y, int64_t N, int64_t K, hipStream_t s,
+                                 const char** kernel_name);
 
 // Kernel launchers: they enqueue on `s` and return the launch status (hipGetLastError read
 // right after the launch).  Arguments are validated by the callers in mq_api.hip.

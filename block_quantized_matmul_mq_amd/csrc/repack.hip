@@ -13,6 +13,10 @@
 // E2M3 code of c / 2 (exact), value i at bits 6 i .. 6 i + 5, plus the bf16 hi + lo parts of
 // its scale d * sc and of its min -dmin * m laid out as the operands of the kernel's bf16
 // scale products.  Rows N..Np-1 are zero.  One thread writes one (step, sub-block, row).
+//
+// Q4_K's row-tiled layout (for the GEMV of long rows; mq_internal.h) moves whole 144-byte
+// blocks: a group of rows stores their super-block 0 blocks one after another, then their
+// super-block 1 blocks, and so on.
 #include "mmq_common.h"
 #include "mq_internal.h"
 
@@ -83,7 +87,33 @@ __global__ __launch_bounds__(256) void repack_q4k_plane_kernel(const uint8_t* __
     }
 }
 
+// Q4_K's row-tiled layout: one thread per 16-byte chunk of the output (block chunk c of
+// row r of the group, super-block s, group g), copied from the GGUF payload; the filler
+// rows of the last group are zero.
+__global__ __launch_bounds__(256) void repack_q4k_row_tiled_kernel(const uint4* __restrict__ W, uint4* __restrict__ Wr,
+                                                                   int64_t N, int64_t chunks, int SB, int R) {
+    const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+    for (int64_t o = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; o < chunks; o += stride) {
+        const int64_t blk = o / 9;
+        const int c = int(o - blk * 9);
+        const int r = int(blk % R);
+        const int64_t gs = blk / R;
+        const int s = int(gs % SB);
+        const int64_t n = (gs / SB) * R + r;
+        Wr[o] = n < N ? W[(n * SB + s) * 9 + c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_repack_q4k_row_tiled(const uint8_t* W, uint8_t* Wr, int64_t N, int64_t K, hipStream_t s) {
+    const int64_t chunks = int64_t(row_tiled_bytes(N, K) / 16);
+    const int64_t want = (chunks + 255) / 256;
+    const int grid = int(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(repack_q4k_row_tiled_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<const uint4*>(W),
+                       reinterpret_cast<uint4*>(Wr), N, chunks, int(K / 256), row_tile_rows(N));
+    return hipGetLastError();
+}
 
 hipError_t launch_repack_q4k_plane(const uint8_t* W, uint8_t* Wp, int64_t N, int64_t K, hipStream_t s) {
     const int64_t Np = f6_weight_rows(N);

@@ -19,6 +19,7 @@ Q4_K = 12
 Q5_K = 13
 Q6_K = 14
 REPACKED = 0x100   # OR-ed into Q8_0 / Q6_K / Q4_K: weights in the layout mq_repack writes
+ROW_TILED = 0x200  # OR-ed into Q4_K: its row-tiled layout (long-row GEMV), from repack(.., Q4_K | ROW_TILED, ..)
 
 MQ_OK = 0
 ERRORS = {
@@ -171,9 +172,10 @@ def repack_bytes(qtype, N, K):
 
 
 def repack(W, qtype, N, K, Wr=None, stream=None):
-    """The repacked layout of a GGUF payload W (uint8 CUDA tensor); use with qtype | REPACKED."""
+    """The repacked layout of a GGUF payload W (uint8 CUDA tensor); use with qtype | REPACKED
+    (or, for qtype = Q4_K | ROW_TILED, the row-tiled layout; use with Q4_K | ROW_TILED)."""
     import torch
-    _weights(W, qtype, N, K, "repack")
+    _weights(W, qtype & ~ROW_TILED, N, K, "repack")
     need = repack_bytes(qtype, N, K)
     if Wr is None:
         Wr = torch.empty(need, dtype=torch.uint8, device=W.device)

@@ -98,6 +98,10 @@ extern "C" {
  * writes (every call that takes a weight type accepts it, except that mq_gemv refuses
  * Q4_K's, which is a plane for mq_gemm only). */
 #define MQ_REPACKED 0x100
+/* OR-ed into MQ_Q4_K only: the weights are in Q4_K's row-tiled layout, which
+ * mq_repack(.., MQ_Q4_K | MQ_ROW_TILED, ..) writes and mq_gemv reads (for rows of
+ * more than 16 super-blocks; see mq_repack). */
+#define MQ_ROW_TILED 0x200
 
 /* Status codes. */
 #define MQ_OK 0
@@ -125,8 +129,9 @@ extern "C" {
 int mq_init(int device);
 
 /* Exact byte size of a GGUF payload of N x K weights of `type` [BD2.3] (of
- * the repacked layout for type | MQ_REPACKED); 0 for an unsupported type or a
- * K that is not a whole number of blocks. */
+ * the repacked layout for type | MQ_REPACKED, of the row-tiled layout for
+ * MQ_Q4_K | MQ_ROW_TILED); 0 for an unsupported type, a K that is not a whole
+ * number of blocks, or (row-tiled) K <= 4096. */
 size_t mq_weight_bytes(int type, int64_t N, int64_t K);
 
 /*
@@ -158,7 +163,17 @@ size_t mq_weight_bytes(int type, int64_t N, int64_t K);
  *            its block dots are the same exact integers.  mq_gemv refuses it
  *            (MQ_ERR_TYPE): decode reads the GGUF payload.
  * Other types have no repacked layout: MQ_ERR_TYPE, and mq_repack_bytes returns
- * 0.  W and Wr must be 16-byte aligned and must not overlap (MQ_ERR_ARG).  Runs on
+ * 0.
+ * MQ_Q4_K | MQ_ROW_TILED (instead of MQ_REPACKED) asks for Q4_K's row-tiled
+ * layout, for the GEMV of rows of more than 16 super-blocks (K > 4096; else
+ * MQ_ERR_SHAPE): rows in groups of R = min(16, ceil(N / 256)); a group stores
+ * its R rows' 144-byte super-block 0 blocks one after another (row order),
+ * then their super-block 1 blocks, and so on, groups in order, the last group
+ * filled with zero rows (mq_repack_bytes = ceil(N / R) R (K / 256) 144).  One
+ * group's super-block is then one contiguous run of R x 144 bytes.  mq_gemv
+ * reads it with type MQ_Q4_K | MQ_ROW_TILED and gives the GGUF payload's
+ * result bit for bit; mq_gemm refuses it (MQ_ERR_TYPE).
+ * W and Wr must be 16-byte aligned and must not overlap (MQ_ERR_ARG).  Runs on
  * `stream`; W may be freed once the stream has passed the call.
  */
 size_t mq_repack_bytes(int type, int64_t N, int64_t K);
@@ -320,7 +335,8 @@ int mq_device_lds_bytes(void);
  *   "quantize_act", "repack";
  *   mq_gemv: "gemv_mfma<q4_K>" (wide: at least two 16-row tiles per CU, 12..16
  *     super-blocks per row), "gemv_mfma_long<q4_K>" (more than 16 super-blocks,
- *     8..16 rows per CU), "gemv_mfma<q6_K>" (wide, GGUF layout, matrix ending
+ *     8..16 rows per CU), "gemv_mfma_long<q4_K row-tiled>" (MQ_Q4_K |
+ *     MQ_ROW_TILED), "gemv_mfma<q6_K>" (wide, GGUF layout, matrix ending
  *     on a 16-byte boundary), "gemv_mfma<q8_0>" / "gemv_mfma<q4_0>" /
  *     "gemv_mfma<q5_0>" (wide, GGUF layout), else "gemv<type>" (with " repacked" for MQ_REPACKED);
  *   mq_gemm: "mmq_f6<q4_K plane>" (MQ_Q4_K | MQ_REPACKED, any M),

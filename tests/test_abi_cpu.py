@@ -193,6 +193,38 @@ def test_repacked_sizes_and_type_flag():
     assert mq.gemm_scratch_bytes(mq.Q6_K | R, 9, 152064, 3584) == mq.gemm_scratch_bytes(mq.Q6_K, 9, 152064, 3584)
 
 
+def test_row_tiled_sizes_and_refusals():
+    """Q4_K's row-tiled layout (MQ_ROW_TILED): the byte counts the library reports equal
+    the oracle's layout; it exists for Q4_K rows of more than 16 super-blocks only; only
+    mq_gemv reads it."""
+    import numpy as np
+    import oracle
+    from block_quantized_matmul_mq_amd import synth
+    T = mq.Q4_K | mq.ROW_TILED
+    assert mq.weight_bytes(T, 3584, 18944) == mq.weight_bytes(mq.Q4_K, 3584, 18944) == 38191104
+    for N, K in [(3, 17 * 256), (301, 17 * 256), (513, 18 * 256), (5000, 20 * 256)]:
+        raw = synth.random_blocks(oracle.Q4_K, N, K, np.random.default_rng(N)).reshape(-1)
+        assert mq.repack_bytes(T, N, K) == mq.weight_bytes(T, N, K) == oracle.q4_k_row_tiled(raw, N, K).size
+    assert mq.weight_bytes(T, 3584, 4096) == 0                      # 16 super-blocks: not a long row
+    assert mq.weight_bytes(mq.Q6_K | mq.ROW_TILED, 3584, 18944) == 0
+    assert mq.weight_bytes(T | mq.REPACKED, 3584, 18944) == 0
+    assert mq.gemm_scratch_bytes(T, 512, 3584, 18944) == 0
+    lib = mq.load()
+    far = FAKE + (1 << 28)
+    nb = mq.weight_bytes(mq.Q4_K, 300, 4352)
+    rb = mq.repack_bytes(T, 300, 4352)
+    assert lib.mq_repack(FAKE, mq.Q6_K | mq.ROW_TILED, 300, 4352, nb, far, rb, None) == -3
+    assert lib.mq_repack(FAKE, T, 300, 4096, mq.weight_bytes(mq.Q4_K, 300, 4096), far, rb, None) == -2
+    assert "more than 16 super-blocks" in mq.last_error()
+    assert lib.mq_repack(FAKE, T, 300, 4352, nb - 144, far, rb, None) == -4          # exact input length
+    assert lib.mq_repack(FAKE, T, 300, 4352, nb, far, rb - 1, None) == -4
+    assert lib.mq_gemv(FAKE, T, FAKE, FAKE, 300, 4096, None) == -2
+    assert lib.mq_gemv(FAKE, mq.Q6_K | mq.ROW_TILED, FAKE, FAKE, 300, 4352, None) == -3
+    assert lib.mq_gemm(FAKE, T, FAKE, FAKE, 40, 300, 4352, None, 0, None) == -3
+    assert "only mq_gemv reads" in mq.last_error()
+    assert lib.mq_debug_gemm_blockdots(FAKE, T, FAKE, FAKE, 40, 300, 4352, None) == -3
+
+
 def test_repack_refusals():
     lib = mq.load()
     nb6 = mq.weight_bytes(mq.Q6_K, 8, 512)

@@ -35,7 +35,7 @@ def test_every_launching_call_reports_a_refused_launch():
     W = to_dev(raw.reshape(-1), dev)
     X = to_dev(synth.activations(M, K, config_index=12, tensor_index=400), dev)
     x = X[0].contiguous()
-    say("refused launches: quantize_act, gemv, gemm (int8), repack, gemm (fp6 plane), block dots")
+    say("refused launches: quantize_act, gemv, gemm (int8), repack, gemm (fp6 plane), block dots, row-tiled")
     refused(lambda: mq.quantize_act(X), "mq_quantize_act: launch of quantize_act")
     Xq = mq.quantize_act(X)
     refused(lambda: mq.gemv(W, mq.Q4_K, x, N, K), "mq_gemv: launch of gemv")
@@ -48,6 +48,15 @@ def test_every_launching_call_reports_a_refused_launch():
     refused(lambda: mq.gemm(Wp, plane, Xq, M, N, K), "mq_gemm: launch of mmq_f6<q4_K plane>")
     Yp = mq.gemm(Wp, plane, Xq, M, N, K)
     refused(lambda: mq.gemm_blockdots(W, mq.Q4_K, Xq, M, N, K), "mq_debug_gemm_blockdots: launch of mmq")
+    # Q4_K's row-tiled layout and the long-row GEMV on it (rows of more than 16 super-blocks)
+    Kt = 17 * 256
+    Wl = to_dev(weights(mq.Q4_K, N, Kt, "random", 401).reshape(-1), dev)
+    xt = to_dev(synth.activations(1, Kt, config_index=12, tensor_index=401)[0], dev)
+    refused(lambda: mq.repack(Wl, mq.Q4_K | mq.ROW_TILED, N, Kt), "mq_repack: launch of repack")
+    Wt = mq.repack(Wl, mq.Q4_K | mq.ROW_TILED, N, Kt)
+    refused(lambda: mq.gemv(Wt, mq.Q4_K | mq.ROW_TILED, xt, N, Kt),
+            "mq_gemv: launch of gemv_mfma_long<q4_K row-tiled>")
+    yt = mq.gemv(Wt, mq.Q4_K | mq.ROW_TILED, xt, N, Kt)
     # two refusals in a row, then the calls launch again
     assert lib.mq_debug_refuse_launches(2) == 0
     for _ in range(2):
@@ -56,7 +65,8 @@ def test_every_launching_call_reports_a_refused_launch():
     y2 = mq.gemv(W, mq.Q4_K, x, N, K)
     Y2 = mq.gemm(W, mq.Q4_K, Xq, M, N, K)
     Yp2 = mq.gemm(Wp, plane, Xq, M, N, K)
+    yt2 = mq.gemv(Wt, mq.Q4_K | mq.ROW_TILED, xt, N, Kt)
     torch.cuda.synchronize()
-    for a, b in ((y, y2), (Y, Y2), (Yp, Yp2)):
+    for a, b in ((y, y2), (Y, Y2), (Yp, Yp2), (yt, yt2)):
         a, b = a.cpu().numpy(), b.cpu().numpy()
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))

@@ -296,6 +296,16 @@ def c5_layer_mix(torch, mq, synth, timer, to_dev, dev, reps):
         y = torch.empty(N, dtype=torch.float32, device=dev)
         g_us = timer.per_launch_us([lambda W=W: mq.gemv(W, qt, x, N, K, y=y) for W in wc], reps)
         gk = mq.last_kernel()
+        tiled_us = None
+        if qt == Q4_K and mq.repack_bytes(Q4_K | ROW_TILED, N, K):
+            # Q4_K's row-tiled layout, kept instead of the GGUF payload when its GEMV is faster
+            # (every copy read once first, as for the 7B decode weights)
+            wt = [mq.repack(W, Q4_K | ROW_TILED, N, K) for W in wc]
+            for W in wt:
+                mq.gemv(W, Q4_K | ROW_TILED, x, N, K, y=y)
+            tiled_us = timer.per_launch_us([lambda W=W: mq.gemv(W, Q4_K | ROW_TILED, x, N, K, y=y) for W in wt],
+                                           reps)
+            del wt
         Y = torch.empty((C5_M, N), dtype=torch.float32, device=dev)
         sc = torch.zeros(max(mq.gemm_scratch_bytes(qt, C5_M, N, K), 256), dtype=torch.uint8, device=dev)
         m_us = timer.per_launch_us([lambda W=W: mq.gemm(W, qt, Xq[K], C5_M, N, K, Y=Y, scratch=sc) for W in wc[:2]],
@@ -318,6 +328,10 @@ def c5_layer_mix(torch, mq, synth, timer, to_dev, dev, reps):
             out[f"{name}_{N}x{K}"].update({"mmq_plane_M2048_us": round(plane_us, 3),
                                            "mmq_plane_M2048_TOPS": round(ops / plane_us / 1e6, 2)})
             m_us = min(m_us, plane_us)
+        if tiled_us is not None:
+            out[f"{name}_{N}x{K}"].update({"gemv_row_tiled_M1_us": round(tiled_us, 3),
+                                           "gemv_row_tiled_M1_GBps": round(nb / tiled_us / 1e3, 1)})
+            g_us = min(g_us, tiled_us)
         layer_gemv_us += uses * g_us
         layer_mmq_us += uses * m_us
         layer_bytes += uses * nb
@@ -328,8 +342,9 @@ def c5_layer_mix(torch, mq, synth, timer, to_dev, dev, reps):
     out["layer"] = {"gemv_M1_us": round(layer_gemv_us, 2), "gemv_M1_GBps": round(layer_bytes / layer_gemv_us / 1e3, 1),
                     "prefill_M2048_us": round(layer_mmq_us + q_us, 2),
                     "prefill_M2048_TOPS": round(layer_ops / (layer_mmq_us + q_us) / 1e6, 2),
-                    "note": "q, k, v, o, gate, up, down; kernel times summed (each Q4_K product in the faster "
-                            "of its GGUF payload and MMQ plane), quantize_act included at M=2048"}
+                    "note": "q, k, v, o, gate, up, down; kernel times summed (each Q4_K GEMV in the faster of its "
+                            "GGUF payload and row-tiled layout, each Q4_K product in the faster of its GGUF payload "
+                            "and MMQ plane), quantize_act included at M=2048"}
     return out
 
 

@@ -341,7 +341,8 @@ int mq_device_lds_bytes(void);
  *     "gemv_mfma<q5_0>" (wide, GGUF layout), else "gemv<type>" (with " repacked" for MQ_REPACKED);
  *   mq_gemm: "mmq_f6<q4_K plane>" (MQ_Q4_K | MQ_REPACKED, any M),
  *     "gemv_q8_mfma<q6_K>" (M <= 8, Q6_K, as gemv_mfma<q6_K>),
- *     "gemv_q8<type>" (other M <= 8 shapes that fit LDS), else "mmq<type>". */
+ *     "gemv_q8<type>" (other M <= 8 shapes that fit LDS), "mmq_kw<q4_K>" (Q4_K,
+ *     GGUF payload, few output tiles: see mq_gemm_scratch_bytes), else "mmq<type>". */
 const char* mq_last_kernel(void);
 
 /* Library version string. */

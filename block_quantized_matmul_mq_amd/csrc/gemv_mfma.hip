@@ -906,15 +906,15 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_q6k_kernel(const uint8_t* __
                 v4i c;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const uint32_t code = ((L[i] >> (4 * part_t)) & 0x0F0F0F0Fu) |
-                                          (((Hb[i] >> (s_lo + 4 * part_t)) & 0x03030303u) << 4);
+                    const uint32_t lo = (L[i] >> (4 * part_t)) & 0x0F0F0F0Fu;
+                    const uint32_t hi = (Hb[i] >> (s_lo + 4 * part_t)) & 0x03030303u;   // the 2 high bits, per byte
                     if constexpr (MR == 4) {
-                        c[i] = int(code);
+                        c[i] = int(lo | (hi << 4));
                     } else {
-                        // code - 32 as signed bytes: flip bit 5; a set bit 5 (code < 32) marks
-                        // a negative result, whose bits 6 and 7 are then set as well
-                        const uint32_t u = code ^ 0x20202020u, neg = u & 0x20202020u;
-                        c[i] = int(u | (neg << 1) | (neg << 2));
+                        // code - 32 as signed bytes: the high bits h = 0..3 of code = 16 h + lo
+                        // give the byte's top nibble h - 2 (0xE, 0xF, 0x0, 0x1), looked up per
+                        // byte with v_perm_b32 (selector bytes 0..3 pick bytes of 0x1000F0E0)
+                        c[i] = int(__builtin_amdgcn_perm(0u, 0x1000F0E0u, hi) | lo);
                     }
                 }
                 const float f = d * sbyte_f(sc4[t], q);

@@ -509,6 +509,16 @@ __device__ __forceinline__ uint4 lds_seg16(const uint8_t* p) {
     return make_uint4(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh),
                       __builtin_amdgcn_alignbyte(w3, w2, sh), __builtin_amdgcn_alignbyte(w4, w3, sh));
 }
+// The same when p is known to be 4-byte aligned: four dword reads, nothing to realign.
+template <bool ALIGNED>
+__device__ __forceinline__ uint4 lds_seg16_if(const uint8_t* p) {
+    if constexpr (ALIGNED) {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+        return make_uint4(q[0], q[1], q[2], q[3]);
+    } else {
+        return lds_seg16(p);
+    }
+}
 __device__ __forceinline__ float lds_f16(const uint8_t* p) {
     return half_bits_to_float(uint32_t(*reinterpret_cast<const uint16_t*>(p)));
 }
@@ -881,9 +891,14 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_q6k_kernel(const uint8_t* __
     const bool a_lane = (n >> 2) == q;
     const uint8_t* a_src = stage + (n & 3) * K + 256 * sc + 16 * q;
 
-    auto compute = [&](const uint8_t* tile, float* pt, int k) __attribute__((always_inline)) {
+    // A block starts 2-byte aligned in the tile; with an even number of super-blocks per row
+    // its offset mod 4 depends on the super-block only (the wave's), so a wave whose blocks
+    // start on dwords reads its segments without realigning them.
+    const bool dword_blocks = ((row_bytes | (sc * TiledItem<kQ6_K>::kSBBytes)) & 3) == 0;   // uniform
+    auto compute = [&](auto aligned_c, const uint8_t* tile, float* pt, int k) __attribute__((always_inline)) {
+        constexpr bool AL = decltype(aligned_c)::value;
         const uint8_t* blk = tile + n * row_bytes + sc * TiledItem<kQ6_K>::kSBBytes;
-        const uint4 scw = lds_seg16(blk + 192);
+        const uint4 scw = lds_seg16_if<AL>(blk + 192);
         const uint32_t sc4[4] = {scw.x, scw.y, scw.z, scw.w};
         const float d = lds_f16(blk + 208);
         const uint32_t s_lo = 2u * uint32_t(q >> 1);
@@ -896,8 +911,8 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_q6k_kernel(const uint8_t* __
             // (one half at a time: hoisting the second half's reads over the first would
             // run out of registers)
             __builtin_amdgcn_sched_barrier(0);
-            const uint4 ql = lds_seg16(blk + 64 * hh + 16 * q);
-            const uint4 qh = lds_seg16(blk + 128 + 32 * hh + 16 * (q & 1));
+            const uint4 ql = lds_seg16_if<AL>(blk + 64 * hh + 16 * q);
+            const uint4 qh = lds_seg16_if<AL>(blk + 128 + 32 * hh + 16 * (q & 1));
             const uint32_t L[4] = {ql.x, ql.y, ql.z, ql.w}, Hb[4] = {qh.x, qh.y, qh.z, qh.w};
 #pragma unroll
             for (int part_t = 0; part_t < 2; ++part_t) {
@@ -976,7 +991,10 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_q6k_kernel(const uint8_t* __
     __syncthreads();   // tile 0 stored
     auto body = [&](auto i_c, int k) __attribute__((always_inline)) {
         constexpr int I = decltype(i_c)::value;   // k % 2
-        if (active) compute(slot(std::integral_constant<int, I>{}), part[I], k);
+        if (active) {
+            if (dword_blocks) compute(std::true_type{}, slot(std::integral_constant<int, I>{}), part[I], k);
+            else compute(std::false_type{}, slot(std::integral_constant<int, I>{}), part[I], k);
+        }
         __builtin_amdgcn_sched_barrier(0);   // keep the phases apart: registers are short
         if (k > 0) row_sums(part[I ^ 1], k - 1);
         __builtin_amdgcn_sched_barrier(0);

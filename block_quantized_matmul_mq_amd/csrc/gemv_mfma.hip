@@ -186,8 +186,10 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_kernel(const uint8_t* 
     };
     // Every wave requests its x before any wave requests weights: a CU returns loads in
     // order, and x queued behind the weight stream would arrive microseconds late.
+    // Only the first item is requested before the x staging: items queued ahead of it hold
+    // up the staging barrier (the CU accepts loads in order), so the rest follow it.
     asm volatile("s_barrier" ::: "memory");
-    static_for<NB - 1>([&](auto b) { issue(b, decltype(b)::value); });
+    issue(std::integral_constant<int, 0>{}, 0);
 
     // Stage x: 8 lanes per 32-block, 4 values (one float4) per lane; plane-major digits.
     if (tid < nquads) {   // uniform per wave: K is a multiple of 256
@@ -212,7 +214,11 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_kernel(const uint8_t* 
             ex[tid >> 3] = -k;
         }
     }
-    wait_barrier<(NB - 1) * 3>();   // x staged; the weight loads stay in flight
+    wait_barrier<3>();   // x staged; the first item's loads stay in flight
+    static_for<NB - 2>([&](auto b) {
+        constexpr int B = decltype(b)::value + 1;
+        issue(std::integral_constant<int, B>{}, B);
+    });
 
     // Lane roles: B column n (row n of the tile) with unit q of this wave's super-block;
     // A row n of lane group q is digit plane n & 3 of unit q's values when n / 4 == q and
@@ -1211,12 +1217,16 @@ const void* wide_kernel(int type) {
     }
 }
 
-// Two slots: one item in flight while the wave computes the other.  Deeper rings were
-// measured slower (7B ffn_up 18944 x 3584: 9.7 us with two slots, 9.8 with three, 10.9 with
-// four): more items in flight per wave keep more tile windows of the matrix open at once,
-// and every wave has to get all of its first items accepted by the memory pipeline before
-// the workgroup barrier of the x staging, so the first compute starts later.
+// Ring slots per wave: three (two items in flight while the wave computes a third) once a
+// workgroup has at least four tiles, else two.  Only the first item is requested before the
+// x staging, the others right after it; issued all before it, deeper rings lost what they
+// gained (7B ffn_up 18944 x 3584: 9.7 us with two slots, 9.8 with three, 10.9 with four),
+// as every wave's items had to be accepted by the memory pipeline before the staging
+// barrier.  With the later issue three slots take ffn_up from 9.41 to 9.19 us and 37888 x
+// 3584 from 16.24 to 15.71 us; at two tiles per workgroup (8192 x 3584) they cost 0.3 us.
 constexpr int kRing = 2;
+constexpr int kRingDeep = 3;
+constexpr int kRingDeepTiles = 4;   // tiles per workgroup from which the deeper ring is taken
 
 struct Plan {
     int grid = 0;
@@ -1228,9 +1238,9 @@ Plan plan(int64_t N, int64_t K, int cu_count) {
     const int64_t T = (N + kTileRows - 1) / kTileRows;
     const int64_t grid = T < cu_count ? T : cu_count;
     const int64_t row_bytes = (K / 256) * 144;
-    // 32-bit buffer offsets: the last prefetch reaches kRing rounds of tiles past the end
+    // 32-bit buffer offsets: the last prefetch reaches kRingDeep rounds of tiles past the end
     if ((T + grid - 1) / grid > kMaxTilesPerGroup ||
-        (T + (kRing + 1) * grid) * kTileRows * row_bytes >= (int64_t(1) << 31))
+        (T + (kRingDeep + 1) * grid) * kTileRows * row_bytes >= (int64_t(1) << 31))
         return p;
     p.grid = int(grid);
     return p;
@@ -1414,7 +1424,11 @@ hipError_t launch_gemv_mfma(const uint8_t* W, const float* x, float* y, int64_t 
     *name = "gemv_mfma<q4_K>";
     int n = int(N), k = int(K), row_bytes = int((K / 256) * 144);
     void* args[] = {&W, &x, &y, &n, &k, &row_bytes};
-    return hipLaunchKernel(reinterpret_cast<const void*>(gemv_mfma_q4k_kernel<kRing>), dim3(p.grid),
+    const int64_t tiles = (N + kTileRows - 1) / kTileRows;
+    const void* kern = tiles >= int64_t(kRingDeepTiles) * p.grid
+                           ? reinterpret_cast<const void*>(gemv_mfma_q4k_kernel<kRingDeep>)
+                           : reinterpret_cast<const void*>(gemv_mfma_q4k_kernel<kRing>);
+    return hipLaunchKernel(kern, dim3(p.grid),
                            dim3(kThreads), args, 0, s);
 }
 

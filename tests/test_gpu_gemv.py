@@ -199,6 +199,27 @@ def test_gemv_wide_matrix_core_path(qtype, N, K, kind):
     assert mq.last_kernel() == f"gemv_mfma<{NAMES[qtype]}>"
 
 
+@pytest.mark.parametrize("qtype", WIDE, ids=[NAMES[t] for t in WIDE])
+@pytest.mark.parametrize("N,K", [(16384 + 16 * 3 + 9, 3584), (37888 + 5, 3072)],
+                         ids=["four_or_five_tiles", "nine_or_ten_tiles"])
+def test_gemv_wide_many_tiles_per_workgroup(qtype, N, K):
+    """The per-wave kernel with many 16-row tiles per workgroup: workgroups with 4, 5, 9 and
+    10 tiles (ring loop groups of two with remainders of 0 and 1), checked on every row of
+    the tiles of the first, second and last workgroups, the first and last 64 tiles and
+    1000 random rows."""
+    import torch
+    G = torch.cuda.get_device_properties(device()).multi_processor_count
+    T = (N + 15) // 16
+    tiles = np.r_[0:64, T - 64:T, np.arange(0, T, G), np.arange(1, T, G), np.arange(G - 1, T, G)]
+    rng = np.random.default_rng(N)
+    rows = np.unique(np.r_[(tiles[:, None] * 16 + np.arange(16)).ravel(), rng.choice(N, 1000, replace=False)])
+    rows = rows[rows < N]
+    raw = weights(qtype, N, K, "random", 13)
+    x = synth.activations(1, K, config_index=10, tensor_index=N % 71)[0]
+    run_gemv(raw, qtype, x, N, K, rows=rows, what="wide, many tiles")
+    assert mq.last_kernel() == f"gemv_mfma<{NAMES[qtype]}>"
+
+
 def test_gemv_q8_0_wide_saturated_codes():
     """Wide Q8_0 runs reach |sum code * v| = 16 * 128 * 2^21 = 2^32 when every code of a
     16-value run is +-127 or -128 and x is constant just below a power of two in a block

@@ -86,6 +86,21 @@ __device__ __forceinline__ uint32_t e2m3_half_code(int k) {
     return (uint32_t(k < 0) << 5) | uint32_t((tbl >> (8 * (a & 7))) & 0x3Fu);
 }
 
+// e2m3_half_code of four 4-bit fields at once (byte i of `nib` holds field i).  SIGNED: each
+// field is a two's-complement k in -8..7 (the high nibble of a signed byte), else k = 0..15.
+// Two eight-entry byte lookups (v_perm_b32: selectors 0..3 pick bytes of the second
+// operand, 4..7 of the first) and a third that takes, per byte, the half named by bit 3.
+template <bool SIGNED>
+__device__ __forceinline__ uint32_t e2m3_half_codes4(uint32_t nib) {
+    constexpr uint32_t t0 = 0x0C080400u, t1 = 0x16141210u;         // k = 0..3, 4..7
+    constexpr uint32_t t2 = SIGNED ? 0x32343638u : 0x1B1A1918u;    // k = -8..-5, or 8..11
+    constexpr uint32_t t3 = SIGNED ? 0x24282C30u : 0x1F1E1D1Cu;    // k = -4..-1, or 12..15
+    const uint32_t sel = nib & 0x07070707u;
+    const uint32_t lo = __builtin_amdgcn_perm(t1, t0, sel);
+    const uint32_t hi = __builtin_amdgcn_perm(t3, t2, sel);
+    return __builtin_amdgcn_perm(hi, lo, ((nib >> 1) & 0x04040404u) | 0x03020100u);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);

@@ -7,11 +7,13 @@
 // sum = sum of the 32 codes.
 //
 // Eight lanes own one block, four values each (one 16-byte load per lane), so
-// a wave quantizes eight blocks and the block reductions are three xor
-// shuffles.  A wave takes the same block of eight consecutive rows, and a
+// a wave quantizes eight blocks and the block reductions are three DPP lane
+// moves.  A wave takes the same block of eight consecutive rows, and a
 // workgroup four consecutive blocks of those rows: each wave's stores of the
 // row-major arrays below then fill whole 64- or 128-byte segments.  The kernel
-// streams X once: it is HBM-bound.
+// streams X once; at large sizes its vector instructions (about 240 per wave)
+// take as long as its memory traffic, so addresses are a wave-uniform base plus
+// a 32-bit lane offset and the fp6 digit codes are looked up four at a time.
 //
 // It also writes the fp6 section of the plane (the operands of the fp6 matrix-unit
 // product; layout in mq_internal.h): each code as q = 16 h + l with h = q >> 4 in [-8, 7]
@@ -35,28 +37,54 @@ __device__ __forceinline__ float product_f32(float a, float b) {
     return a * b;
 }
 
+// Reductions over the eight lanes of a block (a whole wave active): lane i with lanes i ^ 1
+// and i ^ 2 (DPP quad permutations), then with lane 7 - i of its eight (DPP half-row
+// mirror), which after the first two steps holds the other quad's value.  Max and integer
+// sums do not depend on the order.
+__device__ __forceinline__ int dpp_from(int v, int ctrl_sel) {
+    switch (ctrl_sel) {
+        case 0: return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+        case 1: return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+        default: return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    }
+}
+
+__device__ __forceinline__ float block_max8(float a) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+        a = fmaxf(a, __builtin_bit_cast(float, dpp_from(__builtin_bit_cast(int, a), i)));
+    return a;
+}
+
+__device__ __forceinline__ int block_sum8(int s) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) s += dpp_from(s, i);
+    return s;
+}
+
 __global__ __launch_bounds__(256) void quantize_act_kernel(const float4* __restrict__ X,
                                                            uint32_t* __restrict__ codes,
                                                            float* __restrict__ scales,
                                                            int32_t* __restrict__ sums,
                                                            uint32_t* __restrict__ f6, int64_t M, int64_t Mp,
                                                            int KB, int block_groups) {
-    // workgroup: rows 8 rg .. 8 rg + 7 (of Mp) x blocks 4 bg .. 4 bg + 3; wave w: block 4 bg + w
+    // workgroup: rows 8 rg .. 8 rg + 7 (of Mp) x blocks 4 bg .. 4 bg + 3; wave w: block 4 bg + w.
+    // Every address is a base uniform over the wave (64-bit, scalar) plus a 32-bit lane offset.
     const int64_t rg = blockIdx.x / block_groups;
     const int bg = int(blockIdx.x % block_groups);
     const int j = int(threadIdx.x & 7);
-    const int64_t m = 8 * rg + ((threadIdx.x >> 3) & 7);
-    const int kb = 4 * bg + int(threadIdx.x >> 6);
-    const bool in_k = kb < KB;
-    const bool live = in_k && m < M;   // rows M..Mp-1 only get the fp6 section's zeros
-    const int64_t blk = m * KB + kb;
-    const int64_t t = blk * 8 + j;     // this lane's quad of X and of the codes
-    const float4 v = live ? X[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int r = int((threadIdx.x >> 3) & 7);
+    const int kb = 4 * bg + __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+    const int64_t m0 = 8 * rg;
+    const int64_t m = m0 + r;
+    const bool in_k = kb < KB;        // uniform per wave
+    const bool live = in_k && m < M;  // rows M..Mp-1 only get the fp6 section's zeros
+    const int64_t blk0 = m0 * KB + kb;                       // block of the wave's first row
+    const uint32_t row_q = __umul24(uint32_t(r), uint32_t(KB) * 8u) + uint32_t(j);   // this lane's quad past it
+    const float4 v = live ? (X + blk0 * 8)[row_q] : make_float4(0.f, 0.f, 0.f, 0.f);
 
     float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    a = fmaxf(a, __shfl_xor(a, 1, 64));
-    a = fmaxf(a, __shfl_xor(a, 2, 64));
-    a = fmaxf(a, __shfl_xor(a, 4, 64));
+    a = block_max8(a);
     const float d = a / 127.0f;
 
     int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
@@ -66,54 +94,64 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float4* __restr
         q2 = static_cast<int>(fminf(fmaxf(rintf(v.z / d), -127.0f), 127.0f));
         q3 = static_cast<int>(fminf(fmaxf(rintf(v.w / d), -127.0f), 127.0f));
     }
-    int s = q0 + q1 + q2 + q3;
-    s += __shfl_xor(s, 1, 64);
-    s += __shfl_xor(s, 2, 64);
-    s += __shfl_xor(s, 4, 64);
+    const int s = block_sum8(q0 + q1 + q2 + q3);
 
+    const uint32_t w = (uint32_t(q0) & 0xFFu) | ((uint32_t(q1) & 0xFFu) << 8) | ((uint32_t(q2) & 0xFFu) << 16) |
+                       ((uint32_t(q3) & 0xFFu) << 24);   // the four codes as bytes
     if (live) {
-        codes[t] = (uint32_t(q0) & 0xFFu) | ((uint32_t(q1) & 0xFFu) << 8) |
-                   ((uint32_t(q2) & 0xFFu) << 16) | ((uint32_t(q3) & 0xFFu) << 24);
+        (codes + blk0 * 8)[row_q] = w;
         if (j == 0) {
-            scales[blk] = d;
-            sums[blk] = s;
+            const uint32_t row_b = __umul24(uint32_t(r), uint32_t(KB));
+            (scales + blk0)[row_b] = d;
+            (sums + blk0)[row_b] = s;
         }
     }
 
     // ---- the fp6 section (every lane of the wave takes part in the shuffles)
-    auto chunk = [](int a, int b, int c, int e, bool high) {
-        auto dig = [high](int q) { return high ? e2m3_half_code(q >> 4) : e2m3_half_code(q & 15); };
-        return dig(a) | (dig(b) << 6) | (dig(c) << 12) | (dig(e) << 18);
+    // the 6-bit codes of the four values' digits, value i in bits 6 i .. 6 i + 5 (from one
+    // code per byte); h = q >> 4 is the high nibble of q's byte read as signed, l its low one
+    auto chunk = [](uint32_t c) {
+        return (c & 0x3Fu) | ((c >> 2) & 0xFC0u) | ((c >> 4) & 0x3F000u) | ((c >> 6) & 0xFC0000u);
     };
-    const uint32_t ch = chunk(q0, q1, q2, q3, true), cl = chunk(q0, q1, q2, q3, false);
+    const uint32_t ch = chunk(e2m3_half_codes4<true>((w >> 4) & 0x0F0F0F0Fu));
+    const uint32_t cl = chunk(e2m3_half_codes4<false>(w & 0x0F0F0F0Fu));
     // dword k (lanes k = 0..5) of the 192-bit records: bits 32 k .. of lanes' 24-bit chunks
-    const int p = j / 3, r = j % 3;
-    const int src = 4 * p + r;
+    const int p = j / 3, rr = j % 3;
+    const int src = 4 * p + rr;
     const uint32_t h0 = __shfl(ch, src, 8), h1 = __shfl(ch, src + 1, 8);
     const uint32_t l0 = __shfl(cl, src, 8), l1 = __shfl(cl, src + 1, 8);
     if (in_k) {
         const int step = kb >> 1, u = kb & 1;
         uint32_t* slab = f6 + int64_t(step) * 32 * Mp;   // 128 Mp bytes per step
-        const uint32_t dh = (h0 >> (8 * r)) | (h1 << (24 - 8 * r));
-        const uint32_t dl = (l0 >> (8 * r)) | (l1 << (24 - 8 * r));
+        const uint32_t dh = (h0 >> (8 * rr)) | (h1 << (24 - 8 * rr));
+        const uint32_t dl = (l0 >> (8 * rr)) | (l1 << (24 - 8 * rr));
         const uint32_t hilo = bf16_hilo_bits(d);
         const uint32_t thilo = bf16_hilo_bits(product_f32(d, float(s)));
+        // Two dword stores per lane: lanes 0..3 the digits16 records (h, then l), lanes 4, 5
+        // the digits8 records, lane 6 the outer operand record and lane 7 the min operand
+        // record (its two dwords).  Offsets in dwords past the slab, 32-bit (Mp <= 2^20).
+        const uint32_t mp = uint32_t(Mp), mr = uint32_t(m0) + uint32_t(r);
         auto put = [&](int uu, bool zero) {
+            const uint32_t uw = uint32_t(uu);
+            uint32_t o1, o2, v1, v2;
             if (j < 4) {
-                slab[((2 * uu) * Mp + m) * 4 + j] = zero ? 0u : dh;          // digits16, h
-                slab[((2 * uu + 1) * Mp + m) * 4 + j] = zero ? 0u : dl;      // digits16, l
+                o1 = ((2 * uw) * mp + mr) * 4 + j;
+                o2 = o1 + 4 * mp;
+                v1 = dh;
+                v2 = dl;
             } else if (j < 6) {
-                slab[16 * Mp + ((2 * uu) * Mp + m) * 2 + (j - 4)] = zero ? 0u : dh;       // digits8, h
-                slab[16 * Mp + ((2 * uu + 1) * Mp + m) * 2 + (j - 4)] = zero ? 0u : dl;   // digits8, l
-            } else if (j == 6) {
-                uint32_t* o = slab + 24 * Mp + (uu * Mp + m) * 2;                // outer
-                o[0] = zero ? 0u : hilo;
-                o[1] = zero ? 0u : hilo;
+                o1 = 16 * mp + ((2 * uw) * mp + mr) * 2 + (j - 4);
+                o2 = o1 + 2 * mp;
+                v1 = dh;
+                v2 = dl;
             } else {
-                uint32_t* o = slab + 28 * Mp + (uu * Mp + m) * 2;                // min
-                o[0] = zero ? 0u : ((thilo & 0xFFFFu) | (thilo << 16));
-                o[1] = zero ? 0u : ((thilo >> 16) | (thilo & 0xFFFF0000u));
+                o1 = __umul24(j == 6 ? 24u : 28u, mp) + (uw * mp + mr) * 2;
+                o2 = o1 + 1;
+                v1 = j == 6 ? hilo : ((thilo & 0xFFFFu) | (thilo << 16));
+                v2 = j == 6 ? hilo : ((thilo >> 16) | (thilo & 0xFFFF0000u));
             }
+            slab[o1] = zero ? 0u : v1;
+            slab[o2] = zero ? 0u : v2;
         };
         put(u, false);
         if ((KB & 1) && kb == KB - 1) put(1, true);   // the step's second block does not exist

@@ -195,9 +195,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_kernel(const uint8_t* 
     if (tid < nquads) {   // uniform per wave: K is a multiple of 256
         const float4 v = xe;
         float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-        a = fmaxf(a, __shfl_xor(a, 1, 64));
-        a = fmaxf(a, __shfl_xor(a, 2, 64));
-        a = fmaxf(a, __shfl_xor(a, 4, 64));
+        a = lanes8_max(a);
         // amax = m * 2^E, m in [0.5, 1): scale by 2^(21 - E) puts the block in [2^20, 2^21)
         const int k = kFracBits - __builtin_amdgcn_frexp_expf(a);
         uint32_t d0, d1, d2;
@@ -206,9 +204,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_kernel(const uint8_t* 
         *reinterpret_cast<uint32_t*>(xp + K + 4 * tid) = d1;
         *reinterpret_cast<uint32_t*>(xp + 2 * K + 4 * tid) = d2;
         float sm = (v.x + v.y) + (v.z + v.w);
-        sm += __shfl_xor(sm, 1, 64);
-        sm += __shfl_xor(sm, 2, 64);
-        sm += __shfl_xor(sm, 4, 64);
+        sm = lanes8_sum(sm);
         if ((tid & 7) == 0) {
             sums[tid >> 3] = sm;
             ex[tid >> 3] = -k;
@@ -293,8 +289,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_kernel(const uint8_t* 
         s = ((4 * j < wl ? v.x : 0.f) + (4 * j + 1 < wl ? v.y : 0.f)) +
             ((4 * j + 2 < wl ? v.z : 0.f) + (4 * j + 3 < wl ? v.w : 0.f));
     }
-    s += __shfl_xor(s, 1, 64);
-    s += __shfl_xor(s, 2, 64);
+    s = lanes8_sum<2>(s);
     if (j == 0 && r < tiles * kTileRows) {
         const int row = (w0 + (r / kTileRows) * G) * kTileRows + r % kTileRows;
         if (row < N) y[row] = s;
@@ -398,9 +393,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_long_kernel(const uint
     auto compute = [&](const uint8_t* it, const float4 v) {
         // Stage this super-block's x: lane l holds values 4l .. 4l + 3, 8 lanes per 32-block.
         float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-        a = fmaxf(a, __shfl_xor(a, 1, 64));
-        a = fmaxf(a, __shfl_xor(a, 2, 64));
-        a = fmaxf(a, __shfl_xor(a, 4, 64));
+        a = lanes8_max(a);
         const int k = kFracBits - __builtin_amdgcn_frexp_expf(a);
         uint32_t d0, d1, d2;
         transpose3(digits3(v.x, k), digits3(v.y, k), digits3(v.z, k), digits3(v.w, k), d0, d1, d2);
@@ -408,9 +401,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_long_kernel(const uint
         *reinterpret_cast<uint32_t*>(my_xs + 256 + 4 * lane) = d1;
         *reinterpret_cast<uint32_t*>(my_xs + 512 + 4 * lane) = d2;
         float sm = (v.x + v.y) + (v.z + v.w);
-        sm += __shfl_xor(sm, 1, 64);
-        sm += __shfl_xor(sm, 2, 64);
-        sm += __shfl_xor(sm, 4, 64);
+        sm = lanes8_sum(sm);
         if ((lane & 7) == 0) {
             my_sum[lane >> 3] = sm;
             my_ex[lane >> 3] = -k;
@@ -472,8 +463,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_long_kernel(const uint
         const float4 v = *reinterpret_cast<const float4*>(part + rr * kWaves + 4 * j);
         sum = (v.x + v.y) + (v.z + v.w);
     }
-    sum += __shfl_xor(sum, 1, 64);
-    sum += __shfl_xor(sum, 2, 64);
+    sum = lanes8_sum<2>(sum);
     if (j == 0 && rr < rows) y[r0 + rr] = sum;
 }
 
@@ -717,9 +707,7 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(const uint8_t* __r
     if (tid < nquads) {   // uniform per wave: K is a multiple of 256
         const float4 v = xe;
         float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-        am = fmaxf(am, __shfl_xor(am, 1, 64));
-        am = fmaxf(am, __shfl_xor(am, 2, 64));
-        am = fmaxf(am, __shfl_xor(am, 4, 64));
+        am = lanes8_max(am);
         const int k = kFracBits - __builtin_amdgcn_frexp_expf(am);
         uint32_t d0, d1, d2;
         transpose3(digits3(v.x, k), digits3(v.y, k), digits3(v.z, k), digits3(v.w, k), d0, d1, d2);
@@ -727,8 +715,7 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(const uint8_t* __r
         *reinterpret_cast<uint32_t*>(xp + K + 4 * tid) = d1;
         *reinterpret_cast<uint32_t*>(xp + 2 * K + 4 * tid) = d2;
         float sm = (v.x + v.y) + (v.z + v.w);
-        sm += __shfl_xor(sm, 1, 64);
-        sm += __shfl_xor(sm, 2, 64);
+        sm = lanes8_sum<2>(sm);
         if ((tid & 3) == 0) sums[tid >> 2] = sm;
         if ((tid & 7) == 0) ex[tid >> 3] = -k;
     }
@@ -763,8 +750,7 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(const uint8_t* __r
         const float4 v = *reinterpret_cast<const float4*>(pt + r * kWaves + 4 * j);
         float s = ((4 * j < SB ? v.x : 0.f) + (4 * j + 1 < SB ? v.y : 0.f)) +
                   ((4 * j + 2 < SB ? v.z : 0.f) + (4 * j + 3 < SB ? v.w : 0.f));
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
+        s = lanes8_sum<2>(s);
         const int row = (w0 + k * G) * kTileRows + r;
         if (j == 0 && row < N) y[row] = s;
     };
@@ -1124,9 +1110,7 @@ __global__ __launch_bounds__(kThreads) void gemv_wide_kernel(const uint8_t* __re
     if (tid < nquads) {   // uniform per wave: K is a multiple of 256
         const float4 v = xe;
         float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-        am = fmaxf(am, __shfl_xor(am, 1, 64));
-        am = fmaxf(am, __shfl_xor(am, 2, 64));
-        am = fmaxf(am, __shfl_xor(am, 4, 64));
+        am = lanes8_max(am);
         const int k = kFracBits - __builtin_amdgcn_frexp_expf(am);
         uint32_t d0, d1, d2;
         transpose3(digits3(v.x, k), digits3(v.y, k), digits3(v.z, k), digits3(v.w, k), d0, d1, d2);
@@ -1134,8 +1118,7 @@ __global__ __launch_bounds__(kThreads) void gemv_wide_kernel(const uint8_t* __re
         *reinterpret_cast<uint32_t*>(xp + K + 4 * tid) = d1;
         *reinterpret_cast<uint32_t*>(xp + 2 * K + 4 * tid) = d2;
         float sm = (v.x + v.y) + (v.z + v.w);
-        sm += __shfl_xor(sm, 1, 64);
-        sm += __shfl_xor(sm, 2, 64);
+        sm = lanes8_sum<2>(sm);
         if ((tid & 3) == 0) sums[tid >> 2] = sm;
         if ((tid & 7) == 0) ex[tid >> 3] = -k;
     }
@@ -1185,8 +1168,7 @@ __global__ __launch_bounds__(kThreads) void gemv_wide_kernel(const uint8_t* __re
         s = ((4 * j < wl ? v.x : 0.f) + (4 * j + 1 < wl ? v.y : 0.f)) +
             ((4 * j + 2 < wl ? v.z : 0.f) + (4 * j + 3 < wl ? v.w : 0.f));
     }
-    s += __shfl_xor(s, 1, 64);
-    s += __shfl_xor(s, 2, 64);
+    s = lanes8_sum<2>(s);
     if (j == 0 && r < tiles * kTileRows) {
         const int row = (w0 + (r / kTileRows) * G) * kTileRows + r % kTileRows;
         if (row < N) y[row] = s;

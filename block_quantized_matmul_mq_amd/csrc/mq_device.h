@@ -101,6 +101,41 @@ __device__ __forceinline__ uint32_t e2m3_half_codes4(uint32_t nib) {
     return __builtin_amdgcn_perm(hi, lo, ((nib >> 1) & 0x04040404u) | 0x03020100u);
 }
 
+// Reductions over aligned groups of eight lanes (every lane of the wave active): lane i
+// with lanes i ^ 1 and i ^ 2 (DPP quad permutations), then with lane 7 - i of its eight
+// (DPP half-row mirror), which after the first two steps holds the other quad's value.
+// The result equals the xor-butterfly's over lanes i ^ 1, i ^ 2, i ^ 4 bit for bit, also
+// for f32 sums: after each step the lanes of a pair or quad hold the same value, and
+// each addition takes the same two operands (in either order).
+template <int STEP>
+__device__ __forceinline__ int dpp8_partner(int v) {
+    if constexpr (STEP == 0) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    else if constexpr (STEP == 1) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    else return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+}
+
+template <int STEP>
+__device__ __forceinline__ float dpp8_partner(float v) {
+    return __builtin_bit_cast(float, dpp8_partner<STEP>(__builtin_bit_cast(int, v)));
+}
+
+// over groups of four lanes (the first two steps) or eight (all three)
+template <int STEPS = 3>
+__device__ __forceinline__ float lanes8_max(float a) {
+    a = fmaxf(a, dpp8_partner<0>(a));
+    a = fmaxf(a, dpp8_partner<1>(a));
+    if constexpr (STEPS == 3) a = fmaxf(a, dpp8_partner<2>(a));
+    return a;
+}
+
+template <int STEPS = 3, typename T>
+__device__ __forceinline__ T lanes8_sum(T s) {
+    s += dpp8_partner<0>(s);
+    s += dpp8_partner<1>(s);
+    if constexpr (STEPS == 3) s += dpp8_partner<2>(s);
+    return s;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);

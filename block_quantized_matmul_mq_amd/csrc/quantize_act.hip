@@ -37,31 +37,6 @@ __device__ __forceinline__ float product_f32(float a, float b) {
     return a * b;
 }
 
-// Reductions over the eight lanes of a block (a whole wave active): lane i with lanes i ^ 1
-// and i ^ 2 (DPP quad permutations), then with lane 7 - i of its eight (DPP half-row
-// mirror), which after the first two steps holds the other quad's value.  Max and integer
-// sums do not depend on the order.
-__device__ __forceinline__ int dpp_from(int v, int ctrl_sel) {
-    switch (ctrl_sel) {
-        case 0: return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
-        case 1: return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
-        default: return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);  // row_half_mirror
-    }
-}
-
-__device__ __forceinline__ float block_max8(float a) {
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-        a = fmaxf(a, __builtin_bit_cast(float, dpp_from(__builtin_bit_cast(int, a), i)));
-    return a;
-}
-
-__device__ __forceinline__ int block_sum8(int s) {
-#pragma unroll
-    for (int i = 0; i < 3; ++i) s += dpp_from(s, i);
-    return s;
-}
-
 __global__ __launch_bounds__(256) void quantize_act_kernel(const float4* __restrict__ X,
                                                            uint32_t* __restrict__ codes,
                                                            float* __restrict__ scales,
@@ -84,7 +59,7 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float4* __restr
     const float4 v = live ? (X + blk0 * 8)[row_q] : make_float4(0.f, 0.f, 0.f, 0.f);
 
     float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    a = block_max8(a);
+    a = lanes8_max(a);
     const float d = a / 127.0f;
 
     int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
@@ -94,7 +69,7 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float4* __restr
         q2 = static_cast<int>(fminf(fmaxf(rintf(v.z / d), -127.0f), 127.0f));
         q3 = static_cast<int>(fminf(fmaxf(rintf(v.w / d), -127.0f), 127.0f));
     }
-    const int s = block_sum8(q0 + q1 + q2 + q3);
+    const int s = lanes8_sum(q0 + q1 + q2 + q3);
 
     const uint32_t w = (uint32_t(q0) & 0xFFu) | ((uint32_t(q1) & 0xFFu) << 8) | ((uint32_t(q2) & 0xFFu) << 16) |
                        ((uint32_t(q3) & 0xFFu) << 24);   // the four codes as bytes

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float4* __restr
         }
     }
 
-    // ---- the fp6 section (every lane of the wave takes part in the shuffles)
+    // ---- the fp6 section (every lane of the wave takes part in the lane moves)
     // the 6-bit codes of the four values' digits, value i in bits 6 i .. 6 i + 5 (from one
     // code per byte); h = q >> 4 is the high nibble of q's byte read as signed, l its low one
     auto chunk = [](uint32_t c) {
@@ -90,11 +90,18 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float4* __restr
     };
     const uint32_t ch = chunk(e2m3_half_codes4<true>((w >> 4) & 0x0F0F0F0Fu));
     const uint32_t cl = chunk(e2m3_half_codes4<false>(w & 0x0F0F0F0Fu));
-    // dword k (lanes k = 0..5) of the 192-bit records: bits 32 k .. of lanes' 24-bit chunks
-    const int p = j / 3, rr = j % 3;
-    const int src = 4 * p + rr;
-    const uint32_t h0 = __shfl(ch, src, 8), h1 = __shfl(ch, src + 1, 8);
-    const uint32_t l0 = __shfl(cl, src, 8), l1 = __shfl(cl, src + 1, 8);
+    // dword k (lanes k = 0..5) of the 192-bit records: bits 32 k .. of lanes' 24-bit chunks,
+    // from the chunks of lanes 4 (k / 3) + k % 3 and the next one (k or k + 1, then k + 1
+    // or k + 2: the same or the next two lanes, all in the lane's row of 16; DPP row
+    // shifts, whose lanes that would read past the row are among those not stored)
+    const int rr = j % 3;
+    const bool second = j >= 3;
+    const uint32_t ch1 = uint32_t(__builtin_amdgcn_mov_dpp(int(ch), 0x101, 0xF, 0xF, false));   // row_shl:1
+    const uint32_t ch2 = uint32_t(__builtin_amdgcn_mov_dpp(int(ch), 0x102, 0xF, 0xF, false));   // row_shl:2
+    const uint32_t cl1 = uint32_t(__builtin_amdgcn_mov_dpp(int(cl), 0x101, 0xF, 0xF, false));
+    const uint32_t cl2 = uint32_t(__builtin_amdgcn_mov_dpp(int(cl), 0x102, 0xF, 0xF, false));
+    const uint32_t h0 = second ? ch1 : ch, h1 = second ? ch2 : ch1;
+    const uint32_t l0 = second ? cl1 : cl, l1 = second ? cl2 : cl1;
     if (in_k) {
         const int step = kb >> 1, u = kb & 1;
         uint32_t* slab = f6 + int64_t(step) * 32 * Mp;   // 128 Mp bytes per step

@@ -320,9 +320,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
     // Stage x: 8 lanes per 32-block, 4 values (one float4) per lane.
     auto stage = [&](int i, const float4 v) {
         float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-        a = fmaxf(a, __shfl_xor(a, 1, 64));
-        a = fmaxf(a, __shfl_xor(a, 2, 64));
-        a = fmaxf(a, __shfl_xor(a, 4, 64));
+        a = lanes8_max(a);   // (DPP within groups of 8 lanes, all active or all idle)
         // amax = m * 2^E, m in [0.5, 1): scale by 2^(21 - E) puts the block in [2^20, 2^21)
         const int k = kFracBits - __builtin_amdgcn_frexp_expf(a);
         uint32_t d0, d1, d2;
@@ -345,8 +343,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
         *reinterpret_cast<uint32_t*>(p1 + off) = d1;
         *reinterpret_cast<uint32_t*>(p2 + off) = d2;
         float sm = (v.x + v.y) + (v.z + v.w);
-        sm += __shfl_xor(sm, 1, 64);
-        sm += __shfl_xor(sm, 2, 64);
+        sm = lanes8_sum<2>(sm);
         if constexpr (QT == kQ6_K) {
             if ((i & 3) == 0) {            // one 16-run = chunk kc of unit uu
                 sums[4 * uu + kc] = sm;
@@ -354,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
             }
         } else {
             if constexpr (QT != kQ8_0) {
-                sm += __shfl_xor(sm, 4, 64);
+                sm += dpp8_partner<2>(sm);   // the other four lanes of the 32-block
                 if ((i & 7) == 0) sums[i >> 3] = sm;
             }
             if ((i & 7) == 0) ex[i >> 3] = -k;
